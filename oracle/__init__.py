@@ -1,0 +1,261 @@
+"""numpy front end of the plain CPU oracle (oracle/fp4q_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it; the product library never does.
+It shares no code with the HIP path.  bf16 tensors travel as numpy ``uint16``
+bit patterns, fp32 as ``float32``; every result the C side computes in double
+is returned as ``float64`` and rounded to an output dtype only by
+:func:`round_f32` / :func:`round_bf16`.
+"""
+import ctypes as _ct
+import os as _os
+
+import numpy as _np
+
+from . import build as _build
+
+F32, BF16 = 0, 1
+ROW, COL = 0, 1
+RNE, SR = 0, 1
+STE, DGE = 0, 1
+
+_lib = None
+
+
+def lib():
+    """Load oracle/liboracle.so, compiling it first only if it is missing."""
+    global _lib
+    if _lib is None:
+        if not _os.path.exists(_build.LIB):
+            _build.build()
+        L = _ct.CDLL(_build.LIB)
+        P, I64, I32, U64, D = _ct.c_void_p, _ct.c_int64, _ct.c_int, _ct.c_uint64, _ct.c_double
+        sig = {
+            "orc_e2m1_value": (D, [I32]),
+            "orc_e8m0_byte": (I32, [_ct.c_uint32]),
+            "orc_rne_code": (I32, [D]),
+            "orc_sr_code": (I32, [D, _ct.c_uint32]),
+            "orc_philox4x32": (None, [P, P, I32, P]),
+            "orc_sr_bits": (_ct.c_uint32, [U64, U64]),
+            "orc_quantize": (I32, [P, I32, I64, I64, I64, I32, I32, I32, U64, U64, P, P]),
+            "orc_dequantize": (None, [P, P, I64, I64, I32, P]),
+            "orc_round_f32": (None, [P, P, I64]),
+            "orc_round_bf16": (None, [P, P, I64]),
+            "orc_bf16_from_double": (_ct.c_uint16, [D]),
+            "orc_dge_f": (D, [D, D, D]),
+            "orc_dge_fprime": (D, [D, D, D, D]),
+            "orc_grad_estimate": (I32, [I32, P, I32, P, I32, I64, I64, I32, I32, D, D, P, P]),
+            "orc_gemm": (None, [I64, I64, I64, P, P, P, P, I32, P, P]),
+            "orc_gemm_entries": (None, [I64, P, P, P, P, I32, I64, P, P, P, P]),
+            "orc_gemm_intblock": (None, [I64, I64, I64, P, P, P, P, I32, P]),
+            "orc_hcp_residual_entries": (None, [I64, I64, P, P, P, P, P, P, P, I32, I64, P, P,
+                                                P, P]),
+            "orc_e8m0_bytes": (None, [P, I64, P]),
+            "orc_rne_codes": (None, [P, I64, P]),
+            "orc_sr_codes": (None, [P, P, I64, P]),
+            "orc_sr_bits_range": (None, [U64, U64, I64, P]),
+            "orc_dge_f_many": (None, [P, P, I64, D, P]),
+            "orc_dge_fprime_many": (None, [P, P, I64, D, D, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(_ct.c_void_p)
+
+
+def _c(a, dtype):
+    return _np.ascontiguousarray(a, dtype=dtype)
+
+
+def _dtype_of(x):
+    if x.dtype == _np.uint16:
+        return BF16
+    if x.dtype == _np.float32:
+        return F32
+    raise TypeError("oracle takes float32 arrays or bf16 as uint16 bit patterns")
+
+
+# --- element level ---------------------------------------------------------
+
+def e2m1_value(code):
+    return lib().orc_e2m1_value(int(code))
+
+
+def e8m0_byte(amax_bits):
+    return lib().orc_e8m0_byte(int(amax_bits) & 0x7FFFFFFF)
+
+
+def e8m0_bytes(bits):
+    bits = _c(bits, _np.uint32)
+    out = _np.empty(bits.shape, _np.uint8)
+    lib().orc_e8m0_bytes(_p(bits), bits.size, _p(out))
+    return out
+
+
+def rne_codes(y):
+    y = _c(y, _np.float64)
+    out = _np.empty(y.shape, _np.uint8)
+    lib().orc_rne_codes(_p(y), y.size, _p(out))
+    return out
+
+
+def sr_codes(y, u16):
+    y = _c(y, _np.float64)
+    u = _c(u16, _np.uint32)
+    out = _np.empty(y.shape, _np.uint8)
+    lib().orc_sr_codes(_p(y), _p(u), y.size, _p(out))
+    return out
+
+
+def philox4x32(ctr, key, rounds=10):
+    c = _c(ctr, _np.uint32)
+    k = _c(key, _np.uint32)
+    out = _np.empty(4, _np.uint32)
+    lib().orc_philox4x32(_p(c), _p(k), int(rounds), _p(out))
+    return out
+
+
+def sr_bits(seed, pos0, n):
+    out = _np.empty(int(n), _np.uint32)
+    lib().orc_sr_bits_range(int(seed), int(pos0), int(n), _p(out))
+    return out
+
+
+def dge_f(t, delta, k):
+    t = _c(t, _np.float64)
+    d = _c(_np.broadcast_to(delta, t.shape), _np.float64)
+    out = _np.empty(t.shape, _np.float64)
+    lib().orc_dge_f_many(_p(t), _p(d), t.size, float(k), _p(out))
+    return out
+
+
+def dge_fprime(t, delta, k, clamp_max):
+    t = _c(t, _np.float64)
+    d = _c(_np.broadcast_to(delta, t.shape), _np.float64)
+    out = _np.empty(t.shape, _np.float64)
+    lib().orc_dge_fprime_many(_p(t), _p(d), t.size, float(k), float(clamp_max), _p(out))
+    return out
+
+
+# --- tensor level ----------------------------------------------------------
+
+def quantize(x, block, axis=ROW, round=RNE, seed=0, rng_offset=0):
+    """x: [rows, cols] float32 or bf16-as-uint16.  Returns (codes, scales):
+    ROW -> [rows, cols/2], [rows, cols/block]; COL -> [cols, rows/2], [cols, rows/block]."""
+    x = _np.ascontiguousarray(x)
+    dt = _dtype_of(x)
+    rows, cols = x.shape
+    if axis == ROW:
+        codes = _np.empty((rows, cols // 2), _np.uint8)
+        scales = _np.empty((rows, cols // block), _np.uint8)
+    else:
+        codes = _np.empty((cols, rows // 2), _np.uint8)
+        scales = _np.empty((cols, rows // block), _np.uint8)
+    rc = lib().orc_quantize(_p(x), dt, rows, cols, cols, int(block), int(axis), int(round),
+                            int(seed), int(rng_offset), _p(codes), _p(scales))
+    if rc != 0:
+        raise ValueError("oracle quantize: unsupported shape/block")
+    return codes, scales
+
+
+def dequantize(codes, scales, block):
+    """codes [rows, k/2], scales [rows, k/block] -> float64 [rows, k] (exact)."""
+    codes = _c(codes, _np.uint8)
+    scales = _c(scales, _np.uint8)
+    rows, half = codes.shape
+    k = 2 * half
+    out = _np.empty((rows, k), _np.float64)
+    lib().orc_dequantize(_p(codes), _p(scales), rows, k, int(block), _p(out))
+    return out
+
+
+def round_f32(v):
+    v = _c(v, _np.float64)
+    out = _np.empty(v.shape, _np.float32)
+    lib().orc_round_f32(_p(v), _p(out), v.size)
+    return out
+
+
+def round_bf16(v):
+    """Round-to-nearest-even of float64 straight to bf16; returns uint16 bits."""
+    v = _c(v, _np.float64)
+    out = _np.empty(v.shape, _np.uint16)
+    lib().orc_round_bf16(_p(v), _p(out), v.size)
+    return out
+
+
+def bf16_to_f64(bits):
+    """Exact widening of bf16 bit patterns to float64."""
+    b = _c(bits, _np.uint16).astype(_np.uint32) << 16
+    return b.view(_np.float32).astype(_np.float64)
+
+
+def grad_estimate(mode, x, g, block=32, axis=ROW, k=5.0, clamp_max=3.0):
+    """Returns (d, out) in float64: the derivative factor and g*d, both exact
+    before the final rounding to an output dtype."""
+    g = _np.ascontiguousarray(g)
+    rows, cols = g.shape
+    if x is None:
+        x = _np.zeros((1, 1), _np.float32)
+    x = _np.ascontiguousarray(x)
+    d = _np.empty((rows, cols), _np.float64)
+    out = _np.empty((rows, cols), _np.float64)
+    rc = lib().orc_grad_estimate(int(mode), _p(x), _dtype_of(x), _p(g), _dtype_of(g), rows,
+                                 cols, int(block), int(axis), float(k), float(clamp_max),
+                                 _p(d), _p(out))
+    if rc != 0:
+        raise ValueError("oracle grad_estimate: unsupported shape/block")
+    return d, out
+
+
+def gemm(a_codes, a_scales, b_codes, b_scales, block=32):
+    """C = deq(A) deq(B)^T in double, plus S = sum |products|."""
+    ac, as_, bc, bs = (_c(t, _np.uint8) for t in (a_codes, a_scales, b_codes, b_scales))
+    M, N, K = ac.shape[0], bc.shape[0], 2 * ac.shape[1]
+    C = _np.empty((M, N), _np.float64)
+    S = _np.empty((M, N), _np.float64)
+    lib().orc_gemm(M, N, K, _p(ac), _p(as_), _p(bc), _p(bs), int(block), _p(C), _p(S))
+    return C, S
+
+
+def gemm_intblock(a_codes, a_scales, b_codes, b_scales, block=32):
+    ac, as_, bc, bs = (_c(t, _np.uint8) for t in (a_codes, a_scales, b_codes, b_scales))
+    M, N, K = ac.shape[0], bc.shape[0], 2 * ac.shape[1]
+    C = _np.empty((M, N), _np.float64)
+    lib().orc_gemm_intblock(M, N, K, _p(ac), _p(as_), _p(bc), _p(bs), int(block), _p(C))
+    return C
+
+
+def gemm_entries(a_codes, a_scales, b_codes, b_scales, ii, jj, block=32):
+    ac, as_, bc, bs = (_c(t, _np.uint8) for t in (a_codes, a_scales, b_codes, b_scales))
+    K = 2 * ac.shape[1]
+    ii = _c(ii, _np.int64)
+    jj = _c(jj, _np.int64)
+    C = _np.empty(ii.shape, _np.float64)
+    S = _np.empty(ii.shape, _np.float64)
+    lib().orc_gemm_entries(K, _p(ac), _p(as_), _p(bc), _p(bs), int(block), ii.size, _p(ii),
+                           _p(jj), _p(C), _p(S))
+    return C, S
+
+
+def hcp_residual_entries(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, ii, jj):
+    """Residual sum_{c in H} X[i,c]W[c,j] - Xq[i,c]Wq[c,j] at sampled (ii, jj).
+    x: bf16 bits [M, K]; w: bf16 bits [K, N]; wq K-major [N, K/2]."""
+    x = _c(x, _np.uint16)
+    w = _c(w, _np.uint16)
+    K, N = w.shape
+    xqc, xqs, wqc, wqs = (_c(t, _np.uint8) for t in (xq_codes, xq_scales, wq_codes, wq_scales))
+    hot = _c(hot_idx, _np.int32)
+    ii = _c(ii, _np.int64)
+    jj = _c(jj, _np.int64)
+    R = _np.empty(ii.shape, _np.float64)
+    S = _np.empty(ii.shape, _np.float64)
+    lib().orc_hcp_residual_entries(N, K, _p(x), _p(xqc), _p(xqs), _p(w), _p(wqc), _p(wqs),
+                                   _p(hot), hot.size, ii.size, _p(ii), _p(jj), _p(R), _p(S))
+    return R, S

@@ -1,0 +1,160 @@
+"""Pins of the oracle's FP4 GEMM and hot-channel residual: two formulations
+(double sums of dequantised values / exact integer block sums), a library
+matmul of the dequantised operands, identity-coded operands, exhaustive 1x1x32
+code pairs across scale bytes, the error-bound quantity S, and the residual's
+special cases (empty hot set, all channels hot, operands already on the grid)."""
+import numpy as np
+import pytest
+
+from mxfp4_block_scaled_fp4q_amd import inputs
+
+
+def _e2m1(code):
+    s = -1.0 if code & 8 else 1.0
+    e = (code >> 1) & 3
+    m = code & 1
+    return s * (0.5 * m if e == 0 else 2.0 ** (e - 1) * (1 + 0.5 * m))
+
+
+def _qpair(orc, shape_a, shape_b, seed):
+    a = inputs.with_outliers(inputs.normal(shape_a, seed), seed + 1, 20, 50.0)
+    b = inputs.with_outliers(inputs.normal(shape_b, seed + 2), seed + 3, 20, 50.0)
+    return orc.quantize(a, 32), orc.quantize(b, 32)
+
+
+def test_gemm_formulations_and_matmul(orc):
+    (ac, as_), (bc, bs) = _qpair(orc, (48, 128), (40, 128), 21)
+    C, S = orc.gemm(ac, as_, bc, bs)
+    Ci = orc.gemm_intblock(ac, as_, bc, bs)
+    assert np.all(np.abs(C - Ci) <= 1e-13 * S)
+    A = orc.dequantize(ac, as_, 32)
+    B = orc.dequantize(bc, bs, 32)
+    Cm = A @ B.T
+    assert np.all(np.abs(C - Cm) <= 1e-13 * S)
+    assert np.allclose(S, np.abs(A) @ np.abs(B).T, rtol=1e-13, atol=0)
+    assert np.all(S >= np.abs(C))
+    # entry-wise sampler agrees with the full product
+    ii = np.array([0, 47, 13, 5])
+    jj = np.array([0, 39, 7, 33])
+    Ce, Se = orc.gemm_entries(ac, as_, bc, bs, ii, jj)
+    assert np.array_equal(Ce, C[ii, jj]) and np.array_equal(Se, S[ii, jj])
+
+
+def test_gemm_identity_coded(orc):
+    """B codes 1.0 on the diagonal (byte 127): C = deq(A) exactly."""
+    (ac, as_), _ = _qpair(orc, (32, 64), (1, 64), 31)
+    K = 64
+    bc = np.zeros((K, K // 2), np.uint8)
+    for j in range(K):
+        bc[j, j // 2] = (2 << 4) if j & 1 else 2
+    bs = np.full((K, K // 32), 127, np.uint8)
+    C, _ = orc.gemm(ac, as_, bc, bs)
+    assert np.array_equal(C, orc.dequantize(ac, as_, 32))
+
+
+def test_gemm_zero_and_single_block(orc):
+    ac = np.zeros((4, 64), np.uint8)
+    as_ = np.full((4, 4), 127, np.uint8)
+    bc = np.zeros((3, 64), np.uint8)
+    bs = np.full((3, 4), 100, np.uint8)
+    C, S = orc.gemm(ac, as_, bc, bs)
+    assert np.all(C == 0) and np.all(S == 0)
+    ac[1, 16:32] = 0x77  # block 1 of row 1: all 6.0
+    bc[2, 16:32] = 0xAA  # block 1 of row 2: all -1.0
+    as_[1, 1] = 130
+    bs[2, 1] = 120
+    C, _ = orc.gemm(ac, as_, bc, bs)
+    want = 32 * 6.0 * -1.0 * 2.0 ** (130 - 127) * 2.0 ** (120 - 127)
+    assert C[1, 2] == want
+    C[1, 2] = 0
+    assert np.all(C == 0)
+
+
+def test_gemm_1x1x32_exhaustive_code_pairs(orc):
+    """Every pair of codes, in every lane position, across a sweep of scale
+    bytes: C = 32 * v(ca) v(cb) 2^(ea + eb - 254) for a block of equal codes,
+    and lane-wise for a mixed block."""
+    for ea, eb in [(127, 127), (0, 254), (1, 1), (200, 60), (127, 0), (254, 254)]:
+        for ca in range(16):
+            ac = np.full((1, 16), ca | (ca << 4), np.uint8)
+            as_ = np.array([[ea]], np.uint8)
+            bcs = np.array([[cb | (cb << 4)] * 16 for cb in range(16)], np.uint8)
+            bss = np.full((16, 1), eb, np.uint8)
+            C, _ = orc.gemm(ac, as_, bcs, bss)
+            Ci = orc.gemm_intblock(ac, as_, bcs, bss)
+            want = np.array([32 * _e2m1(ca) * _e2m1(cb) * 2.0 ** (ea + eb - 254)
+                             for cb in range(16)])
+            assert np.array_equal(C[0], want) and np.array_equal(Ci[0], want)
+    rng = np.random.default_rng(2)
+    a = rng.integers(0, 16, 32)
+    b = rng.integers(0, 16, 32)
+    ac = (a[0::2] | (a[1::2] << 4)).astype(np.uint8)[None]
+    bc = (b[0::2] | (b[1::2] << 4)).astype(np.uint8)[None]
+    C, _ = orc.gemm(ac, np.array([[127]], np.uint8), bc, np.array([[127]], np.uint8))
+    assert C[0, 0] == sum(_e2m1(int(p)) * _e2m1(int(q)) for p, q in zip(a, b))
+
+
+def test_gemm_nan_scale(orc):
+    ac = np.full((1, 32), 0x22, np.uint8)
+    as_ = np.array([[0xFF, 127]], np.uint8)
+    bc = np.full((1, 32), 0x22, np.uint8)
+    bs = np.array([[127, 127]], np.uint8)
+    assert np.isnan(orc.gemm(ac, as_, bc, bs)[0][0, 0])
+    assert np.isnan(orc.gemm_intblock(ac, as_, bc, bs)[0, 0])
+
+
+def _hcp_case(orc, M, K, N, seed):
+    x = inputs.to_bf16_bits(inputs.normal((M, K), seed))
+    w = inputs.to_bf16_bits(inputs.normal((K, N), seed + 1, 0.02))
+    xqc, xqs = orc.quantize(x, 32)
+    wqc, wqs = orc.quantize(w, 32, axis=orc.COL)
+    return x, w, xqc, xqs, wqc, wqs
+
+
+def test_hcp_empty_and_full(orc):
+    M, K, N = 16, 64, 24
+    x, w, xqc, xqs, wqc, wqs = _hcp_case(orc, M, K, N, 41)
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ii, jj = ii.ravel(), jj.ravel()
+    R, S = orc.hcp_residual_entries(x, xqc, xqs, w, wqc, wqs, np.zeros(0, np.int32), ii, jj)
+    assert np.all(R == 0) and np.all(S == 0)
+    # every channel hot: base + residual = the plain product of the bf16 inputs
+    C, Sb = orc.gemm(xqc, xqs, wqc, wqs)
+    R, S = orc.hcp_residual_entries(x, xqc, xqs, w, wqc, wqs, np.arange(K, dtype=np.int32),
+                                    ii, jj)
+    Y = C.ravel() + R
+    Xd = orc.bf16_to_f64(x)
+    Wd = orc.bf16_to_f64(w)
+    want = (Xd @ Wd).ravel()
+    assert np.all(np.abs(Y - want) <= 1e-12 * (Sb.ravel() + S))
+
+
+def test_hcp_on_grid_is_zero_and_linear(orc):
+    M, K, N = 8, 64, 16
+    # X and W whose hot columns/rows are already FP4 values times the block
+    # scale: quantisation is exact there, so the residual vanishes
+    rng = np.random.default_rng(9)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6.0])
+    xf = (grid[rng.integers(0, 8, (M, K))] * rng.choice([-1, 1], (M, K))).astype(np.float32)
+    xf[:, 0] = 4.0
+    xf[:, 32] = 6.0
+    wf = (grid[rng.integers(0, 8, (K, N))] * 0.25).astype(np.float32)
+    wf[0, :] = 1.0
+    wf[32, :] = 1.5
+    x = inputs.to_bf16_bits(xf)
+    w = inputs.to_bf16_bits(wf)
+    xqc, xqs = orc.quantize(x, 32)
+    wqc, wqs = orc.quantize(w, 32, axis=orc.COL)
+    hot = np.array([1, 5, 33, 63], np.int32)
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    R, _ = orc.hcp_residual_entries(x, xqc, xqs, w, wqc, wqs, hot, ii.ravel(), jj.ravel())
+    assert np.all(R == 0)
+    # residual is additive over disjoint hot sets
+    x, w, xqc, xqs, wqc, wqs = _hcp_case(orc, M, K, N, 51)
+    h1 = np.array([2, 9, 40], np.int32)
+    h2 = np.array([11, 50], np.int32)
+    Ra, _ = orc.hcp_residual_entries(x, xqc, xqs, w, wqc, wqs, h1, ii.ravel(), jj.ravel())
+    Rb, _ = orc.hcp_residual_entries(x, xqc, xqs, w, wqc, wqs, h2, ii.ravel(), jj.ravel())
+    Rab, S = orc.hcp_residual_entries(x, xqc, xqs, w, wqc, wqs, np.concatenate([h1, h2]),
+                                      ii.ravel(), jj.ravel())
+    assert np.all(np.abs(Ra + Rb - Rab) <= 1e-14 * S)

@@ -1,0 +1,143 @@
+"""Pins of the oracle's stochastic rounding and its counter-based RNG:
+published Philox known answers, exact round-up counts over every 16-bit
+random value, outcomes restricted to the two neighbours, unbiasedness of the
+mean over seeds, and uniformity of the random lanes."""
+import os
+
+import numpy as np
+import pytest
+
+from mxfp4_block_scaled_fp4q_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def test_philox_known_answers(orc):
+    n = 0
+    for line in open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        f = line.split()
+        rounds = int(f[0])
+        w = [int(t, 16) for t in f[1:]]
+        out = orc.philox4x32(w[0:4], w[4:6], rounds)
+        assert [int(v) for v in out] == w[6:10]
+        n += 1
+    assert n == 3
+
+
+def test_sr_bits_lane_mapping(orc):
+    seed = 0x0123456789ABCDEF
+    for pos0 in (0, 8, 8 * 12345, (1 << 35) + 16):
+        n = pos0 >> 3
+        out = orc.philox4x32([n & 0xFFFFFFFF, n >> 32, 0, 0],
+                             [seed & 0xFFFFFFFF, seed >> 32], 10)
+        bits = orc.sr_bits(seed, pos0, 8)
+        want = [(int(out[L >> 1]) >> (16 * (L & 1))) & 0xFFFF for L in range(8)]
+        assert [int(b) for b in bits] == want
+
+
+def _lo_hi(m):
+    lo = GRID[np.searchsorted(GRID, m, side="right") - 1]
+    hi = GRID[np.minimum(np.searchsorted(GRID, m, side="right"), 7)]
+    return lo, hi
+
+
+def test_sr_exact_roundup_counts(orc):
+    """Inject every u in [0, 2^16): the number of round-ups is ceil(frac*2^16)."""
+    rng = np.random.default_rng(5)
+    ys = np.concatenate([rng.uniform(0, 6, 40), GRID[:-1] + 2.0 ** -20, [0.3, 1.9999999, 5.99],
+                         [2.0 ** -30, 2.0 ** -140]])
+    u = np.arange(65536, dtype=np.uint32)
+    for y in ys:
+        y32 = float(np.float32(y))
+        lo, hi = _lo_hi(y32)
+        frac = (y32 - lo) / (hi - lo)
+        codes = orc.sr_codes(np.full(65536, y32), u)
+        mags = GRID[codes & 7]
+        assert set(np.unique(mags)) <= {lo, hi}
+        ups = int(np.sum(mags == hi))
+        assert ups == int(np.ceil(frac * 65536)), (y32, ups, frac)
+        # the round-ups are exactly the smallest u values
+        assert np.all(mags[:ups] == hi) and np.all(mags[ups:] == lo)
+
+
+def test_sr_grid_points_fixed_and_saturation(orc):
+    u = np.arange(0, 65536, 97, dtype=np.uint32)
+    for g in GRID:
+        for s in (1.0, -1.0):
+            codes = orc.sr_codes(np.full(u.size, s * g), u)
+            assert np.all(GRID[codes & 7] == g)
+            assert np.all((codes >> 3) == (1 if np.signbit(s * g) else 0))
+    for y in (6.0, 6.5, 7.99):
+        codes = orc.sr_codes(np.full(u.size, y), u)
+        assert np.all(codes == 7)
+
+
+def test_sr_mean_over_seeds_converges(orc):
+    """mean over N seeds of deq(SR(x)) is within 5*delta*s/(2 sqrt N) +
+    delta*s*2^-16 of x for every unsaturated element."""
+    x = inputs.normal((2, 32), 77)
+    x[0, 0] = 3.7  # anchor -> e = -1 for row 0
+    N = 4000
+    acc = np.zeros(x.shape)
+    for seed in range(N):
+        c, s = orc.quantize(x, 32, round=orc.SR, seed=seed + 1)
+        acc += orc.dequantize(c, s, 32)
+    mean = acc / N
+    _, s = orc.quantize(x, 32)
+    scale = np.exp2(s.astype(np.float64) - 127).repeat(32, axis=1)
+    y = np.abs(x) / scale
+    ok = y <= 6
+    lo, hi = _lo_hi(np.minimum(y, 6))
+    delta = (hi - lo) * scale
+    delta[delta == 0] = 2 * scale[delta == 0]
+    bound = 5 * delta / (2 * np.sqrt(N)) + delta * 2.0 ** -16
+    err = np.abs(mean - x)
+    assert np.all(err[ok] <= bound[ok]), np.max(err[ok] / bound[ok])
+
+
+def test_sr_mean_over_counters_unbiased_exactly_representable(orc):
+    """Elements whose frac is a multiple of 2^-16 are rounded up exactly
+    frac*2^16 times over 2^16 independent draws in expectation; check the
+    mean over 2^16 rows of the same values to 6 sigma."""
+    vals = np.array([4.0, 0.3125, 1.125, 2.25, -3.75, 5.5, 0.0, -0.1875] * 4, np.float32)
+    R = 1 << 14
+    x = np.tile(vals, (R, 1))
+    c, s = orc.quantize(x, 32, round=orc.SR, seed=99)
+    d = orc.dequantize(c, s, 32)
+    mean = d.mean(axis=0)
+    lo, hi = _lo_hi(np.abs(vals.astype(np.float64)))
+    p = (np.abs(vals) - lo) / np.where(hi > lo, hi - lo, 1)
+    sd = (hi - lo) * np.sqrt(p * (1 - p) / R)
+    assert np.all(np.abs(mean - vals) <= 6 * sd + 1e-12)
+
+
+def test_sr_lane_uniformity(orc):
+    """chi-square of 2^20 16-bit lanes over 256 bins, and no correlation
+    between adjacent counters."""
+    bits = orc.sr_bits(1234, 0, 1 << 20).astype(np.int64)
+    hist = np.bincount(bits >> 8, minlength=256)
+    exp = bits.size / 256
+    chi2 = float(np.sum((hist - exp) ** 2 / exp))
+    # 255 dof: mean 255, sd ~22.6; 6 sigma
+    assert 255 - 136 < chi2 < 255 + 136, chi2
+    a = bits[:-8].astype(np.float64)
+    b = bits[8:].astype(np.float64)
+    r = np.corrcoef(a, b)[0, 1]
+    assert abs(r) < 6 / np.sqrt(a.size)
+    # different seeds give different streams
+    assert not np.array_equal(orc.sr_bits(1234, 0, 64), orc.sr_bits(1235, 0, 64))
+
+
+def test_sr_uses_logical_index_and_offset(orc):
+    """SR is a pure function of (value, seed, index + offset): a row shard
+    quantized with offset row0*cols equals the same rows of the full run, and
+    a strided (ld > cols) view is not the same as its padding."""
+    x = inputs.normal((8, 64), 31)
+    c, s = orc.quantize(x, 32, round=orc.SR, seed=7)
+    c2, s2 = orc.quantize(x[4:], 32, round=orc.SR, seed=7, rng_offset=4 * 64)
+    assert np.array_equal(c[4:], c2) and np.array_equal(s[4:], s2)
+    c3, _ = orc.quantize(x[4:], 32, round=orc.SR, seed=7)
+    assert not np.array_equal(c3, c2)
