@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled MXFP4 linear-layer hot path on one MI355X.
+
+One step = one forward + backward pass of the LLaMA-1B FFN up-projection
+layer (X bf16 8192x2048, W bf16 2048x5632, dY bf16 8192x5632, MXFP4 block 32)
+through every kernel of the path:
+
+  forward   Q(X, row, RNE)  Q(W, col, RNE)  Y = GEMM 8192x5632x2048 -> bf16
+            DQ(Q(X)) -> bf16 (the QDQ node's output)
+  backward  Q(dY, row, SR seed 1234)  Q(W, row, RNE)  dX = GEMM 8192x2048x5632 -> bf16
+            Q(X, col, RNE)  Q(dY, col, SR seed 1235)  dW = GEMM 2048x5632x8192 -> fp32
+            dW' = DGE(W, col blocks, k=5, clamp 3) applied to dW
+  + once per step the 13B-shaped outlier layer's hot-channel residual is NOT
+    part of this workload (it has its own shape); see --hcp.
+
+`value` = FP4 GEMM flops of the step / step time (TFLOPS), i.e. whole-step
+throughput.  Per-kernel times come from HIP events on the stream the kernels
+run on; the roofline object reports the forward GEMM (the dominant kernel)
+against the dense FP4 MFMA peak, and the quantizer against HBM bandwidth.
+The CPU baseline times the single-threaded oracle on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=20.0)
+    p.add_argument("--hcp", action="store_true",
+                   help="also time the 13B-shaped GEMM + hot-channel residual (reported aside)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mxfp4_block_scaled_fp4q_amd as fq
+    from mxfp4_block_scaled_fp4q_amd import inputs
+
+    fq.lib()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    M, K, N = 8192, 2048, 5632
+    f = inputs.ffn_forward(M, K, N)
+    b = inputs.ffn_backward_grad(M, N)
+
+    def to_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, W, dY = to_bf16(f["X"]), to_bf16(f["W"]), to_bf16(b["dY"])
+    u8 = dict(dtype=torch.uint8, device=dev)
+    bufs = {
+        "xr": (torch.empty((M, K // 2), **u8), torch.empty((M, K // 32), **u8)),
+        "wc": (torch.empty((N, K // 2), **u8), torch.empty((N, K // 32), **u8)),
+        "dyr": (torch.empty((M, N // 2), **u8), torch.empty((M, N // 32), **u8)),
+        "wr": (torch.empty((K, N // 2), **u8), torch.empty((K, N // 32), **u8)),
+        "xc": (torch.empty((K, M // 2), **u8), torch.empty((K, M // 32), **u8)),
+        "dyc": (torch.empty((N, M // 2), **u8), torch.empty((N, M // 32), **u8)),
+    }
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    Xdq = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((K, N), dtype=torch.float32, device=dev)
+    dWo = torch.empty((K, N), dtype=torch.float32, device=dev)
+
+    # (name, callable, algorithmic bytes, algorithmic flops)
+    qb = 2 + 0.5 + 1 / 32  # bf16 in, codes + E8M0 bytes out, per element
+    ops = [
+        ("quant_x_row", lambda: fq.quantize(X, 32, fq.ROW, fq.RNE, codes=bufs["xr"][0],
+                                            scales=bufs["xr"][1]), M * K * qb, 0),
+        ("quant_w_col", lambda: fq.quantize(W, 32, fq.COL, fq.RNE, codes=bufs["wc"][0],
+                                            scales=bufs["wc"][1]), K * N * qb, 0),
+        ("gemm_fwd", lambda: fq.gemm(*bufs["xr"], *bufs["wc"], c=Y),
+         (M + N) * K * (0.5 + 1 / 32) + M * N * 2, 2.0 * M * N * K),
+        ("dequant_x", lambda: fq.dequantize(*bufs["xr"], 32, out=Xdq), M * K * qb, 0),
+        ("quant_dy_row_sr", lambda: fq.quantize(dY, 32, fq.ROW, fq.SR, 1234,
+                                                codes=bufs["dyr"][0], scales=bufs["dyr"][1]),
+         M * N * qb, 0),
+        ("quant_w_row", lambda: fq.quantize(W, 32, fq.ROW, fq.RNE, codes=bufs["wr"][0],
+                                            scales=bufs["wr"][1]), K * N * qb, 0),
+        ("gemm_dx", lambda: fq.gemm(*bufs["dyr"], *bufs["wr"], c=dX),
+         (M + K) * N * (0.5 + 1 / 32) + M * K * 2, 2.0 * M * K * N),
+        ("quant_x_col", lambda: fq.quantize(X, 32, fq.COL, fq.RNE, codes=bufs["xc"][0],
+                                            scales=bufs["xc"][1]), M * K * qb, 0),
+        ("quant_dy_col_sr", lambda: fq.quantize(dY, 32, fq.COL, fq.SR, 1235,
+                                                codes=bufs["dyc"][0], scales=bufs["dyc"][1]),
+         M * N * qb, 0),
+        ("gemm_dw", lambda: fq.gemm(*bufs["xc"], *bufs["dyc"], c=dW),
+         (K + N) * M * (0.5 + 1 / 32) + K * N * 4, 2.0 * K * N * M),
+        ("dge_dw", lambda: fq.grad_estimate(fq.DGE, W, dW, 32, fq.COL, 5.0, 3.0, out=dWo),
+         K * N * (2 + 4 + 4), 0),
+    ]
+    step_flops = sum(o[3] for o in ops)
+
+    nev = len(ops) + 1
+
+    def run_step(evs=None):
+        for i, (_, fn, _, _) in enumerate(ops):
+            if evs is not None:
+                evs[i].record()
+            fn()
+        if evs is not None:
+            evs[len(ops)].record()
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronised on both sides
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    per_op = {}
+    for i, (name, _, nbytes, nflops) in enumerate(ops):
+        ts = [events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]
+        us = float(np.mean(ts)) * 1e3
+        d = {"us": round(us, 2), "us_min": round(float(np.min(ts)) * 1e3, 2)}
+        if nflops:
+            d["TFLOPS"] = round(nflops / (us * 1e-6) / 1e12, 1)
+            d["frac_fp4_peak"] = round(d["TFLOPS"] / PEAK_FP4_TFLOPS, 4)
+        d["GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        d["frac_hbm_peak"] = round(d["GBps"] / PEAK_HBM_GBPS, 4)
+        per_op[name] = d
+
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    g = per_op["gemm_fwd"]
+    roofline = {"bound": "mfma", "achieved": g["TFLOPS"], "peak": PEAK_FP4_TFLOPS,
+                "unit": "TFLOP/s", "frac": g["frac_fp4_peak"], "traffic": None,
+                "kernel": "gemm_fp4_kernel 8192x5632x2048 bf16 out",
+                "per_launch_flops": 2.0 * M * N * K}
+    q = per_op["quant_dy_row_sr"]
+    qr = per_op["quant_x_row"]
+    quant = {"quant_bf16_row_rne_GBps": qr["GBps"], "quant_bf16_row_rne_frac": qr["frac_hbm_peak"],
+             "quant_bf16_row_sr_GBps": q["GBps"], "quant_bf16_row_sr_frac": q["frac_hbm_peak"],
+             "quant_bytes_per_elem": qb}
+
+    extra = {}
+    if args.hcp:
+        extra["outlier_layer"] = bench_outlier_layer(torch, fq, inputs, dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(f, b, step_flops, args.cpu_budget_s)
+
+    out = {
+        "metric": "MXFP4 quantize GB/s + FP4 GEMM TFLOPS (8192x5632x2048), % of roofline",
+        "value": round(value, 1),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": "LLaMA-1B FFN up-proj layer, forward + backward: X bf16 8192x2048 "
+                               "N(0,1), W bf16 2048x5632 N(0,0.02), dY bf16 8192x5632 N(0,1e-3); "
+                               "MXFP4 block 32, E2M1 codes, E8M0 scales, fp32 accumulate",
+                   "global_batch": M, "parallelism": "none (1 GPU)",
+                   "step_fp4_gflop": round(step_flops / 1e9, 2)},
+        "roofline": roofline,
+        "quantize": quant,
+        "kernels": per_op,
+        **extra,
+    }
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
+def bench_outlier_layer(torch, fq, inputs, dev):
+    """13B-shaped layer: fp32 base GEMM 16384x13824x5120 + hot-channel residual."""
+    d = inputs.outlier_layer()
+    M, K = d["X"].shape
+    N = d["W"].shape[1]
+
+    def to_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, W = to_bf16(d["X"]), to_bf16(d["W"])
+    hot = torch.from_numpy(d["hot"]).to(dev)
+    xq = fq.quantize(X, 32, fq.ROW)
+    wq = fq.quantize(W, 32, fq.COL)
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(fq.hcp_workspace_bytes(M, N, hot.numel()), dtype=torch.uint8, device=dev)
+    res = {}
+    for name, fn in (("quant_x_row", lambda: fq.quantize(X, 32, fq.ROW, codes=xq[0], scales=xq[1])),
+                     ("quant_w_col", lambda: fq.quantize(W, 32, fq.COL, codes=wq[0], scales=wq[1])),
+                     ("gemm_fp32", lambda: fq.gemm(xq[0], xq[1], wq[0], wq[1], c=Y)),
+                     ("hcp_residual", lambda: fq.hcp_residual_add(X, xq[0], xq[1], W, wq[0], wq[1],
+                                                                  hot, Y, ws))):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 1)
+    res["gemm_TFLOPS"] = round(2.0 * M * N * K / (res["gemm_fp32_us"] * 1e-6) / 1e12, 1)
+    qb = 2.53125
+    res["quant_x_row_GBps"] = round(M * K * qb / (res["quant_x_row_us"] * 1e-6) / 1e9, 1)
+    res["quant_w_col_GBps"] = round(K * N * qb / (res["quant_w_col_us"] * 1e-6) / 1e9, 1)
+    res["hcp_n_hot"] = int(hot.numel())
+    res["hcp_y_rmw_GBps"] = round(8.0 * M * N / (res["hcp_residual_us"] * 1e-6) / 1e9, 1)
+    return res
+
+
+def cpu_baseline(f, b, step_flops, budget_s):
+    """The CPU oracle (single-threaded, untuned) on a bounded sample of the
+    same step: every quantize/dequantize/DGE on a row slab, each GEMM on a
+    row slab of its output, all extrapolated linearly to the full step."""
+    import oracle as orc
+    M, K = f["X"].shape
+    N = f["W"].shape[1]
+    X, W, dY = f["X"], f["W"], b["dY"]
+    rows = max(8, int(64 * budget_s / 20.0))
+    t = {}
+
+    def timed(key, scale, fn):
+        t0 = time.perf_counter()
+        r = fn()
+        t[key] = (time.perf_counter() - t0) * scale
+        return r
+
+    xs, dys = X[:rows], dY[:rows]
+    xr = timed("quant_x_row", M / rows, lambda: orc.quantize(xs, 32))
+    wc = timed("quant_w_col", 1.0, lambda: orc.quantize(W, 32, axis=orc.COL))
+    timed("dequant_x", M / rows, lambda: orc.dequantize(xr[0], xr[1], 32))
+    dyr = timed("quant_dy_row_sr", M / rows, lambda: orc.quantize(dys, 32, round=orc.SR,
+                                                                   seed=1234))
+    wr = timed("quant_w_row", 1.0, lambda: orc.quantize(W, 32))
+    # column quantisation of a 32-row slab of the transposed operands' sources
+    timed("quant_x_col", M / 32, lambda: orc.quantize(X[:32], 32, axis=orc.COL))
+    timed("quant_dy_col_sr", M / 32, lambda: orc.quantize(dY[:32], 32, axis=orc.COL,
+                                                          round=orc.SR, seed=1235))
+    g = 4
+    timed("gemm_fwd", M / g, lambda: orc.gemm(xr[0][:g], xr[1][:g], wc[0], wc[1]))
+    timed("gemm_dx", M / g, lambda: orc.gemm(dyr[0][:g], dyr[1][:g], wr[0], wr[1]))
+    xc32 = orc.quantize(np.ascontiguousarray(X[:, :g]), 32, axis=orc.COL)
+    dyc = orc.quantize(dY[:, :256], 32, axis=orc.COL, round=orc.SR, seed=1235)
+    timed("gemm_dw", (K / g) * (N / 256), lambda: orc.gemm(xc32[0], xc32[1], dyc[0], dyc[1]))
+    gw = np.zeros((32, N), np.float32)
+    timed("dge_dw", K / 32, lambda: orc.grad_estimate(orc.DGE, W[:32], gw, 32, orc.COL))
+    total = sum(t.values())
+    return {"value": round(step_flops / total / 1e12, 6), "unit": "TFLOPS", "cores": 1,
+            "kind": "oracle",
+            "sample": f"single-threaded C oracle (double precision) on row slabs of the step's "
+                      f"tensors ({rows} rows for row ops, 32 rows for column ops, {g} output "
+                      f"rows/cols per GEMM), extrapolated linearly to one full step; "
+                      f"est. step {total:.1f} s",
+            "est_step_s": round(total, 2),
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/*
+ * libfp4q -- block-scaled MXFP4 linear-layer hot path for AMD MI355X (gfx950).
+ *
+ * C ABI.  All tensor pointers are DEVICE pointers owned by the caller; the
+ * library keeps no pointer after a call returns.  Every compute call enqueues
+ * its kernels on `stream` (a hipStream_t passed as void*, NULL = the default
+ * stream) and returns without synchronising: a fault inside a kernel surfaces
+ * at the caller's next synchronisation.  Arguments are validated on the host
+ * before anything is launched; a call that returns a status other than
+ * FP4Q_OK has launched nothing (except FP4Q_ERR_HIP, where a launch was
+ * attempted and failed).  The library never aborts; fp4q_last_error() gives a
+ * thread-local detail string for the last failing call.  Calls are reentrant
+ * and thread-safe.
+ *
+ * Formats (sources: the MSRA FP4-training summary page, sec. 一, and the
+ * outlier-dynamics page, sec. 1.1, for E2M1 on [-6, 6]; the low-precision
+ * overview page, sec. 1.1, for the 8-bit exponent-only E8M0 scale; the MXFP4
+ * tutorial page, sec. 4.1, for block scaling over 16..128 elements):
+ *   - element: E2M1, 4-bit code = sign<<3 | magnitude code, magnitudes
+ *     {0, 0.5, 1, 1.5, 2, 3, 4, 6}; two codes per byte, the element with the
+ *     lower index along the block axis in the low nibble;
+ *   - scale: one E8M0 byte per block, value 2^(byte-127), 0xFF = NaN;
+ *     byte = clamp(floor(log2 amax) - 2, -127, 127) + 127, so the block's
+ *     largest magnitude divided by the scale lies in [4, 8);
+ *   - quantised operands are "K-major": [rows, K/2] code bytes and
+ *     [rows, K/block] scale bytes, both dense row-major.
+ *
+ * Dtype codes: FP4Q_F32 = IEEE binary32, FP4Q_BF16 = bfloat16.
+ * All pointers must be 16-byte aligned and every row stride (in bytes) a
+ * multiple of 16, or the call returns FP4Q_ERR_ALIGNMENT; the one exception
+ * is fp4q_gemm's C, which only needs its element alignment (any ld_c >= N).
+ */
+#ifndef LIBFP4Q_H
+#define LIBFP4Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4Q_ABI_VERSION 1
+
+typedef enum {
+    FP4Q_OK = 0,
+    FP4Q_ERR_INVALID = 1,     /* null pointer, bad size, bad enum, bad block */
+    FP4Q_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+    FP4Q_ERR_ALIGNMENT = 3,   /* pointer or row stride not 16-byte aligned */
+    FP4Q_ERR_WORKSPACE = 4,   /* caller workspace too small */
+    FP4Q_ERR_HIP = 5          /* a HIP launch or query failed */
+} fp4q_status_t;
+
+typedef enum { FP4Q_F32 = 0, FP4Q_BF16 = 1 } fp4q_dtype_t;
+typedef enum { FP4Q_RNE = 0, FP4Q_SR = 1 } fp4q_round_t;
+typedef enum {
+    FP4Q_BLOCK_ROW = 0, /* blocks along the contiguous (last) dim  */
+    FP4Q_BLOCK_COL = 1  /* blocks down the strided (first) dim     */
+} fp4q_axis_t;
+typedef enum { FP4Q_STE = 0, FP4Q_DGE = 1 } fp4q_grad_t;
+
+/*
+ * fp4q_quantize -- fused block amax, E8M0 scale, scale-and-round onto E2M1,
+ * and nibble packing: Q(x) = s * round(x / s) (MXFP4 tutorial page, sec. 2.1)
+ * with a shared power-of-two scale per block.
+ *
+ *   x        [rows, cols] bf16 or fp32, row stride ld_x elements (ld_x >= cols).
+ *   block    16, 32, 64 or 128.
+ *   axis     FP4Q_BLOCK_ROW: block j of row r = columns [j*block, (j+1)*block);
+ *              codes [rows, cols/2], scales [rows, cols/block]; needs
+ *              cols % block == 0.
+ *            FP4Q_BLOCK_COL: block j of column c = rows [j*block, (j+1)*block);
+ *              codes [cols, rows/2] and scales [cols, rows/block], i.e. the
+ *              K-major quantisation of x^T; needs rows % block == 0.
+ *   round    FP4Q_RNE: nearest, ties to the even code; FP4Q_SR: stochastic
+ *            rounding floor + (u < frac) (low-precision overview page,
+ *            sec. 3.2) between the two neighbouring E2M1 values, with
+ *            u = 16 random bits from Philox4x32-10 (Salmon et al., SC'11):
+ *            key = seed, counter = (pos >> 3), bits (pos & 7) of the output
+ *            as 16-bit lanes, pos = r*cols + c + rng_offset (the element's
+ *            logical row-major index in x plus the offset).  A row shard
+ *            starting at row r0 reproduces the unsharded result with
+ *            rng_offset = r0*cols.  Ignored for RNE.
+ *   |x/s| > 6 saturates to 6.  A block holding NaN or Inf gets scale 0xFF and
+ *   all-zero codes.  The sign bit is kept (negative values that round to 0
+ *   give code 0x8).
+ */
+fp4q_status_t fp4q_quantize(const void* x, fp4q_dtype_t x_dtype, int64_t rows, int64_t cols,
+                            int64_t ld_x, int32_t block, fp4q_axis_t axis, fp4q_round_t round,
+                            uint64_t seed, uint64_t rng_offset, uint8_t* codes, uint8_t* scales,
+                            void* stream);
+
+/*
+ * fp4q_dequantize -- the QDQ partner (MXFP4 tutorial page, sec. 6.1): element
+ * value(code) * 2^(byte-127), exact in fp32 and bf16 (results beyond the fp32
+ * range become Inf; byte 0xFF gives NaN for the whole block).
+ *   codes [rows, k/2], scales [rows, k/block] -> y [rows, k] dense, bf16/fp32.
+ *   k % block == 0.
+ */
+fp4q_status_t fp4q_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                              int64_t k, int32_t block, void* y, fp4q_dtype_t y_dtype,
+                              void* stream);
+
+/*
+ * fp4q_grad_estimate -- backward of Q: out = grad * d elementwise.
+ *   FP4Q_STE: d = 1 (MXFP4 tutorial page, sec. 3.1); x may be NULL.
+ *   FP4Q_DGE: the derivative of the differentiable staircase of the MSRA
+ *     FP4-training summary page, sec. 二: on the E2M1 interval of width delta
+ *     holding m = |x|/s (s = x's own block scale, recomputed here with the same
+ *     block and axis as x's quantisation), with u = 2(m - lo)/delta - 1,
+ *     d = min((1/k) |u|^(1/k - 1), clamp_max); m > 6 (saturated) gives d = 1;
+ *     a block holding NaN/Inf gives NaN.
+ *   x, grad, out: dense [rows, cols]; axis/block as in fp4q_quantize.
+ *   k >= 1, clamp_max > 0.  The result is rounded to out_dtype once.
+ */
+fp4q_status_t fp4q_grad_estimate(fp4q_grad_t mode, const void* x, fp4q_dtype_t x_dtype,
+                                 const void* grad, fp4q_dtype_t g_dtype, int64_t rows,
+                                 int64_t cols, int32_t block, fp4q_axis_t axis, float k,
+                                 float clamp_max, void* out, fp4q_dtype_t out_dtype,
+                                 void* stream);
+
+/*
+ * fp4q_gemm -- FP4 x FP4 GEMM with per-block scales and fp32 accumulation
+ * (the FP4 GEMMs that carry over 95% of the compute, MSRA FP4-training
+ * summary page, sec. 四):
+ *   C[i,j] (+)= sum_k deq(A[i,k]) * deq(B[j,k])
+ *   A: a_codes [M, K/2], a_scales [M, K/32]; B: b_codes [N, K/2],
+ *   b_scales [N, K/32] (both K-major, block 32, as fp4q_quantize writes them);
+ *   C: [M, N] row-major with row stride ld_c elements, bf16 or fp32 (bf16 is
+ *   the round-to-nearest-even of the fp32 accumulator).
+ *   block must be 32 (FP4Q_ERR_UNSUPPORTED otherwise); K % 128 == 0;
+ *   accumulate = 1 adds into an fp32 C (bf16 C: FP4Q_ERR_UNSUPPORTED).
+ *   M, N >= 1 are arbitrary (edge tiles are masked).  Deterministic: no
+ *   atomics, no split-K.
+ */
+fp4q_status_t fp4q_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                        const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+                        int32_t block, void* c, fp4q_dtype_t c_dtype, int64_t ld_c,
+                        int32_t accumulate, void* stream);
+
+/*
+ * fp4q_hcp_workspace_bytes -- bytes of device workspace fp4q_hcp_residual_add
+ * needs for these sizes.
+ */
+size_t fp4q_hcp_workspace_bytes(int64_t M, int64_t N, int32_t n_hot);
+
+/*
+ * fp4q_hcp_residual_add -- hot-channel compensation in the dual-kernel mode of
+ * the outlier-dynamics page, sec. 3.1 (base GEMM and residual GEMM run as
+ * separate kernels, then add).  Using that section's error decomposition, the
+ * residual replaces the quantised operands' product on the hot channels H by
+ * the bf16 operands' product:
+ *   Y[i,j] += sum_{c in H} ( X[i,c] W[c,j] - Xq[i,c] Wq[c,j] )
+ * computed as one bf16 GEMM with fp32 accumulation over the gathered operands
+ * [X_H | Xq_H] and [W_H ; -Wq_H].
+ *   x   bf16 [M, K] dense;  xq_codes/xq_scales: its ROW block-32 quantisation.
+ *   w   bf16 [K, N] dense;  wq_codes/wq_scales: its COL block-32 (K-major)
+ *       quantisation, [N, K/2] and [N, K/32].
+ *   hot_idx  int32 [n_hot] device array of distinct channels in [0, K)
+ *       (not checked: it lives on the device).  n_hot = 0 is a no-op.
+ *   y   fp32 [M, N] dense, read and written.
+ *   workspace  >= fp4q_hcp_workspace_bytes(M, N, n_hot) device bytes.
+ */
+fp4q_status_t fp4q_hcp_residual_add(int64_t M, int64_t N, int64_t K, const void* x,
+                                    const uint8_t* xq_codes, const uint8_t* xq_scales,
+                                    const void* w, const uint8_t* wq_codes,
+                                    const uint8_t* wq_scales, const int32_t* hot_idx,
+                                    int32_t n_hot, float* y, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+const char* fp4q_status_string(fp4q_status_t s);
+const char* fp4q_last_error(void);
+int32_t fp4q_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFP4Q_H */

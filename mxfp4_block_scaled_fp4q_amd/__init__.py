@@ -1,0 +1,188 @@
+"""Python binding of libfp4q, the block-scaled MXFP4 linear-layer hot path for
+AMD MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in ``include/libfp4q.h``; torch supplies device memory and the
+current stream.  There is no fallback: if ``libfp4q.so`` has not been built,
+loading the library raises.
+"""
+import ctypes as _ct
+import os as _os
+
+_HERE = _os.path.dirname(_os.path.abspath(__file__))
+LIB_PATH = _os.path.join(_HERE, "libfp4q.so")
+
+F32, BF16 = 0, 1
+ROW, COL = 0, 1
+RNE, SR = 0, 1
+STE, DGE = 0, 1
+
+STATUS = {0: "FP4Q_OK", 1: "FP4Q_ERR_INVALID", 2: "FP4Q_ERR_UNSUPPORTED",
+          3: "FP4Q_ERR_ALIGNMENT", 4: "FP4Q_ERR_WORKSPACE", 5: "FP4Q_ERR_HIP"}
+
+EXPORTS = ["fp4q_quantize", "fp4q_dequantize", "fp4q_grad_estimate", "fp4q_gemm",
+           "fp4q_hcp_workspace_bytes", "fp4q_hcp_residual_add", "fp4q_status_string",
+           "fp4q_last_error", "fp4q_abi_version"]
+
+
+class Fp4qError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libfp4q.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not _os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run "
+                              "mxfp4_block_scaled_fp4q_amd/build.py (or __graft_entry__.build())")
+        L = _ct.CDLL(LIB_PATH)
+        P, I64, I32, U64, F, SZ = (_ct.c_void_p, _ct.c_int64, _ct.c_int32, _ct.c_uint64,
+                                   _ct.c_float, _ct.c_size_t)
+        sig = {
+            "fp4q_quantize": (I32, [P, I32, I64, I64, I64, I32, I32, I32, U64, U64, P, P, P]),
+            "fp4q_dequantize": (I32, [P, P, I64, I64, I32, P, I32, P]),
+            "fp4q_grad_estimate": (I32, [I32, P, I32, P, I32, I64, I64, I32, I32, F, F, P, I32,
+                                         P]),
+            "fp4q_gemm": (I32, [I64, I64, I64, P, P, P, P, I32, P, I32, I64, I32, P]),
+            "fp4q_hcp_workspace_bytes": (SZ, [I64, I64, I32]),
+            "fp4q_hcp_residual_add": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, P, SZ,
+                                            P]),
+            "fp4q_status_string": (_ct.c_char_p, [I32]),
+            "fp4q_last_error": (_ct.c_char_p, []),
+            "fp4q_abi_version": (I32, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise Fp4qError(status, lib().fp4q_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return _ct.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dt(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"libfp4q takes bf16 or fp32 tensors, got {t.dtype}")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return _ct.c_void_p(s.cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libfp4q takes device (cuda) tensors")
+
+
+def quantize(x, block=32, axis=ROW, rounding=RNE, seed=0, rng_offset=0, codes=None, scales=None,
+             stream=None):
+    """Fused MXFP4 quantisation of a 2-D bf16/fp32 tensor (row stride from x).
+    Returns (codes uint8, scales uint8): ROW -> [R, C/2], [R, C/block];
+    COL -> [C, R/2], [C, R/block] (the K-major quantisation of x^T)."""
+    torch = _torch()
+    _need_cuda(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    if axis == ROW:
+        cshape, sshape = (rows, cols // 2), (rows, cols // block)
+    else:
+        cshape, sshape = (cols, rows // 2), (cols, rows // block)
+    if codes is None:
+        codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
+    _check(lib().fp4q_quantize(_ptr(x), _dt(x), rows, cols, x.stride(0), block, axis, rounding,
+                               seed, rng_offset, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def dequantize(codes, scales, block=32, out_dtype=None, out=None, stream=None):
+    """codes [R, K/2] + scales [R, K/block] -> dense [R, K] bf16 (default) or fp32."""
+    torch = _torch()
+    _need_cuda(codes, scales)
+    rows, k = codes.shape[0], codes.shape[1] * 2
+    if out is None:
+        out = torch.empty((rows, k), dtype=out_dtype or torch.bfloat16, device=codes.device)
+    _check(lib().fp4q_dequantize(_ptr(codes), _ptr(scales), rows, k, block, _ptr(out), _dt(out),
+                                 _stream(stream)))
+    return out
+
+
+def grad_estimate(mode, x, grad, block=32, axis=ROW, k=5.0, clamp_max=3.0, out_dtype=None,
+                  out=None, stream=None):
+    """STE (mode 0) or DGE (mode 1) backward of the quantiser: out = grad * d."""
+    torch = _torch()
+    _need_cuda(x, grad)
+    rows, cols = grad.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype or grad.dtype, device=grad.device)
+    xdt = _dt(x) if x is not None else F32
+    _check(lib().fp4q_grad_estimate(mode, _ptr(x), xdt, _ptr(grad), _dt(grad), rows, cols, block,
+                                    axis, float(k), float(clamp_max), _ptr(out), _dt(out),
+                                    _stream(stream)))
+    return out
+
+
+def gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=None, c=None, accumulate=False,
+         block=32, stream=None):
+    """C[M,N] (+)= deq(A) deq(B)^T with A [M, K/2]+[M, K/32], B [N, K/2]+[N, K/32]."""
+    torch = _torch()
+    _need_cuda(a_codes, a_scales, b_codes, b_scales)
+    M, N, K = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
+    if b_codes.shape[1] * 2 != K:
+        raise ValueError("A and B K dimensions differ")
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=a_codes.device)
+    _check(lib().fp4q_gemm(M, N, K, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
+                           _ptr(b_scales), block, _ptr(c), _dt(c), c.stride(0),
+                           1 if accumulate else 0, _stream(stream)))
+    return c
+
+
+def hcp_workspace_bytes(M, N, n_hot):
+    return int(lib().fp4q_hcp_workspace_bytes(M, N, n_hot))
+
+
+def hcp_residual_add(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, y, workspace=None,
+                     stream=None):
+    """y[M,N] (fp32, in place) += sum_{c in hot} X[:,c] W[c,:] - Xq[:,c] Wq[c,:]."""
+    torch = _torch()
+    _need_cuda(x, w, y, hot_idx)
+    M, K = x.shape
+    N = w.shape[1]
+    n_hot = hot_idx.numel()
+    need = hcp_workspace_bytes(M, N, n_hot)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().fp4q_hcp_residual_add(M, N, K, _ptr(x), _ptr(xq_codes), _ptr(xq_scales), _ptr(w),
+                                       _ptr(wq_codes), _ptr(wq_scales), _ptr(hot_idx), n_hot,
+                                       _ptr(y), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)))
+    return y

@@ -1,0 +1,198 @@
+// libfp4q C ABI: host-side validation, status reporting and kernel dispatch.
+// Every entry point checks its arguments before touching the device and
+// launches nothing when it returns an error other than FP4Q_ERR_HIP.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/libfp4q.h"
+#include "fp4q_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fp4q_status_t fail(fp4q_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+fp4q_status_t fail(fp4q_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+fp4q_status_t hip_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return FP4Q_OK;
+    return fail(FP4Q_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool valid_block(int32_t b) { return b == 16 || b == 32 || b == 64 || b == 128; }
+bool valid_dtype(int d) { return d == FP4Q_F32 || d == FP4Q_BF16; }
+int64_t esize(int d) { return d == FP4Q_BF16 ? 2 : 4; }
+
+// Index arithmetic inside the streaming kernels is 32-bit over 8-element
+// chunks; element counts up to 2^33 are accepted.
+constexpr int64_t kMaxElems = (int64_t)1 << 33;
+
+}  // namespace
+
+extern "C" {
+
+int32_t fp4q_abi_version(void) { return FP4Q_ABI_VERSION; }
+
+const char* fp4q_last_error(void) { return g_err; }
+
+const char* fp4q_status_string(fp4q_status_t s) {
+    switch (s) {
+        case FP4Q_OK: return "ok";
+        case FP4Q_ERR_INVALID: return "invalid argument";
+        case FP4Q_ERR_UNSUPPORTED: return "unsupported";
+        case FP4Q_ERR_ALIGNMENT: return "misaligned pointer or stride";
+        case FP4Q_ERR_WORKSPACE: return "workspace too small";
+        case FP4Q_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+fp4q_status_t fp4q_quantize(const void* x, fp4q_dtype_t x_dtype, int64_t rows, int64_t cols,
+                            int64_t ld_x, int32_t block, fp4q_axis_t axis, fp4q_round_t round,
+                            uint64_t seed, uint64_t rng_offset, uint8_t* codes, uint8_t* scales,
+                            void* stream) {
+    if (!x || !codes || !scales) return fail(FP4Q_ERR_INVALID, "quantize: null pointer");
+    if (!valid_dtype(x_dtype)) return fail(FP4Q_ERR_INVALID, "quantize: bad x dtype %d", x_dtype);
+    if (rows <= 0 || cols <= 0)
+        return fail(FP4Q_ERR_INVALID, "quantize: rows=%lld cols=%lld", (long long)rows,
+                    (long long)cols);
+    if (ld_x < cols) return fail(FP4Q_ERR_INVALID, "quantize: ld_x < cols");
+    if (!valid_block(block)) return fail(FP4Q_ERR_INVALID, "quantize: block %d", block);
+    if (axis != FP4Q_BLOCK_ROW && axis != FP4Q_BLOCK_COL)
+        return fail(FP4Q_ERR_INVALID, "quantize: bad axis");
+    if (round != FP4Q_RNE && round != FP4Q_SR) return fail(FP4Q_ERR_INVALID, "quantize: bad round");
+    if (axis == FP4Q_BLOCK_ROW && cols % block)
+        return fail(FP4Q_ERR_INVALID, "quantize: cols %% block != 0 for ROW blocks");
+    if (axis == FP4Q_BLOCK_COL && rows % block)
+        return fail(FP4Q_ERR_INVALID, "quantize: rows %% block != 0 for COL blocks");
+    if (rows > kMaxElems / ld_x) return fail(FP4Q_ERR_INVALID, "quantize: tensor too large");
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) ||
+        (ld_x * esize(x_dtype)) % 16)
+        return fail(FP4Q_ERR_ALIGNMENT, "quantize: pointers and row stride must be 16-byte aligned");
+    hipError_t e;
+    if (axis == FP4Q_BLOCK_ROW)
+        e = fp4q::launch_quantize_row(x, x_dtype, rows, cols, ld_x, block, round == FP4Q_SR, seed,
+                                      rng_offset, codes, scales, (hipStream_t)stream);
+    else
+        e = fp4q::launch_quantize_col(x, x_dtype, rows, cols, ld_x, block, round == FP4Q_SR, seed,
+                                      rng_offset, codes, scales, (hipStream_t)stream);
+    return hip_status(e, "quantize launch");
+}
+
+fp4q_status_t fp4q_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                              int64_t k, int32_t block, void* y, fp4q_dtype_t y_dtype,
+                              void* stream) {
+    if (!codes || !scales || !y) return fail(FP4Q_ERR_INVALID, "dequantize: null pointer");
+    if (!valid_dtype(y_dtype)) return fail(FP4Q_ERR_INVALID, "dequantize: bad y dtype");
+    if (rows <= 0 || k <= 0) return fail(FP4Q_ERR_INVALID, "dequantize: bad sizes");
+    if (!valid_block(block)) return fail(FP4Q_ERR_INVALID, "dequantize: block %d", block);
+    if (k % block) return fail(FP4Q_ERR_INVALID, "dequantize: k %% block != 0");
+    if (rows > kMaxElems / k) return fail(FP4Q_ERR_INVALID, "dequantize: tensor too large");
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(y))
+        return fail(FP4Q_ERR_ALIGNMENT, "dequantize: pointers must be 16-byte aligned");
+    return hip_status(fp4q::launch_dequantize(codes, scales, rows, k, block, y, y_dtype,
+                                              (hipStream_t)stream),
+                      "dequantize launch");
+}
+
+fp4q_status_t fp4q_grad_estimate(fp4q_grad_t mode, const void* x, fp4q_dtype_t x_dtype,
+                                 const void* grad, fp4q_dtype_t g_dtype, int64_t rows,
+                                 int64_t cols, int32_t block, fp4q_axis_t axis, float k,
+                                 float clamp_max, void* out, fp4q_dtype_t out_dtype,
+                                 void* stream) {
+    if (mode != FP4Q_STE && mode != FP4Q_DGE) return fail(FP4Q_ERR_INVALID, "grad: bad mode");
+    if (!grad || !out || (mode == FP4Q_DGE && !x))
+        return fail(FP4Q_ERR_INVALID, "grad: null pointer");
+    if (!valid_dtype(g_dtype) || !valid_dtype(out_dtype) ||
+        (mode == FP4Q_DGE && !valid_dtype(x_dtype)))
+        return fail(FP4Q_ERR_INVALID, "grad: bad dtype");
+    if (rows <= 0 || cols <= 0) return fail(FP4Q_ERR_INVALID, "grad: bad sizes");
+    if (rows > kMaxElems / cols) return fail(FP4Q_ERR_INVALID, "grad: tensor too large");
+    if (!aligned16(grad) || !aligned16(out) || (x && !aligned16(x)))
+        return fail(FP4Q_ERR_ALIGNMENT, "grad: pointers must be 16-byte aligned");
+    if (mode == FP4Q_STE)
+        return hip_status(fp4q::launch_ste(grad, g_dtype, rows * cols, out, out_dtype,
+                                           (hipStream_t)stream),
+                          "ste launch");
+    if (!valid_block(block)) return fail(FP4Q_ERR_INVALID, "grad: block %d", block);
+    if (axis != FP4Q_BLOCK_ROW && axis != FP4Q_BLOCK_COL)
+        return fail(FP4Q_ERR_INVALID, "grad: bad axis");
+    if (axis == FP4Q_BLOCK_ROW && cols % block)
+        return fail(FP4Q_ERR_INVALID, "grad: cols %% block != 0 for ROW blocks");
+    if (axis == FP4Q_BLOCK_COL && rows % block)
+        return fail(FP4Q_ERR_INVALID, "grad: rows %% block != 0 for COL blocks");
+    if (!(k >= 1.0f) || !(k < 1e30f)) return fail(FP4Q_ERR_INVALID, "grad: k must be >= 1");
+    if (!(clamp_max > 0.0f)) return fail(FP4Q_ERR_INVALID, "grad: clamp_max must be > 0");
+    return hip_status(fp4q::launch_dge(x, x_dtype, grad, g_dtype, rows, cols, block, axis, k,
+                                       clamp_max, out, out_dtype, (hipStream_t)stream),
+                      "dge launch");
+}
+
+fp4q_status_t fp4q_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                        const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,
+                        int32_t block, void* c, fp4q_dtype_t c_dtype, int64_t ld_c,
+                        int32_t accumulate, void* stream) {
+    if (!a_codes || !a_scales || !b_codes || !b_scales || !c)
+        return fail(FP4Q_ERR_INVALID, "gemm: null pointer");
+    if (M <= 0 || N <= 0 || K <= 0) return fail(FP4Q_ERR_INVALID, "gemm: bad sizes");
+    if (!valid_dtype(c_dtype)) return fail(FP4Q_ERR_INVALID, "gemm: bad C dtype");
+    if (!valid_block(block)) return fail(FP4Q_ERR_INVALID, "gemm: block %d", block);
+    if (block != 32)
+        return fail(FP4Q_ERR_UNSUPPORTED, "gemm: only block 32 (the MX hardware block)");
+    if (K % 128) return fail(FP4Q_ERR_INVALID, "gemm: K %% 128 != 0");
+    if (ld_c < N) return fail(FP4Q_ERR_INVALID, "gemm: ld_c < N");
+    if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
+        return fail(FP4Q_ERR_INVALID, "gemm: dimension too large");
+    if (accumulate != 0 && accumulate != 1) return fail(FP4Q_ERR_INVALID, "gemm: accumulate");
+    if (accumulate && c_dtype != FP4Q_F32)
+        return fail(FP4Q_ERR_UNSUPPORTED, "gemm: accumulate needs an fp32 C");
+    if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) ||
+        !aligned16(b_scales) || ((uintptr_t)c % (uintptr_t)esize(c_dtype)))
+        return fail(FP4Q_ERR_ALIGNMENT,
+                    "gemm: operand pointers must be 16-byte aligned, C element-aligned");
+    return hip_status(fp4q::launch_gemm_fp4(M, N, K, a_codes, a_scales, b_codes, b_scales, c,
+                                            c_dtype, ld_c, accumulate != 0, (hipStream_t)stream),
+                      "gemm launch");
+}
+
+size_t fp4q_hcp_workspace_bytes(int64_t M, int64_t N, int32_t n_hot) {
+    if (M <= 0 || N <= 0 || n_hot < 0) return 0;
+    return fp4q::hcp_workspace_bytes(M, N, n_hot);
+}
+
+fp4q_status_t fp4q_hcp_residual_add(int64_t M, int64_t N, int64_t K, const void* x,
+                                    const uint8_t* xq_codes, const uint8_t* xq_scales,
+                                    const void* w, const uint8_t* wq_codes,
+                                    const uint8_t* wq_scales, const int32_t* hot_idx,
+                                    int32_t n_hot, float* y, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    if (M <= 0 || N <= 0 || K <= 0 || n_hot < 0) return fail(FP4Q_ERR_INVALID, "hcp: bad sizes");
+    if (n_hot > K) return fail(FP4Q_ERR_INVALID, "hcp: n_hot > K");
+    if (K % 32) return fail(FP4Q_ERR_INVALID, "hcp: K %% 32 != 0");
+    if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
+        return fail(FP4Q_ERR_INVALID, "hcp: dimension too large");
+    if (n_hot == 0) return FP4Q_OK;
+    if (!x || !xq_codes || !xq_scales || !w || !wq_codes || !wq_scales || !hot_idx || !y ||
+        !workspace)
+        return fail(FP4Q_ERR_INVALID, "hcp: null pointer");
+    if (!aligned16(x) || !aligned16(xq_codes) || !aligned16(xq_scales) || !aligned16(w) ||
+        !aligned16(wq_codes) || !aligned16(wq_scales) || !aligned16(hot_idx) || !aligned16(y) ||
+        !aligned16(workspace))
+        return fail(FP4Q_ERR_ALIGNMENT, "hcp: pointers must be 16-byte aligned");
+    const size_t need = fp4q::hcp_workspace_bytes(M, N, n_hot);
+    if (workspace_bytes < need)
+        return fail(FP4Q_ERR_WORKSPACE, "hcp: workspace %zu < %zu bytes", workspace_bytes, need);
+    return hip_status(fp4q::launch_hcp(M, N, K, x, xq_codes, xq_scales, w, wq_codes, wq_scales,
+                                       hot_idx, n_hot, y, workspace, (hipStream_t)stream),
+                      "hcp launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal launcher interface between the C-ABI layer (fp4q_api.hip) and the
+// kernel translation units.  Launchers assume validated arguments.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+// n / d for n < 2^31 with a precomputed multiplier (Granlund & Montgomery,
+// "Division by invariant integers using multiplication", PLDI'94, round-up
+// variant): q = (umulhi(n, mul) + n) >> shift.
+struct FastDiv {
+    uint32_t d, mul, shift;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    f.shift = l;
+    f.mul = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+    return f;
+}
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv f) {
+    return (__umulhi(n, f.mul) + n) >> f.shift;
+}
+
+enum DType { F32 = 0, BF16 = 1 };
+
+hipError_t launch_quantize_row(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                               int block, bool sr, uint64_t seed, uint64_t off, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s);
+hipError_t launch_quantize_col(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                               int block, bool sr, uint64_t seed, uint64_t off, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s);
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                             int block, void* y, int ydtype, hipStream_t s);
+hipError_t launch_ste(const void* g, int gdtype, int64_t n, void* out, int odtype, hipStream_t s);
+hipError_t launch_dge(const void* x, int xdtype, const void* g, int gdtype, int64_t rows,
+                      int64_t cols, int block, int axis, float k, float clamp_max, void* out,
+                      int odtype, hipStream_t s);
+hipError_t launch_gemm_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
+                           const uint8_t* as, const uint8_t* bc, const uint8_t* bs, void* c,
+                           int cdtype, int64_t ldc, bool accumulate, hipStream_t s);
+size_t hcp_workspace_bytes(int64_t M, int64_t N, int32_t n_hot);
+hipError_t launch_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
+                      const uint8_t* xqs, const void* w, const uint8_t* wqc, const uint8_t* wqs,
+                      const int32_t* hot, int32_t n_hot, float* y, void* ws, hipStream_t s);
+
+}  // namespace fp4q

@@ -1,0 +1,153 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/libfp4q.h declares, and rejects bad arguments on the host (status
+codes) before anything reaches the device."""
+import ctypes as ct
+import os
+import re
+
+import pytest
+
+import mxfp4_block_scaled_fp4q_amd as fq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "libfp4q.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fq.LIB_PATH):
+        pytest.fail("libfp4q.so not built (run __graft_entry__.build())")
+    return fq.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4q_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert set(names) == set(fq.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strings(L):
+    assert L.fp4q_abi_version() == 1
+    for s in range(6):
+        assert L.fp4q_status_string(s).decode()
+    assert L.fp4q_status_string(99).decode() == "unknown status"
+
+
+FAKE = ct.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
+FAKE_MIS = ct.c_void_p(0x10008)   # misaligned
+NUL = ct.c_void_p(0)
+
+
+def q(L, x=FAKE, dt=1, rows=64, cols=64, ld=64, block=32, axis=0, rnd=0, codes=FAKE,
+      scales=FAKE):
+    return L.fp4q_quantize(x, dt, rows, cols, ld, block, axis, rnd, 0, 0, codes, scales, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=NUL), 1), (dict(codes=NUL), 1), (dict(scales=NUL), 1),
+    (dict(dt=7), 1), (dict(rows=0), 1), (dict(cols=-1), 1), (dict(ld=32), 1),
+    (dict(block=8), 1), (dict(block=48), 1), (dict(block=256), 1),
+    (dict(axis=2), 1), (dict(rnd=3), 1),
+    (dict(cols=48, ld=48), 1),               # ROW needs cols % block == 0
+    (dict(rows=48, axis=1), 1),              # COL needs rows % block == 0
+    (dict(x=FAKE_MIS), 3), (dict(codes=FAKE_MIS), 3), (dict(scales=FAKE_MIS), 3),
+    (dict(ld=68), 3),                        # bf16 row stride 136 bytes
+    (dict(rows=1 << 40), 1),                 # too large
+])
+def test_quantize_validation(L, kw, status):
+    assert q(L, **kw) == status
+    assert L.fp4q_last_error().decode()
+
+
+def test_dequantize_validation(L):
+    d = L.fp4q_dequantize
+    assert d(NUL, FAKE, 4, 64, 32, FAKE, 1, NUL) == 1
+    assert d(FAKE, FAKE, 4, 64, 24, FAKE, 1, NUL) == 1
+    assert d(FAKE, FAKE, 4, 48, 32, FAKE, 1, NUL) == 1
+    assert d(FAKE, FAKE, 4, 64, 32, FAKE, 5, NUL) == 1
+    assert d(FAKE, FAKE, 4, 64, 32, FAKE_MIS, 1, NUL) == 3
+
+
+def test_grad_validation(L):
+    g = L.fp4q_grad_estimate
+    # DGE needs x
+    assert g(1, NUL, 1, FAKE, 1, 64, 64, 32, 0, 5.0, 3.0, FAKE, 1, NUL) == 1
+    assert g(2, FAKE, 1, FAKE, 1, 64, 64, 32, 0, 5.0, 3.0, FAKE, 1, NUL) == 1
+    assert g(1, FAKE, 1, FAKE, 1, 64, 64, 32, 0, 0.5, 3.0, FAKE, 1, NUL) == 1  # k < 1
+    assert g(1, FAKE, 1, FAKE, 1, 64, 64, 32, 0, 5.0, 0.0, FAKE, 1, NUL) == 1  # clamp <= 0
+    assert g(1, FAKE, 1, FAKE, 1, 64, 48, 32, 0, 5.0, 3.0, FAKE, 1, NUL) == 1  # ROW cols%b
+    assert g(1, FAKE, 1, FAKE, 1, 48, 64, 32, 1, 5.0, 3.0, FAKE, 1, NUL) == 1  # COL rows%b
+    assert g(1, FAKE, 1, FAKE_MIS, 1, 64, 64, 32, 0, 5.0, 3.0, FAKE, 1, NUL) == 3
+    assert g(0, NUL, 1, FAKE, 1, 0, 64, 32, 0, 5.0, 3.0, FAKE, 1, NUL) == 1
+
+
+def test_gemm_validation(L):
+    g = L.fp4q_gemm
+    ok = dict(M=64, N=64, K=256, a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, blk=32, c=FAKE, cdt=0,
+              ldc=64, acc=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return g(a["M"], a["N"], a["K"], a["a"], a["sa"], a["b"], a["sb"], a["blk"], a["c"],
+                 a["cdt"], a["ldc"], a["acc"], NUL)
+    assert call(a=NUL) == 1
+    assert call(M=0) == 1
+    assert call(blk=16) == 2            # valid block, not the MX hardware block
+    assert call(blk=12) == 1
+    assert call(K=192) == 1             # K % 128
+    assert call(ldc=32) == 1
+    assert call(acc=1, cdt=1) == 2      # accumulate into bf16
+    assert call(acc=2) == 1
+    assert call(c=ct.c_void_p(0x10002)) == 3   # fp32 C not 4-byte aligned
+    assert call(a=FAKE_MIS) == 3
+    assert call(sb=FAKE_MIS) == 3
+
+
+def test_hcp_validation(L):
+    h = L.fp4q_hcp_residual_add
+    ws = L.fp4q_hcp_workspace_bytes(128, 64, 10)
+    assert ws >= (128 + 64) * 64 * 2
+    assert L.fp4q_hcp_workspace_bytes(128, 64, 0) == 0
+    args = [128, 64, 256, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, ws, NUL]
+    bad = list(args)
+    bad[13] = ws - 1
+    assert h(*bad) == 4
+    bad = list(args)
+    bad[10] = 300        # n_hot > K
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[2] = 100         # K % 32
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[3] = NUL
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[11] = FAKE_MIS
+    assert h(*bad) == 3
+    bad = list(args)
+    bad[10] = 0          # no hot channels: a no-op that touches nothing
+    bad[3] = NUL
+    assert h(*bad) == 0
+
+
+def test_fastdiv_formula():
+    """The 32-bit division-by-invariant multiplier the streaming kernels use
+    (Granlund & Montgomery round-up variant), checked against // on the host."""
+    import random
+    random.seed(3)
+    for d in [1, 2, 3, 7, 64, 176, 256, 640, 704, 2047, 2048, 2049, (1 << 31) - 1] + \
+            [random.randrange(1, 1 << 31) for _ in range(200)]:
+        l = 0
+        while (1 << l) < d:
+            l += 1
+        mul = ((1 << 32) * ((1 << l) - d)) // d + 1
+        assert mul < (1 << 32)
+        for n in [0, 1, d - 1, d, d + 1, (1 << 31) - 1] + \
+                [random.randrange(0, 1 << 31) for _ in range(500)]:
+            assert ((((n * mul) >> 32) + n) >> l) == n // d
