@@ -160,7 +160,7 @@ def main():
              "quant_bf16_row_sr_GBps": q["GBps"], "quant_bf16_row_sr_frac": q["frac_hbm_peak"],
              "quant_bytes_per_elem": qb}
 
-    extra = {}
+    extra = {"copy_ceiling_GBps": copy_ceiling(torch, dev)}
     if args.hcp:
         extra["outlier_layer"] = bench_outlier_layer(torch, fq, inputs, dev)
 
@@ -194,6 +194,27 @@ def main():
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
+
+
+def copy_ceiling(torch, dev):
+    """Attainable HBM bandwidth of a plain device copy (torch's copy kernel),
+    1 GiB read + 1 GiB written, the reference point for the streaming kernels."""
+    n = 1 << 28
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    secs = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b
+    return round(2 * 4 * n / secs / 1e9, 1)
 
 
 def bench_outlier_layer(torch, fq, inputs, dev):

@@ -36,20 +36,109 @@ namespace fp4q {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 static constexpr int BM = 256, BN = 256;
 static constexpr int BKB = 64;  // K bytes per step (128 fp4 elements)
 static constexpr int kThreads = 256;
-static constexpr int FRAG = 1024;                    // bytes per LDS fragment
-static constexpr int STAGE = 2 * 16 * FRAG;          // A + B fragments per stage
+static constexpr int FRAG = 1024;               // bytes per LDS fragment
+#ifndef FP4Q_GEMM_NSTAGE
+#define FP4Q_GEMM_NSTAGE 3
+#endif
+static constexpr int NSTAGE = FP4Q_GEMM_NSTAGE; // LDS ring depth (3 or 4)
+static constexpr int OFF_B = 16 * FRAG;         // B fragments within a stage
+static constexpr int OFF_SA = 32 * FRAG;        // A scale words (256 x 4 B)
+static constexpr int OFF_SB = 32 * FRAG + 1024; // B scale words
+static constexpr int STAGE = 32 * FRAG + 2048;
+static constexpr int LOADS_PER_STEP = 10;       // per wave: 8 fragments + 2 scale rows
 static constexpr int GROUP_M = 4;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+#define FP4Q_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
+
+struct StepSrc {
+    const uint8_t* ga[4];
+    const uint8_t* gb[4];
+    const uint8_t* gsa;
+    const uint8_t* gsb;
+};
+
+// Issue the 10 direct-to-LDS loads of K step kt of this wave into `stage`.
+__device__ __forceinline__ void issue_step(const StepSrc& src, int kt, uint8_t* stage, int wave) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int f = wave * 4 + q;
+        __builtin_amdgcn_global_load_lds((const void*)(src.ga[q] + (int64_t)kt * BKB),
+                                         (lds_ptr_t)(stage + f * FRAG), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(src.gb[q] + (int64_t)kt * BKB),
+                                         (lds_ptr_t)(stage + OFF_B + f * FRAG), 16, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds((const void*)(src.gsa + kt * 4),
+                                     (lds_ptr_t)(stage + OFF_SA + wave * 256), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(src.gsb + kt * 4),
+                                     (lds_ptr_t)(stage + OFF_SB + wave * 256), 4, 0, 0);
+}
+
+struct Frags {
+    uint4 a[4], b[4];
+};
+
+// This wave's A and B fragments of half kk (K bytes kk*32 .. kk*32+31) of a
+// staged step: 8 conflict-free 16-byte LDS reads.
+__device__ __forceinline__ void read_frags(const uint8_t* base, int kk, int wm, int wn, int lane,
+                                           Frags& F) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        F.a[i] = *(const uint4*)(base + ((wm * 4 + i) * 2 + kk) * FRAG + lane * 16);
+        F.b[i] = *(const uint4*)(base + OFF_B + ((wn * 4 + i) * 2 + kk) * FRAG + lane * 16);
+    }
+}
+
+// Scale words of this lane's MFMA rows (A) and columns (B), shifted so that
+// byte 0 / byte 2 are the K blocks of halves 0 / 1 for this lane's 32-element
+// K chunk.
+__device__ __forceinline__ void read_scales(const uint8_t* base, int wm, int wn, int lane,
+                                            uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+    const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sa[i] = *(const uint32_t*)(base + OFF_SA + (wm * 128 + i * 32 + l32) * 4) >> (8 * half);
+        sb[i] = *(const uint32_t*)(base + OFF_SB + (wn * 128 + i * 32 + l32) * 4) >> (8 * half);
+    }
+}
+
+// 16 MFMAs: the 4 x 4 tiles of this wave on half kk of a K step.
+__device__ __forceinline__ void mfma_half(const Frags& F, const uint32_t (&sa)[4],
+                                          const uint32_t (&sb)[4], int kk, v16f (&acc)[4][4]) {
+    v8i fa[4], fb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        fa[i] = (v8i){(int)F.a[i].x, (int)F.a[i].y, (int)F.a[i].z, (int)F.a[i].w, 0, 0, 0, 0};
+        fb[i] = (v8i){(int)F.b[i].x, (int)F.b[i].y, (int)F.b[i].z, (int)F.b[i].w, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fa[i], fb[j], acc[i][j], 4, 4, 0, (int)(sa[i] >> (16 * kk)), 0,
+                (int)(sb[j] >> (16 * kk)));
+}
 
 template <int OUT_BF16, int ACCUM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(
     int M, int N, int K, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, void* __restrict__ cptr,
     int64_t ldc, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+    // The LDS ring stages are separate objects, so the compiler can tell the
+    // stage being read from the stages the in-flight loads write.
+    __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
+#if FP4Q_GEMM_NSTAGE == 4
+    __shared__ __attribute__((aligned(16))) uint8_t st3[STAGE];
+#endif
 
     // ---- tile index: XCD-contiguous, then grouped along M ----
     const int nwg = gridDim.x;
@@ -71,36 +160,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int half = lane >> 5;  // which 16-byte half of a 32-byte fragment row
+    const int half = lane >> 5;
     const int l32 = lane & 31;
     const int64_t kbytes = K / 2;
     const int kscale = K / 32;
     const int ksteps = K / 128;
 
-    // Global sources of this lane's 8 fragment loads per step: wave w loads
-    // A fragments f = 4w..4w+3 and B fragments f = 4w..4w+3, f = rg*2 + kk.
-    const uint8_t* ga[4];
-    const uint8_t* gb[4];
+    // Global sources of this lane's loads.  Fragment f = rg*2 + kk holds rows
+    // rg*32 .. rg*32+31 and K bytes kk*32 .. kk*32+31 of the step; wave w
+    // loads fragments 4w .. 4w+3 of A and of B (one 16-byte load per lane,
+    // written by the load straight into LDS at fragment base + lane*16), and
+    // the scale words of rows 64w .. 64w+63 of A and of B.
+    StepSrc src;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int f = wave * 4 + q;
         const int rg = f >> 1, kk = f & 1;
         const int ra = min(m0 + rg * 32 + l32, M - 1);
         const int rb = min(n0 + rg * 32 + l32, N - 1);
-        ga[q] = ac + (int64_t)ra * kbytes + kk * 32 + half * 16;
-        gb[q] = bc + (int64_t)rb * kbytes + kk * 32 + half * 16;
+        src.ga[q] = ac + (int64_t)ra * kbytes + kk * 32 + half * 16;
+        src.gb[q] = bc + (int64_t)rb * kbytes + kk * 32 + half * 16;
     }
-    // Scale rows this lane feeds to its MFMAs: A rows of the wave's 4 row
-    // groups, B rows of its 4 column groups.
-    const uint32_t* sa_ptr[4];
-    const uint32_t* sb_ptr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ra = min(m0 + wm * 128 + i * 32 + l32, M - 1);
-        const int rb = min(n0 + wn * 128 + i * 32 + l32, N - 1);
-        sa_ptr[i] = (const uint32_t*)(as + (int64_t)ra * kscale);
-        sb_ptr[i] = (const uint32_t*)(bs + (int64_t)rb * kscale);
-    }
+    src.gsa = as + (int64_t)min(m0 + wave * 64 + lane, M - 1) * kscale;
+    src.gsb = bs + (int64_t)min(n0 + wave * 64 + lane, N - 1) * kscale;
 
     v16f acc[4][4];
 #pragma unroll
@@ -110,99 +192,138 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    uint4 pa[4], pb[4];
-    uint32_t sa_cur[4], sb_cur[4], sa_nxt[4], sb_nxt[4];
-
-    auto gload = [&](int kt) {
+    // Software pipeline over K steps t (LDS ring of NSTAGE stages, two
+    // halves kk per step): while the MFMAs of (t, 0) run, the fragments of
+    // (t, 1) are read and the loads of step t+NSTAGE-1 are issued; one
+    // barrier per step, after which the scales and (t+1, 0) fragments are
+    // read while the MFMAs of (t, 1) run.  The barrier follows an lgkmcnt(0)
+    // wait, so every wave has finished reading stage t before anyone refills
+    // it (at step t+1).
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            pa[q] = *(const uint4*)(ga[q] + (int64_t)kt * BKB);
-            pb[q] = *(const uint4*)(gb[q] + (int64_t)kt * BKB);
-        }
-    };
-    auto sload = [&](int kt, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa[i] = sa_ptr[i][kt] >> (8 * half);
-            sb[i] = sb_ptr[i][kt] >> (8 * half);
-        }
-    };
-    auto lds_store = [&](int buf) {
-        uint8_t* base = lds + buf * STAGE;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int f = wave * 4 + q;
-            *(uint4*)(base + f * FRAG + lane * 16) = pa[q];
-            *(uint4*)(base + 16 * FRAG + f * FRAG + lane * 16) = pb[q];
-        }
-    };
-
-    gload(0);
-    sload(0, sa_cur, sb_cur);
-    lds_store(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < ksteps; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < ksteps;
-        if (more) {
-            gload(kt + 1);
-            sload(kt + 1, sa_nxt, sb_nxt);
-        }
-        const uint8_t* base = lds + buf * STAGE;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            v8i fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 a = *(const uint4*)(base + ((wm * 4 + i) * 2 + kk) * FRAG + lane * 16);
-                const uint4 b =
-                    *(const uint4*)(base + 16 * FRAG + ((wn * 4 + i) * 2 + kk) * FRAG + lane * 16);
-                fa[i] = (v8i){(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-                fb[i] = (v8i){(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fa[i], fb[j], acc[i][j], 4, 4, 0, (int)(sa_cur[i] >> (16 * kk)), 0,
-                        (int)(sb_cur[j] >> (16 * kk)));
-        }
-        if (more) {
-            lds_store(buf ^ 1);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sa_cur[i] = sa_nxt[i];
-                sb_cur[i] = sb_nxt[i];
-            }
-        }
-        __syncthreads();
+    for (int s = 0; s < NSTAGE - 1; ++s) {
+        uint8_t* stg = s == 0 ? st0 : s == 1 ? st1 : st2;
+        if (s < ksteps) issue_step(src, s, stg, wave);
     }
+    if (ksteps >= NSTAGE - 1) {
+        FP4Q_WAIT_VMCNT(LOADS_PER_STEP * (NSTAGE - 2));
+    } else {
+        FP4Q_WAIT_VMCNT(0);
+    }
+    __builtin_amdgcn_s_barrier();
+    Frags FA, FB;
+    uint32_t sa[4], sb[4], sa_n[4], sb_n[4];
+    read_scales(st0, wm, wn, lane, sa, sb);
+    read_frags(st0, 0, wm, wn, lane, FA);
 
-    // ---- epilogue ----
+#define FP4Q_GEMM_STEP(t, CUR, NEXT1, NEXTL)                                    \
+    do {                                                                        \
+        read_frags(CUR, 1, wm, wn, lane, FB);                                   \
+        const bool issued_ = (t) + NSTAGE - 1 < ksteps;                         \
+        if (issued_) issue_step(src, (t) + NSTAGE - 1, NEXTL, wave);            \
+        mfma_half(FA, sa, sb, 0, acc);                                          \
+        if (issued_) {                                                          \
+            __builtin_amdgcn_s_waitcnt(((LOADS_PER_STEP * (NSTAGE - 2)) & 0xF) |  \
+                                       (((LOADS_PER_STEP * (NSTAGE - 2)) >> 4) << 14) | 0x70); \
+        } else {                                                                \
+            __builtin_amdgcn_s_waitcnt(0x70);                                   \
+        }                                                                       \
+        __builtin_amdgcn_s_barrier();                                           \
+        if ((t) + 1 < ksteps) {                                                 \
+            read_scales(NEXT1, wm, wn, lane, sa_n, sb_n);                       \
+            read_frags(NEXT1, 0, wm, wn, lane, FA);                             \
+        }                                                                       \
+        mfma_half(FB, sa, sb, 1, acc);                                          \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                         \
+            sa[q] = sa_n[q];                                                    \
+            sb[q] = sb_n[q];                                                    \
+        }                                                                       \
+    } while (0)
+
+#if FP4Q_GEMM_NSTAGE == 4
+    for (int kt = 0; kt < ksteps; kt += 4) {
+        FP4Q_GEMM_STEP(kt, st0, st1, st3);
+        if (kt + 1 < ksteps) FP4Q_GEMM_STEP(kt + 1, st1, st2, st0);
+        if (kt + 2 < ksteps) FP4Q_GEMM_STEP(kt + 2, st2, st3, st1);
+        if (kt + 3 < ksteps) FP4Q_GEMM_STEP(kt + 3, st3, st0, st2);
+    }
+#else
+    for (int kt = 0; kt < ksteps; kt += 3) {
+        FP4Q_GEMM_STEP(kt, st0, st1, st2);
+        if (kt + 1 < ksteps) FP4Q_GEMM_STEP(kt + 1, st1, st2, st0);
+        if (kt + 2 < ksteps) FP4Q_GEMM_STEP(kt + 2, st2, st0, st1);
+    }
+#endif
+#undef FP4Q_GEMM_STEP
+
+    // ---- epilogue: through LDS, so every lane writes 16 contiguous bytes ----
+    // Each wave stages its 128 x 128 sub-tile 32 rows at a time in a private
+    // LDS region (row pitch padded by 16 bytes), then reads it back as
+    // 16-byte row chunks: 16 lanes cover one 128-column row.
+    __syncthreads();  // all waves are done with the operand stages
+    constexpr int ESZ = OUT_BF16 ? 2 : 4;
+    constexpr int PITCH = 128 * ESZ + 16;
+    uint8_t* reg = OUT_BF16 ? st0 + wave * (32 * PITCH)
+                            : (wave < 2 ? st0 : st1) + (wave & 1) * (32 * PITCH);
+    const int row0 = m0 + wm * 128;
+    const int col0 = n0 + wn * 128;
+    const bool vec_ok = ((ldc * ESZ) % 16 == 0) && (((uintptr_t)cptr & 15) == 0);
+    constexpr int CHUNK_ELEMS = 16 / ESZ;       // elements per 16-byte chunk
+    constexpr int LANES_PER_ROW = 128 / CHUNK_ELEMS;
+    constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn * 128 + j * 32 + l32;
-            if (col >= N) continue;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (row < M) {
-                    const int64_t off = (int64_t)row * ldc + col;
-                    const float v = acc[i][j][r];
+                const int rl = 8 * (r >> 2) + 4 * half + (r & 3);
+                const int cl = j * 32 + l32;
+                if (OUT_BF16)
+                    *(uint16_t*)(reg + rl * PITCH + cl * 2) = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+                else
+                    *(float*)(reg + rl * PITCH + cl * 4) = acc[i][j][r];
+            }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
+        __builtin_amdgcn_wave_barrier();
+        const int rbase = row0 + i * 32;
+#pragma unroll
+        for (int p = 0; p < 32 / ROWS_PER_PASS; ++p) {
+            const int rl = p * ROWS_PER_PASS + lane / LANES_PER_ROW;
+            const int ce = (lane % LANES_PER_ROW) * CHUNK_ELEMS;
+            const uint4 v = *(const uint4*)(reg + rl * PITCH + ce * ESZ);
+            const int row = rbase + rl;
+            const int col = col0 + ce;
+            if (row >= M) continue;
+            const int64_t off = (int64_t)row * ldc + col;
+            if (vec_ok && col + CHUNK_ELEMS <= N) {
+                if (ACCUM) {
+                    float4 o = *(const float4*)((const float*)cptr + off);
+                    o.x += as_f32(v.x);
+                    o.y += as_f32(v.y);
+                    o.z += as_f32(v.z);
+                    o.w += as_f32(v.w);
+                    *(float4*)((float*)cptr + off) = o;
+                } else if (OUT_BF16) {
+                    *(uint4*)((uint16_t*)cptr + off) = v;
+                } else {
+                    *(uint4*)((float*)cptr + off) = v;
+                }
+            } else {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < CHUNK_ELEMS; ++e) {
+                    if (col + e >= N) break;
                     if (OUT_BF16) {
-                        ((uint16_t*)cptr)[off] = (uint16_t)f32_to_bf16_bits(v);
+                        ((uint16_t*)cptr)[off + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
                     } else if (ACCUM) {
-                        ((float*)cptr)[off] += v;
+                        ((float*)cptr)[off + e] += as_f32(w[e]);
                     } else {
-                        ((float*)cptr)[off] = v;
+                        ((float*)cptr)[off + e] = as_f32(w[e]);
                     }
                 }
             }
         }
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -212,15 +333,16 @@ hipError_t launch_gemm_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
     dim3 grid((unsigned)(tiles_m * tiles_n));
+    const size_t shmem = 0;
     if (cdtype == BF16)
-        gemm_fp4_kernel<1, 0><<<grid, kThreads, 0, s>>>((int)M, (int)N, (int)K, ac, as, bc, bs, c,
-                                                        ldc, tiles_m, tiles_n);
+        gemm_fp4_kernel<1, 0><<<grid, kThreads, shmem, s>>>((int)M, (int)N, (int)K, ac, as, bc, bs,
+                                                            c, ldc, tiles_m, tiles_n);
     else if (accumulate)
-        gemm_fp4_kernel<0, 1><<<grid, kThreads, 0, s>>>((int)M, (int)N, (int)K, ac, as, bc, bs, c,
-                                                        ldc, tiles_m, tiles_n);
+        gemm_fp4_kernel<0, 1><<<grid, kThreads, shmem, s>>>((int)M, (int)N, (int)K, ac, as, bc, bs,
+                                                            c, ldc, tiles_m, tiles_n);
     else
-        gemm_fp4_kernel<0, 0><<<grid, kThreads, 0, s>>>((int)M, (int)N, (int)K, ac, as, bc, bs, c,
-                                                        ldc, tiles_m, tiles_n);
+        gemm_fp4_kernel<0, 0><<<grid, kThreads, shmem, s>>>((int)M, (int)N, (int)K, ac, as, bc, bs,
+                                                            c, ldc, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
