@@ -215,42 +215,68 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(
     read_scales(st0, wm, wn, lane, sa, sb);
     read_frags(st0, 0, wm, wn, lane, FA);
 
-#define FP4Q_GEMM_STEP(t, CUR, NEXT1, NEXTL)                                    \
-    do {                                                                        \
-        read_frags(CUR, 1, wm, wn, lane, FB);                                   \
-        const bool issued_ = (t) + NSTAGE - 1 < ksteps;                         \
-        if (issued_) issue_step(src, (t) + NSTAGE - 1, NEXTL, wave);            \
-        mfma_half(FA, sa, sb, 0, acc);                                          \
-        if (issued_) {                                                          \
-            __builtin_amdgcn_s_waitcnt(((LOADS_PER_STEP * (NSTAGE - 2)) & 0xF) |  \
+// One K step.  ISSUE: whether step t+NSTAGE-1 exists (its loads are issued
+// here); LAST: whether t is the final step.  Both are compile-time in the
+// steady-state loop, so its body has no branches; the few tail steps use
+// the run-time form.  sched_barrier(0) keeps the first MFMA half above the
+// barrier, so the MFMA pipe has work queued while the wave waits there.
+#define FP4Q_GEMM_STEP(t, CUR, NEXT1, NEXTL, ISSUE, LAST)                          \
+    do {                                                                           \
+        read_frags(CUR, 1, wm, wn, lane, FB);                                      \
+        if (ISSUE) issue_step(src, (t) + NSTAGE - 1, NEXTL, wave);                  \
+        mfma_half(FA, sa, sb, 0, acc);                                             \
+        __builtin_amdgcn_sched_barrier(0);                                         \
+        if (ISSUE) {                                                               \
+            __builtin_amdgcn_s_waitcnt(((LOADS_PER_STEP * (NSTAGE - 2)) & 0xF) |     \
                                        (((LOADS_PER_STEP * (NSTAGE - 2)) >> 4) << 14) | 0x70); \
-        } else {                                                                \
-            __builtin_amdgcn_s_waitcnt(0x70);                                   \
-        }                                                                       \
-        __builtin_amdgcn_s_barrier();                                           \
-        if ((t) + 1 < ksteps) {                                                 \
-            read_scales(NEXT1, wm, wn, lane, sa_n, sb_n);                       \
-            read_frags(NEXT1, 0, wm, wn, lane, FA);                             \
-        }                                                                       \
-        mfma_half(FB, sa, sb, 1, acc);                                          \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                         \
-            sa[q] = sa_n[q];                                                    \
-            sb[q] = sb_n[q];                                                    \
-        }                                                                       \
+        } else {                                                                   \
+            __builtin_amdgcn_s_waitcnt(0x70);                                      \
+        }                                                                          \
+        __builtin_amdgcn_s_barrier();                                              \
+        __builtin_amdgcn_sched_barrier(0);                                         \
+        if (!(LAST)) {                                                             \
+            read_scales(NEXT1, wm, wn, lane, sa_n, sb_n);                          \
+            read_frags(NEXT1, 0, wm, wn, lane, FA);                                \
+        }                                                                          \
+        mfma_half(FB, sa, sb, 1, acc);                                             \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                            \
+            sa[q] = sa_n[q];                                                       \
+            sb[q] = sb_n[q];                                                       \
+        }                                                                          \
     } while (0)
 
+    // steady state: every step of an unrolled group issues a later step
+    int kt = 0;
 #if FP4Q_GEMM_NSTAGE == 4
-    for (int kt = 0; kt < ksteps; kt += 4) {
-        FP4Q_GEMM_STEP(kt, st0, st1, st3);
-        if (kt + 1 < ksteps) FP4Q_GEMM_STEP(kt + 1, st1, st2, st0);
-        if (kt + 2 < ksteps) FP4Q_GEMM_STEP(kt + 2, st2, st3, st1);
-        if (kt + 3 < ksteps) FP4Q_GEMM_STEP(kt + 3, st3, st0, st2);
+    for (; kt + 3 + NSTAGE - 1 < ksteps; kt += 4) {
+        FP4Q_GEMM_STEP(kt, st0, st1, st3, true, false);
+        FP4Q_GEMM_STEP(kt + 1, st1, st2, st0, true, false);
+        FP4Q_GEMM_STEP(kt + 2, st2, st3, st1, true, false);
+        FP4Q_GEMM_STEP(kt + 3, st3, st0, st2, true, false);
+    }
+    // tail (kt % 4 == 0 here)
+    for (; kt < ksteps; kt += 4) {
+        FP4Q_GEMM_STEP(kt, st0, st1, st3, kt + NSTAGE - 1 < ksteps, kt + 1 == ksteps);
+        if (kt + 1 < ksteps)
+            FP4Q_GEMM_STEP(kt + 1, st1, st2, st0, kt + NSTAGE < ksteps, kt + 2 == ksteps);
+        if (kt + 2 < ksteps)
+            FP4Q_GEMM_STEP(kt + 2, st2, st3, st1, kt + NSTAGE + 1 < ksteps, kt + 3 == ksteps);
+        if (kt + 3 < ksteps)
+            FP4Q_GEMM_STEP(kt + 3, st3, st0, st2, kt + NSTAGE + 2 < ksteps, kt + 4 == ksteps);
     }
 #else
-    for (int kt = 0; kt < ksteps; kt += 3) {
-        FP4Q_GEMM_STEP(kt, st0, st1, st2);
-        if (kt + 1 < ksteps) FP4Q_GEMM_STEP(kt + 1, st1, st2, st0);
-        if (kt + 2 < ksteps) FP4Q_GEMM_STEP(kt + 2, st2, st0, st1);
+    for (; kt + 2 + NSTAGE - 1 < ksteps; kt += 3) {
+        FP4Q_GEMM_STEP(kt, st0, st1, st2, true, false);
+        FP4Q_GEMM_STEP(kt + 1, st1, st2, st0, true, false);
+        FP4Q_GEMM_STEP(kt + 2, st2, st0, st1, true, false);
+    }
+    // tail (kt % 3 == 0 here)
+    for (; kt < ksteps; kt += 3) {
+        FP4Q_GEMM_STEP(kt, st0, st1, st2, kt + NSTAGE - 1 < ksteps, kt + 1 == ksteps);
+        if (kt + 1 < ksteps)
+            FP4Q_GEMM_STEP(kt + 1, st1, st2, st0, kt + NSTAGE < ksteps, kt + 2 == ksteps);
+        if (kt + 2 < ksteps)
+            FP4Q_GEMM_STEP(kt + 2, st2, st0, st1, kt + NSTAGE + 1 < ksteps, kt + 3 == ksteps);
     }
 #endif
 #undef FP4Q_GEMM_STEP

@@ -19,7 +19,7 @@
 //
 // HBM-streaming: ROW mirrors the ROW quantizer (lanes own 8 elements, DPP
 // amax across the block's lanes); COL mirrors the COL quantizer (lanes own 8
-// or 4 adjacent columns and walk a block of rows).
+// adjacent columns x 8 rows, DPP amax across the block's lanes).
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -146,122 +146,111 @@ __global__ __launch_bounds__(kThreads) void dge_row_kernel(const void* __restric
 }
 
 // ---------------------------------------------------------------------------
-// DGE, COL blocks: a lane owns 8 adjacent columns and one block of rows; the
-// x rows of a sub-block stay in registers as raw bits between the amax pass
-// and the gradient pass (blocks larger than a sub-block re-read x).
+// DGE, COL blocks: a lane owns 8 adjacent columns x 8 consecutive rows; the
+// block/8 lanes of one column block are adjacent and reduce the column amax
+// with DPP, as in the COL quantizer.  x stays in registers as raw bits
+// between the amax and the gradient pass.
 // ---------------------------------------------------------------------------
 template <int XB, int GB, int OB, int BLOCK>
 __global__ __launch_bounds__(kThreads) void dge_col_kernel(const void* __restrict__ x,
                                                            const void* __restrict__ g,
                                                            int64_t rows, int64_t cols,
                                                            void* __restrict__ out, DgeParams P,
-                                                           int64_t ncg, int64_t nrb) {
+                                                           int64_t ncg, int64_t nrb,
+                                                           int64_t n_cchunks) {
     constexpr int XW = XB ? 4 : 8;  // 32-bit words per 8 x values
-    constexpr int SUBMAX = XB ? 32 : 16;
-    constexpr int SUB = BLOCK < SUBMAX ? BLOCK : SUBMAX;
-    constexpr int NSUB = BLOCK / SUB;
+    constexpr int G = BLOCK / 8;
+    constexpr int CG_PER_WAVE = 64 / G;
     const int lane = threadIdx.x & 63;
-    const int64_t cg = (int64_t)blockIdx.x * 64 + lane;
-    const int64_t rb = (int64_t)blockIdx.y * (kThreads / 64) + (threadIdx.x >> 6);
-    if (cg >= ncg || rb >= nrb) return;
-    const int64_t c0 = cg * 8;
-    const bool full = ((cols & 7) == 0) && (c0 + 8 <= cols);
-    const int64_t r0 = rb * BLOCK;
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (wave >= nrb * n_cchunks) return;  // whole wave
+    const int64_t rb = wave / n_cchunks;
+    const int64_t cg = (wave - rb * n_cchunks) * CG_PER_WAVE + lane / G;
+    const int rq = lane % G;
+    const bool cg_ok = cg < ncg;
+    const int64_t c0 = (cg_ok ? cg : 0) * 8;
+    const bool full = cg_ok && ((cols & 7) == 0) && (c0 + 8 <= cols);
+    const int64_t r0 = rb * BLOCK + rq * 8;
 
-    auto ldx = [&](int64_t r, uint32_t (&w)[XW]) {
+    uint32_t xs[8][XW];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t r = r0 + i;
         if (full) {
             const uint4* q = XB ? (const uint4*)((const uint16_t*)x + r * cols + c0)
                                 : (const uint4*)((const float*)x + r * cols + c0);
             const uint4 a = q[0];
-            w[0] = a.x;
-            w[1] = a.y;
-            w[2] = a.z;
-            w[3] = a.w;
+            xs[i][0] = a.x;
+            xs[i][1] = a.y;
+            xs[i][2] = a.z;
+            xs[i][3] = a.w;
             if (!XB) {
                 const uint4 b = q[1];
-                w[4 % XW] = b.x;
-                w[5 % XW] = b.y;
-                w[6 % XW] = b.z;
-                w[7 % XW] = b.w;
+                xs[i][4 % XW] = b.x;
+                xs[i][5 % XW] = b.y;
+                xs[i][6 % XW] = b.z;
+                xs[i][7 % XW] = b.w;
             }
         } else {
             uint32_t e[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int64_t c = c0 + j;
-                e[j] = c < cols ? (XB ? (uint32_t)((const uint16_t*)x)[r * cols + c]
-                                      : ((const uint32_t*)x)[r * cols + c])
-                                : 0u;
+                e[j] = (cg_ok && c < cols) ? (XB ? (uint32_t)((const uint16_t*)x)[r * cols + c]
+                                                 : ((const uint32_t*)x)[r * cols + c])
+                                           : 0u;
             }
 #pragma unroll
-            for (int j = 0; j < XW; ++j) w[j] = XB ? (e[2 * j] | (e[2 * j + 1] << 16)) : e[j];
+            for (int j = 0; j < XW; ++j) xs[i][j] = XB ? (e[2 * j] | (e[2 * j + 1] << 16)) : e[j];
         }
-    };
-    auto xbits = [&](const uint32_t (&w)[XW], int j) -> uint32_t {
-        if (XB) return (j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16);
-        return w[j];
-    };
-    auto ldg = [&](int64_t r, float (&f)[8]) {
-        if (full) {
-            load8<GB>(g, r * cols + c0, f);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int64_t c = c0 + j;
-                f[j] = c < cols ? (GB ? bf16_lo(((const uint16_t*)g)[r * cols + c])
-                                      : ((const float*)g)[r * cols + c])
-                                : 0.0f;
-            }
-        }
-    };
-
-    uint32_t amax[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) amax[j] = 0;
-    uint32_t xs[SUB][XW];
-    for (int sb = 0; sb < NSUB; ++sb) {
-#pragma unroll
-        for (int i = 0; i < SUB; ++i) ldx(r0 + sb * SUB + i, xs[i]);
-#pragma unroll
-        for (int i = 0; i < SUB; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) amax[j] = max(amax[j], xbits(xs[i], j) & 0x7FFFFFFFu);
     }
+    auto xbits = [&](int i, int j) -> uint32_t {
+        if (XB) return (j & 1) ? (xs[i][j >> 1] & 0xFFFF0000u) : (xs[i][j >> 1] << 16);
+        return xs[i][j];
+    };
     float inv[8];
     bool nf[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        nf[j] = amax[j] >= 0x7F800000u;
-        inv[j] = e8m0_inv_scale_f32(nf[j] ? 0u : e8m0_from_amax(amax[j]));
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = max(m, xbits(i, j) & 0x7FFFFFFFu);
+        m = group_max_u32<G>(m);
+        nf[j] = m >= 0x7F800000u;
+        inv[j] = e8m0_inv_scale_f32(nf[j] ? 0u : e8m0_from_amax(m));
     }
-    for (int sb = 0; sb < NSUB; ++sb) {
-        if (NSUB > 1) {
+    if (!cg_ok) return;
 #pragma unroll
-            for (int i = 0; i < SUB; ++i) ldx(r0 + sb * SUB + i, xs[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < SUB; ++i) {
-            const int64_t r = r0 + sb * SUB + i;
-            float gf[8], o[8];
-            ldg(r, gf);
+    for (int i = 0; i < 8; ++i) {
+        const int64_t r = r0 + i;
+        float gf[8], o[8];
+        if (full) {
+            load8<GB>(g, r * cols + c0, gf);
+        } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float d =
-                    nf[j] ? __builtin_nanf("") : dge_factor(as_f32(xbits(xs[i], j)), inv[j], P);
-                o[j] = gf[j] * d;
+                const int64_t c = c0 + j;
+                gf[j] = c < cols ? (GB ? bf16_lo(((const uint16_t*)g)[r * cols + c])
+                                       : ((const float*)g)[r * cols + c])
+                                 : 0.0f;
             }
-            if (full) {
-                store8<OB>(out, r * cols + c0, o);
-            } else {
+        }
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int64_t c = c0 + j;
-                    if (c < cols) {
-                        if (OB)
-                            ((uint16_t*)out)[r * cols + c] = (uint16_t)f32_to_bf16_bits(o[j]);
-                        else
-                            ((float*)out)[r * cols + c] = o[j];
-                    }
+        for (int j = 0; j < 8; ++j) {
+            const float d = nf[j] ? __builtin_nanf("") : dge_factor(as_f32(xbits(i, j)), inv[j], P);
+            o[j] = gf[j] * d;
+        }
+        if (full) {
+            store8<OB>(out, r * cols + c0, o);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t c = c0 + j;
+                if (c < cols) {
+                    if (OB)
+                        ((uint16_t*)out)[r * cols + c] = (uint16_t)f32_to_bf16_bits(o[j]);
+                    else
+                        ((float*)out)[r * cols + c] = o[j];
                 }
             }
         }
@@ -296,12 +285,14 @@ static void dge_dispatch(const void* x, const void* g, int64_t rows, int64_t col
     } else {
         const int64_t ncg = (cols + 7) / 8;
         const int64_t nrb = rows / block;
-        dim3 grid((unsigned)((ncg + 63) / 64), (unsigned)((nrb + 3) / 4));
+        const int64_t cgw = 64 / (block / 8);
+        const int64_t ncc = (ncg + cgw - 1) / cgw;
+        dim3 grid((unsigned)((nrb * ncc + 3) / 4));
         switch (block) {
-            case 16: dge_col_kernel<XB, GB, OB, 16><<<grid, kThreads, 0, s>>>(x, g, rows, cols, out, P, ncg, nrb); break;
-            case 32: dge_col_kernel<XB, GB, OB, 32><<<grid, kThreads, 0, s>>>(x, g, rows, cols, out, P, ncg, nrb); break;
-            case 64: dge_col_kernel<XB, GB, OB, 64><<<grid, kThreads, 0, s>>>(x, g, rows, cols, out, P, ncg, nrb); break;
-            default: dge_col_kernel<XB, GB, OB, 128><<<grid, kThreads, 0, s>>>(x, g, rows, cols, out, P, ncg, nrb); break;
+            case 16: dge_col_kernel<XB, GB, OB, 16><<<grid, kThreads, 0, s>>>(x, g, rows, cols, out, P, ncg, nrb, ncc); break;
+            case 32: dge_col_kernel<XB, GB, OB, 32><<<grid, kThreads, 0, s>>>(x, g, rows, cols, out, P, ncg, nrb, ncc); break;
+            case 64: dge_col_kernel<XB, GB, OB, 64><<<grid, kThreads, 0, s>>>(x, g, rows, cols, out, P, ncg, nrb, ncc); break;
+            default: dge_col_kernel<XB, GB, OB, 128><<<grid, kThreads, 0, s>>>(x, g, rows, cols, out, P, ncg, nrb, ncc); break;
         }
     }
 }

@@ -16,10 +16,11 @@
 //    saturating), which matches the E2M1 rounding rule bit for bit; each lane
 //    writes one 32-bit word of codes, the block's first lane its scale byte.
 //  * quantize_col_kernel: blocks down the strided dim (K-major output of x^T).
-//    Each lane owns 8 (bf16) or 4 (fp32) adjacent columns and walks a block of
-//    rows with coalesced 16-byte row loads, so the column amax needs no
-//    cross-lane traffic and no LDS; it then packs row pairs of one column into
-//    bytes and writes each column's block of codes as one 8/16-byte store.
+//    Each lane owns 8 (bf16) or 4 (fp32) adjacent columns x 8 rows, read with
+//    coalesced 16-byte row loads; the block/8 lanes of one column block are
+//    adjacent, so the column amax is a lane-local max plus a DPP reduction
+//    (no LDS transpose is needed: each lane packs its rows of a column into
+//    one 32-bit code word, and the group's words are contiguous).
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -190,165 +191,147 @@ hipError_t launch_quantize_row(const void* x, int dtype, int64_t rows, int64_t c
 // ---------------------------------------------------------------------------
 // COL
 // ---------------------------------------------------------------------------
-// One lane: CPT adjacent columns (16 bytes of a row) x one block of rows,
-// processed in sub-blocks of SUB rows held in registers.  Blocks larger than
-// SUB take two passes over the rows (amax, then quantise); the second pass
-// re-reads rows the first just touched.
+// One lane: CPT adjacent columns (16 bytes of a row: 8 bf16 or 4 fp32) x 8
+// consecutive rows.  The block/8 lanes holding one block's rows are adjacent,
+// so the column amax is a lane-local max over 8 rows followed by the same DPP
+// group reduction as the ROW kernel.  Each lane packs its 8 rows of a column
+// into one 32-bit word of that column's K-major code row; the group's words
+// are contiguous.  Waves walk (row block, column chunk) pairs row-block-major
+// so neighbouring waves read neighbouring bytes.
 template <int IN_BF16, int BLOCK, int SR>
 __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
     const void* __restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t k0, uint32_t k1,
-    uint64_t rng_off, int64_t ncg, int64_t nrb, int rb_per_wave) {
-    constexpr int CPT = IN_BF16 ? 8 : 4;   // columns per lane
-    constexpr int SUB = BLOCK < 32 ? BLOCK : 32;
-    constexpr int NSUB = BLOCK / SUB;
+    uint64_t rng_off, int64_t ncg, int64_t nrb, int64_t n_cchunks) {
+    constexpr int CPT = IN_BF16 ? 8 : 4;  // columns per lane
+    constexpr int G = BLOCK / 8;          // lanes per block
+    constexpr int CG_PER_WAVE = 64 / G;
     const int lane = threadIdx.x & 63;
-    const int64_t cg = (int64_t)blockIdx.x * 64 + lane;
-    const int64_t rb0 = ((int64_t)blockIdx.y * (kThreads / 64) + (threadIdx.x >> 6)) * rb_per_wave;
-    if (cg >= ncg) return;
-    const int64_t c0 = cg * CPT;
-    const bool full = (c0 + CPT) <= cols;
-    const int64_t half_rows = rows / 2;
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (wave >= nrb * n_cchunks) return;  // whole wave: no DPP partner is lost
+    const int64_t rb = wave / n_cchunks;
+    const int64_t cg = (wave - rb * n_cchunks) * CG_PER_WAVE + lane / G;
+    const int rq = lane % G;
+    const bool cg_ok = cg < ncg;
+    const int64_t c0 = (cg_ok ? cg : 0) * CPT;
+    const bool full = cg_ok && (c0 + CPT) <= cols;
+    const int64_t r0 = rb * BLOCK + rq * 8;
 
-    auto load_row = [&](int64_t r, uint32_t (&v)[4]) {
+    // 8 rows x 16 bytes
+    uint32_t v[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t r = r0 + i;
         if (full) {
             const uint4 t = IN_BF16 ? *(const uint4*)((const uint16_t*)xv + r * ld + c0)
                                     : *(const uint4*)((const float*)xv + r * ld + c0);
-            v[0] = t.x;
-            v[1] = t.y;
-            v[2] = t.z;
-            v[3] = t.w;
+            v[i][0] = t.x;
+            v[i][1] = t.y;
+            v[i][2] = t.z;
+            v[i][3] = t.w;
+        } else if (IN_BF16) {
+            const uint16_t* x = (const uint16_t*)xv + r * ld;
+            uint32_t e[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) e[j] = (cg_ok && c0 + j < cols) ? x[c0 + j] : 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[i][j] = e[2 * j] | (e[2 * j + 1] << 16);
         } else {
-            if (IN_BF16) {
-                const uint16_t* x = (const uint16_t*)xv + r * ld;
-                uint32_t e[8];
+            const uint32_t* x = (const uint32_t*)xv + r * ld;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) e[j] = (c0 + j < cols) ? x[c0 + j] : 0u;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = e[2 * j] | (e[2 * j + 1] << 16);
-            } else {
-                const uint32_t* x = (const uint32_t*)xv + r * ld;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = (c0 + j < cols) ? x[c0 + j] : 0u;
-            }
+            for (int j = 0; j < 4; ++j) v[i][j] = (cg_ok && c0 + j < cols) ? x[c0 + j] : 0u;
         }
-    };
-    // fp32 bits of column j of a loaded row
-    auto col_bits = [&](const uint32_t (&v)[4], int j) -> uint32_t {
-        if (IN_BF16) return (j & 1) ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16);
-        return v[j];
+    }
+    // fp32 bits of column j of row i
+    auto col_bits = [&](int i, int j) -> uint32_t {
+        if (IN_BF16) return (j & 1) ? (v[i][j >> 1] & 0xFFFF0000u) : (v[i][j >> 1] << 16);
+        return v[i][j];
     };
 
-    for (int it = 0; it < rb_per_wave; ++it) {
-        const int64_t rb = rb0 + it;
-        if (rb >= nrb) break;
-        const int64_t r0 = rb * BLOCK;
-        uint32_t amax[CPT];
+    uint32_t amax[CPT];
+    if (IN_BF16) {
+        // packed 16-bit maxima of column pairs, reduced across the group
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) amax[j] = 0;
-        uint32_t v[SUB][4];
-        if (NSUB > 1) {
-            for (int sb = 0; sb < NSUB; ++sb) {
+        for (int p = 0; p < 4; ++p) {
+            u16x2_t m = __builtin_bit_cast(u16x2_t, v[0][p] & 0x7FFF7FFFu);
 #pragma unroll
-                for (int i = 0; i < SUB; ++i) load_row(r0 + sb * SUB + i, v[i]);
-#pragma unroll
-                for (int i = 0; i < SUB; ++i)
-#pragma unroll
-                    for (int j = 0; j < CPT; ++j)
-                        amax[j] = max(amax[j], col_bits(v[i], j) & 0x7FFFFFFFu);
-            }
+            for (int i = 1; i < 8; ++i)
+                m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, v[i][p] & 0x7FFF7FFFu));
+            uint32_t w = __builtin_bit_cast(uint32_t, m);
+            // a 16-bit-lane max across the group: both halves are non-negative
+            // 15-bit magnitudes, so a 32-bit max of each half works separately
+            uint32_t lo = group_max_u32<G>(w & 0xFFFFu);
+            uint32_t hi = group_max_u32<G>(w >> 16);
+            amax[2 * p] = lo << 16;
+            amax[2 * p + 1] = hi << 16;
         }
-        for (int sb = 0; sb < NSUB; ++sb) {
-            const int64_t rs = r0 + sb * SUB;
-#pragma unroll
-            for (int i = 0; i < SUB; ++i) load_row(rs + i, v[i]);
-            if (NSUB == 1) {
-#pragma unroll
-                for (int i = 0; i < SUB; ++i)
-#pragma unroll
-                    for (int j = 0; j < CPT; ++j)
-                        amax[j] = max(amax[j], col_bits(v[i], j) & 0x7FFFFFFFu);
-            }
-            uint32_t out[CPT][SUB / 8];
-#pragma unroll
-            for (int j = 0; j < CPT; ++j)
-#pragma unroll
-                for (int q = 0; q < SUB / 8; ++q) out[j][q] = 0;
-            if (!SR) {
-#pragma unroll
-                for (int j = 0; j < CPT; ++j) {
-                    const bool nf = amax[j] >= 0x7F800000u;
-                    const float sc = e8m0_scale_f32(nf ? 0xFFu : e8m0_from_amax(amax[j]));
-#pragma unroll
-                    for (int p = 0; p < SUB / 2; ++p) {
-                        uint32_t& dst = out[j][p / 4];
-                        if (IN_BF16) {
-                            const uint32_t a = col_bits(v[2 * p], j) >> 16;
-                            const uint32_t b = col_bits(v[2 * p + 1], j) & 0xFFFF0000u;
-                            const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, a | b);
-                            switch (p & 3) {
-                                case 0: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(dst, pr, sc, 0); break;
-                                case 1: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(dst, pr, sc, 1); break;
-                                case 2: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(dst, pr, sc, 2); break;
-                                default: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(dst, pr, sc, 3); break;
-                            }
-                        } else {
-                            const float a = as_f32(col_bits(v[2 * p], j));
-                            const float b = as_f32(col_bits(v[2 * p + 1], j));
-                            switch (p & 3) {
-                                case 0: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dst, a, b, sc, 0); break;
-                                case 1: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dst, a, b, sc, 1); break;
-                                case 2: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dst, a, b, sc, 2); break;
-                                default: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dst, a, b, sc, 3); break;
-                            }
-                        }
-                    }
-                }
-            } else {
-                float inv[CPT];
-#pragma unroll
-                for (int j = 0; j < CPT; ++j) {
-                    const bool nf = amax[j] >= 0x7F800000u;
-                    inv[j] = e8m0_inv_scale_f32(nf ? 0u : e8m0_from_amax(amax[j]));
-                }
-#pragma unroll
-                for (int i = 0; i < SUB; ++i) {
-                    uint32_t rnd[8];
-                    const uint64_t p0 = (uint64_t)(rs + i) * (uint64_t)cols + (uint64_t)c0 + rng_off;
-                    sr_bits8(p0, k0, k1, rnd);
-#pragma unroll
-                    for (int j = 0; j < CPT; ++j) {
-                        const uint32_t code = sr_code(as_f32(col_bits(v[i], j)), inv[j], rnd[j]);
-                        out[j][i / 8] |= code << (4 * (i & 7));
-                    }
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                if (c0 + j >= cols) break;
-                const bool nf = amax[j] >= 0x7F800000u;
-                uint8_t* dst = codes + (c0 + j) * half_rows + rs / 2;
-                if (SUB == 32) {
-                    uint4 t;
-                    t.x = nf ? 0u : out[j][0];
-                    t.y = nf ? 0u : out[j][1 % (SUB / 8)];
-                    t.z = nf ? 0u : out[j][2 % (SUB / 8)];
-                    t.w = nf ? 0u : out[j][3 % (SUB / 8)];
-                    *(uint4*)dst = t;
-                } else {
-                    uint2 t;
-                    t.x = nf ? 0u : out[j][0];
-                    t.y = nf ? 0u : out[j][1 % (SUB / 8)];
-                    *(uint2*)dst = t;
-                }
-            }
-        }
+    } else {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            if (c0 + j >= cols) break;
-            const bool nf = amax[j] >= 0x7F800000u;
-            scales[(c0 + j) * nrb + rb] = (uint8_t)(nf ? 0xFFu : e8m0_from_amax(amax[j]));
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = max(m, v[i][j] & 0x7FFFFFFFu);
+            amax[j] = group_max_u32<G>(m);
         }
+    }
+
+    uint32_t out[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) out[j] = 0;
+    if (!SR) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const bool nf = amax[j] >= 0x7F800000u;
+            const float sc = e8m0_scale_f32(nf ? 0xFFu : e8m0_from_amax(amax[j]));
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                if (IN_BF16) {
+                    const uint32_t a = col_bits(2 * p, j) >> 16;
+                    const uint32_t b = col_bits(2 * p + 1, j) & 0xFFFF0000u;
+                    const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, a | b);
+                    switch (p) {
+                        case 0: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out[j], pr, sc, 0); break;
+                        case 1: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out[j], pr, sc, 1); break;
+                        case 2: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out[j], pr, sc, 2); break;
+                        default: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out[j], pr, sc, 3); break;
+                    }
+                } else {
+                    const float a = as_f32(col_bits(2 * p, j));
+                    const float b = as_f32(col_bits(2 * p + 1, j));
+                    switch (p) {
+                        case 0: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j], a, b, sc, 0); break;
+                        case 1: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j], a, b, sc, 1); break;
+                        case 2: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j], a, b, sc, 2); break;
+                        default: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j], a, b, sc, 3); break;
+                    }
+                }
+            }
+        }
+    } else {
+        float inv[CPT];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const bool nf = amax[j] >= 0x7F800000u;
+            inv[j] = e8m0_inv_scale_f32(nf ? 0u : e8m0_from_amax(amax[j]));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t rnd[8];
+            const uint64_t p0 = (uint64_t)(r0 + i) * (uint64_t)cols + (uint64_t)c0 + rng_off;
+            sr_bits8(p0, k0, k1, rnd);
+#pragma unroll
+            for (int j = 0; j < CPT; ++j)
+                out[j] |= sr_code(as_f32(col_bits(i, j)), inv[j], rnd[j]) << (4 * i);
+        }
+    }
+    if (!cg_ok) return;
+    const int64_t half_rows = rows / 2;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        if (c0 + j >= cols) break;
+        const bool nf = amax[j] >= 0x7F800000u;
+        *(uint32_t*)(codes + (c0 + j) * half_rows + r0 / 2) = nf ? 0u : out[j];
+        if (rq == 0) scales[(c0 + j) * nrb + rb] = (uint8_t)(nf ? 0xFFu : e8m0_from_amax(amax[j]));
     }
 }
 
@@ -356,23 +339,23 @@ template <int IN_BF16, int SR>
 static hipError_t col_dispatch(int block, dim3 grid, hipStream_t s, const void* x, int64_t rows,
                                int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
                                uint32_t k0, uint32_t k1, uint64_t off, int64_t ncg, int64_t nrb,
-                               int rbw) {
+                               int64_t ncc) {
     switch (block) {
         case 16:
             quantize_col_kernel<IN_BF16, 16, SR><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, ncg, nrb, rbw);
+                x, rows, cols, ld, codes, scales, k0, k1, off, ncg, nrb, ncc);
             break;
         case 32:
             quantize_col_kernel<IN_BF16, 32, SR><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, ncg, nrb, rbw);
+                x, rows, cols, ld, codes, scales, k0, k1, off, ncg, nrb, ncc);
             break;
         case 64:
             quantize_col_kernel<IN_BF16, 64, SR><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, ncg, nrb, rbw);
+                x, rows, cols, ld, codes, scales, k0, k1, off, ncg, nrb, ncc);
             break;
         default:
             quantize_col_kernel<IN_BF16, 128, SR><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, ncg, nrb, rbw);
+                x, rows, cols, ld, codes, scales, k0, k1, off, ncg, nrb, ncc);
             break;
     }
     return hipGetLastError();
@@ -384,23 +367,20 @@ hipError_t launch_quantize_col(const void* x, int dtype, int64_t rows, int64_t c
     const int cpt = dtype == BF16 ? 8 : 4;
     const int64_t ncg = (cols + cpt - 1) / cpt;
     const int64_t nrb = rows / block;
-    // Enough waves to fill the chip (a few per SIMD), then more row blocks per
-    // wave so each lane writes longer runs of every code row.
-    const int64_t col_wgs = (ncg + 63) / 64;
-    int rbw = 1;
-    while (rbw < 8 && col_wgs * ((nrb + 4 * rbw * 2 - 1) / (4 * rbw * 2)) * 4 >= 8192) rbw *= 2;
-    const int64_t wgs_y = (nrb + 4 * rbw - 1) / (4 * rbw);
-    dim3 grid((unsigned)col_wgs, (unsigned)wgs_y);
+    const int64_t cg_per_wave = 64 / (block / 8);
+    const int64_t ncc = (ncg + cg_per_wave - 1) / cg_per_wave;
+    const int64_t waves = nrb * ncc;
+    dim3 grid((unsigned)((waves + 3) / 4));
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     if (dtype == BF16)
         return sr ? col_dispatch<1, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1,
-                                       off, ncg, nrb, rbw)
+                                       off, ncg, nrb, ncc)
                   : col_dispatch<1, 0>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1,
-                                       off, ncg, nrb, rbw);
+                                       off, ncg, nrb, ncc);
     return sr ? col_dispatch<0, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1, off,
-                                   ncg, nrb, rbw)
+                                   ncg, nrb, ncc)
               : col_dispatch<0, 0>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1, off,
-                                   ncg, nrb, rbw);
+                                   ncg, nrb, ncc);
 }
 
 }  // namespace fp4q
