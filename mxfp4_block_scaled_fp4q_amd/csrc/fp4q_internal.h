@@ -42,6 +42,10 @@ hipError_t launch_dge(const void* x, int xdtype, const void* g, int gdtype, int6
 hipError_t launch_gemm_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
                            const uint8_t* as, const uint8_t* bc, const uint8_t* bs, void* c,
                            int cdtype, int64_t ldc, bool accumulate, hipStream_t s);
+// C[M,N] (fp32, row stride ldc) += A B^T for bf16 A [M,K], B [N,K] (K % 32 == 0),
+// on the FP4 GEMM's pipeline with bf16 MFMAs.
+hipError_t launch_gemm_bf16_accum(int64_t M, int64_t N, int64_t K, const uint16_t* a,
+                                  const uint16_t* b, float* c, int64_t ldc, hipStream_t s);
 size_t hcp_workspace_bytes(int64_t M, int64_t N, int32_t n_hot);
 hipError_t launch_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
                       const uint8_t* xqs, const void* w, const uint8_t* wqc, const uint8_t* wqs,

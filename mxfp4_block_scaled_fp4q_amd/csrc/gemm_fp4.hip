@@ -37,6 +37,9 @@ namespace fp4q {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// Native 4 x 32-bit vectors (HIP's uint4 is a class with unions, which the
+// compiler does not always split into registers).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 static constexpr int BM = 256, BN = 256;
 static constexpr int BKB = 64;  // K bytes per step (128 fp4 elements)
@@ -50,7 +53,11 @@ static constexpr int OFF_B = 16 * FRAG;         // B fragments within a stage
 static constexpr int OFF_SA = 32 * FRAG;        // A scale words (256 x 4 B)
 static constexpr int OFF_SB = 32 * FRAG + 1024; // B scale words
 static constexpr int STAGE = 32 * FRAG + 2048;
-static constexpr int LOADS_PER_STEP = 10;       // per wave: 8 fragments + 2 scale rows
+// per wave and K step: 8 fragment loads, plus 2 scale-row loads for FP4
+template <int BF16OPS>
+struct StepLoads {
+    static constexpr int n = BF16OPS ? 8 : 10;
+};
 static constexpr int GROUP_M = 4;
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -64,7 +71,46 @@ struct StepSrc {
     const uint8_t* gsb;
 };
 
-// Issue the 10 direct-to-LDS loads of K step kt of this wave into `stage`.
+#ifndef FP4Q_GEMM_DMA
+#define FP4Q_GEMM_DMA 0
+#endif
+
+// Register staging of one K step's operands (used when the loads go
+// global -> VGPR -> LDS instead of straight into LDS).
+struct StepRegs {
+    u32x4 a[4], b[4];
+    uint32_t sa, sb;
+};
+
+template <int BF16OPS>
+__device__ __forceinline__ void load_step(const StepSrc& src, int kt, StepRegs& R) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        R.a[q] = *(const u32x4*)(src.ga[q] + (int64_t)kt * BKB);
+        R.b[q] = *(const u32x4*)(src.gb[q] + (int64_t)kt * BKB);
+    }
+    if (!BF16OPS) {
+        R.sa = *(const uint32_t*)(src.gsa + kt * 4);
+        R.sb = *(const uint32_t*)(src.gsb + kt * 4);
+    }
+}
+
+template <int BF16OPS>
+__device__ __forceinline__ void store_step(const StepRegs& R, uint8_t* stage, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int f = wave * 4 + q;
+        *(u32x4*)(stage + f * FRAG + lane * 16) = R.a[q];
+        *(u32x4*)(stage + OFF_B + f * FRAG + lane * 16) = R.b[q];
+    }
+    if (!BF16OPS) {
+        *(uint32_t*)(stage + OFF_SA + wave * 256 + lane * 4) = R.sa;
+        *(uint32_t*)(stage + OFF_SB + wave * 256 + lane * 4) = R.sb;
+    }
+}
+
+// Issue the direct-to-LDS loads of K step kt of this wave into `stage`.
+template <int BF16OPS>
 __device__ __forceinline__ void issue_step(const StepSrc& src, int kt, uint8_t* stage, int wave) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -74,14 +120,16 @@ __device__ __forceinline__ void issue_step(const StepSrc& src, int kt, uint8_t* 
         __builtin_amdgcn_global_load_lds((const void*)(src.gb[q] + (int64_t)kt * BKB),
                                          (lds_ptr_t)(stage + OFF_B + f * FRAG), 16, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds((const void*)(src.gsa + kt * 4),
-                                     (lds_ptr_t)(stage + OFF_SA + wave * 256), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(src.gsb + kt * 4),
-                                     (lds_ptr_t)(stage + OFF_SB + wave * 256), 4, 0, 0);
+    if (!BF16OPS) {
+        __builtin_amdgcn_global_load_lds((const void*)(src.gsa + kt * 4),
+                                         (lds_ptr_t)(stage + OFF_SA + wave * 256), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(src.gsb + kt * 4),
+                                         (lds_ptr_t)(stage + OFF_SB + wave * 256), 4, 0, 0);
+    }
 }
 
 struct Frags {
-    uint4 a[4], b[4];
+    u32x4 a[4], b[4];
 };
 
 // This wave's A and B fragments of half kk (K bytes kk*32 .. kk*32+31) of a
@@ -90,8 +138,8 @@ __device__ __forceinline__ void read_frags(const uint8_t* base, int kk, int wm, 
                                            Frags& F) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        F.a[i] = *(const uint4*)(base + ((wm * 4 + i) * 2 + kk) * FRAG + lane * 16);
-        F.b[i] = *(const uint4*)(base + OFF_B + ((wn * 4 + i) * 2 + kk) * FRAG + lane * 16);
+        F.a[i] = *(const u32x4*)(base + ((wm * 4 + i) * 2 + kk) * FRAG + lane * 16);
+        F.b[i] = *(const u32x4*)(base + OFF_B + ((wn * 4 + i) * 2 + kk) * FRAG + lane * 16);
     }
 }
 
@@ -108,9 +156,28 @@ __device__ __forceinline__ void read_scales(const uint8_t* base, int wm, int wn,
     }
 }
 
-// 16 MFMAs: the 4 x 4 tiles of this wave on half kk of a K step.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// 16 MFMAs: the 4 x 4 tiles of this wave on half kk of a K step.  FP4: the
+// scaled MFMA on E2M1 operands (64 K elements per half); BF16: plain bf16
+// MFMAs (16 K elements per half, the same 16 bytes per lane).
+template <int BF16OPS>
 __device__ __forceinline__ void mfma_half(const Frags& F, const uint32_t (&sa)[4],
                                           const uint32_t (&sb)[4], int kk, v16f (&acc)[4][4]) {
+    if (BF16OPS) {
+        bf16x8_t ha[4], hb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ha[i] = __builtin_bit_cast(bf16x8_t, F.a[i]);
+            hb[i] = __builtin_bit_cast(bf16x8_t, F.b[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[i], hb[j], acc[i][j], 0, 0, 0);
+        return;
+    }
     v8i fa[4], fb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -126,7 +193,7 @@ __device__ __forceinline__ void mfma_half(const Frags& F, const uint32_t (&sa)[4
                 (int)(sb[j] >> (16 * kk)));
 }
 
-template <int OUT_BF16, int ACCUM>
+template <int OUT_BF16, int ACCUM, int BF16OPS>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(
     int M, int N, int K, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, void* __restrict__ cptr,
@@ -162,9 +229,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(
     const int wm = wave >> 1, wn = wave & 1;
     const int half = lane >> 5;
     const int l32 = lane & 31;
-    const int64_t kbytes = K / 2;
+    // bytes per operand row; each K step consumes 64 of them
+    const int64_t kbytes = BF16OPS ? (int64_t)K * 2 : K / 2;
     const int kscale = K / 32;
-    const int ksteps = K / 128;
+    const int ksteps = (int)(kbytes / BKB);
+    constexpr int LOADS_PER_STEP = StepLoads<BF16OPS>::n;
 
     // Global sources of this lane's loads.  Fragment f = rg*2 + kk holds rows
     // rg*32 .. rg*32+31 and K bytes kk*32 .. kk*32+31 of the step; wave w
@@ -181,8 +250,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(
         src.ga[q] = ac + (int64_t)ra * kbytes + kk * 32 + half * 16;
         src.gb[q] = bc + (int64_t)rb * kbytes + kk * 32 + half * 16;
     }
-    src.gsa = as + (int64_t)min(m0 + wave * 64 + lane, M - 1) * kscale;
-    src.gsb = bs + (int64_t)min(n0 + wave * 64 + lane, N - 1) * kscale;
+    src.gsa = BF16OPS ? nullptr : as + (int64_t)min(m0 + wave * 64 + lane, M - 1) * kscale;
+    src.gsb = BF16OPS ? nullptr : bs + (int64_t)min(n0 + wave * 64 + lane, N - 1) * kscale;
 
     v16f acc[4][4];
 #pragma unroll
@@ -199,10 +268,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(
     // read while the MFMAs of (t, 1) run.  The barrier follows an lgkmcnt(0)
     // wait, so every wave has finished reading stage t before anyone refills
     // it (at step t+1).
+#if FP4Q_GEMM_DMA
 #pragma unroll
     for (int s = 0; s < NSTAGE - 1; ++s) {
         uint8_t* stg = s == 0 ? st0 : s == 1 ? st1 : st2;
-        if (s < ksteps) issue_step(src, s, stg, wave);
+        if (s < ksteps) issue_step<BF16OPS>(src, s, stg, wave);
     }
     if (ksteps >= NSTAGE - 1) {
         FP4Q_WAIT_VMCNT(LOADS_PER_STEP * (NSTAGE - 2));
@@ -211,8 +281,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(
     }
     __builtin_amdgcn_s_barrier();
     Frags FA, FB;
-    uint32_t sa[4], sb[4], sa_n[4], sb_n[4];
-    read_scales(st0, wm, wn, lane, sa, sb);
+    uint32_t sa[4] = {0, 0, 0, 0}, sb[4] = {0, 0, 0, 0}, sa_n[4] = {0, 0, 0, 0},
+             sb_n[4] = {0, 0, 0, 0};
+    if (!BF16OPS) read_scales(st0, wm, wn, lane, sa, sb);
     read_frags(st0, 0, wm, wn, lane, FA);
 
 // One K step.  ISSUE: whether step t+NSTAGE-1 exists (its loads are issued
@@ -223,8 +294,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(
 #define FP4Q_GEMM_STEP(t, CUR, NEXT1, NEXTL, ISSUE, LAST)                          \
     do {                                                                           \
         read_frags(CUR, 1, wm, wn, lane, FB);                                      \
-        if (ISSUE) issue_step(src, (t) + NSTAGE - 1, NEXTL, wave);                  \
-        mfma_half(FA, sa, sb, 0, acc);                                             \
+        if (ISSUE) issue_step<BF16OPS>(src, (t) + NSTAGE - 1, NEXTL, wave);         \
+        mfma_half<BF16OPS>(FA, sa, sb, 0, acc);                                    \
         __builtin_amdgcn_sched_barrier(0);                                         \
         if (ISSUE) {                                                               \
             __builtin_amdgcn_s_waitcnt(((LOADS_PER_STEP * (NSTAGE - 2)) & 0xF) |     \
@@ -235,10 +306,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(
         __builtin_amdgcn_s_barrier();                                              \
         __builtin_amdgcn_sched_barrier(0);                                         \
         if (!(LAST)) {                                                             \
-            read_scales(NEXT1, wm, wn, lane, sa_n, sb_n);                          \
+            if (!BF16OPS) read_scales(NEXT1, wm, wn, lane, sa_n, sb_n);            \
             read_frags(NEXT1, 0, wm, wn, lane, FA);                                \
         }                                                                          \
-        mfma_half(FB, sa, sb, 1, acc);                                             \
+        mfma_half<BF16OPS>(FB, sa, sb, 1, acc);                                    \
         _Pragma("unroll") for (int q = 0; q < 4; ++q) {                            \
             sa[q] = sa_n[q];                                                       \
             sb[q] = sb_n[q];                                                       \
@@ -277,6 +348,59 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp4_kernel(
             FP4Q_GEMM_STEP(kt + 1, st1, st2, st0, kt + NSTAGE < ksteps, kt + 2 == ksteps);
         if (kt + 2 < ksteps)
             FP4Q_GEMM_STEP(kt + 2, st2, st0, st1, kt + NSTAGE + 1 < ksteps, kt + 3 == ksteps);
+    }
+#endif
+#else
+    // Register-staged pipeline: the loads of step t+3 are issued during
+    // step t into registers and written to their LDS stage during step t+1,
+    // so each load has a full step to arrive; the compiler tracks the
+    // register dependencies (no LDS-DMA aliasing to reason about).
+    StepRegs R;
+    load_step<BF16OPS>(src, 0, R);
+    store_step<BF16OPS>(R, st0, wave, lane);
+    if (ksteps > 1) {
+        load_step<BF16OPS>(src, 1, R);
+        store_step<BF16OPS>(R, st1, wave, lane);
+    }
+    if (ksteps > 2) load_step<BF16OPS>(src, 2, R);
+    __syncthreads();
+    Frags FA, FB;
+    uint32_t sa[4] = {0, 0, 0, 0}, sb[4] = {0, 0, 0, 0}, sa_n[4] = {0, 0, 0, 0},
+             sb_n[4] = {0, 0, 0, 0};
+    if (!BF16OPS) read_scales(st0, wm, wn, lane, sa, sb);
+    read_frags(st0, 0, wm, wn, lane, FA);
+
+#define FP4Q_GEMM_STEP(t, CUR, NEXT1, NEXTL, ISSUE, LAST)                          \
+    do {                                                                           \
+        read_frags(CUR, 1, wm, wn, lane, FB);                                      \
+        mfma_half<BF16OPS>(FA, sa, sb, 0, acc);                                    \
+        if ((t) + 2 < ksteps) store_step<BF16OPS>(R, NEXTL, wave, lane);           \
+        if ((t) + 3 < ksteps) load_step<BF16OPS>(src, (t) + 3, R);                 \
+        __builtin_amdgcn_sched_barrier(0);                                         \
+        __builtin_amdgcn_s_waitcnt(0xC07F);                                        \
+        __builtin_amdgcn_s_barrier();                                              \
+        __builtin_amdgcn_sched_barrier(0);                                         \
+        if (!(LAST)) {                                                             \
+            if (!BF16OPS) read_scales(NEXT1, wm, wn, lane, sa_n, sb_n);            \
+            read_frags(NEXT1, 0, wm, wn, lane, FA);                                \
+        }                                                                          \
+        mfma_half<BF16OPS>(FB, sa, sb, 1, acc);                                    \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                            \
+            sa[q] = sa_n[q];                                                       \
+            sb[q] = sb_n[q];                                                       \
+        }                                                                          \
+    } while (0)
+
+    int kt = 0;
+    for (; kt + 2 + 3 < ksteps; kt += 3) {
+        FP4Q_GEMM_STEP(kt, st0, st1, st2, true, false);
+        FP4Q_GEMM_STEP(kt + 1, st1, st2, st0, true, false);
+        FP4Q_GEMM_STEP(kt + 2, st2, st0, st1, true, false);
+    }
+    for (; kt < ksteps; kt += 3) {
+        FP4Q_GEMM_STEP(kt, st0, st1, st2, true, kt + 1 == ksteps);
+        if (kt + 1 < ksteps) FP4Q_GEMM_STEP(kt + 1, st1, st2, st0, true, kt + 2 == ksteps);
+        if (kt + 2 < ksteps) FP4Q_GEMM_STEP(kt + 2, st2, st0, st1, true, kt + 3 == ksteps);
     }
 #endif
 #undef FP4Q_GEMM_STEP
@@ -359,16 +483,26 @@ hipError_t launch_gemm_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
     dim3 grid((unsigned)(tiles_m * tiles_n));
-    const size_t shmem = 0;
     if (cdtype == BF16)
-        gemm_fp4_kernel<1, 0><<<grid, kThreads, shmem, s>>>((int)M, (int)N, (int)K, ac, as, bc, bs,
-                                                            c, ldc, tiles_m, tiles_n);
+        gemm_fp4_kernel<1, 0, 0><<<grid, kThreads, 0, s>>>((int)M, (int)N, (int)K, ac, as, bc, bs,
+                                                           c, ldc, tiles_m, tiles_n);
     else if (accumulate)
-        gemm_fp4_kernel<0, 1><<<grid, kThreads, shmem, s>>>((int)M, (int)N, (int)K, ac, as, bc, bs,
-                                                            c, ldc, tiles_m, tiles_n);
+        gemm_fp4_kernel<0, 1, 0><<<grid, kThreads, 0, s>>>((int)M, (int)N, (int)K, ac, as, bc, bs,
+                                                           c, ldc, tiles_m, tiles_n);
     else
-        gemm_fp4_kernel<0, 0><<<grid, kThreads, shmem, s>>>((int)M, (int)N, (int)K, ac, as, bc, bs,
-                                                            c, ldc, tiles_m, tiles_n);
+        gemm_fp4_kernel<0, 0, 0><<<grid, kThreads, 0, s>>>((int)M, (int)N, (int)K, ac, as, bc, bs,
+                                                           c, ldc, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_accum(int64_t M, int64_t N, int64_t K, const uint16_t* a,
+                                  const uint16_t* b, float* c, int64_t ldc, hipStream_t s) {
+    const int tiles_m = (int)((M + BM - 1) / BM);
+    const int tiles_n = (int)((N + BN - 1) / BN);
+    dim3 grid((unsigned)(tiles_m * tiles_n));
+    gemm_fp4_kernel<0, 1, 1><<<grid, kThreads, 0, s>>>((int)M, (int)N, (int)K, (const uint8_t*)a,
+                                                       nullptr, (const uint8_t*)b, nullptr, c, ldc,
+                                                       tiles_m, tiles_n);
     return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@
 //
 // which swaps, on H only, the FP4 operands' product for the bf16 operands'
 // product (every error term of both operands on those channels).  It runs as
-// one bf16 GEMM of depth K' = 2|H| (padded to 64):
+// one bf16 GEMM of depth K' = 2|H| (padded to 32):
 //   A' = [X_H | Xq_H]    [M, K']   (gathered, dequantised)
 //   B' = [W_H ; -Wq_H]^T [N, K']   (gathered, K-major)
 // with fp32 accumulation, added into the fp32 Y in the epilogue.  The hot
@@ -23,10 +23,10 @@
 //  * hcp_gather_x: one lane = 8 consecutive K' slots of one row of A'.
 //  * hcp_gather_w: one lane = one column j and 8 consecutive K' slots; lanes
 //    of a wave take consecutive j, so the reads of W's hot rows coalesce.
-//  * hcp_gemm_bf16: the FP4 GEMM's structure (256 x 256 workgroup tile, four
-//    128 x 128 waves, LDS in MFMA fragment order, double-buffered) on
-//    v_mfma_f32_32x32x16_bf16; lane l supplies row l % 32, K elements
-//    [8 (l / 32), 8 (l / 32) + 8).
+//  * the residual GEMM runs on the FP4 GEMM's kernel instantiated for bf16
+//    operands (v_mfma_f32_32x32x16_bf16: lane l supplies row l % 32, K
+//    elements [8 (l / 32), 8 (l / 32) + 8) -- the same 16 bytes per lane as
+//    an FP4 fragment), adding into the fp32 Y in its epilogue.
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -49,7 +49,7 @@ __device__ __forceinline__ float deq_nibble(const uint8_t* codes_row, const uint
 
 static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-static int64_t padded_k(int32_t n_hot) { return (int64_t)round_up((size_t)(2 * n_hot), 64); }
+static int64_t padded_k(int32_t n_hot) { return (int64_t)round_up((size_t)(2 * n_hot), 32); }
 
 size_t hcp_workspace_bytes(int64_t M, int64_t N, int32_t n_hot) {
     if (n_hot <= 0) return 0;
@@ -120,118 +120,6 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_w(const uint16_t* __restr
     *(uint4*)(b + j * kp + h0) = o;
 }
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-
-static constexpr int BM = 256, BN = 256;
-static constexpr int BKE = 64;   // K elements per step
-static constexpr int FRAG = 1024;
-static constexpr int NFRAG = 8 * (BKE / 16);  // fragments per operand per stage (32)
-static constexpr int STAGE = 2 * NFRAG * FRAG;
-
-__global__ __launch_bounds__(kThreads, 1) void hcp_gemm_bf16(int M, int N, int kp,
-                                                             const uint16_t* __restrict__ a,
-                                                             const uint16_t* __restrict__ b,
-                                                             float* __restrict__ y, int tiles_m,
-                                                             int tiles_n) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int nwg = gridDim.x;
-    int wg = blockIdx.x;
-    {
-        const int full = (nwg / 8) * 8;
-        if (wg < full) wg = (wg % 8) * (full / 8) + wg / 8;
-    }
-    const int per_group = 4 * tiles_n;
-    const int grp = wg / per_group;
-    const int first_m = grp * 4;
-    const int gsize = min(4, tiles_m - first_m);
-    const int in_grp = wg - grp * per_group;
-    const int tm = first_m + in_grp % gsize;
-    const int tn = in_grp / gsize;
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int half = lane >> 5, l32 = lane & 31;
-    const int ksteps = kp / BKE;
-
-    // wave w loads fragments f = 8w .. 8w+7 of each operand, f = rg*4 + kk
-    const uint16_t* ga[8];
-    const uint16_t* gb[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int f = wave * 8 + q;
-        const int rg = f >> 2, kk = f & 3;
-        const int ra = min(m0 + rg * 32 + l32, M - 1);
-        const int rb = min(n0 + rg * 32 + l32, N - 1);
-        ga[q] = a + (int64_t)ra * kp + kk * 16 + half * 8;
-        gb[q] = b + (int64_t)rb * kp + kk * 16 + half * 8;
-    }
-    v16f acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    uint4 pa[8], pb[8];
-    auto gload = [&](int kt) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            pa[q] = *(const uint4*)(ga[q] + (int64_t)kt * BKE);
-            pb[q] = *(const uint4*)(gb[q] + (int64_t)kt * BKE);
-        }
-    };
-    auto lds_store = [&](int buf) {
-        uint8_t* base = lds + buf * STAGE;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int f = wave * 8 + q;
-            *(uint4*)(base + f * FRAG + lane * 16) = pa[q];
-            *(uint4*)(base + NFRAG * FRAG + f * FRAG + lane * 16) = pb[q];
-        }
-    };
-    gload(0);
-    lds_store(0);
-    __syncthreads();
-    for (int kt = 0; kt < ksteps; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < ksteps;
-        if (more) gload(kt + 1);
-        const uint8_t* base = lds + buf * STAGE;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            bf16x8_t fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                fa[i] = *(const bf16x8_t*)(base + ((wm * 4 + i) * 4 + kk) * FRAG + lane * 16);
-                fb[i] = *(const bf16x8_t*)(base + NFRAG * FRAG + ((wn * 4 + i) * 4 + kk) * FRAG +
-                                           lane * 16);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-        if (more) lds_store(buf ^ 1);
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn * 128 + j * 32 + l32;
-            if (col >= N) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (row < M) y[(int64_t)row * N + col] += acc[i][j][r];
-            }
-        }
-}
-
 hipError_t launch_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
                       const uint8_t* xqs, const void* w, const uint8_t* wqc, const uint8_t* wqs,
                       const int32_t* hot, int32_t n_hot, float* y, void* ws, hipStream_t s) {
@@ -252,14 +140,7 @@ hipError_t launch_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    // Per call: the attribute is per device and the call is cheap.
-    e = hipFuncSetAttribute((const void*)hcp_gemm_bf16,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE);
-    if (e != hipSuccess) return e;
-    hcp_gemm_bf16<<<dim3((unsigned)(tiles_m * tiles_n)), kThreads, 2 * STAGE, s>>>(
-        (int)M, (int)N, (int)kp, ap, bp, y, tiles_m, tiles_n);
-    return hipGetLastError();
+    return launch_gemm_bf16_accum(M, N, kp, ap, bp, y, N, s);
 }
 
 }  // namespace fp4q

@@ -16,11 +16,11 @@
 //    saturating), which matches the E2M1 rounding rule bit for bit; each lane
 //    writes one 32-bit word of codes, the block's first lane its scale byte.
 //  * quantize_col_kernel: blocks down the strided dim (K-major output of x^T).
-//    Each lane owns 8 (bf16) or 4 (fp32) adjacent columns x 8 rows, read with
-//    coalesced 16-byte row loads; the block/8 lanes of one column block are
-//    adjacent, so the column amax is a lane-local max plus a DPP reduction
-//    (no LDS transpose is needed: each lane packs its rows of a column into
-//    one 32-bit code word, and the group's words are contiguous).
+//    A workgroup owns one block of rows x 512 (bf16) / 256 (fp32) columns;
+//    each wave reads a quarter of the block's rows as contiguous 1 KB row
+//    segments (8 or 4 columns per lane), the four partial column maxima
+//    meet in LDS, and each column's block of codes is staged in LDS and
+//    written as one contiguous store.
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -191,36 +191,38 @@ hipError_t launch_quantize_row(const void* x, int dtype, int64_t rows, int64_t c
 // ---------------------------------------------------------------------------
 // COL
 // ---------------------------------------------------------------------------
-// One lane: CPT adjacent columns (16 bytes of a row: 8 bf16 or 4 fp32) x 8
-// consecutive rows.  The block/8 lanes holding one block's rows are adjacent,
-// so the column amax is a lane-local max over 8 rows followed by the same DPP
-// group reduction as the ROW kernel.  Each lane packs its 8 rows of a column
-// into one 32-bit word of that column's K-major code row; the group's words
-// are contiguous.  Waves walk (row block, column chunk) pairs row-block-major
-// so neighbouring waves read neighbouring bytes.
+// One workgroup: one block of BLOCK rows x 64*CPT columns (512 bf16 / 256
+// fp32).  Wave w owns rows [w*RPW, (w+1)*RPW) of the block (RPW = BLOCK/4),
+// lane l owns columns [l*CPT, (l+1)*CPT): every row load of a wave is one
+// contiguous 1 KB segment.  Column maxima of the four row slices meet in
+// LDS; each lane then quantises its RPW rows of its CPT columns into
+// RPW/2 code bytes per column, staged in LDS so that each column's block of
+// codes leaves as one contiguous 8/16/32/64-byte store.
 template <int IN_BF16, int BLOCK, int SR>
 __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
     const void* __restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t k0, uint32_t k1,
-    uint64_t rng_off, int64_t ncg, int64_t nrb, int64_t n_cchunks) {
+    uint64_t rng_off, int64_t nrb, int64_t n_cchunks) {
     constexpr int CPT = IN_BF16 ? 8 : 4;  // columns per lane
-    constexpr int G = BLOCK / 8;          // lanes per block
-    constexpr int CG_PER_WAVE = 64 / G;
-    const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    if (wave >= nrb * n_cchunks) return;  // whole wave: no DPP partner is lost
-    const int64_t rb = wave / n_cchunks;
-    const int64_t cg = (wave - rb * n_cchunks) * CG_PER_WAVE + lane / G;
-    const int rq = lane % G;
-    const bool cg_ok = cg < ncg;
-    const int64_t c0 = (cg_ok ? cg : 0) * CPT;
-    const bool full = cg_ok && (c0 + CPT) <= cols;
-    const int64_t r0 = rb * BLOCK + rq * 8;
+    constexpr int COLS = 64 * CPT;        // columns per workgroup
+    constexpr int RPW = BLOCK / 4;        // rows per wave
+    constexpr int WPC = (RPW + 7) / 8;    // 32-bit code words per column per lane
+                                          // (block 16: 4 rows -> the low 16 bits)
+    __shared__ uint32_t part[4][COLS];                 // per-wave column maxima
+    __shared__ __attribute__((aligned(16))) uint32_t cstage[COLS][BLOCK / 8];  // codes
 
-    // 8 rows x 16 bytes
-    uint32_t v[8][4];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t rb = blockIdx.x / n_cchunks;
+    const int64_t cc = blockIdx.x - rb * n_cchunks;
+    const int64_t c0 = cc * COLS + lane * CPT;
+    const bool lane_ok = c0 < cols;
+    const bool full = (c0 + CPT) <= cols;
+    const int64_t r0 = rb * BLOCK + wave * RPW;
+
+    uint32_t v[RPW][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < RPW; ++i) {
         const int64_t r = r0 + i;
         if (full) {
             const uint4 t = IN_BF16 ? *(const uint4*)((const uint16_t*)xv + r * ld + c0)
@@ -233,76 +235,66 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
             const uint16_t* x = (const uint16_t*)xv + r * ld;
             uint32_t e[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) e[j] = (cg_ok && c0 + j < cols) ? x[c0 + j] : 0u;
+            for (int j = 0; j < 8; ++j) e[j] = (c0 + j < cols) ? x[c0 + j] : 0u;
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[i][j] = e[2 * j] | (e[2 * j + 1] << 16);
         } else {
             const uint32_t* x = (const uint32_t*)xv + r * ld;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[i][j] = (cg_ok && c0 + j < cols) ? x[c0 + j] : 0u;
+            for (int j = 0; j < 4; ++j) v[i][j] = (c0 + j < cols) ? x[c0 + j] : 0u;
         }
     }
-    // fp32 bits of column j of row i
     auto col_bits = [&](int i, int j) -> uint32_t {
         if (IN_BF16) return (j & 1) ? (v[i][j >> 1] & 0xFFFF0000u) : (v[i][j >> 1] << 16);
         return v[i][j];
     };
 
-    uint32_t amax[CPT];
-    if (IN_BF16) {
-        // packed 16-bit maxima of column pairs, reduced across the group
+    // column maxima of this wave's rows, then across the four waves
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            u16x2_t m = __builtin_bit_cast(u16x2_t, v[0][p] & 0x7FFF7FFFu);
+    for (int j = 0; j < CPT; ++j) {
+        uint32_t m = 0;
 #pragma unroll
-            for (int i = 1; i < 8; ++i)
-                m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, v[i][p] & 0x7FFF7FFFu));
-            uint32_t w = __builtin_bit_cast(uint32_t, m);
-            // a 16-bit-lane max across the group: both halves are non-negative
-            // 15-bit magnitudes, so a 32-bit max of each half works separately
-            uint32_t lo = group_max_u32<G>(w & 0xFFFFu);
-            uint32_t hi = group_max_u32<G>(w >> 16);
-            amax[2 * p] = lo << 16;
-            amax[2 * p + 1] = hi << 16;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            uint32_t m = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) m = max(m, v[i][j] & 0x7FFFFFFFu);
-            amax[j] = group_max_u32<G>(m);
-        }
+        for (int i = 0; i < RPW; ++i) m = max(m, col_bits(i, j) & 0x7FFFFFFFu);
+        part[wave][lane * CPT + j] = m;
     }
-
-    uint32_t out[CPT];
+    __syncthreads();
+    uint32_t amax[CPT];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) out[j] = 0;
+    for (int j = 0; j < CPT; ++j)
+        amax[j] = max(max(part[0][lane * CPT + j], part[1][lane * CPT + j]),
+                      max(part[2][lane * CPT + j], part[3][lane * CPT + j]));
+
+    uint32_t out[CPT][WPC];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+#pragma unroll
+        for (int q = 0; q < WPC; ++q) out[j][q] = 0;
     if (!SR) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             const bool nf = amax[j] >= 0x7F800000u;
             const float sc = e8m0_scale_f32(nf ? 0xFFu : e8m0_from_amax(amax[j]));
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
+            for (int p = 0; p < RPW / 2; ++p) {
+                uint32_t& dst = out[j][p / 4];
                 if (IN_BF16) {
                     const uint32_t a = col_bits(2 * p, j) >> 16;
                     const uint32_t b = col_bits(2 * p + 1, j) & 0xFFFF0000u;
                     const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, a | b);
-                    switch (p) {
-                        case 0: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out[j], pr, sc, 0); break;
-                        case 1: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out[j], pr, sc, 1); break;
-                        case 2: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out[j], pr, sc, 2); break;
-                        default: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out[j], pr, sc, 3); break;
+                    switch (p & 3) {
+                        case 0: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(dst, pr, sc, 0); break;
+                        case 1: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(dst, pr, sc, 1); break;
+                        case 2: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(dst, pr, sc, 2); break;
+                        default: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(dst, pr, sc, 3); break;
                     }
                 } else {
                     const float a = as_f32(col_bits(2 * p, j));
                     const float b = as_f32(col_bits(2 * p + 1, j));
-                    switch (p) {
-                        case 0: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j], a, b, sc, 0); break;
-                        case 1: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j], a, b, sc, 1); break;
-                        case 2: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j], a, b, sc, 2); break;
-                        default: out[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j], a, b, sc, 3); break;
+                    switch (p & 3) {
+                        case 0: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dst, a, b, sc, 0); break;
+                        case 1: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dst, a, b, sc, 1); break;
+                        case 2: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dst, a, b, sc, 2); break;
+                        default: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dst, a, b, sc, 3); break;
                     }
                 }
             }
@@ -315,47 +307,73 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
             inv[j] = e8m0_inv_scale_f32(nf ? 0u : e8m0_from_amax(amax[j]));
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < RPW; ++i) {
             uint32_t rnd[8];
             const uint64_t p0 = (uint64_t)(r0 + i) * (uint64_t)cols + (uint64_t)c0 + rng_off;
             sr_bits8(p0, k0, k1, rnd);
 #pragma unroll
             for (int j = 0; j < CPT; ++j)
-                out[j] |= sr_code(as_f32(col_bits(i, j)), inv[j], rnd[j]) << (4 * i);
+                out[j][i / 8] |= sr_code(as_f32(col_bits(i, j)), inv[j], rnd[j]) << (4 * (i & 7));
         }
     }
-    if (!cg_ok) return;
-    const int64_t half_rows = rows / 2;
+    // stage: column (lane*CPT + j), words [wave*WPC, (wave+1)*WPC) of its block
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-        if (c0 + j >= cols) break;
         const bool nf = amax[j] >= 0x7F800000u;
-        *(uint32_t*)(codes + (c0 + j) * half_rows + r0 / 2) = nf ? 0u : out[j];
-        if (rq == 0) scales[(c0 + j) * nrb + rb] = (uint8_t)(nf ? 0xFFu : e8m0_from_amax(amax[j]));
+        if (RPW >= 8) {
+#pragma unroll
+            for (int q = 0; q < WPC; ++q)
+                cstage[lane * CPT + j][wave * WPC + q] = nf ? 0u : out[j][q];
+        } else {
+            ((uint16_t*)cstage[lane * CPT + j])[wave] = (uint16_t)(nf ? 0u : out[j][0]);
+        }
+    }
+    if (wave == 0 && lane_ok) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j)
+            if (c0 + j < cols)
+                scales[(c0 + j) * nrb + rb] =
+                    (uint8_t)(amax[j] >= 0x7F800000u ? 0xFFu : e8m0_from_amax(amax[j]));
+    }
+    __syncthreads();
+    // store: thread t writes whole columns' code blocks (BLOCK/2 bytes each)
+    const int64_t half_rows = rows / 2;
+    constexpr int WORDS = BLOCK / 8;
+    for (int col = threadIdx.x; col < COLS; col += kThreads) {
+        const int64_t c = cc * COLS + col;
+        if (c >= cols) break;
+        uint8_t* dst = codes + c * half_rows + rb * (BLOCK / 2);
+        const uint32_t* src = cstage[col];
+        if (WORDS >= 4) {
+#pragma unroll
+            for (int q = 0; q < WORDS; q += 4)
+                *(uint4*)(dst + 4 * q) = make_uint4(src[q], src[q + 1], src[q + 2], src[q + 3]);
+        } else {
+            *(uint2*)dst = make_uint2(src[0], src[1 % WORDS]);
+        }
     }
 }
 
 template <int IN_BF16, int SR>
 static hipError_t col_dispatch(int block, dim3 grid, hipStream_t s, const void* x, int64_t rows,
                                int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
-                               uint32_t k0, uint32_t k1, uint64_t off, int64_t ncg, int64_t nrb,
-                               int64_t ncc) {
+                               uint32_t k0, uint32_t k1, uint64_t off, int64_t nrb, int64_t ncc) {
     switch (block) {
         case 16:
             quantize_col_kernel<IN_BF16, 16, SR><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, ncg, nrb, ncc);
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, ncc);
             break;
         case 32:
             quantize_col_kernel<IN_BF16, 32, SR><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, ncg, nrb, ncc);
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, ncc);
             break;
         case 64:
             quantize_col_kernel<IN_BF16, 64, SR><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, ncg, nrb, ncc);
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, ncc);
             break;
         default:
             quantize_col_kernel<IN_BF16, 128, SR><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, ncg, nrb, ncc);
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, ncc);
             break;
     }
     return hipGetLastError();
@@ -364,23 +382,20 @@ static hipError_t col_dispatch(int block, dim3 grid, hipStream_t s, const void* 
 hipError_t launch_quantize_col(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                                int block, bool sr, uint64_t seed, uint64_t off, uint8_t* codes,
                                uint8_t* scales, hipStream_t s) {
-    const int cpt = dtype == BF16 ? 8 : 4;
-    const int64_t ncg = (cols + cpt - 1) / cpt;
+    const int64_t cols_per_wg = dtype == BF16 ? 512 : 256;
+    const int64_t ncc = (cols + cols_per_wg - 1) / cols_per_wg;
     const int64_t nrb = rows / block;
-    const int64_t cg_per_wave = 64 / (block / 8);
-    const int64_t ncc = (ncg + cg_per_wave - 1) / cg_per_wave;
-    const int64_t waves = nrb * ncc;
-    dim3 grid((unsigned)((waves + 3) / 4));
+    dim3 grid((unsigned)(nrb * ncc));
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     if (dtype == BF16)
         return sr ? col_dispatch<1, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1,
-                                       off, ncg, nrb, ncc)
+                                       off, nrb, ncc)
                   : col_dispatch<1, 0>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1,
-                                       off, ncg, nrb, ncc);
+                                       off, nrb, ncc);
     return sr ? col_dispatch<0, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1, off,
-                                   ncg, nrb, ncc)
+                                   nrb, ncc)
               : col_dispatch<0, 0>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1, off,
-                                   ncg, nrb, ncc);
+                                   nrb, ncc);
 }
 
 }  // namespace fp4q
