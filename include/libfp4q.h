@@ -128,7 +128,9 @@ fp4q_status_t fp4q_grad_estimate(fp4q_grad_t mode, const void* x, fp4q_dtype_t x
  *   b_scales [N, K/32] (both K-major, block 32, as fp4q_quantize writes them);
  *   C: [M, N] row-major with row stride ld_c elements, bf16 or fp32 (bf16 is
  *   the round-to-nearest-even of the fp32 accumulator).
- *   block must be 32 (FP4Q_ERR_UNSUPPORTED otherwise); K % 128 == 0;
+ *   block must be 32 (FP4Q_ERR_UNSUPPORTED otherwise); K % 128 == 0 and
+ *   K < 2^24 (larger K: FP4Q_ERR_UNSUPPORTED, since 256 rows of codes are
+ *   addressed with 32-bit offsets); M, N < 2^31.
  *   accumulate = 1 adds into an fp32 C (bf16 C: FP4Q_ERR_UNSUPPORTED).
  *   M, N >= 1 are arbitrary (edge tiles are masked).  Deterministic: no
  *   atomics, no split-K.
@@ -157,7 +159,8 @@ size_t fp4q_hcp_workspace_bytes(int64_t M, int64_t N, int32_t n_hot);
  *   w   bf16 [K, N] dense;  wq_codes/wq_scales: its COL block-32 (K-major)
  *       quantisation, [N, K/2] and [N, K/32].
  *   hot_idx  int32 [n_hot] device array of distinct channels in [0, K)
- *       (not checked: it lives on the device).  n_hot = 0 is a no-op.
+ *       (not checked: it lives on the device).  n_hot = 0 is a no-op;
+ *       n_hot <= min(K, 2^20) (above 2^20: FP4Q_ERR_UNSUPPORTED).
  *   y   fp32 [M, N] dense, read and written.
  *   workspace  >= fp4q_hcp_workspace_bytes(M, N, n_hot) device bytes.
  */

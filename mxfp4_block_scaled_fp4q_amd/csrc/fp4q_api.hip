@@ -151,6 +151,8 @@ fp4q_status_t fp4q_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
     if (ld_c < N) return fail(FP4Q_ERR_INVALID, "gemm: ld_c < N");
     if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
         return fail(FP4Q_ERR_INVALID, "gemm: dimension too large");
+    if (K >= ((int64_t)1 << 24))
+        return fail(FP4Q_ERR_UNSUPPORTED, "gemm: K must be below 2^24");
     if (accumulate != 0 && accumulate != 1) return fail(FP4Q_ERR_INVALID, "gemm: accumulate");
     if (accumulate && c_dtype != FP4Q_F32)
         return fail(FP4Q_ERR_UNSUPPORTED, "gemm: accumulate needs an fp32 C");
@@ -179,6 +181,7 @@ fp4q_status_t fp4q_hcp_residual_add(int64_t M, int64_t N, int64_t K, const void*
     if (K % 32) return fail(FP4Q_ERR_INVALID, "hcp: K %% 32 != 0");
     if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
         return fail(FP4Q_ERR_INVALID, "hcp: dimension too large");
+    if (n_hot > (1 << 20)) return fail(FP4Q_ERR_UNSUPPORTED, "hcp: n_hot above 2^20");
     if (n_hot == 0) return FP4Q_OK;
     if (!x || !xq_codes || !xq_scales || !w || !wq_codes || !wq_scales || !hot_idx || !y ||
         !workspace)

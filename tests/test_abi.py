@@ -101,6 +101,7 @@ def test_gemm_validation(L):
     assert call(blk=16) == 2            # valid block, not the MX hardware block
     assert call(blk=12) == 1
     assert call(K=192) == 1             # K % 128
+    assert call(K=1 << 24) == 2         # 256 rows of codes exceed 32-bit offsets
     assert call(ldc=32) == 1
     assert call(acc=1, cdt=1) == 2      # accumulate into bf16
     assert call(acc=2) == 1
@@ -112,7 +113,7 @@ def test_gemm_validation(L):
 def test_hcp_validation(L):
     h = L.fp4q_hcp_residual_add
     ws = L.fp4q_hcp_workspace_bytes(128, 64, 10)
-    assert ws >= (128 + 64) * 64 * 2
+    assert ws >= (128 + 64) * (2 * 10) * 2   # gathered bf16 operands, 2 n_hot columns
     assert L.fp4q_hcp_workspace_bytes(128, 64, 0) == 0
     args = [128, 64, 256, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, ws, NUL]
     bad = list(args)
@@ -121,6 +122,10 @@ def test_hcp_validation(L):
     bad = list(args)
     bad[10] = 300        # n_hot > K
     assert h(*bad) == 1
+    bad = list(args)
+    bad[2] = 1 << 22
+    bad[10] = (1 << 20) + 1    # more hot channels than the residual GEMM addresses
+    assert h(*bad) == 2
     bad = list(args)
     bad[2] = 100         # K % 32
     assert h(*bad) == 1
