@@ -24,18 +24,22 @@
 // one wave's MFMAs run while the other waits on LDS or the barrier.  The K
 // loop steps 64 bytes per operand row (128 FP4 or 32 bf16 elements).
 //
-// Loads are coalesced: four consecutive lanes read one row's 64 bytes of
-// the step (buffer loads against per-tile ranges, so rows past M or N read
-// as zero), and are written to LDS in MFMA fragment order (fragment = 32
-// rows x 32 bytes, 16 bytes per lane), with the 16-byte slot XOR-swizzled by
-// the lane half and the fragment half so that both these writes and the
-// MFMA-side 16-byte reads are free of bank conflicts.  A 3-stage LDS ring
-// keeps two steps resident ahead of the one being computed: a step's loads
-// are issued three steps early into registers and written to LDS one step
-// later.  Scale words (4 bytes per row per step) travel with the codes.  The
-// epilogue stages each wave's tile in LDS so every lane writes 16
-// contiguous bytes.  Workgroups are remapped so that consecutive tiles of a
-// grouped (4 tile-rows) order run on the same XCD and share its L2.
+// Operands go global -> LDS directly (buffer loads with the LDS bit, so no
+// registers are spent on staging) through a 4-stage ring, issued three
+// steps ahead of their use.  Each code load instruction fills one 1 KB
+// region of 16 rows x 64 bytes in lane order; lane 4j + p fetches chunk
+// p ^ ((j / 4) % 4) of row j, so the four lanes of a row read its 64 bytes
+// together while the rotated chunk order makes the MFMA-side 16-byte reads
+// (lane = row) free of bank conflicts.  Scale bytes are fetched in groups of
+// 8 K steps (32 contiguous bytes per row, eight lanes per row) into a
+// double-buffered LDS ring, a group being loaded during the first half of
+// the group before it; the cost of a load instruction on this path grows
+// with the number of distinct rows it touches, so this is 8x cheaper than a
+// 4-byte word per row per step.  Rows past M or N read as zero (per-tile
+// buffer ranges).  The epilogue stages each wave's tile in LDS so every lane
+// writes 16 contiguous bytes.  Workgroups are remapped so that consecutive
+// tiles of a grouped (4 tile-rows) order run on the same XCD and share its
+// L2.
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -47,19 +51,25 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 // Native 4 x 32-bit vectors (HIP's uint4 is a class with unions, which the
 // compiler does not always split into registers).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 static constexpr int BM = 256, BN = 256;
 static constexpr int BKB = 64;                  // operand bytes per row per K step
-static constexpr int FRAG = 1024;               // bytes per LDS fragment
-static constexpr int OFF_B = 16 * FRAG;         // B fragments within a stage
-static constexpr int OFF_SA = 32 * FRAG;        // A scale words (256 x 4 B)
-static constexpr int OFF_SB = 32 * FRAG + 1024; // B scale words
-static constexpr int STAGE = 32 * FRAG + 2048;
+static constexpr int REGION = 1024;             // 16 rows x 64 bytes
+static constexpr int OFF_B = 16 * REGION;       // B codes within a stage
+static constexpr int STAGE = 32 * REGION;       // one K step of A and B codes
+static constexpr int SG = 8;                    // K steps per scale group
+static constexpr int SGB = 4 * SG;              // scale bytes per row per group
+static constexpr int SCALE_BUF = 512 * SGB;     // A rows 0..255, then B rows
 static constexpr int GROUP_M = 4;
 static constexpr int BUF_FLAGS = 0x00020000;    // buffer resource word 3: raw 32-bit data
 #ifndef FP4Q_GEMM_WN
 #define FP4Q_GEMM_WN 4
 #endif
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 at maximum).
+#define FP4Q_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
 
 template <int WN>
 struct Layout {
@@ -67,77 +77,56 @@ struct Layout {
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int TN = 8 / WN;          // 32-column MFMA tiles per wave
     static constexpr int WCOLS = 32 * TN;      // columns per wave
-    static constexpr int LPO = 16 / WAVES;     // 16-row load slices per operand per wave
-    static constexpr int SPW = 8 / WAVES;      // scale words per lane per step
+    static constexpr int RPW = 16 / WAVES;     // 1 KB code regions per operand per wave per step
+    static_assert(WAVES == 8, "the scale-group schedule assumes 8 waves");
 };
 
-// 16-byte slot of (row r in 0..31, lane half h, fragment half kk) within a
-// fragment: the MFMA lane h*32 + r, XOR-swizzled in bits 2 and 3.  A 16-lane
-// LDS access group then covers 16 distinct slots both when lanes are
-// (4 rows x 4 chunks of a row) and when they are 16 consecutive MFMA lanes.
-__device__ __forceinline__ int frag_slot(int r, int h, int kk) {
-    return (h * 32 + r) ^ (h << 2) ^ (kk << 3);
-}
+// 16-byte slot of chunk c (bytes 16c .. 16c+15 of the step) of row j within
+// a 16-row region.
+__device__ __forceinline__ int region_slot(int j, int c) { return 4 * j + (c ^ ((j >> 2) & 3)); }
 
 // Load sources: buffer resources whose ranges end at the operand's last row
-// inside this tile (rows past M or N read as zero), per-slice row offsets of
-// this lane (32-bit; they alone decide whether a row is in range), and the
-// scalar byte offset of the current K step.
+// inside this tile (rows past M or N read as zero), 32-bit per-lane offsets
+// (they alone decide whether a row is in range), and the scalar byte offset
+// of the current K step.
 template <int WN>
 struct Src {
-    __amdgpu_buffer_rsrc_t ra, rb, rs0, rs1;  // rs1: second scale word (4-wave layout)
-    uint32_t vrow[Layout<WN>::LPO];
-    uint32_t vs[Layout<WN>::SPW];
-    int soff, soff_s;
+    __amdgpu_buffer_rsrc_t ra, rb, rsc;  // rsc: scales of this wave's pieces (A or B)
+    uint32_t vrow[Layout<WN>::RPW];
+    uint32_t vsc[4];  // scale piece offsets, by piece index % 4 (word swizzle)
+    int soff;
 };
 
-template <int WN>
-struct StepRegs {
-    u32x4 a[Layout<WN>::LPO], b[Layout<WN>::LPO];
-    uint32_t s[Layout<WN>::SPW];
-};
-
-// Loads the K step the sources point at into registers and advances them.
+// Direct-to-LDS loads of the K step the sources point at into `stage`; the
+// sources then advance to the next step if `advance` (past the end of K the
+// last step is re-issued into a stage nobody reads again, so every step
+// issues the same number of loads and the waits are compile-time).
 template <int WN, int BF16OPS>
-__device__ __forceinline__ void load_step(Src<WN>& src, StepRegs<WN>& R) {
+__device__ __forceinline__ void issue_codes(Src<WN>& src, uint8_t* stage, int wave, bool advance) {
     using L = Layout<WN>;
 #pragma unroll
-    for (int q = 0; q < L::LPO; ++q) {
-        R.a[q] = __builtin_amdgcn_raw_buffer_load_b128(src.ra, src.vrow[q], src.soff, 0);
-        R.b[q] = __builtin_amdgcn_raw_buffer_load_b128(src.rb, src.vrow[q], src.soff, 0);
+    for (int q = 0; q < L::RPW; ++q) {
+        const int rho = q * L::WAVES + wave;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.ra, (lds_ptr_t)(stage + rho * REGION), 16,
+                                                 src.vrow[q], src.soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rb, (lds_ptr_t)(stage + OFF_B + rho * REGION),
+                                                 16, src.vrow[q], src.soff, 0, 0);
     }
-    if (!BF16OPS) {
-#pragma unroll
-        for (int j = 0; j < L::SPW; ++j)
-            R.s[j] = __builtin_amdgcn_raw_buffer_load_b32(j == 0 ? src.rs0 : src.rs1, src.vs[j],
-                                                          src.soff_s, 0);
-    }
-    src.soff += BKB;
-    src.soff_s += 4;
+    src.soff += advance ? BKB : 0;
 }
 
-// Writes a loaded step into `stage`: slice q of wave w is rows
-// (q*WAVES + w)*16 .. +15; `lds_lane` is this lane's swizzled offset within
-// a slice (chunk c = lane % 4 of row lane / 4 goes to fragment half c / 2,
-// lane half c % 2).
-template <int WN, int BF16OPS>
-__device__ __forceinline__ void store_step(const StepRegs<WN>& R, uint8_t* stage, int wave,
-                                           int lane, int lds_lane) {
-    using L = Layout<WN>;
-#pragma unroll
-    for (int q = 0; q < L::LPO; ++q) {
-        const int idx = q * L::WAVES + wave;
-        const int off = (idx >> 1) * (2 * FRAG) + (idx & 1) * 256 + lds_lane;
-        *(u32x4*)(stage + off) = R.a[q];
-        *(u32x4*)(stage + OFF_B + off) = R.b[q];
-    }
-    if (!BF16OPS) {
-        // scale word j of this lane belongs to combined row index
-        // (j * WAVES + wave) * 64 + lane: A rows 0..255, then B rows
-#pragma unroll
-        for (int j = 0; j < L::SPW; ++j)
-            *(uint32_t*)(stage + OFF_SA + ((j * L::WAVES + wave) * 64 + lane) * 4) = R.s[j];
-    }
+// Scale piece P (0..7) of this wave for group g: combined rows
+// wave*64 + P*8 .. +7 (A rows 0..255, then B rows), 32 bytes each; lane
+// 8j + pos loads word pos ^ (P % 4) of the piece's row j, so that in LDS
+// word s of row R sits at R*32 + 4 (s ^ ((R / 8) % 4)).  The group offset
+// is part of the per-lane offset so the range check covers it.
+template <int WN, int P>
+__device__ __forceinline__ void issue_scale_piece(const Src<WN>& src, uint8_t* sbuf, int wave,
+                                                  int kscale, int g) {
+    const uint32_t voff = src.vsc[P & 3] + (uint32_t)(P * 8 * kscale + g * SGB);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rsc,
+                                             (lds_ptr_t)(sbuf + (wave * 64 + P * 8) * SGB), 4,
+                                             voff, 0, 0, 0);
 }
 
 template <int WN>
@@ -145,33 +134,34 @@ struct Frags {
     u32x4 a[4], b[Layout<WN>::TN];
 };
 
-// This wave's A and B fragments of half kk of a staged step.
+// This wave's A and B fragments of one half of a staged step; `off` is this
+// lane's offset within a 32-row group for that half (row lane % 32, chunk
+// 2 kk + lane / 32).
 template <int WN>
-__device__ __forceinline__ void read_frags(const uint8_t* base, int kk, int wm, int wn, int lane,
+__device__ __forceinline__ void read_frags(const uint8_t* base, int off, int wm, int wn,
                                            Frags<WN>& F) {
     using L = Layout<WN>;
-    const int slot = frag_slot(lane & 31, lane >> 5, kk) * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        F.a[i] = *(const u32x4*)(base + ((wm * 4 + i) * 2 + kk) * FRAG + slot);
+    for (int i = 0; i < 4; ++i) F.a[i] = *(const u32x4*)(base + (wm * 4 + i) * 2 * REGION + off);
 #pragma unroll
     for (int j = 0; j < L::TN; ++j)
-        F.b[j] = *(const u32x4*)(base + OFF_B + ((wn * L::TN + j) * 2 + kk) * FRAG + slot);
+        F.b[j] = *(const u32x4*)(base + OFF_B + (wn * L::TN + j) * 2 * REGION + off);
 }
 
-// Scale words (4 K blocks of 32 elements each) of this lane's MFMA rows (A)
-// and columns (B).
+// Scale words (4 K blocks of 32 elements each) of step word s of a group
+// for this lane's MFMA rows (A) and columns (B); `sx` is this lane's
+// swizzled byte offset 4 (s ^ ((lane % 32) / 8 % 4)) of that word.
 template <int WN>
-__device__ __forceinline__ void read_scales(const uint8_t* base, int wm, int wn, int lane,
+__device__ __forceinline__ void read_scales(const uint8_t* sbuf, int sx, int wm, int wn, int lane,
                                             uint32_t (&sa)[4], uint32_t (&sb)[Layout<WN>::TN]) {
     using L = Layout<WN>;
     const int l32 = lane & 31;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        sa[i] = *(const uint32_t*)(base + OFF_SA + (wm * 128 + i * 32 + l32) * 4);
+        sa[i] = *(const uint32_t*)(sbuf + (wm * 128 + i * 32 + l32) * SGB + sx);
 #pragma unroll
     for (int j = 0; j < L::TN; ++j)
-        sb[j] = *(const uint32_t*)(base + OFF_SB + (wn * L::WCOLS + j * 32 + l32) * 4);
+        sb[j] = *(const uint32_t*)(sbuf + (256 + wn * L::WCOLS + j * 32 + l32) * SGB + sx);
 }
 
 // Shifts raw scale words so that byte 2 kk is the K block of half kk for
@@ -230,6 +220,9 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st3[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t sc0[SCALE_BUF];
+    __shared__ __attribute__((aligned(16))) uint8_t sc1[SCALE_BUF];
 
     // ---- tile index: XCD-contiguous, then grouped along M ----
     const int nwg = gridDim.x;
@@ -266,29 +259,27 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
                                                    rows_a * kbytes, BUF_FLAGS);
         src.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(bc + (int64_t)n0 * kbytes), (short)0,
                                                    rows_b * kbytes, BUF_FLAGS);
+        // lane 4j + p of a region loads chunk p ^ ((j / 4) % 4) of row j
+        const int j = lane >> 2;
+        const int c = (lane & 3) ^ ((j >> 2) & 3);
 #pragma unroll
-        for (int q = 0; q < L::LPO; ++q)
-            src.vrow[q] = (uint32_t)(((q * L::WAVES + wave) * 16 + (lane >> 2)) * kbytes +
-                                     (lane & 3) * 16);
-        const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(as + (int64_t)m0 * kscale), (short)0, rows_a * kscale, BUF_FLAGS);
-        const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(bs + (int64_t)n0 * kscale), (short)0, rows_b * kscale, BUF_FLAGS);
+        for (int q = 0; q < L::RPW; ++q)
+            src.vrow[q] = (uint32_t)(((q * L::WAVES + wave) * 16 + j) * kbytes + c * 16);
+        // waves 0..3 fetch A scale rows, waves 4..7 B scale rows
+        src.rsc = wave < 4 ? __builtin_amdgcn_make_buffer_rsrc((void*)(as + (int64_t)m0 * kscale),
+                                                               (short)0, rows_a * kscale, BUF_FLAGS)
+                           : __builtin_amdgcn_make_buffer_rsrc((void*)(bs + (int64_t)n0 * kscale),
+                                                               (short)0, rows_b * kscale, BUF_FLAGS);
+        const int sbase = ((wave & 3) * 64 + (lane >> 3)) * kscale;
 #pragma unroll
-        for (int j = 0; j < L::SPW; ++j) {
-            const int cw = j * L::WAVES + wave;  // combined row / 64: A rows, then B rows
-            if (j == 0)
-                src.rs0 = cw < 4 ? rsa : rsb;
-            else
-                src.rs1 = cw < 4 ? rsa : rsb;
-            src.vs[j] = (uint32_t)(((cw & 3) * 64 + lane) * kscale);
-        }
+        for (int q = 0; q < 4; ++q) src.vsc[q] = (uint32_t)(sbase + (((lane & 7) ^ q) << 2));
         src.soff = 0;
-        src.soff_s = 0;
     }
-    // this lane's chunk c = lane % 4 of row lane / 4 in a 16-row slice
-    const int lds_lane = ((lane & 3) >> 1) * FRAG +
-                         frag_slot(lane >> 2, lane & 1, (lane & 3) >> 1) * 16;
+    // this lane's offsets within a 32-row group: row lane % 32, chunk
+    // 2 kk + lane / 32
+    const int off0 = (l32 >> 4) * REGION + region_slot(l32 & 15, half) * 16;
+    const int off1 = (l32 >> 4) * REGION + region_slot(l32 & 15, 2 + half) * 16;
+    const int sxor = (l32 >> 3) & 3;  // scale word swizzle of this lane's rows
 
     v16f acc[4][TN];
 #pragma unroll
@@ -307,68 +298,110 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
     for (int j = 0; j < TN; ++j) sb[j] = rb[j] = 0;
     const int sh = 8 * half;
 
-    // Software pipeline over K steps t, LDS ring of 3 stages: the loads of
-    // step t + 3 are issued in step t into registers and written to their
-    // stage in step t + 1.  Each step computes two halves (K bytes 0..31 and
-    // 32..63 of the step); order within a step, fenced against the
-    // compiler's scheduler:
-    //   1. shift the step's scale words; read the fragments of (t, 1);
+    // Software pipeline over K steps t with a 4-stage code ring: step t
+    // issues the code loads of step t + 3 into the stage step t - 1 used
+    // (every wave finished reading it before the previous barrier), and, in
+    // the first half of each scale group, two scale pieces of the next group
+    // into the other scale buffer (its previous group ended before).  Each
+    // step computes two halves (K bytes 0..31 and 32..63 of the step); order
+    // within a step, fenced against the compiler's scheduler:
+    //   1. shift the step's scale words; read the fragments of (t, 1); issue
+    //      loads;
     //   2. MFMAs of (t, 0), whose fragments were read during step t - 1;
-    //      write the registers loaded during step t - 1 (step t + 2) to the
-    //      stage that step t - 1 used; issue the loads of step t + 3;
-    //   3. lgkmcnt(0) (this wave's LDS traffic), then one workgroup barrier,
-    //      which orders those writes and every wave's reads of that stage;
+    //   3. wait for this wave's loads of step t + 1 (later loads stay in
+    //      flight) and its LDS reads, then one workgroup barrier;
     //   4. read the scales and (t + 1, 0) fragments; MFMAs of (t, 1).
-    // LDS reads thus always run under MFMAs of the other half.
-    StepRegs<WN> R;
-    load_step<WN, BF16OPS>(src, R);
-    store_step<WN, BF16OPS>(R, st0, wave, lane, lds_lane);
-    if (ksteps > 1) {
-        load_step<WN, BF16OPS>(src, R);
-        store_step<WN, BF16OPS>(R, st1, wave, lane, lds_lane);
+    // The loop is unrolled by one scale group (8 steps, two turns of the
+    // ring), so every load count and wait is a compile-time constant.
+    constexpr int LC = 2 * L::RPW;  // code loads per wave per step
+    // loads issued after the code loads of step t + 1, at the end of step t
+    // with t % 8 == p: those of steps t - 1 and t plus the scale pieces
+    // issued after the code loads in step t - 2
+#define FP4Q_PIECES(p) ((BF16OPS || ((p) & 7) >= 4) ? 0 : 2)
+#define FP4Q_BEHIND(p) (FP4Q_PIECES((p) + 6) + LC + FP4Q_PIECES((p) + 7) + LC + FP4Q_PIECES(p))
+    if (!BF16OPS) {
+        issue_scale_piece<WN, 0>(src, sc0, wave, kscale, 0);
+        issue_scale_piece<WN, 1>(src, sc0, wave, kscale, 0);
+        issue_scale_piece<WN, 2>(src, sc0, wave, kscale, 0);
+        issue_scale_piece<WN, 3>(src, sc0, wave, kscale, 0);
+        issue_scale_piece<WN, 4>(src, sc0, wave, kscale, 0);
+        issue_scale_piece<WN, 5>(src, sc0, wave, kscale, 0);
+        issue_scale_piece<WN, 6>(src, sc0, wave, kscale, 0);
+        issue_scale_piece<WN, 7>(src, sc0, wave, kscale, 0);
     }
-    if (ksteps > 2) load_step<WN, BF16OPS>(src, R);
-    __syncthreads();
-    if (!BF16OPS) read_scales<WN>(st0, wm, wn, lane, ra, rb);
-    read_frags<WN>(st0, 0, wm, wn, lane, FA);
+    issue_codes<WN, BF16OPS>(src, st0, wave, 1 < ksteps);
+    issue_codes<WN, BF16OPS>(src, st1, wave, 2 < ksteps);
+    issue_codes<WN, BF16OPS>(src, st2, wave, 3 < ksteps);
+    FP4Q_WAIT_VMCNT(2 * LC);
+    __builtin_amdgcn_s_barrier();
+    if (!BF16OPS) read_scales<WN>(sc0, sxor << 2, wm, wn, lane, ra, rb);
+    read_frags<WN>(st0, off0, wm, wn, FA);
 
-// LAST is 2 in the steady-state loop (every later step exists, so the
-// step's loads are unconditional), else whether t is the final step.
-#define FP4Q_GEMM_STEP(t, CUR, NEXT1, NEXTL, LAST)                                 \
-    do {                                                                           \
-        __builtin_amdgcn_sched_barrier(0);                                         \
-        if (!BF16OPS) shift_scales<WN>(ra, rb, sh, sa, sb);                        \
-        read_frags<WN>(CUR, 1, wm, wn, lane, FB);                                  \
-        __builtin_amdgcn_sched_barrier(0);                                         \
-        mfma_half<WN, BF16OPS, 0>(FA, sa, sb, acc);                                \
-        if ((LAST) == 2 || (t) + 2 < ksteps)                                       \
-            store_step<WN, BF16OPS>(R, NEXTL, wave, lane, lds_lane);               \
-        if ((LAST) == 2 || (t) + 3 < ksteps) load_step<WN, BF16OPS>(src, R);       \
-        __builtin_amdgcn_sched_barrier(0);                                         \
-        __builtin_amdgcn_s_waitcnt(0xC07F);                                        \
-        __builtin_amdgcn_s_barrier();                                              \
-        __builtin_amdgcn_sched_barrier(0);                                         \
-        if ((LAST) != 1) {                                                         \
-            if (!BF16OPS) read_scales<WN>(NEXT1, wm, wn, lane, ra, rb);            \
-            read_frags<WN>(NEXT1, 0, wm, wn, lane, FA);                            \
-        }                                                                          \
-        mfma_half<WN, BF16OPS, 1>(FB, sa, sb, acc);                                \
+// One K step t = kt + P (P = t % 16, compile-time; its position in the
+// scale group is P % 8).  SCUR / SNXT: scale buffers of this group and the
+// next.  The final step's reads of a next step are harmless (in-bounds,
+// unused), so no step is special.
+#define FP4Q_GEMM_STEP(P, CUR, NEXT1, NEXTL, SCUR, SNXT)                             \
+    do {                                                                             \
+        const int t_ = kt + (P);                                                     \
+        __builtin_amdgcn_sched_barrier(0);                                           \
+        if (!BF16OPS) shift_scales<WN>(ra, rb, sh, sa, sb);                          \
+        read_frags<WN>(CUR, off1, wm, wn, FB);                                       \
+        issue_codes<WN, BF16OPS>(src, NEXTL, wave, t_ + 4 < ksteps);                 \
+        if (FP4Q_PIECES(P)) {                                                        \
+            issue_scale_piece<WN, 2 * ((P) & 3)>(src, SNXT, wave, kscale, t_ / SG + 1); \
+            issue_scale_piece<WN, 2 * ((P) & 3) + 1>(src, SNXT, wave, kscale, t_ / SG + 1); \
+        }                                                                            \
+        __builtin_amdgcn_sched_barrier(0);                                           \
+        mfma_half<WN, BF16OPS, 0>(FA, sa, sb, acc);                                  \
+        __builtin_amdgcn_sched_barrier(0);                                           \
+        FP4Q_WAIT_VMCNT(FP4Q_BEHIND(P));                                             \
+        __builtin_amdgcn_s_waitcnt(0xC07F);                                          \
+        __builtin_amdgcn_s_barrier();                                                \
+        __builtin_amdgcn_sched_barrier(0);                                           \
+        if (!BF16OPS)                                                                \
+            read_scales<WN>(((P) & 7) == 7 ? SNXT : SCUR, (((P) + 1) & 7 ^ sxor) << 2, wm, wn, \
+                            lane, ra, rb);                                           \
+        read_frags<WN>(NEXT1, off0, wm, wn, FA);                                     \
+        mfma_half<WN, BF16OPS, 1>(FB, sa, sb, acc);                                  \
     } while (0)
 
-    // The ring position of step t is t % 3; NEXTL is the stage written
-    // during step t (the one step t - 1 used).
+// Eight steps of one scale group starting at t = kt + O; GUARD(P) says
+// whether step kt + P exists (compile-time true in full turns).
+#define FP4Q_GEMM_GROUP(O, SCUR, SNXT, GUARD)                                        \
+    do {                                                                             \
+        if (GUARD(O + 0)) FP4Q_GEMM_STEP(O + 0, st0, st1, st3, SCUR, SNXT);          \
+        if (GUARD(O + 1)) FP4Q_GEMM_STEP(O + 1, st1, st2, st0, SCUR, SNXT);          \
+        if (GUARD(O + 2)) FP4Q_GEMM_STEP(O + 2, st2, st3, st1, SCUR, SNXT);          \
+        if (GUARD(O + 3)) FP4Q_GEMM_STEP(O + 3, st3, st0, st2, SCUR, SNXT);          \
+        if (GUARD(O + 4)) FP4Q_GEMM_STEP(O + 4, st0, st1, st3, SCUR, SNXT);          \
+        if (GUARD(O + 5)) FP4Q_GEMM_STEP(O + 5, st1, st2, st0, SCUR, SNXT);          \
+        if (GUARD(O + 6)) FP4Q_GEMM_STEP(O + 6, st2, st3, st1, SCUR, SNXT);          \
+        if (GUARD(O + 7)) FP4Q_GEMM_STEP(O + 7, st3, st0, st2, SCUR, SNXT);          \
+    } while (0)
+#define FP4Q_ALL(P) true
+#define FP4Q_EXISTS(P) (kt + (P) < ksteps)
+
+    // Step t uses code stage t % 4 and scale buffer (t / 8) % 2; a turn of
+    // the loops covers two groups so both buffers are named at compile time
+    // (the compiler then sees that scale reads and the loads in flight touch
+    // different LDS objects).
     int kt = 0;
-    for (; kt + 2 + 3 < ksteps; kt += 3) {
-        FP4Q_GEMM_STEP(kt, st0, st1, st2, 2);
-        FP4Q_GEMM_STEP(kt + 1, st1, st2, st0, 2);
-        FP4Q_GEMM_STEP(kt + 2, st2, st0, st1, 2);
+    for (; kt + 2 * SG <= ksteps; kt += 2 * SG) {
+        FP4Q_GEMM_GROUP(0, sc0, sc1, FP4Q_ALL);
+        FP4Q_GEMM_GROUP(8, sc1, sc0, FP4Q_ALL);
     }
-    for (; kt < ksteps; kt += 3) {
-        FP4Q_GEMM_STEP(kt, st0, st1, st2, kt + 1 == ksteps);
-        if (kt + 1 < ksteps) FP4Q_GEMM_STEP(kt + 1, st1, st2, st0, kt + 2 == ksteps);
-        if (kt + 2 < ksteps) FP4Q_GEMM_STEP(kt + 2, st2, st0, st1, kt + 3 == ksteps);
+    if (kt < ksteps) {
+        FP4Q_GEMM_GROUP(0, sc0, sc1, FP4Q_EXISTS);
+        FP4Q_GEMM_GROUP(8, sc1, sc0, FP4Q_EXISTS);
     }
+#undef FP4Q_GEMM_GROUP
 #undef FP4Q_GEMM_STEP
+#undef FP4Q_ALL
+#undef FP4Q_EXISTS
+#undef FP4Q_PIECES
+#undef FP4Q_BEHIND
+    FP4Q_WAIT_VMCNT(0);  // the re-issued loads past the end of K have landed
 
     // ---- epilogue: through LDS, so every lane writes 16 contiguous bytes ----
     // Each wave stages its tile 32 rows at a time in a private LDS region
@@ -377,10 +410,11 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
     __syncthreads();  // all waves are done with the operand stages
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int PITCH = L::WCOLS * ESZ + 16;
-    constexpr int REGION = 32 * PITCH;
-    constexpr int PER_STAGE = STAGE / REGION;  // wave regions that fit in one stage
+    constexpr int EREG = 32 * PITCH;
+    constexpr int PER_STAGE = STAGE / EREG;  // wave regions that fit in one stage
+    static_assert(L::WAVES <= 3 * PER_STAGE, "epilogue regions fit in three stages");
     uint8_t* reg = (wave / PER_STAGE == 0 ? st0 : wave / PER_STAGE == 1 ? st1 : st2) +
-                   (wave % PER_STAGE) * REGION;
+                   (wave % PER_STAGE) * EREG;
     const int row0 = m0 + wm * 128;
     const int col0 = n0 + wn * L::WCOLS;
     const bool vec_ok = ((ldc * ESZ) % 16 == 0) && (((uintptr_t)cptr & 15) == 0);
