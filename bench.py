@@ -14,9 +14,12 @@ through every kernel of the path:
     part of this workload (it has its own shape); see --hcp.
 
 `value` = FP4 GEMM flops of the step / step time (TFLOPS), i.e. whole-step
-throughput.  Per-kernel times come from HIP events on the stream the kernels
-run on; the roofline object reports the forward GEMM (the dominant kernel)
-against the dense FP4 MFMA peak, and the quantizer against HBM bandwidth.
+throughput over the timed steps.  The roofline object reports the forward
+GEMM (the dominant kernel) against the dense FP4 MFMA peak, its launch time
+taken from HIP events around it inside the timed region (on the stream the
+kernels run on, created without a system-scope fence so that recording them
+does not flush L2), and its HBM traffic from committed counter runs.  A second
+pass with an event between every two kernels gives the per-kernel table.
 The CPU baseline times the single-threaded oracle on a bounded sample.
 """
 import argparse
@@ -43,7 +46,71 @@ def parse():
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--hcp", action="store_true",
                    help="also time the 13B-shaped GEMM + hot-channel residual (reported aside)")
+    p.add_argument("--profile-op", default=None,
+                   help="run only this step kernel (or 'copy', a plain 256 MiB device copy) "
+                        "--reps times and exit: the target of rocprofv3 counter runs")
+    p.add_argument("--reps", type=int, default=10)
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemm_fwd_traffic.json")
+KERNEL_SRC = os.path.join(HERE, "mxfp4_block_scaled_fp4q_amd", "csrc", "gemm_fp4.hip")
+
+
+def measured_traffic():
+    """HBM bytes per forward-GEMM launch from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE runs, scaled by a plain copy's counters -- only while
+    the GEMM source is the one those counters were taken on (else None)."""
+    import hashlib
+    import json as _json
+    try:
+        rec = _json.load(open(TRAFFIC_FILE))
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != src:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+class HipEvents:
+    """HIP events created with hipEventDisableSystemFence, recorded on the
+    stream the kernels run on: a plain event's record releases to system
+    scope, which writes the L2 back and charges that to the kernel before
+    it (several microseconds after a GEMM that leaves its output in L2)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, torch):
+        import ctypes
+        self.ct = ctypes
+        self.L = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.made = []
+
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        self._check(self.L.hipEventCreateWithFlags(self.ct.byref(ev), self.DISABLE_SYSTEM_FENCE),
+                    "hipEventCreateWithFlags")
+        self.made.append(ev)
+        return ev
+
+    def record(self, ev):
+        self._check(self.L.hipEventRecord(ev, self.stream), "hipEventRecord")
+
+    def elapsed_us(self, a, b):
+        ms = self.ct.c_float()
+        self._check(self.L.hipEventElapsedTime(self.ct.byref(ms), a, b), "hipEventElapsedTime")
+        return ms.value * 1e3
+
+    def close(self):
+        for ev in self.made:
+            self.L.hipEventDestroy(ev)
+        self.made = []
 
 
 def main():
@@ -112,35 +179,67 @@ def main():
     ]
     step_flops = sum(o[3] for o in ops)
 
-    nev = len(ops) + 1
+    if args.profile_op is not None:
+        if args.profile_op == "copy":
+            n = 64 << 20
+            a = torch.ones(n, dtype=torch.float32, device=dev)
+            b = torch.empty_like(a)
+            fn = lambda: b.copy_(a)
+        else:
+            fn = dict((o[0], o[1]) for o in ops)[args.profile_op]
+        for _ in range(args.reps):
+            fn()
+        torch.cuda.synchronize()
+        return
 
-    def run_step(evs=None):
+    nev = len(ops) + 1
+    i_fwd = [o[0] for o in ops].index("gemm_fwd")
+
+    hev = HipEvents(torch)
+
+    def run_step(evs=None, fwd_evs=None):
         for i, (_, fn, _, _) in enumerate(ops):
             if evs is not None:
-                evs[i].record()
+                hev.record(evs[i])
+            if fwd_evs is not None and i == i_fwd:
+                hev.record(fwd_evs[0])
             fn()
+            if fwd_evs is not None and i == i_fwd:
+                hev.record(fwd_evs[1])
         if evs is not None:
-            evs[len(ops)].record()
+            hev.record(evs[len(ops)])
 
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, synchronised on both sides
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    # Timed region: exactly `steps` steps, synchronised on both sides.  The
+    # only events inside it bracket the forward GEMM (the roofline kernel),
+    # on the stream every kernel is launched on.
+    fwd_events = [[hev.create() for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        run_step(events[s])
+        run_step(fwd_evs=fwd_events[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    fwd_us = [hev.elapsed_us(e[0], e[1]) for e in fwd_events]
+
+    # Per-kernel breakdown: the same steps again with an event between every
+    # two kernels (each event adds a little queue turnaround to the kernel
+    # after it, so these times are slight upper bounds).
+    events = [[hev.create() for _ in range(nev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        run_step(events[s])
+    torch.cuda.synchronize()
 
     per_op = {}
     for i, (name, _, nbytes, nflops) in enumerate(ops):
-        ts = [events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]
-        us = float(np.mean(ts)) * 1e3
-        d = {"us": round(us, 2), "us_min": round(float(np.min(ts)) * 1e3, 2)}
+        ts = [hev.elapsed_us(events[s][i], events[s][i + 1]) for s in range(args.steps)]
+        us = float(np.mean(ts))
+        d = {"us": round(us, 2), "us_min": round(float(np.min(ts)), 2)}
         if nflops:
             d["TFLOPS"] = round(nflops / (us * 1e-6) / 1e12, 1)
             d["frac_fp4_peak"] = round(d["TFLOPS"] / PEAK_FP4_TFLOPS, 4)
@@ -148,12 +247,17 @@ def main():
         d["frac_hbm_peak"] = round(d["GBps"] / PEAK_HBM_GBPS, 4)
         per_op[name] = d
 
+    hev.close()
     value = step_flops / (ms_per_step * 1e-3) / 1e12
-    g = per_op["gemm_fwd"]
-    roofline = {"bound": "mfma", "achieved": g["TFLOPS"], "peak": PEAK_FP4_TFLOPS,
-                "unit": "TFLOP/s", "frac": g["frac_fp4_peak"], "traffic": None,
+    fwd_flops = 2.0 * M * N * K
+    fwd_mean_us = float(np.mean(fwd_us))
+    achieved = fwd_flops / (fwd_mean_us * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4_TFLOPS, 4),
+                "traffic": measured_traffic(),
                 "kernel": "gemm_fp4_kernel 8192x5632x2048 bf16 out",
-                "per_launch_flops": 2.0 * M * N * K}
+                "per_launch_flops": fwd_flops, "launch_us_mean": round(fwd_mean_us, 2),
+                "launch_us_min": round(float(np.min(fwd_us)), 2)}
     q = per_op["quant_dy_row_sr"]
     qr = per_op["quant_x_row"]
     quant = {"quant_bf16_row_rne_GBps": qr["GBps"], "quant_bf16_row_rne_frac": qr["frac_hbm_peak"],
