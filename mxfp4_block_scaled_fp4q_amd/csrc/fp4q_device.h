@@ -104,53 +104,83 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     return o;
 }
 
-// 16-bit random lanes for the 8 consecutive logical positions p0 .. p0+7:
-// position p uses half (p & 1) of word ((p & 7) >> 1) of the Philox output
-// for counter p >> 3 (64-bit, in words 0..1; words 2..3 zero), key = seed.
-// u[j] receives the bits of position p0 + j.
-__device__ __forceinline__ void sr_bits8(uint64_t p0, uint32_t k0, uint32_t k1, uint32_t u[8]) {
-    uint64_t n = p0 >> 3;
-    uint32_t s = (uint32_t)(p0 & 7);
-    Philox4 a = philox4x32_10((uint32_t)n, (uint32_t)(n >> 32), 0u, 0u, k0, k1);
-    if (s == 0) {
+// Words of the 16-bit lanes S .. S+7 of the 16-lane stream a, b (lane q is
+// half q & 1 of word q >> 1), two lanes per word, low half first.
+template <int S>
+__device__ __forceinline__ void sr_lanes_from(const Philox4& a, const Philox4& b, uint32_t w[4]) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) u[j] = (a.v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-    } else {
-        uint64_t n1 = n + 1;
-        Philox4 b = philox4x32_10((uint32_t)n1, (uint32_t)(n1 >> 32), 0u, 0u, k0, k1);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t q = s + (uint32_t)j;
-            uint32_t w = (q < 8) ? a.v[(q >> 1) & 3] : b.v[((q - 8) >> 1) & 3];
-            u[j] = (w >> (16 * (q & 1))) & 0xFFFFu;
-        }
+    for (int k = 0; k < 4; ++k) {
+        const int q0 = S + 2 * k, q1 = S + 2 * k + 1;
+        const uint32_t x0 = q0 < 8 ? a.v[(q0 >> 1) & 3] : b.v[((q0 - 8) >> 1) & 3];
+        const uint32_t x1 = q1 < 8 ? a.v[(q1 >> 1) & 3] : b.v[((q1 - 8) >> 1) & 3];
+        w[k] = ((x0 >> (16 * (q0 & 1))) & 0xFFFFu) | (((x1 >> (16 * (q1 & 1))) & 0xFFFFu) << 16);
     }
 }
 
-// Stochastic rounding of one element x (finite, in a block with inverse scale
-// inv = 2^-e) to a 4-bit E2M1 code, with 16 random bits u:
-//   m = |x| / 2^e;  lo, hi = neighbouring grid values;  round up iff
-//   u < (m - lo) / (hi - lo) * 2^16;  m >= 6 gives 6.
-// Working variable q = m * 2^(128 - E), E = max(biased exponent of m, 127),
-// puts every grid interval at unit width: q in [0, 2) for m < 1 (step 0.5),
-// q in [2, 4) for m in [1, 8) (steps 0.5, 1, 2); the code is
-// 2 (E - 127) + floor(q) (+1 on round-up), capped at 7.  All of this is exact
-// in fp32 while m is normal.  When m is below the normal range (only possible
-// for a nonzero x far below its block max) the exact threshold is under 1, so
-// the decision is "round up iff u == 0 and x != 0": T is raised to 0.5 there.
-__device__ __forceinline__ uint32_t sr_code(float x, float inv, uint32_t u) {
-    uint32_t xb = as_u32(x);
-    float m = fabsf(x) * inv;
-    uint32_t mb = as_u32(m);
-    uint32_t E = max(mb >> 23, 127u);
-    float q = m * as_f32((255u - E) << 23);
-    float fl = floorf(q);
-    float T = (q - fl) * 65536.0f;
-    if ((xb & 0x7FFFFFFFu) != 0u && fl == 0.0f) T = fmaxf(T, 0.5f);
-    uint32_t up = ((float)u < T) ? 1u : 0u;
-    uint32_t code = 2u * (E - 127u) + (uint32_t)fl + up;
-    code = min(code, 7u);
-    return code | ((xb >> 28) & 8u);
+// Random words for the 8 consecutive logical positions p0 .. p0+7:
+// position p uses half (p & 1) of word ((p & 7) >> 1) of the Philox output
+// for counter p >> 3 (64-bit, in words 0..1; words 2..3 zero), key = seed.
+// w[k] receives the 16-bit lanes of positions p0 + 2k (low half) and
+// p0 + 2k + 1 (high half); aligned p0 (the common case) is one call.
+__device__ __forceinline__ void sr_words8(uint64_t p0, uint32_t k0, uint32_t k1, uint32_t w[4]) {
+    const uint64_t n = p0 >> 3;
+    const uint32_t s = (uint32_t)(p0 & 7);
+    const Philox4 a = philox4x32_10((uint32_t)n, (uint32_t)(n >> 32), 0u, 0u, k0, k1);
+    if (s == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = a.v[k];
+        return;
+    }
+    const uint64_t n1 = n + 1;
+    const Philox4 b = philox4x32_10((uint32_t)n1, (uint32_t)(n1 >> 32), 0u, 0u, k0, k1);
+    switch (s) {  // static lane indexing keeps everything in registers
+        case 1: sr_lanes_from<1>(a, b, w); break;
+        case 2: sr_lanes_from<2>(a, b, w); break;
+        case 3: sr_lanes_from<3>(a, b, w); break;
+        case 4: sr_lanes_from<4>(a, b, w); break;
+        case 5: sr_lanes_from<5>(a, b, w); break;
+        case 6: sr_lanes_from<6>(a, b, w); break;
+        default: sr_lanes_from<7>(a, b, w); break;
+    }
+}
+
+// Stochastic rounding to E2M1 with 16 random bits u per element, as gfx950's
+// v_cvt_scalef32_sr_pk_fp4_f32 performs it: for m = |x| / scale below 6 the
+// fraction of m between its two neighbouring grid values is truncated to 22
+// bits, the instruction's 22-bit random field is added, and a carry rounds
+// up; m >= 6 gives 6.  With u placed at the top of that field (the field's
+// low 6 bits zero) this is exactly: round up iff u + floor(frac * 2^16) >=
+// 2^16.  The field of the first element of a pair is bits 31..10 of the
+// random word (word = u << 16), that of the second bits 30..9 (u << 15);
+// the two overlap, so each element of a pair gets its own conversion.
+//
+// The instruction writes only the selected byte of its destination and the
+// compiler does not tie the builtin's `old` operand to it, so only byte 0 of
+// a result is used and the rest is masked off.
+//
+// Code byte of the pair (x0, x1) sharing scale sc: x0 with random word
+// seed0 = u0 << 16 (low nibble of the first conversion), x1 with
+// seed1 = u1 << 15 (high nibble of the second).
+__device__ __forceinline__ uint32_t sr_pair(float x0, float x1, float sc, uint32_t seed0,
+                                            uint32_t seed1) {
+    const uint32_t a = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, (f32x2_t){x0, x1}, seed0, sc, 0);
+    const uint32_t b = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, (f32x2_t){x0, x1}, seed1, sc, 0);
+    return (a & 0x0Fu) | (b & 0xF0u);
+}
+
+// Random words of the pair whose lanes are the low (first element) and high
+// (second element) halves of one Philox word w.
+__device__ __forceinline__ uint32_t sr_seed_lo(uint32_t w) { return w << 16; }
+__device__ __forceinline__ uint32_t sr_seed_hi(uint32_t w) { return (w >> 1) & 0x7FFF8000u; }
+
+// 8 values sharing one scale (a row-direction chunk) whose 16-bit lanes are
+// the halves of w[0..3] (see sr_words8), packed two codes per byte.
+__device__ __forceinline__ uint32_t sr_pack8(const float x[8], float sc, const uint32_t w[4]) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        r |= sr_pair(x[2 * k], x[2 * k + 1], sc, sr_seed_lo(w[k]), sr_seed_hi(w[k])) << (8 * k);
+    return r;
 }
 
 }  // namespace fp4q

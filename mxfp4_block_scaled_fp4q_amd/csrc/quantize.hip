@@ -118,21 +118,21 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(
                                                                   as_f32(w[u][7]), sc, 3);
             }
         } else {
-            const float inv = e8m0_inv_scale_f32(byte);
+            const float sc = e8m0_scale_f32(byte);
             const uint32_t r = rowi[u];
             const uint32_t cc = (valid ? g : 0u) - r * cpr.d;
             const uint64_t p0 = (uint64_t)r * (uint64_t)cols + (uint64_t)cc * 8u + rng_off;
-            uint32_t rnd[8];
-            sr_bits8(p0, k0, k1, rnd);
+            uint32_t wr[4];
+            sr_words8(p0, k0, k1, wr);
+            float xf[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                float xf;
                 if (IN_BF16)
-                    xf = (j & 1) ? bf16_hi(w[u][j >> 1]) : bf16_lo(w[u][j >> 1]);
+                    xf[j] = (j & 1) ? bf16_hi(w[u][j >> 1]) : bf16_lo(w[u][j >> 1]);
                 else
-                    xf = as_f32(w[u][j]);
-                packed |= sr_code(xf, inv, rnd[j]) << (4 * j);
+                    xf[j] = as_f32(w[u][j]);
             }
+            packed = sr_pack8(xf, sc, wr);
         }
         if (nonfinite) packed = 0;
         if (valid) {
@@ -300,20 +300,29 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
             }
         }
     } else {
-        float inv[CPT];
+        float sc[CPT];
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             const bool nf = amax[j] >= 0x7F800000u;
-            inv[j] = e8m0_inv_scale_f32(nf ? 0u : e8m0_from_amax(amax[j]));
+            sc[j] = e8m0_scale_f32(nf ? 0u : e8m0_from_amax(amax[j]));
         }
+        // rows i, i+1 of a column form one code byte (byte (i % 8) / 2 of word
+        // i / 8); column j's 16-bit lane is half j & 1 of word j / 2 of the
+        // row's random words
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            uint32_t rnd[8];
+        for (int i = 0; i < RPW; i += 2) {
+            uint32_t w0[4], w1[4];
             const uint64_t p0 = (uint64_t)(r0 + i) * (uint64_t)cols + (uint64_t)c0 + rng_off;
-            sr_bits8(p0, k0, k1, rnd);
+            sr_words8(p0, k0, k1, w0);
+            sr_words8(p0 + (uint64_t)cols, k0, k1, w1);
 #pragma unroll
-            for (int j = 0; j < CPT; ++j)
-                out[j][i / 8] |= sr_code(as_f32(col_bits(i, j)), inv[j], rnd[j]) << (4 * (i & 7));
+            for (int j = 0; j < CPT; ++j) {
+                const uint32_t u0 = (w0[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+                const uint32_t u1 = (w1[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+                out[j][i / 8] |= sr_pair(as_f32(col_bits(i, j)), as_f32(col_bits(i + 1, j)), sc[j],
+                                         u0 << 16, u1 << 15)
+                                 << (8 * ((i & 7) >> 1));
+            }
         }
     }
     // stage: column (lane*CPT + j), words [wave*WPC, (wave+1)*WPC) of its block

@@ -133,10 +133,14 @@ int orc_rne_code(double y) {
     return sign | best;
 }
 
-/* Stochastic rounding on the E2M1 grid, magnitude form of floor + (u < frac)
- * ([P2 sec. 3.2]): lo = largest grid value <= |y|, hi = the next one,
- * frac = (|y| - lo) / (hi - lo); round up iff u16 < frac * 2^16 (exact
- * comparison: every quantity is exact in double).  |y| >= 6 gives 6. */
+/* Stochastic rounding on the E2M1 grid, magnitude form of "round up with
+ * probability equal to the fractional distance" ([P2 sec. 3.2]) at 16-bit
+ * resolution: lo = largest grid value <= |y|, hi = the next one,
+ * frac = (|y| - lo) / (hi - lo); the fraction truncated to 16 bits and the
+ * 16 random bits are added, and a carry out of 16 bits rounds up:
+ * round up iff u16 + floor(frac * 2^16) >= 2^16, so P(up) =
+ * floor(frac * 2^16) / 2^16, within 2^-16 of frac (every quantity is exact in
+ * double).  |y| >= 6 gives 6. */
 int orc_sr_code(double y, uint32_t u16) {
     int sign = signbit(y) ? 8 : 0;
     double m = fabs(y);
@@ -144,7 +148,7 @@ int orc_sr_code(double y, uint32_t u16) {
     int lo = 0;
     while (lo < 7 && E2M1_MAG[lo + 1] <= m) ++lo;
     double frac = (m - E2M1_MAG[lo]) / (E2M1_MAG[lo + 1] - E2M1_MAG[lo]);
-    int up = ((double)u16 < frac * 65536.0);
+    int up = ((double)u16 + floor(frac * 65536.0) >= 65536.0);
     return sign | (lo + up);
 }
 

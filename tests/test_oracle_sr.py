@@ -45,7 +45,8 @@ def _lo_hi(m):
 
 
 def test_sr_exact_roundup_counts(orc):
-    """Inject every u in [0, 2^16): the number of round-ups is ceil(frac*2^16)."""
+    """Inject every u in [0, 2^16): the number of round-ups is floor(frac*2^16)
+    and they are the largest u values (u + floor(frac*2^16) carries)."""
     rng = np.random.default_rng(5)
     ys = np.concatenate([rng.uniform(0, 6, 40), GRID[:-1] + 2.0 ** -20, [0.3, 1.9999999, 5.99],
                          [2.0 ** -30, 2.0 ** -140]])
@@ -58,9 +59,9 @@ def test_sr_exact_roundup_counts(orc):
         mags = GRID[codes & 7]
         assert set(np.unique(mags)) <= {lo, hi}
         ups = int(np.sum(mags == hi))
-        assert ups == int(np.ceil(frac * 65536)), (y32, ups, frac)
-        # the round-ups are exactly the smallest u values
-        assert np.all(mags[:ups] == hi) and np.all(mags[ups:] == lo)
+        assert ups == int(np.floor(frac * 65536)), (y32, ups, frac)
+        # the round-ups are exactly the largest u values
+        assert np.all(mags[65536 - ups:] == hi) and np.all(mags[:65536 - ups] == lo)
 
 
 def test_sr_grid_points_fixed_and_saturation(orc):
