@@ -191,57 +191,70 @@ hipError_t launch_quantize_row(const void* x, int dtype, int64_t rows, int64_t c
 // ---------------------------------------------------------------------------
 // COL
 // ---------------------------------------------------------------------------
-// One workgroup: one block of BLOCK rows x 64*CPT columns (512 bf16 / 256
-// fp32).  Wave w owns rows [w*RPW, (w+1)*RPW) of the block (RPW = BLOCK/4),
-// lane l owns columns [l*CPT, (l+1)*CPT): every row load of a wave is one
-// contiguous 1 KB segment.  Column maxima of the four row slices meet in
-// LDS; each lane then quantises its RPW rows of its CPT columns into
-// RPW/2 code bytes per column, staged in LDS so that each column's block of
-// codes leaves as one contiguous 8/16/32/64-byte store.
-template <int IN_BF16, int BLOCK, int SR>
+// One workgroup (256 threads) quantises a tile of 256 rows x TC columns
+// (TC = 128 bf16 / 64 fp32, 256 bytes of each row).  Thread (rg, cg) =
+// (tid / 16, tid % 16) holds rows rg*16 .. rg*16+15 of columns
+// cg*CPT .. cg*CPT+CPT-1, one 16-byte load per row, so a wave's load covers
+// four 256-byte row segments.  Block maxima over the BLOCK/16 row groups of a
+// block meet in LDS.  Each thread turns its 16 rows of a column into 8 code
+// bytes; they are staged in LDS per column, and the tile's output (each
+// column's 128 contiguous code bytes, i.e. K-major rows of the transposed
+// operand) leaves with eight consecutive lanes writing one whole 128-byte
+// line, which is what makes this layout change run at streaming speed.
+// ALIGNED (cols and the offset multiples of 8): every row's positions
+// c0 .. c0+CPT-1 lie in one Philox counter, so each row takes one call.
+template <int IN_BF16, int BLOCK, int SR, int ALIGNED>
 __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
     const void* __restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t k0, uint32_t k1,
-    uint64_t rng_off, int64_t nrb, int64_t n_cchunks) {
-    constexpr int CPT = IN_BF16 ? 8 : 4;  // columns per lane
-    constexpr int COLS = 64 * CPT;        // columns per workgroup
-    constexpr int RPW = BLOCK / 4;        // rows per wave
-    constexpr int WPC = (RPW + 7) / 8;    // 32-bit code words per column per lane
-                                          // (block 16: 4 rows -> the low 16 bits)
-    __shared__ uint32_t part[4][COLS];                 // per-wave column maxima
-    __shared__ __attribute__((aligned(16))) uint32_t cstage[COLS][BLOCK / 8];  // codes
+    uint64_t rng_off, int64_t nrb, int64_t n_ctiles) {
+    constexpr int CPT = IN_BF16 ? 8 : 4;  // columns per thread
+    constexpr int TC = 16 * CPT;          // columns per tile
+    constexpr int TR = 256;               // rows per tile
+    constexpr int RPT = 16;               // rows per thread
+    constexpr int NPB = BLOCK / RPT;      // row groups per block
+    constexpr int BPT = TR / BLOCK;       // blocks per tile (per column)
+    constexpr int PITCH = TR / 2 + 16;    // staged code bytes per column (padded)
+    static_assert(kThreads == 256, "16 x 16 thread layout");
+    __shared__ uint32_t part[NPB > 1 ? 16 : 1][TC];
+    __shared__ __attribute__((aligned(16))) uint8_t cst[TC * PITCH];
+    __shared__ uint8_t sst[TC][BPT];
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t rb = blockIdx.x / n_cchunks;
-    const int64_t cc = blockIdx.x - rb * n_cchunks;
-    const int64_t c0 = cc * COLS + lane * CPT;
-    const bool lane_ok = c0 < cols;
-    const bool full = (c0 + CPT) <= cols;
-    const int64_t r0 = rb * BLOCK + wave * RPW;
+    const int tid = threadIdx.x;
+    const int cg = tid & 15, rg = tid >> 4;
+    const int64_t trow = blockIdx.x / n_ctiles;
+    const int64_t tcol = blockIdx.x - trow * n_ctiles;
+    const int64_t r0 = trow * TR;                       // first row of the tile
+    const int64_t c0 = tcol * TC + cg * CPT;            // first column of this thread
+    const int vrows = (int)min<int64_t>(rows - r0, TR);  // a multiple of 16
+    const bool rows_ok = rg * RPT < vrows;
+    const bool full = c0 + CPT <= cols;
 
-    uint32_t v[RPW][4];
+    uint32_t v[RPT][4];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int64_t r = r0 + i;
-        if (full) {
+    for (int i = 0; i < RPT; ++i) {
+        const int64_t r = r0 + rg * RPT + i;
+        if (rows_ok && full) {
             const uint4 t = IN_BF16 ? *(const uint4*)((const uint16_t*)xv + r * ld + c0)
                                     : *(const uint4*)((const float*)xv + r * ld + c0);
             v[i][0] = t.x;
             v[i][1] = t.y;
             v[i][2] = t.z;
             v[i][3] = t.w;
-        } else if (IN_BF16) {
+        } else if (rows_ok && IN_BF16) {
             const uint16_t* x = (const uint16_t*)xv + r * ld;
             uint32_t e[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) e[j] = (c0 + j < cols) ? x[c0 + j] : 0u;
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[i][j] = e[2 * j] | (e[2 * j + 1] << 16);
-        } else {
+        } else if (rows_ok) {
             const uint32_t* x = (const uint32_t*)xv + r * ld;
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[i][j] = (c0 + j < cols) ? x[c0 + j] : 0u;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[i][j] = 0u;
         }
     }
     auto col_bits = [&](int i, int j) -> uint32_t {
@@ -249,38 +262,44 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
         return v[i][j];
     };
 
-    // column maxima of this wave's rows, then across the four waves
+    // block maxima: this thread's 16 rows, then across the block's row groups
+    uint32_t amax[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         uint32_t m = 0;
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) m = max(m, col_bits(i, j) & 0x7FFFFFFFu);
-        part[wave][lane * CPT + j] = m;
+        for (int i = 0; i < RPT; ++i) m = max(m, col_bits(i, j) & 0x7FFFFFFFu);
+        amax[j] = m;
     }
-    __syncthreads();
-    uint32_t amax[CPT];
+    if (NPB > 1) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j)
-        amax[j] = max(max(part[0][lane * CPT + j], part[1][lane * CPT + j]),
-                      max(part[2][lane * CPT + j], part[3][lane * CPT + j]));
-
-    uint32_t out[CPT][WPC];
-#pragma unroll
-    for (int j = 0; j < CPT; ++j)
-#pragma unroll
-        for (int q = 0; q < WPC; ++q) out[j][q] = 0;
-    if (!SR) {
+        for (int j = 0; j < CPT; ++j) part[NPB > 1 ? rg : 0][cg * CPT + j] = amax[j];
+        __syncthreads();
+        const int g0 = (rg / NPB) * NPB;
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const bool nf = amax[j] >= 0x7F800000u;
-            const float sc = e8m0_scale_f32(nf ? 0xFFu : e8m0_from_amax(amax[j]));
+            uint32_t m = 0;
 #pragma unroll
-            for (int p = 0; p < RPW / 2; ++p) {
+            for (int q = 0; q < NPB; ++q) m = max(m, part[NPB > 1 ? g0 + q : 0][cg * CPT + j]);
+            amax[j] = m;
+        }
+    }
+
+    // 16 rows of each column -> 8 code bytes (rows 2p, 2p+1 -> byte p)
+    uint32_t out[CPT][2];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const bool nf = amax[j] >= 0x7F800000u;
+        const uint32_t byte = nf ? 0xFFu : e8m0_from_amax(amax[j]);
+        const float sc = e8m0_scale_f32(nf ? 0u : byte);
+        out[j][0] = out[j][1] = 0;
+        if (!SR) {
+#pragma unroll
+            for (int p = 0; p < RPT / 2; ++p) {
                 uint32_t& dst = out[j][p / 4];
                 if (IN_BF16) {
-                    const uint32_t a = col_bits(2 * p, j) >> 16;
-                    const uint32_t b = col_bits(2 * p + 1, j) & 0xFFFF0000u;
-                    const bf16x2_t pr = __builtin_bit_cast(bf16x2_t, a | b);
+                    const bf16x2_t pr = __builtin_bit_cast(
+                        bf16x2_t, (col_bits(2 * p, j) >> 16) | (col_bits(2 * p + 1, j) & 0xFFFF0000u));
                     switch (p & 3) {
                         case 0: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(dst, pr, sc, 0); break;
                         case 1: dst = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(dst, pr, sc, 1); break;
@@ -299,90 +318,117 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
                 }
             }
         }
-    } else {
+        if (nf) out[j][0] = out[j][1] = 0;  // SR codes are filled in below
+        if ((rg % NPB) == 0 && rows_ok) sst[cg * CPT + j][rg / NPB] = (uint8_t)byte;
+    }
+    if (SR) {
+        // column j's 16-bit lane of row r is half j & 1 of word j / 2 of the
+        // random words of positions r*cols + c0 .. +7
         float sc[CPT];
+        bool nf[CPT];
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const bool nf = amax[j] >= 0x7F800000u;
-            sc[j] = e8m0_scale_f32(nf ? 0u : e8m0_from_amax(amax[j]));
+            nf[j] = amax[j] >= 0x7F800000u;
+            sc[j] = e8m0_scale_f32(nf[j] ? 0u : e8m0_from_amax(amax[j]));
         }
-        // rows i, i+1 of a column form one code byte (byte (i % 8) / 2 of word
-        // i / 8); column j's 16-bit lane is half j & 1 of word j / 2 of the
-        // row's random words
 #pragma unroll
-        for (int i = 0; i < RPW; i += 2) {
+        for (int p = 0; p < RPT / 2; ++p) {
+            const int64_t r = r0 + rg * RPT + 2 * p;
             uint32_t w0[4], w1[4];
-            const uint64_t p0 = (uint64_t)(r0 + i) * (uint64_t)cols + (uint64_t)c0 + rng_off;
-            sr_words8(p0, k0, k1, w0);
-            sr_words8(p0 + (uint64_t)cols, k0, k1, w1);
+            const uint64_t q0 = (uint64_t)r * (uint64_t)cols + (uint64_t)c0 + rng_off;
+            if (ALIGNED) {
+                // bf16: lanes 0..7 of counter q0 / 8; fp32: lanes 0..3 or 4..7
+                const uint64_t n0 = q0 >> 3, n1 = (q0 + (uint64_t)cols) >> 3;
+                const Philox4 a = philox4x32_10((uint32_t)n0, (uint32_t)(n0 >> 32), 0u, 0u, k0, k1);
+                const Philox4 b = philox4x32_10((uint32_t)n1, (uint32_t)(n1 >> 32), 0u, 0u, k0, k1);
+                const bool hi4 = !IN_BF16 && (q0 & 4);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    w0[k] = (IN_BF16 || k >= 2) ? a.v[k] : (hi4 ? a.v[k + 2] : a.v[k]);
+                    w1[k] = (IN_BF16 || k >= 2) ? b.v[k] : (hi4 ? b.v[k + 2] : b.v[k]);
+                }
+            } else {
+                sr_words8(q0, k0, k1, w0);
+                sr_words8(q0 + (uint64_t)cols, k0, k1, w1);
+            }
 #pragma unroll
             for (int j = 0; j < CPT; ++j) {
                 const uint32_t u0 = (w0[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
                 const uint32_t u1 = (w1[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-                out[j][i / 8] |= sr_pair(as_f32(col_bits(i, j)), as_f32(col_bits(i + 1, j)), sc[j],
-                                         u0 << 16, u1 << 15)
-                                 << (8 * ((i & 7) >> 1));
+                const uint32_t bt = sr_pair(as_f32(col_bits(2 * p, j)), as_f32(col_bits(2 * p + 1, j)),
+                                            sc[j], u0 << 16, u1 << 15);
+                out[j][p / 4] |= (nf[j] ? 0u : bt) << (8 * (p & 3));
             }
+            // one row pair at a time: interleaving the pairs' Philox chains
+            // only raises register pressure (and lowers occupancy)
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // stage: column (lane*CPT + j), words [wave*WPC, (wave+1)*WPC) of its block
+    // stage: column cg*CPT + j, bytes rg*8 .. rg*8+7 of its tile segment
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const bool nf = amax[j] >= 0x7F800000u;
-        if (RPW >= 8) {
-#pragma unroll
-            for (int q = 0; q < WPC; ++q)
-                cstage[lane * CPT + j][wave * WPC + q] = nf ? 0u : out[j][q];
-        } else {
-            ((uint16_t*)cstage[lane * CPT + j])[wave] = (uint16_t)(nf ? 0u : out[j][0]);
-        }
-    }
-    if (wave == 0 && lane_ok) {
-#pragma unroll
-        for (int j = 0; j < CPT; ++j)
-            if (c0 + j < cols)
-                scales[(c0 + j) * nrb + rb] =
-                    (uint8_t)(amax[j] >= 0x7F800000u ? 0xFFu : e8m0_from_amax(amax[j]));
-    }
+    for (int j = 0; j < CPT; ++j)
+        *(uint2*)(cst + (cg * CPT + j) * PITCH + rg * 8) = make_uint2(out[j][0], out[j][1]);
     __syncthreads();
-    // store: thread t writes whole columns' code blocks (BLOCK/2 bytes each)
+
+    // codes: each column's vrows/2 bytes; eight consecutive lanes write one
+    // 128-byte line when the column stride allows 16-byte stores
     const int64_t half_rows = rows / 2;
-    constexpr int WORDS = BLOCK / 8;
-    for (int col = threadIdx.x; col < COLS; col += kThreads) {
-        const int64_t c = cc * COLS + col;
-        if (c >= cols) break;
-        uint8_t* dst = codes + c * half_rows + rb * (BLOCK / 2);
-        const uint32_t* src = cstage[col];
-        if (WORDS >= 4) {
+    const int vbytes = vrows / 2;
+    const int64_t cbase = tcol * TC;
+    if ((half_rows & 15) == 0) {
 #pragma unroll
-            for (int q = 0; q < WORDS; q += 4)
-                *(uint4*)(dst + 4 * q) = make_uint4(src[q], src[q + 1], src[q + 2], src[q + 3]);
-        } else {
-            *(uint2*)dst = make_uint2(src[0], src[1 % WORDS]);
+        for (int k = 0; k < TC * 8 / kThreads; ++k) {
+            const int idx = k * kThreads + tid;
+            const int col = idx >> 3, ch = idx & 7;
+            const int64_t c = cbase + col;
+            if (c < cols && ch * 16 < vbytes)
+                *(uint4*)(codes + c * half_rows + r0 / 2 + ch * 16) =
+                    *(const uint4*)(cst + col * PITCH + ch * 16);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < TC * 16 / kThreads; ++k) {
+            const int idx = k * kThreads + tid;
+            const int col = idx >> 4, ch = idx & 15;
+            const int64_t c = cbase + col;
+            if (c < cols && ch * 8 < vbytes)
+                *(uint2*)(codes + c * half_rows + r0 / 2 + ch * 8) =
+                    *(const uint2*)(cst + col * PITCH + ch * 8);
+        }
+    }
+    // scales: each column's vrows/BLOCK bytes
+    if (tid < TC) {
+        const int64_t c = cbase + tid;
+        if (c < cols) {
+            const int nb = vrows / BLOCK;
+            uint8_t* dst = scales + c * nrb + r0 / BLOCK;
+#pragma unroll
+            for (int b2 = 0; b2 < BPT; ++b2)
+                if (b2 < nb) dst[b2] = sst[tid][b2];
         }
     }
 }
 
-template <int IN_BF16, int SR>
+template <int IN_BF16, int SR, int AL>
 static hipError_t col_dispatch(int block, dim3 grid, hipStream_t s, const void* x, int64_t rows,
                                int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
-                               uint32_t k0, uint32_t k1, uint64_t off, int64_t nrb, int64_t ncc) {
+                               uint32_t k0, uint32_t k1, uint64_t off, int64_t nrb, int64_t nct) {
     switch (block) {
         case 16:
-            quantize_col_kernel<IN_BF16, 16, SR><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, ncc);
+            quantize_col_kernel<IN_BF16, 16, SR, AL><<<grid, kThreads, 0, s>>>(
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct);
             break;
         case 32:
-            quantize_col_kernel<IN_BF16, 32, SR><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, ncc);
+            quantize_col_kernel<IN_BF16, 32, SR, AL><<<grid, kThreads, 0, s>>>(
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct);
             break;
         case 64:
-            quantize_col_kernel<IN_BF16, 64, SR><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, ncc);
+            quantize_col_kernel<IN_BF16, 64, SR, AL><<<grid, kThreads, 0, s>>>(
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct);
             break;
         default:
-            quantize_col_kernel<IN_BF16, 128, SR><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, ncc);
+            quantize_col_kernel<IN_BF16, 128, SR, AL><<<grid, kThreads, 0, s>>>(
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct);
             break;
     }
     return hipGetLastError();
@@ -391,20 +437,29 @@ static hipError_t col_dispatch(int block, dim3 grid, hipStream_t s, const void* 
 hipError_t launch_quantize_col(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                                int block, bool sr, uint64_t seed, uint64_t off, uint8_t* codes,
                                uint8_t* scales, hipStream_t s) {
-    const int64_t cols_per_wg = dtype == BF16 ? 512 : 256;
-    const int64_t ncc = (cols + cols_per_wg - 1) / cols_per_wg;
+    const int64_t cols_per_tile = dtype == BF16 ? 128 : 64;
+    const int64_t nct = (cols + cols_per_tile - 1) / cols_per_tile;
+    const int64_t nrt = (rows + 255) / 256;
     const int64_t nrb = rows / block;
-    dim3 grid((unsigned)(nrb * ncc));
+    dim3 grid((unsigned)(nrt * nct));
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-    if (dtype == BF16)
-        return sr ? col_dispatch<1, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1,
-                                       off, nrb, ncc)
-                  : col_dispatch<1, 0>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1,
-                                       off, nrb, ncc);
-    return sr ? col_dispatch<0, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1, off,
-                                   nrb, ncc)
-              : col_dispatch<0, 0>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1, off,
-                                   nrb, ncc);
+    const bool al = (cols % 8) == 0 && (off % 8) == 0;
+    if (dtype == BF16) {
+        if (!sr)
+            return col_dispatch<1, 0, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1,
+                                         off, nrb, nct);
+        return al ? col_dispatch<1, 1, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0,
+                                          k1, off, nrb, nct)
+                  : col_dispatch<1, 1, 0>(block, grid, s, x, rows, cols, ld, codes, scales, k0,
+                                          k1, off, nrb, nct);
+    }
+    if (!sr)
+        return col_dispatch<0, 0, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1, off,
+                                     nrb, nct);
+    return al ? col_dispatch<0, 1, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1,
+                                      off, nrb, nct)
+              : col_dispatch<0, 1, 0>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1,
+                                      off, nrb, nct);
 }
 
 }  // namespace fp4q
