@@ -179,7 +179,10 @@ __device__ __forceinline__ void shift_scales(const uint32_t (&ra)[4],
 // The 4 x TN MFMAs of this wave on half KK of a K step.  FP4: the scaled
 // MFMA on E2M1 operands (64 K elements per half), its byte select picking
 // byte 2 KK of the lane's (pre-shifted) scale words; BF16: plain bf16 MFMAs
-// (16 K elements per half, the same 16 bytes per lane).
+// (16 K elements per half, the same 16 bytes per lane).  B is the MFMA's
+// first operand, so each accumulator holds the transposed tile: register r
+// of lane l is C[row l % 32][column 8 (r / 4) + 4 (l / 32) + r % 4], four
+// consecutive columns per register group, which the epilogue stores whole.
 template <int WN, int BF16OPS, int KK>
 __device__ __forceinline__ void mfma_half(const Frags<WN>& F, const uint32_t (&sa)[4],
                                           const uint32_t (&sb)[Layout<WN>::TN],
@@ -191,7 +194,7 @@ __device__ __forceinline__ void mfma_half(const Frags<WN>& F, const uint32_t (&s
 #pragma unroll
             for (int j = 0; j < L::TN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8_t, F.a[i]), __builtin_bit_cast(bf16x8_t, F.b[j]),
+                    __builtin_bit_cast(bf16x8_t, F.b[j]), __builtin_bit_cast(bf16x8_t, F.a[i]),
                     acc[i][j], 0, 0, 0);
         return;
     }
@@ -203,7 +206,7 @@ __device__ __forceinline__ void mfma_half(const Frags<WN>& F, const uint32_t (&s
             const v8i fb =
                 (v8i){(int)F.b[j].x, (int)F.b[j].y, (int)F.b[j].z, (int)F.b[j].w, 0, 0, 0, 0};
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fa, fb, acc[i][j], 4, 4, 2 * KK, (int)sa[i], 2 * KK, (int)sb[j]);
+                fb, fa, acc[i][j], 4, 4, 2 * KK, (int)sb[j], 2 * KK, (int)sa[i]);
         }
     }
 }
@@ -405,8 +408,9 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
 
     // ---- epilogue: through LDS, so every lane writes 16 contiguous bytes ----
     // Each wave stages its tile 32 rows at a time in a private LDS region
-    // (row pitch padded by 16 bytes), then reads it back as 16-byte row
-    // chunks.
+    // (row pitch padded by 16 bytes; a lane writes its four consecutive
+    // columns of a row as one 8- or 16-byte access), then reads it back as
+    // 16-byte row chunks.
     __syncthreads();  // all waves are done with the operand stages
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int PITCH = L::WCOLS * ESZ + 16;
@@ -426,14 +430,21 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rl = 8 * (r >> 2) + 4 * half + (r & 3);
-                const int cl = j * 32 + l32;
-                if (OUT_BF16)
-                    *(uint16_t*)(reg + rl * PITCH + cl * 2) =
-                        (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
-                else
-                    *(float*)(reg + rl * PITCH + cl * 4) = acc[i][j][r];
+            for (int g = 0; g < 4; ++g) {
+                // row l32 of the pass, columns cl .. cl+3 of the wave's tile
+                const int cl = j * 32 + 8 * g + 4 * half;
+                uint8_t* dst = reg + l32 * PITCH + cl * ESZ;
+                const v16f& a = acc[i][j];
+                if (OUT_BF16) {
+                    // round-to-nearest-even packs (v_cvt_pk_bf16_f32)
+                    const bf16x2_t p0 = {(__bf16)a[4 * g], (__bf16)a[4 * g + 1]};
+                    const bf16x2_t p1 = {(__bf16)a[4 * g + 2], (__bf16)a[4 * g + 3]};
+                    *(uint2*)dst = make_uint2(__builtin_bit_cast(uint32_t, p0),
+                                              __builtin_bit_cast(uint32_t, p1));
+                } else {
+                    *(u32x4*)dst = (u32x4){as_u32(a[4 * g]), as_u32(a[4 * g + 1]),
+                                           as_u32(a[4 * g + 2]), as_u32(a[4 * g + 3])};
+                }
             }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
         __builtin_amdgcn_wave_barrier();
