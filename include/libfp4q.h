@@ -91,6 +91,28 @@ fp4q_status_t fp4q_quantize(const void* x, fp4q_dtype_t x_dtype, int64_t rows, i
                             void* stream);
 
 /*
+ * fp4q_quantize_dual -- both block orientations of one tensor in one pass:
+ * exactly the outputs of
+ *   fp4q_quantize(x, ..., block, FP4Q_BLOCK_ROW, round_row, seed_row,
+ *                 rng_offset, row_codes, row_scales)
+ *   fp4q_quantize(x, ..., block, FP4Q_BLOCK_COL, round_col, seed_col,
+ *                 rng_offset, col_codes, col_scales)
+ * (layouts, rounding and random streams as there), reading x once.  A
+ * training step needs an activation, a weight and an output gradient in both
+ * orientations (forward GEMM operand and backward transposed operand, the
+ * pages' forward/backward split of the FP4 linear layer, MSRA FP4-training
+ * summary page, sec. 四), so one read serves both.
+ *   rows % block == 0 and cols % block == 0; other arguments and errors as
+ *   fp4q_quantize.  bf16 input runs fused; fp32 input runs as the two
+ *   separate passes.
+ */
+fp4q_status_t fp4q_quantize_dual(const void* x, fp4q_dtype_t x_dtype, int64_t rows, int64_t cols,
+                                 int64_t ld_x, int32_t block, fp4q_round_t round_row,
+                                 uint64_t seed_row, fp4q_round_t round_col, uint64_t seed_col,
+                                 uint64_t rng_offset, uint8_t* row_codes, uint8_t* row_scales,
+                                 uint8_t* col_codes, uint8_t* col_scales, void* stream);
+
+/*
  * fp4q_dequantize -- the QDQ partner (MXFP4 tutorial page, sec. 6.1): element
  * value(code) * 2^(byte-127), exact in fp32 and bf16 (results beyond the fp32
  * range become Inf; byte 0xFF gives NaN for the whole block).

@@ -20,7 +20,8 @@ STE, DGE = 0, 1
 STATUS = {0: "FP4Q_OK", 1: "FP4Q_ERR_INVALID", 2: "FP4Q_ERR_UNSUPPORTED",
           3: "FP4Q_ERR_ALIGNMENT", 4: "FP4Q_ERR_WORKSPACE", 5: "FP4Q_ERR_HIP"}
 
-EXPORTS = ["fp4q_quantize", "fp4q_dequantize", "fp4q_grad_estimate", "fp4q_gemm",
+EXPORTS = ["fp4q_quantize", "fp4q_quantize_dual", "fp4q_dequantize", "fp4q_grad_estimate",
+           "fp4q_gemm",
            "fp4q_hcp_workspace_bytes", "fp4q_hcp_residual_add", "fp4q_status_string",
            "fp4q_last_error", "fp4q_abi_version"]
 
@@ -46,6 +47,8 @@ def lib():
                                    _ct.c_float, _ct.c_size_t)
         sig = {
             "fp4q_quantize": (I32, [P, I32, I64, I64, I64, I32, I32, I32, U64, U64, P, P, P]),
+            "fp4q_quantize_dual": (I32, [P, I32, I64, I64, I64, I32, I32, U64, I32, U64, U64, P, P,
+                                         P, P, P]),
             "fp4q_dequantize": (I32, [P, P, I64, I64, I32, P, I32, P]),
             "fp4q_grad_estimate": (I32, [I32, P, I32, P, I32, I64, I64, I32, I32, F, F, P, I32,
                                          P]),
@@ -121,6 +124,28 @@ def quantize(x, block=32, axis=ROW, rounding=RNE, seed=0, rng_offset=0, codes=No
     _check(lib().fp4q_quantize(_ptr(x), _dt(x), rows, cols, x.stride(0), block, axis, rounding,
                                seed, rng_offset, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
+
+
+def quantize_dual(x, block=32, round_row=RNE, seed_row=0, round_col=RNE, seed_col=0,
+                  rng_offset=0, out=None, stream=None):
+    """Both orientations in one pass: returns ((row codes, row scales),
+    (col codes, col scales)), identical to quantize(x, block, ROW, round_row,
+    seed_row, rng_offset) and quantize(x, block, COL, round_col, seed_col,
+    rng_offset).  `out` may give the four output tensors."""
+    torch = _torch()
+    _need_cuda(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    if out is None:
+        u8 = dict(dtype=torch.uint8, device=x.device)
+        out = (torch.empty((rows, cols // 2), **u8), torch.empty((rows, cols // block), **u8),
+               torch.empty((cols, rows // 2), **u8), torch.empty((cols, rows // block), **u8))
+    rc, rs, cc, cs = out
+    _check(lib().fp4q_quantize_dual(_ptr(x), _dt(x), rows, cols, x.stride(0), block, round_row,
+                                    seed_row, round_col, seed_col, rng_offset, _ptr(rc), _ptr(rs),
+                                    _ptr(cc), _ptr(cs), _stream(stream)))
+    return (rc, rs), (cc, cs)
 
 
 def dequantize(codes, scales, block=32, out_dtype=None, out=None, stream=None):

@@ -87,6 +87,47 @@ fp4q_status_t fp4q_quantize(const void* x, fp4q_dtype_t x_dtype, int64_t rows, i
     return hip_status(e, "quantize launch");
 }
 
+fp4q_status_t fp4q_quantize_dual(const void* x, fp4q_dtype_t x_dtype, int64_t rows, int64_t cols,
+                                 int64_t ld_x, int32_t block, fp4q_round_t round_row,
+                                 uint64_t seed_row, fp4q_round_t round_col, uint64_t seed_col,
+                                 uint64_t rng_offset, uint8_t* row_codes, uint8_t* row_scales,
+                                 uint8_t* col_codes, uint8_t* col_scales, void* stream) {
+    if (!x || !row_codes || !row_scales || !col_codes || !col_scales)
+        return fail(FP4Q_ERR_INVALID, "quantize_dual: null pointer");
+    if (!valid_dtype(x_dtype)) return fail(FP4Q_ERR_INVALID, "quantize_dual: bad x dtype %d", x_dtype);
+    if (rows <= 0 || cols <= 0)
+        return fail(FP4Q_ERR_INVALID, "quantize_dual: rows=%lld cols=%lld", (long long)rows,
+                    (long long)cols);
+    if (ld_x < cols) return fail(FP4Q_ERR_INVALID, "quantize_dual: ld_x < cols");
+    if (!valid_block(block)) return fail(FP4Q_ERR_INVALID, "quantize_dual: block %d", block);
+    if ((round_row != FP4Q_RNE && round_row != FP4Q_SR) ||
+        (round_col != FP4Q_RNE && round_col != FP4Q_SR))
+        return fail(FP4Q_ERR_INVALID, "quantize_dual: bad round");
+    if (rows % block || cols % block)
+        return fail(FP4Q_ERR_INVALID, "quantize_dual: rows and cols must be multiples of block");
+    if (rows > kMaxElems / ld_x) return fail(FP4Q_ERR_INVALID, "quantize_dual: tensor too large");
+    if (!aligned16(x) || !aligned16(row_codes) || !aligned16(row_scales) || !aligned16(col_codes) ||
+        !aligned16(col_scales) || (ld_x * esize(x_dtype)) % 16)
+        return fail(FP4Q_ERR_ALIGNMENT,
+                    "quantize_dual: pointers and row stride must be 16-byte aligned");
+    hipError_t e;
+    if (x_dtype == FP4Q_BF16) {
+        e = fp4q::launch_quantize_dual(x, rows, cols, ld_x, block, round_row == FP4Q_SR, seed_row,
+                                       round_col == FP4Q_SR, seed_col, rng_offset, row_codes,
+                                       row_scales, col_codes, col_scales, (hipStream_t)stream);
+    } else {
+        // fp32 input: the two passes run as separate launches
+        e = fp4q::launch_quantize_row(x, x_dtype, rows, cols, ld_x, block, round_row == FP4Q_SR,
+                                      seed_row, rng_offset, row_codes, row_scales,
+                                      (hipStream_t)stream);
+        if (e == hipSuccess)
+            e = fp4q::launch_quantize_col(x, x_dtype, rows, cols, ld_x, block,
+                                          round_col == FP4Q_SR, seed_col, rng_offset, col_codes,
+                                          col_scales, (hipStream_t)stream);
+    }
+    return hip_status(e, "quantize_dual launch");
+}
+
 fp4q_status_t fp4q_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                               int64_t k, int32_t block, void* y, fp4q_dtype_t y_dtype,
                               void* stream) {

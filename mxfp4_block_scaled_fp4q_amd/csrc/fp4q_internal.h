@@ -33,6 +33,10 @@ hipError_t launch_quantize_row(const void* x, int dtype, int64_t rows, int64_t c
 hipError_t launch_quantize_col(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                                int block, bool sr, uint64_t seed, uint64_t off, uint8_t* codes,
                                uint8_t* scales, hipStream_t s);
+hipError_t launch_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ld, int block,
+                                bool sr_row, uint64_t seed_row, bool sr_col, uint64_t seed_col,
+                                uint64_t off, uint8_t* codes_r, uint8_t* scales_r,
+                                uint8_t* codes_c, uint8_t* scales_c, hipStream_t s);
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
                              int block, void* y, int ydtype, hipStream_t s);
 hipError_t launch_ste(const void* g, int gdtype, int64_t n, void* out, int odtype, hipStream_t s);

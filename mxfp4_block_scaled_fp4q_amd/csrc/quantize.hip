@@ -191,28 +191,43 @@ hipError_t launch_quantize_row(const void* x, int dtype, int64_t rows, int64_t c
 // ---------------------------------------------------------------------------
 // COL
 // ---------------------------------------------------------------------------
-// One workgroup (256 threads) quantises a tile of 256 rows x TC columns
-// (TC = 128 bf16 / 64 fp32, 256 bytes of each row).  Thread (rg, cg) =
-// (tid / 16, tid % 16) holds rows rg*16 .. rg*16+15 of columns
+// One workgroup (256 threads) quantises a tile of TR = 16*RPT rows x TC
+// columns (TC = 128 bf16 / 64 fp32, 256 bytes of each row; RPT = 16, or 8
+// where the stochastic passes need the registers).  Thread (rg, cg) =
+// (tid / 16, tid % 16) holds rows rg*RPT .. rg*RPT+RPT-1 of columns
 // cg*CPT .. cg*CPT+CPT-1, one 16-byte load per row, so a wave's load covers
-// four 256-byte row segments.  Block maxima over the BLOCK/16 row groups of a
-// block meet in LDS.  Each thread turns its 16 rows of a column into 8 code
-// bytes; they are staged in LDS per column, and the tile's output (each
-// column's 128 contiguous code bytes, i.e. K-major rows of the transposed
-// operand) leaves with eight consecutive lanes writing one whole 128-byte
-// line, which is what makes this layout change run at streaming speed.
+// four 256-byte row segments.  Block maxima over the BLOCK/RPT row groups of
+// a block meet in LDS.  Each thread turns its RPT rows of a column into RPT/2
+// code bytes; they are staged in LDS per column, and the tile's output (each
+// column's TR/2 contiguous code bytes, i.e. K-major rows of the transposed
+// operand) leaves as one contiguous segment per column (128 or 64 bytes)
+// written by consecutive lanes, which is what makes this layout change run
+// at streaming speed.
 // ALIGNED (cols and the offset multiples of 8): every row's positions
 // c0 .. c0+CPT-1 lie in one Philox counter, so each row takes one call.
-template <int IN_BF16, int BLOCK, int SR, int ALIGNED>
+//
+// ROW != 0 (bf16 only, cols % BLOCK == 0): the same pass also writes the ROW
+// quantisation of the tile (ROW = 1 nearest-even, 2 stochastic with key
+// kr0, kr1, 3 stochastic with the column pass's key, so one Philox stream
+// serves both): each thread's 8 columns of a row are a quarter/half/... of a
+// row block whose BLOCK/8 threads are adjacent lanes of one 16-lane row,
+// so the row-block maximum is a DPP reduction.
+template <int IN_BF16, int BLOCK, int SR, int ALIGNED, int ROW, int RPT>
 __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
     const void* __restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t k0, uint32_t k1,
-    uint64_t rng_off, int64_t nrb, int64_t n_ctiles) {
+    uint64_t rng_off, int64_t nrb, int64_t n_ctiles, uint8_t* __restrict__ codes_r,
+    uint8_t* __restrict__ scales_r, uint32_t kr0, uint32_t kr1) {
+    static_assert(ROW == 0 || IN_BF16, "the fused row pass is for bf16 input");
+    static_assert(ROW != 3 || SR, "a shared random stream needs the stochastic column pass");
+    constexpr int RG = BLOCK / 8;  // lanes per row block (fused row pass)
     constexpr int CPT = IN_BF16 ? 8 : 4;  // columns per thread
     constexpr int TC = 16 * CPT;          // columns per tile
-    constexpr int TR = 256;               // rows per tile
-    constexpr int RPT = 16;               // rows per thread
+    constexpr int TR = 16 * RPT;          // rows per tile (RPT rows per thread: 16, or 8
+                                          // where the stochastic passes need registers)
     constexpr int NPB = BLOCK / RPT;      // row groups per block
+    constexpr int WPT = RPT / 8;          // code words per column per thread
+    static_assert(RPT == 8 || RPT == 16, "8 or 16 rows per thread");
     constexpr int BPT = TR / BLOCK;       // blocks per tile (per column)
     constexpr int PITCH = TR / 2 + 16;    // staged code bytes per column (padded)
     static_assert(kThreads == 256, "16 x 16 thread layout");
@@ -226,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
     const int64_t tcol = blockIdx.x - trow * n_ctiles;
     const int64_t r0 = trow * TR;                       // first row of the tile
     const int64_t c0 = tcol * TC + cg * CPT;            // first column of this thread
-    const int vrows = (int)min<int64_t>(rows - r0, TR);  // a multiple of 16
+    const int vrows = (int)min<int64_t>(rows - r0, TR);  // a multiple of the block
     const bool rows_ok = rg * RPT < vrows;
     const bool full = c0 + CPT <= cols;
 
@@ -261,6 +276,72 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
         if (IN_BF16) return (j & 1) ? (v[i][j >> 1] & 0xFFFF0000u) : (v[i][j >> 1] << 16);
         return v[i][j];
     };
+    // E8M0 byte of the row block holding thread row i (DPP maximum over the
+    // block's RG lanes)
+    auto row_byte = [&](int i) -> uint32_t {
+        const u16x2_t m0 = __builtin_bit_cast(u16x2_t, v[i][0] & 0x7FFF7FFFu);
+        const u16x2_t m1 = __builtin_bit_cast(u16x2_t, v[i][1] & 0x7FFF7FFFu);
+        const u16x2_t m2 = __builtin_bit_cast(u16x2_t, v[i][2] & 0x7FFF7FFFu);
+        const u16x2_t m3 = __builtin_bit_cast(u16x2_t, v[i][3] & 0x7FFF7FFFu);
+        const u16x2_t mm = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1),
+                                                     __builtin_elementwise_max(m2, m3));
+        const uint32_t ra = group_max_u32<RG>(((uint32_t)max(mm.x, mm.y)) << 16);
+        return ra >= 0x7F800000u ? 0xFFu : e8m0_from_amax(ra);
+    };
+
+    if (ROW == 1 || ROW == 2) {
+        // ROW blocks: rows of this thread, 8 columns each, BLOCK/8 lanes per block
+        constexpr int G = BLOCK / 8;
+        const int64_t rcodes = cols / 2, rscales = cols / BLOCK;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int64_t r = r0 + rg * RPT + i;
+            const u16x2_t m0 = __builtin_bit_cast(u16x2_t, v[i][0] & 0x7FFF7FFFu);
+            const u16x2_t m1 = __builtin_bit_cast(u16x2_t, v[i][1] & 0x7FFF7FFFu);
+            const u16x2_t m2 = __builtin_bit_cast(u16x2_t, v[i][2] & 0x7FFF7FFFu);
+            const u16x2_t m3 = __builtin_bit_cast(u16x2_t, v[i][3] & 0x7FFF7FFFu);
+            const u16x2_t mm = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1),
+                                                         __builtin_elementwise_max(m2, m3));
+            const uint32_t ra = group_max_u32<G>(((uint32_t)max(mm.x, mm.y)) << 16);
+            const bool rnf = ra >= 0x7F800000u;
+            const uint32_t rbyte = rnf ? 0xFFu : e8m0_from_amax(ra);
+            const float rsc = e8m0_scale_f32(rnf ? 0u : rbyte);
+            uint32_t packed = 0;
+            if (ROW == 1) {
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                    packed, __builtin_bit_cast(bf16x2_t, v[i][0]), rsc, 0);
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                    packed, __builtin_bit_cast(bf16x2_t, v[i][1]), rsc, 1);
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                    packed, __builtin_bit_cast(bf16x2_t, v[i][2]), rsc, 2);
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                    packed, __builtin_bit_cast(bf16x2_t, v[i][3]), rsc, 3);
+            } else {
+                uint32_t wr[4];
+                const uint64_t q0 = (uint64_t)r * (uint64_t)cols + (uint64_t)c0 + rng_off;
+                if (ALIGNED) {
+                    const uint64_t n0 = q0 >> 3;
+                    const Philox4 a =
+                        philox4x32_10((uint32_t)n0, (uint32_t)(n0 >> 32), 0u, 0u, kr0, kr1);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) wr[k] = a.v[k];
+                } else {
+                    sr_words8(q0, kr0, kr1, wr);
+                }
+                float xf[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    xf[j] = (j & 1) ? bf16_hi(v[i][j >> 1]) : bf16_lo(v[i][j >> 1]);
+                packed = sr_pack8(xf, rsc, wr);
+            }
+            if (rnf) packed = 0;
+            if (rows_ok && c0 < cols) {
+                *(uint32_t*)(codes_r + r * rcodes + c0 / 2) = packed;
+                if ((cg % G) == 0) scales_r[r * rscales + c0 / BLOCK] = (uint8_t)rbyte;
+            }
+            if (ROW == 2) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
 
     // block maxima: this thread's 16 rows, then across the block's row groups
     uint32_t amax[CPT];
@@ -286,13 +367,14 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
     }
 
     // 16 rows of each column -> 8 code bytes (rows 2p, 2p+1 -> byte p)
-    uint32_t out[CPT][2];
+    uint32_t out[CPT][WPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const bool nf = amax[j] >= 0x7F800000u;
         const uint32_t byte = nf ? 0xFFu : e8m0_from_amax(amax[j]);
         const float sc = e8m0_scale_f32(nf ? 0u : byte);
-        out[j][0] = out[j][1] = 0;
+#pragma unroll
+        for (int q = 0; q < WPT; ++q) out[j][q] = 0;
         if (!SR) {
 #pragma unroll
             for (int p = 0; p < RPT / 2; ++p) {
@@ -318,7 +400,9 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
                 }
             }
         }
-        if (nf) out[j][0] = out[j][1] = 0;  // SR codes are filled in below
+        if (nf)
+#pragma unroll
+            for (int q = 0; q < WPT; ++q) out[j][q] = 0;  // SR codes are filled in below
         if ((rg % NPB) == 0 && rows_ok) sst[cg * CPT + j][rg / NPB] = (uint8_t)byte;
     }
     if (SR) {
@@ -335,7 +419,10 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
         for (int p = 0; p < RPT / 2; ++p) {
             const int64_t r = r0 + rg * RPT + 2 * p;
             uint32_t w0[4], w1[4];
-            const uint64_t q0 = (uint64_t)r * (uint64_t)cols + (uint64_t)c0 + rng_off;
+            uint64_t q0 = (uint64_t)r * (uint64_t)cols + (uint64_t)c0 + rng_off;
+            // keeps each pair's Philox chains in place (hoisting all of them
+            // to the top of the loop multiplies the live registers)
+            asm volatile("" : "+v"(q0));
             if (ALIGNED) {
                 // bf16: lanes 0..7 of counter q0 / 8; fp32: lanes 0..3 or 4..7
                 const uint64_t n0 = q0 >> 3, n1 = (q0 + (uint64_t)cols) >> 3;
@@ -359,27 +446,52 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
                                             sc[j], u0 << 16, u1 << 15);
                 out[j][p / 4] |= (nf[j] ? 0u : bt) << (8 * (p & 3));
             }
+            if (ROW == 3) {
+                // the same words give rows 2p and 2p+1 their ROW codes
+                const int64_t rcodes = cols / 2, rscales = cols / BLOCK;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int i = 2 * p + h;
+                    const uint32_t rbyte = row_byte(i);
+                    float xf[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        xf[j] = (j & 1) ? bf16_hi(v[i][j >> 1]) : bf16_lo(v[i][j >> 1]);
+                    uint32_t packed = sr_pack8(xf, e8m0_scale_f32(rbyte == 0xFFu ? 0u : rbyte),
+                                               h ? w1 : w0);
+                    if (rbyte == 0xFFu) packed = 0;
+                    if (rows_ok && c0 < cols) {
+                        *(uint32_t*)(codes_r + (r + h) * rcodes + c0 / 2) = packed;
+                        if ((cg % RG) == 0) scales_r[(r + h) * rscales + c0 / BLOCK] = (uint8_t)rbyte;
+                    }
+                }
+            }
             // one row pair at a time: interleaving the pairs' Philox chains
             // only raises register pressure (and lowers occupancy)
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // stage: column cg*CPT + j, bytes rg*8 .. rg*8+7 of its tile segment
+    // stage: column cg*CPT + j, bytes rg*RPT/2 .. of its tile segment
 #pragma unroll
-    for (int j = 0; j < CPT; ++j)
-        *(uint2*)(cst + (cg * CPT + j) * PITCH + rg * 8) = make_uint2(out[j][0], out[j][1]);
+    for (int j = 0; j < CPT; ++j) {
+        if (WPT == 2)
+            *(uint2*)(cst + (cg * CPT + j) * PITCH + rg * 8) = make_uint2(out[j][0], out[j][WPT - 1]);
+        else
+            *(uint32_t*)(cst + (cg * CPT + j) * PITCH + rg * 4) = out[j][0];
+    }
     __syncthreads();
 
-    // codes: each column's vrows/2 bytes; eight consecutive lanes write one
-    // 128-byte line when the column stride allows 16-byte stores
+    // codes: each column's vrows/2 bytes, written by TR/32 consecutive lanes
+    // with 16-byte stores when the column stride allows them
     const int64_t half_rows = rows / 2;
     const int vbytes = vrows / 2;
     const int64_t cbase = tcol * TC;
+    constexpr int CH16 = TR / 32;  // 16-byte chunks per column segment
     if ((half_rows & 15) == 0) {
 #pragma unroll
-        for (int k = 0; k < TC * 8 / kThreads; ++k) {
+        for (int k = 0; k < TC * CH16 / kThreads; ++k) {
             const int idx = k * kThreads + tid;
-            const int col = idx >> 3, ch = idx & 7;
+            const int col = idx / CH16, ch = idx % CH16;
             const int64_t c = cbase + col;
             if (c < cols && ch * 16 < vbytes)
                 *(uint4*)(codes + c * half_rows + r0 / 2 + ch * 16) =
@@ -387,9 +499,9 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < TC * 16 / kThreads; ++k) {
+        for (int k = 0; k < TC * 2 * CH16 / kThreads; ++k) {
             const int idx = k * kThreads + tid;
-            const int col = idx >> 4, ch = idx & 15;
+            const int col = idx / (2 * CH16), ch = idx % (2 * CH16);
             const int64_t c = cbase + col;
             if (c < cols && ch * 8 < vbytes)
                 *(uint2*)(codes + c * half_rows + r0 / 2 + ch * 8) =
@@ -409,26 +521,38 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
     }
 }
 
-template <int IN_BF16, int SR, int AL>
-static hipError_t col_dispatch(int block, dim3 grid, hipStream_t s, const void* x, int64_t rows,
+// Rows per thread of the column-pass tile: 8 where a stochastic pass runs
+// (its Philox chains need the registers), else 16.
+template <int SR, int ROW>
+struct ColRows {
+    static constexpr int value = (SR || ROW >= 2) ? 8 : 16;
+};
+
+template <int IN_BF16, int SR, int AL, int ROW>
+static hipError_t col_dispatch(int block, int64_t nct, hipStream_t s, const void* x, int64_t rows,
                                int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
-                               uint32_t k0, uint32_t k1, uint64_t off, int64_t nrb, int64_t nct) {
+                               uint32_t k0, uint32_t k1, uint64_t off, int64_t nrb,
+                               uint8_t* codes_r = nullptr, uint8_t* scales_r = nullptr,
+                               uint32_t kr0 = 0, uint32_t kr1 = 0) {
+    constexpr int RPT = ColRows<SR, ROW>::value;
+    const int64_t nrt = (rows + 16 * RPT - 1) / (16 * RPT);
+    const dim3 grid((unsigned)(nrt * nct));
     switch (block) {
         case 16:
-            quantize_col_kernel<IN_BF16, 16, SR, AL><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct);
+            quantize_col_kernel<IN_BF16, 16, SR, AL, ROW, RPT><<<grid, kThreads, 0, s>>>(
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct, codes_r, scales_r, kr0, kr1);
             break;
         case 32:
-            quantize_col_kernel<IN_BF16, 32, SR, AL><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct);
+            quantize_col_kernel<IN_BF16, 32, SR, AL, ROW, RPT><<<grid, kThreads, 0, s>>>(
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct, codes_r, scales_r, kr0, kr1);
             break;
         case 64:
-            quantize_col_kernel<IN_BF16, 64, SR, AL><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct);
+            quantize_col_kernel<IN_BF16, 64, SR, AL, ROW, RPT><<<grid, kThreads, 0, s>>>(
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct, codes_r, scales_r, kr0, kr1);
             break;
         default:
-            quantize_col_kernel<IN_BF16, 128, SR, AL><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct);
+            quantize_col_kernel<IN_BF16, 128, SR, AL, ROW, RPT><<<grid, kThreads, 0, s>>>(
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct, codes_r, scales_r, kr0, kr1);
             break;
     }
     return hipGetLastError();
@@ -439,27 +563,60 @@ hipError_t launch_quantize_col(const void* x, int dtype, int64_t rows, int64_t c
                                uint8_t* scales, hipStream_t s) {
     const int64_t cols_per_tile = dtype == BF16 ? 128 : 64;
     const int64_t nct = (cols + cols_per_tile - 1) / cols_per_tile;
-    const int64_t nrt = (rows + 255) / 256;
     const int64_t nrb = rows / block;
-    dim3 grid((unsigned)(nrt * nct));
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     const bool al = (cols % 8) == 0 && (off % 8) == 0;
     if (dtype == BF16) {
         if (!sr)
-            return col_dispatch<1, 0, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1,
-                                         off, nrb, nct);
-        return al ? col_dispatch<1, 1, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0,
-                                          k1, off, nrb, nct)
-                  : col_dispatch<1, 1, 0>(block, grid, s, x, rows, cols, ld, codes, scales, k0,
-                                          k1, off, nrb, nct);
+            return col_dispatch<1, 0, 1, 0>(block, nct, s, x, rows, cols, ld, codes, scales, k0,
+                                            k1, off, nrb);
+        return al ? col_dispatch<1, 1, 1, 0>(block, nct, s, x, rows, cols, ld, codes, scales, k0,
+                                             k1, off, nrb)
+                  : col_dispatch<1, 1, 0, 0>(block, nct, s, x, rows, cols, ld, codes, scales, k0,
+                                             k1, off, nrb);
     }
     if (!sr)
-        return col_dispatch<0, 0, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1, off,
-                                     nrb, nct);
-    return al ? col_dispatch<0, 1, 1>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1,
-                                      off, nrb, nct)
-              : col_dispatch<0, 1, 0>(block, grid, s, x, rows, cols, ld, codes, scales, k0, k1,
-                                      off, nrb, nct);
+        return col_dispatch<0, 0, 1, 0>(block, nct, s, x, rows, cols, ld, codes, scales, k0, k1,
+                                        off, nrb);
+    return al ? col_dispatch<0, 1, 1, 0>(block, nct, s, x, rows, cols, ld, codes, scales, k0, k1,
+                                         off, nrb)
+              : col_dispatch<0, 1, 0, 0>(block, nct, s, x, rows, cols, ld, codes, scales, k0, k1,
+                                         off, nrb);
+}
+
+// Both quantisations of a bf16 tensor in one pass (rows and cols multiples
+// of the block): ROW blocks into codes_r/scales_r, COL blocks into
+// codes_c/scales_c, each exactly as its own launch would write them.
+hipError_t launch_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ld, int block,
+                                bool sr_row, uint64_t seed_row, bool sr_col, uint64_t seed_col,
+                                uint64_t off, uint8_t* codes_r, uint8_t* scales_r,
+                                uint8_t* codes_c, uint8_t* scales_c, hipStream_t s) {
+    const int64_t nct = (cols + 127) / 128;
+    const int64_t nrb = rows / block;
+    const uint32_t k0 = (uint32_t)seed_col, k1 = (uint32_t)(seed_col >> 32);
+    const uint32_t kr0 = (uint32_t)seed_row, kr1 = (uint32_t)(seed_row >> 32);
+    const bool al = (cols % 8) == 0 && (off % 8) == 0;
+#define FP4Q_DUAL(SRC, AL, ROW)                                                                 \
+    return col_dispatch<1, SRC, AL, ROW>(block, nct, s, x, rows, cols, ld, codes_c, scales_c, k0, \
+                                         k1, off, nrb, codes_r, scales_r, kr0, kr1)
+    const bool shared = sr_row && sr_col && seed_row == seed_col;
+    if (al) {
+        if (sr_col) {
+            if (shared) FP4Q_DUAL(1, 1, 3);
+            if (sr_row) FP4Q_DUAL(1, 1, 2);
+            FP4Q_DUAL(1, 1, 1);
+        }
+        if (sr_row) FP4Q_DUAL(0, 1, 2);
+        FP4Q_DUAL(0, 1, 1);
+    }
+    if (sr_col) {
+        if (shared) FP4Q_DUAL(1, 0, 3);
+        if (sr_row) FP4Q_DUAL(1, 0, 2);
+        FP4Q_DUAL(1, 0, 1);
+    }
+    if (sr_row) FP4Q_DUAL(0, 0, 2);
+    FP4Q_DUAL(0, 0, 1);
+#undef FP4Q_DUAL
 }
 
 }  // namespace fp4q

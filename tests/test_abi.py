@@ -156,3 +156,22 @@ def test_fastdiv_formula():
         for n in [0, 1, d - 1, d, d + 1, (1 << 31) - 1] + \
                 [random.randrange(0, 1 << 31) for _ in range(500)]:
             assert ((((n * mul) >> 32) + n) >> l) == n // d
+
+
+def test_quantize_dual_validation(L):
+    d = L.fp4q_quantize_dual
+
+    def call(x=FAKE, dt=1, rows=64, cols=64, ld=64, block=32, rr=0, rc=1, a=FAKE, b=FAKE,
+             c=FAKE, e=FAKE):
+        return d(x, dt, rows, cols, ld, block, rr, 1, rc, 2, 0, a, b, c, e, NUL)
+    assert call(x=NUL) == 1
+    assert call(e=NUL) == 1
+    assert call(rows=48) == 1          # rows % block
+    assert call(cols=48, ld=48) == 1   # cols % block
+    assert call(rr=2) == 1
+    assert call(rc=5) == 1
+    assert call(block=24) == 1
+    assert call(ld=32) == 1
+    assert call(c=FAKE_MIS) == 3
+    assert call(ld=68) == 3            # bf16 row stride 136 bytes
+    assert L.fp4q_last_error().decode()

@@ -91,7 +91,8 @@ def test_every_bf16_pattern(orc, block):
 def test_fp32_special_values(orc):
     """Random fp32 bit patterns (subnormals, NaN, Inf included), plus blocks
     whose elements sit far below the block maximum (scaled values in the
-    subnormal range, where SR must still round up for u == 0)."""
+    subnormal range, where the truncated 16-bit fraction is 0 and SR keeps
+    the lower neighbour)."""
     rng = np.random.default_rng(21)
     bits = rng.integers(0, 1 << 32, (128, 256), dtype=np.uint64).astype(np.uint32)
     x = bits.view(np.float32).copy()
