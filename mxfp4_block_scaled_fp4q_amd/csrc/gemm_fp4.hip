@@ -78,7 +78,9 @@ struct Layout {
     static constexpr int TN = 8 / WN;          // 32-column MFMA tiles per wave
     static constexpr int WCOLS = 32 * TN;      // columns per wave
     static constexpr int RPW = 16 / WAVES;     // 1 KB code regions per operand per wave per step
-    static_assert(WAVES == 8, "the scale-group schedule assumes 8 waves");
+    static constexpr int SROWS = 512 / WAVES;  // scale rows (A then B) fetched per wave
+    static constexpr int SPIECES = SROWS / 8;  // 8-row scale pieces per wave per group
+    static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
 };
 
 // 16-byte slot of chunk c (bytes 16c .. 16c+15 of the step) of row j within
@@ -115,18 +117,18 @@ __device__ __forceinline__ void issue_codes(Src<WN>& src, uint8_t* stage, int wa
     src.soff += advance ? BKB : 0;
 }
 
-// Scale piece P (0..7) of this wave for group g: combined rows
-// wave*64 + P*8 .. +7 (A rows 0..255, then B rows), 32 bytes each; lane
-// 8j + pos loads word pos ^ (P % 4) of the piece's row j, so that in LDS
-// word s of row R sits at R*32 + 4 (s ^ ((R / 8) % 4)).  The group offset
-// is part of the per-lane offset so the range check covers it.
-template <int WN, int P>
+// Scale piece P (0 .. SPIECES-1, a compile-time constant after unrolling)
+// of this wave for group g: combined rows wave*SROWS + P*8 .. +7 (A rows
+// 0..255, then B rows), 32 bytes each; lane 8j + pos loads word
+// pos ^ (P % 4) of the piece's row j, so that in LDS word s of row R sits at
+// R*32 + 4 (s ^ ((R / 8) % 4)) (SROWS / 8 is a multiple of 4).  The group
+// offset is part of the per-lane offset so the range check covers it.
+template <int WN>
 __device__ __forceinline__ void issue_scale_piece(const Src<WN>& src, uint8_t* sbuf, int wave,
-                                                  int kscale, int g) {
+                                                  int kscale, int g, int P) {
     const uint32_t voff = src.vsc[P & 3] + (uint32_t)(P * 8 * kscale + g * SGB);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rsc,
-                                             (lds_ptr_t)(sbuf + (wave * 64 + P * 8) * SGB), 4,
-                                             voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src.rsc, (lds_ptr_t)(sbuf + (wave * Layout<WN>::SROWS + P * 8) * SGB), 4, voff, 0, 0, 0);
 }
 
 template <int WN>
@@ -268,12 +270,13 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
 #pragma unroll
         for (int q = 0; q < L::RPW; ++q)
             src.vrow[q] = (uint32_t)(((q * L::WAVES + wave) * 16 + j) * kbytes + c * 16);
-        // waves 0..3 fetch A scale rows, waves 4..7 B scale rows
-        src.rsc = wave < 4 ? __builtin_amdgcn_make_buffer_rsrc((void*)(as + (int64_t)m0 * kscale),
-                                                               (short)0, rows_a * kscale, BUF_FLAGS)
-                           : __builtin_amdgcn_make_buffer_rsrc((void*)(bs + (int64_t)n0 * kscale),
-                                                               (short)0, rows_b * kscale, BUF_FLAGS);
-        const int sbase = ((wave & 3) * 64 + (lane >> 3)) * kscale;
+        // the first half of the waves fetch A scale rows, the second half B
+        constexpr int HW = L::WAVES / 2;
+        src.rsc = wave < HW ? __builtin_amdgcn_make_buffer_rsrc((void*)(as + (int64_t)m0 * kscale),
+                                                                (short)0, rows_a * kscale, BUF_FLAGS)
+                            : __builtin_amdgcn_make_buffer_rsrc((void*)(bs + (int64_t)n0 * kscale),
+                                                                (short)0, rows_b * kscale, BUF_FLAGS);
+        const int sbase = ((wave % HW) * L::SROWS + (lane >> 3)) * kscale;
 #pragma unroll
         for (int q = 0; q < 4; ++q) src.vsc[q] = (uint32_t)(sbase + (((lane & 7) ^ q) << 2));
         src.soff = 0;
@@ -320,17 +323,11 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
     // loads issued after the code loads of step t + 1, at the end of step t
     // with t % 8 == p: those of steps t - 1 and t plus the scale pieces
     // issued after the code loads in step t - 2
-#define FP4Q_PIECES(p) ((BF16OPS || ((p) & 7) >= 4) ? 0 : 2)
+#define FP4Q_PIECES(p) ((BF16OPS || ((p) & 7) >= 4) ? 0 : L::SPIECES / 4)
 #define FP4Q_BEHIND(p) (FP4Q_PIECES((p) + 6) + LC + FP4Q_PIECES((p) + 7) + LC + FP4Q_PIECES(p))
     if (!BF16OPS) {
-        issue_scale_piece<WN, 0>(src, sc0, wave, kscale, 0);
-        issue_scale_piece<WN, 1>(src, sc0, wave, kscale, 0);
-        issue_scale_piece<WN, 2>(src, sc0, wave, kscale, 0);
-        issue_scale_piece<WN, 3>(src, sc0, wave, kscale, 0);
-        issue_scale_piece<WN, 4>(src, sc0, wave, kscale, 0);
-        issue_scale_piece<WN, 5>(src, sc0, wave, kscale, 0);
-        issue_scale_piece<WN, 6>(src, sc0, wave, kscale, 0);
-        issue_scale_piece<WN, 7>(src, sc0, wave, kscale, 0);
+#pragma unroll
+        for (int q = 0; q < L::SPIECES; ++q) issue_scale_piece<WN>(src, sc0, wave, kscale, 0, q);
     }
     issue_codes<WN, BF16OPS>(src, st0, wave, 1 < ksteps);
     issue_codes<WN, BF16OPS>(src, st1, wave, 2 < ksteps);
@@ -352,8 +349,9 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
         read_frags<WN>(CUR, off1, wm, wn, FB);                                       \
         issue_codes<WN, BF16OPS>(src, NEXTL, wave, t_ + 4 < ksteps);                 \
         if (FP4Q_PIECES(P)) {                                                        \
-            issue_scale_piece<WN, 2 * ((P) & 3)>(src, SNXT, wave, kscale, t_ / SG + 1); \
-            issue_scale_piece<WN, 2 * ((P) & 3) + 1>(src, SNXT, wave, kscale, t_ / SG + 1); \
+            _Pragma("unroll") for (int q_ = 0; q_ < L::SPIECES / 4; ++q_)              \
+                issue_scale_piece<WN>(src, SNXT, wave, kscale, t_ / SG + 1,            \
+                                      ((P) & 3) * (L::SPIECES / 4) + q_);              \
         }                                                                            \
         __builtin_amdgcn_sched_barrier(0);                                           \
         mfma_half<WN, BF16OPS, 0>(FA, sa, sb, acc);                                  \
@@ -416,8 +414,11 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
     constexpr int PITCH = L::WCOLS * ESZ + 16;
     constexpr int EREG = 32 * PITCH;
     constexpr int PER_STAGE = STAGE / EREG;  // wave regions that fit in one stage
-    static_assert(L::WAVES <= 3 * PER_STAGE, "epilogue regions fit in three stages");
-    uint8_t* reg = (wave / PER_STAGE == 0 ? st0 : wave / PER_STAGE == 1 ? st1 : st2) +
+    static_assert(L::WAVES <= 4 * PER_STAGE, "epilogue regions fit in the four stages");
+    uint8_t* reg = (wave / PER_STAGE == 0   ? st0
+                    : wave / PER_STAGE == 1 ? st1
+                    : wave / PER_STAGE == 2 ? st2
+                                            : st3) +
                    (wave % PER_STAGE) * EREG;
     const int row0 = m0 + wm * 128;
     const int col0 = n0 + wn * L::WCOLS;

@@ -237,8 +237,16 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
 
     const int tid = threadIdx.x;
     const int cg = tid & 15, rg = tid >> 4;
-    const int64_t trow = blockIdx.x / n_ctiles;
-    const int64_t tcol = blockIdx.x - trow * n_ctiles;
+    // Workgroups are dealt to the eight XCDs in turn; remap so that each XCD
+    // takes a contiguous run of tiles (row-major), whose partial-line writes
+    // (row codes and scales, column scales) then meet in that XCD's L2.
+    int64_t wg = blockIdx.x;
+    {
+        const int64_t full = ((int64_t)gridDim.x / 8) * 8;
+        if (wg < full) wg = (wg % 8) * (full / 8) + wg / 8;
+    }
+    const int64_t trow = wg / n_ctiles;
+    const int64_t tcol = wg - trow * n_ctiles;
     const int64_t r0 = trow * TR;                       // first row of the tile
     const int64_t c0 = tcol * TC + cg * CPT;            // first column of this thread
     const int vrows = (int)min<int64_t>(rows - r0, TR);  // a multiple of the block
@@ -514,9 +522,22 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
         if (c < cols) {
             const int nb = vrows / BLOCK;
             uint8_t* dst = scales + c * nrb + r0 / BLOCK;
+            if (nb == BPT && BPT >= 4 && ((uintptr_t)dst % BPT) == 0) {
+                uint32_t w[BPT >= 4 ? BPT / 4 : 1];
 #pragma unroll
-            for (int b2 = 0; b2 < BPT; ++b2)
-                if (b2 < nb) dst[b2] = sst[tid][b2];
+                for (int q = 0; q < BPT / 4; ++q)
+                    w[q] = sst[tid][4 * q] | (sst[tid][4 * q + 1] << 8) |
+                           (sst[tid][4 * q + 2] << 16) | ((uint32_t)sst[tid][4 * q + 3] << 24);
+                if (BPT == 8)
+                    *(uint2*)dst = make_uint2(w[0], w[BPT / 4 - 1]);
+                else
+#pragma unroll
+                    for (int q = 0; q < BPT / 4; ++q) ((uint32_t*)dst)[q] = w[q];
+            } else {
+#pragma unroll
+                for (int b2 = 0; b2 < BPT; ++b2)
+                    if (b2 < nb) dst[b2] = sst[tid][b2];
+            }
         }
     }
 }
