@@ -333,13 +333,16 @@ def bench_outlier_layer(torch, fq, inputs, dev):
     xq = fq.quantize(X, 32, fq.ROW)
     wq = fq.quantize(W, 32, fq.COL)
     Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    Y2 = torch.empty((M, N), dtype=torch.float32, device=dev)
     ws = torch.empty(fq.hcp_workspace_bytes(M, N, hot.numel()), dtype=torch.uint8, device=dev)
     res = {}
     for name, fn in (("quant_x_row", lambda: fq.quantize(X, 32, fq.ROW, codes=xq[0], scales=xq[1])),
                      ("quant_w_col", lambda: fq.quantize(W, 32, fq.COL, codes=wq[0], scales=wq[1])),
                      ("gemm_fp32", lambda: fq.gemm(xq[0], xq[1], wq[0], wq[1], c=Y)),
                      ("hcp_residual", lambda: fq.hcp_residual_add(X, xq[0], xq[1], W, wq[0], wq[1],
-                                                                  hot, Y, ws))):
+                                                                  hot, Y, ws)),
+                     ("gemm_hcp_single", lambda: fq.gemm_hcp(X, xq[0], xq[1], W, wq[0], wq[1], hot,
+                                                             y=Y2, workspace=ws))):
         fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -357,6 +360,13 @@ def bench_outlier_layer(torch, fq, inputs, dev):
     res["quant_w_col_GBps"] = round(K * N * qb / (res["quant_w_col_us"] * 1e-6) / 1e9, 1)
     res["hcp_n_hot"] = int(hot.numel())
     res["hcp_y_rmw_GBps"] = round(8.0 * M * N / (res["hcp_residual_us"] * 1e-6) / 1e9, 1)
+    # dual-kernel mode (base GEMM, then the residual's read-modify-write of Y)
+    # against the single kernel that writes Y once
+    res["hcp_two_kernel_total_us"] = round(res["gemm_fp32_us"] + res["hcp_residual_us"], 1)
+    kp = (2 * int(hot.numel()) + 31) // 32 * 32
+    res["gemm_hcp_single_flops"] = 2.0 * M * N * K + 2.0 * M * N * kp
+    res["gemm_hcp_single_TFLOPS"] = round(res["gemm_hcp_single_flops"] /
+                                          (res["gemm_hcp_single_us"] * 1e-6) / 1e12, 1)
     return res
 
 

@@ -193,6 +193,30 @@ fp4q_status_t fp4q_hcp_residual_add(int64_t M, int64_t N, int64_t K, const void*
                                     int32_t n_hot, float* y, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/*
+ * fp4q_gemm_hcp -- hot-channel compensation in the single-kernel mode of the
+ * outlier-dynamics page, sec. 3.1 (the hot-channel terms are computed inside
+ * the main GEMM instead of by a second kernel):
+ *   Y[i,j] = sum_k Xq[i,k] Wq[k,j]
+ *          + sum_{c in H} ( X[i,c] W[c,j] - Xq[i,c] Wq[c,j] )
+ * i.e. fp4q_gemm into an fp32 Y followed by fp4q_hcp_residual_add, in one
+ * GEMM kernel: its FP4 K loop over all K, then a bf16 K loop over the
+ * gathered [X_H | Xq_H] and [W_H ; -Wq_H] into the same fp32 accumulators.
+ * Y is written once and never read (no fp32 read-modify-write of Y).
+ *   x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, n_hot, workspace:
+ *       as fp4q_hcp_residual_add (block 32 quantisations: X ROW, W COL).
+ *   y   fp32 [M, N], row stride ld_y >= N elements, written.
+ *   K % 128 == 0 and K < 2^24 as fp4q_gemm; n_hot <= min(K, 2^20).
+ *   n_hot = 0: Y is the plain FP4 GEMM (x, w, hot_idx, workspace may be NULL).
+ *   Summation order differs from the two-call form (one accumulator), so
+ *   results agree with it to fp32 rounding, not bit for bit.
+ */
+fp4q_status_t fp4q_gemm_hcp(int64_t M, int64_t N, int64_t K, const void* x,
+                            const uint8_t* xq_codes, const uint8_t* xq_scales, const void* w,
+                            const uint8_t* wq_codes, const uint8_t* wq_scales,
+                            const int32_t* hot_idx, int32_t n_hot, float* y, int64_t ld_y,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 const char* fp4q_status_string(fp4q_status_t s);
 const char* fp4q_last_error(void);
 int32_t fp4q_abi_version(void);

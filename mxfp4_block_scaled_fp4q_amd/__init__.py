@@ -22,7 +22,8 @@ STATUS = {0: "FP4Q_OK", 1: "FP4Q_ERR_INVALID", 2: "FP4Q_ERR_UNSUPPORTED",
 
 EXPORTS = ["fp4q_quantize", "fp4q_quantize_dual", "fp4q_dequantize", "fp4q_grad_estimate",
            "fp4q_gemm",
-           "fp4q_hcp_workspace_bytes", "fp4q_hcp_residual_add", "fp4q_status_string",
+           "fp4q_hcp_workspace_bytes", "fp4q_hcp_residual_add", "fp4q_gemm_hcp",
+           "fp4q_status_string",
            "fp4q_last_error", "fp4q_abi_version"]
 
 
@@ -56,6 +57,7 @@ def lib():
             "fp4q_hcp_workspace_bytes": (SZ, [I64, I64, I32]),
             "fp4q_hcp_residual_add": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, P, SZ,
                                             P]),
+            "fp4q_gemm_hcp": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, I64, P, SZ, P]),
             "fp4q_status_string": (_ct.c_char_p, [I32]),
             "fp4q_last_error": (_ct.c_char_p, []),
             "fp4q_abi_version": (I32, []),
@@ -210,4 +212,24 @@ def hcp_residual_add(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, y,
                                        _ptr(wq_codes), _ptr(wq_scales), _ptr(hot_idx), n_hot,
                                        _ptr(y), _ptr(workspace), workspace.numel(),
                                        _stream(stream)))
+    return y
+
+
+def gemm_hcp(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, y=None, workspace=None,
+             stream=None):
+    """Y[M,N] (fp32) = Xq Wq + sum_{c in hot} X[:,c] W[c,:] - Xq[:,c] Wq[c,:], in one GEMM
+    kernel (fp4q_gemm_hcp); returns y."""
+    torch = _torch()
+    _need_cuda(x, w, hot_idx)
+    M, K = x.shape
+    N = w.shape[1]
+    n_hot = hot_idx.numel()
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    need = hcp_workspace_bytes(M, N, n_hot)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().fp4q_gemm_hcp(M, N, K, _ptr(x), _ptr(xq_codes), _ptr(xq_scales), _ptr(w),
+                               _ptr(wq_codes), _ptr(wq_scales), _ptr(hot_idx), n_hot, _ptr(y),
+                               y.stride(0), _ptr(workspace), workspace.numel(), _stream(stream)))
     return y

@@ -239,4 +239,41 @@ fp4q_status_t fp4q_hcp_residual_add(int64_t M, int64_t N, int64_t K, const void*
                       "hcp launch");
 }
 
+fp4q_status_t fp4q_gemm_hcp(int64_t M, int64_t N, int64_t K, const void* x,
+                            const uint8_t* xq_codes, const uint8_t* xq_scales, const void* w,
+                            const uint8_t* wq_codes, const uint8_t* wq_scales,
+                            const int32_t* hot_idx, int32_t n_hot, float* y, int64_t ld_y,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    if (M <= 0 || N <= 0 || K <= 0 || n_hot < 0)
+        return fail(FP4Q_ERR_INVALID, "gemm_hcp: bad sizes");
+    if (!xq_codes || !xq_scales || !wq_codes || !wq_scales || !y)
+        return fail(FP4Q_ERR_INVALID, "gemm_hcp: null pointer");
+    if (K % 128) return fail(FP4Q_ERR_INVALID, "gemm_hcp: K %% 128 != 0");
+    if (ld_y < N) return fail(FP4Q_ERR_INVALID, "gemm_hcp: ld_y < N");
+    if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
+        return fail(FP4Q_ERR_INVALID, "gemm_hcp: dimension too large");
+    if (K >= ((int64_t)1 << 24))
+        return fail(FP4Q_ERR_UNSUPPORTED, "gemm_hcp: K must be below 2^24");
+    if (n_hot > K) return fail(FP4Q_ERR_INVALID, "gemm_hcp: n_hot > K");
+    if (n_hot > (1 << 20)) return fail(FP4Q_ERR_UNSUPPORTED, "gemm_hcp: n_hot above 2^20");
+    if (!aligned16(xq_codes) || !aligned16(xq_scales) || !aligned16(wq_codes) ||
+        !aligned16(wq_scales) || ((uintptr_t)y % 4))
+        return fail(FP4Q_ERR_ALIGNMENT,
+                    "gemm_hcp: operand pointers must be 16-byte aligned, y 4-byte aligned");
+    if (n_hot > 0) {
+        if (!x || !w || !hot_idx || !workspace)
+            return fail(FP4Q_ERR_INVALID, "gemm_hcp: null pointer");
+        if (!aligned16(x) || !aligned16(w) || !aligned16(hot_idx) || !aligned16(workspace))
+            return fail(FP4Q_ERR_ALIGNMENT, "gemm_hcp: pointers must be 16-byte aligned");
+        const size_t need = fp4q::hcp_workspace_bytes(M, N, n_hot);
+        if (workspace_bytes < need)
+            return fail(FP4Q_ERR_WORKSPACE, "gemm_hcp: workspace %zu < %zu bytes",
+                        workspace_bytes, need);
+    }
+    return hip_status(fp4q::launch_gemm_hcp(M, N, K, x, xq_codes, xq_scales, w, wq_codes,
+                                            wq_scales, hot_idx, n_hot, y, ld_y, workspace,
+                                            (hipStream_t)stream),
+                      "gemm_hcp launch");
+}
+
 }  // extern "C"

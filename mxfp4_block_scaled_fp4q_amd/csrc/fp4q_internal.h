@@ -50,9 +50,19 @@ hipError_t launch_gemm_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
 // on the FP4 GEMM's pipeline with bf16 MFMAs.
 hipError_t launch_gemm_bf16_accum(int64_t M, int64_t N, int64_t K, const uint16_t* a,
                                   const uint16_t* b, float* c, int64_t ldc, hipStream_t s);
+// C[M,N] (fp32, row stride ldc) = A B^T over FP4 operands (as launch_gemm_fp4)
+// plus ha hb^T over kp-deep bf16 operands (kp % 32 == 0), in one kernel.
+hipError_t launch_gemm_fp4_hot(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
+                               const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                               const uint16_t* ha, const uint16_t* hb, int64_t kp, float* c,
+                               int64_t ldc, hipStream_t s);
 size_t hcp_workspace_bytes(int64_t M, int64_t N, int32_t n_hot);
 hipError_t launch_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
                       const uint8_t* xqs, const void* w, const uint8_t* wqc, const uint8_t* wqs,
                       const int32_t* hot, int32_t n_hot, float* y, void* ws, hipStream_t s);
+hipError_t launch_gemm_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
+                           const uint8_t* xqs, const void* w, const uint8_t* wqc,
+                           const uint8_t* wqs, const int32_t* hot, int32_t n_hot, float* y,
+                           int64_t ldy, void* ws, hipStream_t s);
 
 }  // namespace fp4q

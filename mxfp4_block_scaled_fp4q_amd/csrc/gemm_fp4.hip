@@ -40,6 +40,8 @@
 // writes 16 contiguous bytes.  Workgroups are remapped so that consecutive
 // tiles of a grouped (4 tile-rows) order run on the same XCD and share its
 // L2.
+#include <type_traits>
+
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -117,18 +119,32 @@ __device__ __forceinline__ void issue_codes(Src<WN>& src, uint8_t* stage, int wa
     src.soff += advance ? BKB : 0;
 }
 
-// Scale piece P (0 .. SPIECES-1, a compile-time constant after unrolling)
-// of this wave for group g: combined rows wave*SROWS + P*8 .. +7 (A rows
-// 0..255, then B rows), 32 bytes each; lane 8j + pos loads word
-// pos ^ (P % 4) of the piece's row j, so that in LDS word s of row R sits at
-// R*32 + 4 (s ^ ((R / 8) % 4)) (SROWS / 8 is a multiple of 4).  The group
-// offset is part of the per-lane offset so the range check covers it.
-template <int WN>
+// Scale piece P (0 .. SPIECES-1) of this wave for group g: combined rows
+// wave*SROWS + P*8 .. +7 (A rows 0..255, then B rows), 32 bytes each; lane
+// 8j + pos loads word pos ^ (P % 4) of the piece's row j, so that in LDS word
+// s of row R sits at R*32 + 4 (s ^ ((R / 8) % 4)) (SROWS / 8 is a multiple of
+// 4).  The group offset is part of the per-lane offset so the range check
+// covers it.
+template <int WN, int P>
 __device__ __forceinline__ void issue_scale_piece(const Src<WN>& src, uint8_t* sbuf, int wave,
-                                                  int kscale, int g, int P) {
-    const uint32_t voff = src.vsc[P & 3] + (uint32_t)(P * 8 * kscale + g * SGB);
+                                                  int kscale, int g) {
+    // the uniform part as one scalar, so that the compiler does not keep a
+    // hoisted per-piece vector offset live across the K loop
+    uint32_t soff = (uint32_t)(P * 8 * kscale + g * SGB);
+    asm volatile("" : "+s"(soff));
+    const uint32_t voff = src.vsc[P & 3] + soff;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         src.rsc, (lds_ptr_t)(sbuf + (wave * Layout<WN>::SROWS + P * 8) * SGB), 4, voff, 0, 0, 0);
+}
+
+// Pieces P0 .. P0+N-1.
+template <int WN, int P0, int N>
+__device__ __forceinline__ void issue_scale_pieces(const Src<WN>& src, uint8_t* sbuf, int wave,
+                                                   int kscale, int g) {
+    if constexpr (N > 0) {
+        issue_scale_piece<WN, P0>(src, sbuf, wave, kscale, g);
+        issue_scale_pieces<WN, P0 + 1, N - 1>(src, sbuf, wave, kscale, g);
+    }
 }
 
 template <int WN>
@@ -213,44 +229,31 @@ __device__ __forceinline__ void mfma_half(const Frags<WN>& F, const uint32_t (&s
     }
 }
 
-template <int WN, int OUT_BF16, int ACCUM, int BF16OPS>
-__global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
-    int M, int N, int K, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
-    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, void* __restrict__ cptr,
-    int64_t ldc, int tiles_m, int tiles_n) {
+// The LDS ring stages and scale buffers: separate objects, so the compiler
+// sees that loads in flight into one stage and reads of another do not
+// alias; the epilogue reuses the stages.
+__shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+__shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+__shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
+__shared__ __attribute__((aligned(16))) uint8_t st3[STAGE];
+__shared__ __attribute__((aligned(16))) uint8_t sc0[SCALE_BUF];
+__shared__ __attribute__((aligned(16))) uint8_t sc1[SCALE_BUF];
+
+// One K loop of the workgroup's tile over operands ac / bc (K-major rows, K
+// elements deep; FP4 with scales as, bs, or bf16 without), accumulating into
+// acc.  Leaves no loads in flight; the caller synchronises before the stages
+// are reused.
+template <int WN, int BF16OPS>
+__device__ __forceinline__ void gemm_kloop(v16f (&acc)[4][Layout<WN>::TN],
+                                           const uint8_t* __restrict__ ac,
+                                           const uint8_t* __restrict__ as,
+                                           const uint8_t* __restrict__ bc,
+                                           const uint8_t* __restrict__ bs, int K, int M, int N,
+                                           int m0, int n0, int wave, int lane, int wm, int wn,
+                                           int half, int l32, int off0, int off1, int sxor) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot instantiate buffer resources
     using L = Layout<WN>;
     constexpr int TN = L::TN;
-    // The LDS ring stages are separate objects; the epilogue reuses them.
-    __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st3[STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t sc0[SCALE_BUF];
-    __shared__ __attribute__((aligned(16))) uint8_t sc1[SCALE_BUF];
-
-    // ---- tile index: XCD-contiguous, then grouped along M ----
-    const int nwg = gridDim.x;
-    int wg = blockIdx.x;
-    {
-        const int full = (nwg / 8) * 8;
-        if (wg < full) wg = (wg % 8) * (full / 8) + wg / 8;
-    }
-    const int per_group = GROUP_M * tiles_n;
-    const int grp = wg / per_group;
-    const int first_m = grp * GROUP_M;
-    const int gsize = min(GROUP_M, tiles_m - first_m);
-    const int in_grp = wg - grp * per_group;
-    const int tm = first_m + in_grp % gsize;
-    const int tn = in_grp / gsize;
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
-    const int half = lane >> 5;
-    const int l32 = lane & 31;
     // bytes per operand row (< 2^23, checked by the caller); each K step
     // consumes 64 of them
     const int kbytes = BF16OPS ? K * 2 : K / 2;
@@ -281,20 +284,6 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
         for (int q = 0; q < 4; ++q) src.vsc[q] = (uint32_t)(sbase + (((lane & 7) ^ q) << 2));
         src.soff = 0;
     }
-    // this lane's offsets within a 32-row group: row lane % 32, chunk
-    // 2 kk + lane / 32
-    const int off0 = (l32 >> 4) * REGION + region_slot(l32 & 15, half) * 16;
-    const int off1 = (l32 >> 4) * REGION + region_slot(l32 & 15, 2 + half) * 16;
-    const int sxor = (l32 >> 3) & 3;  // scale word swizzle of this lane's rows
-
-    v16f acc[4][TN];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
     Frags<WN> FA, FB;
     // sa/sb: shifted scale words of the step being computed; ra/rb: raw
     // words of the next step, read after the barrier that publishes it.
@@ -325,10 +314,7 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
     // issued after the code loads in step t - 2
 #define FP4Q_PIECES(p) ((BF16OPS || ((p) & 7) >= 4) ? 0 : L::SPIECES / 4)
 #define FP4Q_BEHIND(p) (FP4Q_PIECES((p) + 6) + LC + FP4Q_PIECES((p) + 7) + LC + FP4Q_PIECES(p))
-    if (!BF16OPS) {
-#pragma unroll
-        for (int q = 0; q < L::SPIECES; ++q) issue_scale_piece<WN>(src, sc0, wave, kscale, 0, q);
-    }
+    if (!BF16OPS) issue_scale_pieces<WN, 0, L::SPIECES>(src, sc0, wave, kscale, 0);
     issue_codes<WN, BF16OPS>(src, st0, wave, 1 < ksteps);
     issue_codes<WN, BF16OPS>(src, st1, wave, 2 < ksteps);
     issue_codes<WN, BF16OPS>(src, st2, wave, 3 < ksteps);
@@ -348,11 +334,9 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
         if (!BF16OPS) shift_scales<WN>(ra, rb, sh, sa, sb);                          \
         read_frags<WN>(CUR, off1, wm, wn, FB);                                       \
         issue_codes<WN, BF16OPS>(src, NEXTL, wave, t_ + 4 < ksteps);                 \
-        if (FP4Q_PIECES(P)) {                                                        \
-            _Pragma("unroll") for (int q_ = 0; q_ < L::SPIECES / 4; ++q_)              \
-                issue_scale_piece<WN>(src, SNXT, wave, kscale, t_ / SG + 1,            \
-                                      ((P) & 3) * (L::SPIECES / 4) + q_);              \
-        }                                                                            \
+        if (FP4Q_PIECES(P))                                                          \
+            issue_scale_pieces<WN, ((P) & 3) * (L::SPIECES / 4), L::SPIECES / 4>(        \
+                src, SNXT, wave, kscale, t_ / SG + 1);                                   \
         __builtin_amdgcn_sched_barrier(0);                                           \
         mfma_half<WN, BF16OPS, 0>(FA, sa, sb, acc);                                  \
         __builtin_amdgcn_sched_barrier(0);                                           \
@@ -403,6 +387,72 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
 #undef FP4Q_PIECES
 #undef FP4Q_BEHIND
     FP4Q_WAIT_VMCNT(0);  // the re-issued loads past the end of K have landed
+#endif
+}
+
+// OPS: 0 = FP4 operands; 1 = bf16 operands (ac, bc hold bf16 rows, no
+// scales); 2 = FP4 over K, then bf16 over the kp-deep operands ha, hb into
+// the same accumulators (the single-kernel hot-channel compensation).
+template <int WN, int OUT_BF16, int ACCUM, int OPS>
+__global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
+    int M, int N, int K, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
+    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, void* __restrict__ cptr,
+    int64_t ldc, int tiles_m, int tiles_n, const uint8_t* __restrict__ ha,
+    const uint8_t* __restrict__ hb, int kp) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot instantiate buffer resources
+    using L = Layout<WN>;
+    constexpr int TN = L::TN;
+
+    // ---- tile index: XCD-contiguous, then grouped along M ----
+    const int nwg = gridDim.x;
+    int wg = blockIdx.x;
+    {
+        const int full = (nwg / 8) * 8;
+        if (wg < full) wg = (wg % 8) * (full / 8) + wg / 8;
+    }
+    const int per_group = GROUP_M * tiles_n;
+    const int grp = wg / per_group;
+    const int first_m = grp * GROUP_M;
+    const int gsize = min(GROUP_M, tiles_m - first_m);
+    const int in_grp = wg - grp * per_group;
+    const int tm = first_m + in_grp % gsize;
+    const int tn = in_grp / gsize;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    // this lane's offsets within a 32-row group: row lane % 32, chunk
+    // 2 kk + lane / 32
+    const int off0 = (l32 >> 4) * REGION + region_slot(l32 & 15, half) * 16;
+    const int off1 = (l32 >> 4) * REGION + region_slot(l32 & 15, 2 + half) * 16;
+    const int sxor = (l32 >> 3) & 3;  // scale word swizzle of this lane's rows
+
+    v16f acc[4][TN];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+
+#define FP4Q_KLOOP(BF, A_, AS_, B_, BS_, KD_)                                              \
+    gemm_kloop<WN, BF>(acc, A_, AS_, B_, BS_, KD_, M, N, m0, n0, wave, lane, wm, wn, half, l32, \
+                       off0, off1, sxor)
+    if (OPS == 1) {
+        FP4Q_KLOOP(1, ac, as, bc, bs, K);
+    } else {
+        FP4Q_KLOOP(0, ac, as, bc, bs, K);
+        if (OPS == 2 && kp > 0) {
+            __syncthreads();  // every wave is done with the stages before they refill
+            FP4Q_KLOOP(1, ha, nullptr, hb, nullptr, kp);
+        }
+    }
+#undef FP4Q_KLOOP
 
     // ---- epilogue: through LDS, so every lane writes 16 contiguous bytes ----
     // Each wave stages its tile 32 rows at a time in a private LDS region
@@ -492,16 +542,17 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
 #endif
 }
 
-template <int OUT_BF16, int ACCUM, int BF16OPS>
+template <int OUT_BF16, int ACCUM, int OPS>
 static void launch_tiles(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                          const uint8_t* b, const uint8_t* bs, void* c, int64_t ldc,
-                         hipStream_t s) {
+                         hipStream_t s, const uint8_t* ha = nullptr, const uint8_t* hb = nullptr,
+                         int64_t kp = 0) {
     constexpr int WN = FP4Q_GEMM_WN;
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
-    gemm_fp4_kernel<WN, OUT_BF16, ACCUM, BF16OPS>
+    gemm_fp4_kernel<WN, OUT_BF16, ACCUM, OPS>
         <<<dim3((unsigned)(tiles_m * tiles_n)), Layout<WN>::THREADS, 0, s>>>(
-            (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m, tiles_n);
+            (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m, tiles_n, ha, hb, (int)kp);
 }
 
 hipError_t launch_gemm_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
@@ -520,6 +571,15 @@ hipError_t launch_gemm_bf16_accum(int64_t M, int64_t N, int64_t K, const uint16_
                                   const uint16_t* b, float* c, int64_t ldc, hipStream_t s) {
     launch_tiles<0, 1, 1>(M, N, K, (const uint8_t*)a, nullptr, (const uint8_t*)b, nullptr, c, ldc,
                           s);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp4_hot(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
+                               const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                               const uint16_t* ha, const uint16_t* hb, int64_t kp, float* c,
+                               int64_t ldc, hipStream_t s) {
+    launch_tiles<0, 0, 2>(M, N, K, ac, as, bc, bs, c, ldc, s, (const uint8_t*)ha,
+                          (const uint8_t*)hb, kp);
     return hipGetLastError();
 }
 

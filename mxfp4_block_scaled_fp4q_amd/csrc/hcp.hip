@@ -19,6 +19,11 @@
 // to precompute and cache them, sec. 3.2).  All dequantised values are exact
 // in bf16 and every bf16 x bf16 product is exact in fp32.
 //
+// Single-kernel ("S") mode of the same section: the FP4 GEMM kernel runs its
+// FP4 K loop over all K and then a bf16 K loop over the same A', B' into the
+// same fp32 accumulators, so Y = Xq Wq + residual is written once and the
+// fp32 read-modify-write of Y disappears.
+//
 // Kernels:
 //  * hcp_gather_x: one lane = 8 consecutive K' slots of one row of A'.
 //  * hcp_gather_w: one lane = one column j and 8 consecutive K' slots; lanes
@@ -120,10 +125,11 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_w(const uint16_t* __restr
     *(uint4*)(b + j * kp + h0) = o;
 }
 
-hipError_t launch_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
-                      const uint8_t* xqs, const void* w, const uint8_t* wqc, const uint8_t* wqs,
-                      const int32_t* hot, int32_t n_hot, float* y, void* ws, hipStream_t s) {
-    if (n_hot <= 0) return hipSuccess;
+// Gathers the hot operands into the workspace: A' [M, kp] then B' [N, kp].
+static hipError_t gather_hot(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
+                             const uint8_t* xqs, const void* w, const uint8_t* wqc,
+                             const uint8_t* wqs, const int32_t* hot, int32_t n_hot, void* ws,
+                             hipStream_t s, uint16_t** ap_out, uint16_t** bp_out) {
     const int64_t kp = padded_k(n_hot);
     uint16_t* ap = (uint16_t*)ws;
     uint16_t* bp = (uint16_t*)((uint8_t*)ws + round_up((size_t)(M * kp * 2), 256));
@@ -138,9 +144,30 @@ hipError_t launch_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint
         hcp_gather_w<<<grid, kThreads, 0, s>>>((const uint16_t*)w, wqc, wqs, hot, n_hot, N, K, kp,
                                                bp);
     }
-    hipError_t e = hipGetLastError();
+    *ap_out = ap;
+    *bp_out = bp;
+    return hipGetLastError();
+}
+
+hipError_t launch_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
+                      const uint8_t* xqs, const void* w, const uint8_t* wqc, const uint8_t* wqs,
+                      const int32_t* hot, int32_t n_hot, float* y, void* ws, hipStream_t s) {
+    if (n_hot <= 0) return hipSuccess;
+    uint16_t *ap, *bp;
+    hipError_t e = gather_hot(M, N, K, x, xqc, xqs, w, wqc, wqs, hot, n_hot, ws, s, &ap, &bp);
     if (e != hipSuccess) return e;
-    return launch_gemm_bf16_accum(M, N, kp, ap, bp, y, N, s);
+    return launch_gemm_bf16_accum(M, N, padded_k(n_hot), ap, bp, y, N, s);
+}
+
+hipError_t launch_gemm_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
+                           const uint8_t* xqs, const void* w, const uint8_t* wqc,
+                           const uint8_t* wqs, const int32_t* hot, int32_t n_hot, float* y,
+                           int64_t ldy, void* ws, hipStream_t s) {
+    if (n_hot <= 0) return launch_gemm_fp4(M, N, K, xqc, xqs, wqc, wqs, y, F32, ldy, false, s);
+    uint16_t *ap, *bp;
+    hipError_t e = gather_hot(M, N, K, x, xqc, xqs, w, wqc, wqs, hot, n_hot, ws, s, &ap, &bp);
+    if (e != hipSuccess) return e;
+    return launch_gemm_fp4_hot(M, N, K, xqc, xqs, wqc, wqs, ap, bp, padded_k(n_hot), y, ldy, s);
 }
 
 }  // namespace fp4q

@@ -175,3 +175,40 @@ def test_quantize_dual_validation(L):
     assert call(c=FAKE_MIS) == 3
     assert call(ld=68) == 3            # bf16 row stride 136 bytes
     assert L.fp4q_last_error().decode()
+
+
+def test_gemm_hcp_validation(L):
+    h = L.fp4q_gemm_hcp
+    ws = L.fp4q_hcp_workspace_bytes(128, 64, 10)
+    args = [128, 64, 256, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, 64, FAKE, ws, NUL]
+    bad = list(args)
+    bad[14] = ws - 1
+    assert h(*bad) == 4
+    bad = list(args)
+    bad[10] = 300        # n_hot > K
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[2] = 1 << 22
+    bad[10] = (1 << 20) + 1
+    assert h(*bad) == 2
+    bad = list(args)
+    bad[2] = 160         # K % 128 (the FP4 GEMM's K step)
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[2] = 1 << 24     # K beyond the GEMM's 32-bit row offsets
+    assert h(*bad) == 2
+    bad = list(args)
+    bad[12] = 63         # ld_y < N
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[3] = NUL         # x needed when there are hot channels
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[4] = NUL         # quantised X always needed
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[11] = ct.c_void_p(0x10002)   # y not 4-byte aligned
+    assert h(*bad) == 3
+    bad = list(args)
+    bad[6] = FAKE_MIS    # W codes not 16-byte aligned
+    assert h(*bad) == 3

@@ -197,3 +197,58 @@ def test_hcp_empty_is_noop(orc):
                         dev(wq[1]), torch.zeros(0, dtype=torch.int32, device="cuda"), y)
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(y), y0)
+
+
+@pytest.mark.parametrize("M,N,K,n_hot,ld_pad", [(64, 96, 256, 23, 0), (300, 257, 512, 46, 3),
+                                                (1, 33, 128, 1, 0), (128, 128, 256, 256, 0),
+                                                (513, 260, 384, 0, 1)])
+def test_gemm_hcp_single_kernel(orc, M, N, K, n_hot, ld_pad):
+    """fp4q_gemm_hcp: Y = Xq Wq + residual in one kernel, against the oracle's
+    base GEMM plus its residual entries, over the sum of both bounds; columns
+    past N (ld_y padding) stay untouched."""
+    x = inputs.to_bf16_bits(inputs.normal((M, K), M + K + 1))
+    w = inputs.to_bf16_bits(inputs.normal((K, N), N + K + 1, 0.02))
+    hot = inputs.hot_channels(K, 13, n_hot / K) if n_hot else np.zeros(0, np.int32)
+    assert hot.size == n_hot
+    xq = orc.quantize(x, 32)
+    wq = orc.quantize(w, 32, axis=orc.COL)
+    C, S = orc.gemm(xq[0], xq[1], wq[0], wq[1])
+    y = torch.full((M, N + ld_pad), float("nan"), dtype=torch.float32, device="cuda")
+    fq.gemm_hcp(dev_bf16(x), dev(xq[0]), dev(xq[1]), dev_bf16(w), dev(wq[0]), dev(wq[1]),
+                dev(hot), y=y[:, :N])
+    torch.cuda.synchronize()
+    full = host_bits(y)
+    if ld_pad:
+        assert np.isnan(full[:, N:]).all(), "gemm_hcp wrote past N"
+    got = full[:, :N]
+    if n_hot:
+        ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        R, SR = orc.hcp_residual_entries(x, xq[0], xq[1], w, wq[0], wq[1], hot, ii.ravel(),
+                                         jj.ravel())
+        C = C + R.reshape(M, N)
+        S = S + SR.reshape(M, N)
+    check_gemm_f32(got, C, S, f"gemm_hcp {M}x{N}x{K} hot={n_hot}")
+
+
+def test_outlier_layer_single_kernel_hcp(orc):
+    """16384 x 13824 x 5120 with 461 hot channels in one kernel, on sampled
+    outputs, and equal to the two-call form within the same bound."""
+    d = inputs.outlier_layer()
+    X, W, hot = d["X"], d["W"], d["hot"]
+    A = orc.quantize(X, 32)
+    B = orc.quantize(W, 32, axis=orc.COL)
+    Ad = (dev(A[0]), dev(A[1]))
+    Bd = (dev(B[0]), dev(B[1]))
+    xd, wd, hd = dev_bf16(X), dev_bf16(W), dev(hot)
+    y = fq.gemm_hcp(xd, Ad[0], Ad[1], wd, Bd[0], Bd[1], hd)
+    torch.cuda.synchronize()
+    M, N = y.shape
+    ii, jj = sample_positions(M, N, 7)
+    C, S = orc.gemm_entries(A[0], A[1], B[0], B[1], ii, jj)
+    R, SR = orc.hcp_residual_entries(X, A[0], A[1], W, B[0], B[1], hot, ii, jj)
+    check_gemm_f32(host_bits(y)[ii, jj], C + R, S + SR, "13B single-kernel hcp")
+    y2 = fq.gemm(Ad[0], Ad[1], Bd[0], Bd[1], out_dtype=torch.float32)
+    fq.hcp_residual_add(xd, Ad[0], Ad[1], wd, Bd[0], Bd[1], hd, y2)
+    torch.cuda.synchronize()
+    a, b = host_bits(y)[ii, jj].astype(np.float64), host_bits(y2)[ii, jj].astype(np.float64)
+    assert np.all(np.abs(a - b) <= 2 * GEMM_REL * (S + SR)), "single-kernel vs two-call"
