@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint32_t* __
             o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[u], sc, 2));
             o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[u], sc, 3));
             if (nan_blk) o.x = o.y = o.z = o.w = 0x7FC07FC0u;
-            ((uint4*)y)[g] = o;
+            store_nt((uint4*)y + g, o);
         } else {
             f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], sc, 0);
             f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[u], sc, 1);
@@ -62,8 +62,8 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint32_t* __
                 o0.x = o0.y = o0.z = o0.w = 0x7FC00000u;
                 o1 = o0;
             }
-            ((uint4*)y)[2 * g] = o0;
-            ((uint4*)y)[2 * g + 1] = o1;
+            store_nt((uint4*)y + 2 * g, o0);
+            store_nt((uint4*)y + 2 * g + 1, o1);
         }
     }
 }

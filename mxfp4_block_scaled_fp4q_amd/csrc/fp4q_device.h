@@ -19,6 +19,14 @@ __device__ __forceinline__ float as_f32(uint32_t u) { return __uint_as_float(u);
 __device__ __forceinline__ uint32_t as_u32(float f) { return __float_as_uint(f); }
 
 // fp32 value of the low / high bf16 of a packed pair (exact).
+// 16-byte store with the non-temporal hint, for outputs this path does not
+// read back soon (a dequantised or gradient tensor): they then do not
+// displace data in the caches that the next kernels read.
+__device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store((v4u){v.x, v.y, v.z, v.w}, (v4u*)p);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f32(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f32(w & 0xFFFF0000u); }
 

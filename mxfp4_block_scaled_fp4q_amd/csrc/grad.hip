@@ -81,11 +81,11 @@ __device__ __forceinline__ void store8(void* p, int64_t e0, const float (&f)[8])
         v.y = pack_bf16x2(f[2], f[3]);
         v.z = pack_bf16x2(f[4], f[5]);
         v.w = pack_bf16x2(f[6], f[7]);
-        *(uint4*)((uint16_t*)p + e0) = v;
+        store_nt((uint4*)((uint16_t*)p + e0), v);
     } else {
         uint4* q = (uint4*)((float*)p + e0);
-        q[0] = make_uint4(as_u32(f[0]), as_u32(f[1]), as_u32(f[2]), as_u32(f[3]));
-        q[1] = make_uint4(as_u32(f[4]), as_u32(f[5]), as_u32(f[6]), as_u32(f[7]));
+        store_nt(q, make_uint4(as_u32(f[0]), as_u32(f[1]), as_u32(f[2]), as_u32(f[3])));
+        store_nt(q + 1, make_uint4(as_u32(f[4]), as_u32(f[5]), as_u32(f[6]), as_u32(f[7])));
     }
 }
 
