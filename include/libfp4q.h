@@ -155,7 +155,10 @@ fp4q_status_t fp4q_grad_estimate(fp4q_grad_t mode, const void* x, fp4q_dtype_t x
  *   addressed with 32-bit offsets); M, N < 2^31.
  *   accumulate = 1 adds into an fp32 C (bf16 C: FP4Q_ERR_UNSUPPORTED).
  *   M, N >= 1 are arbitrary (edge tiles are masked).  Deterministic: no
- *   atomics, no split-K.
+ *   atomics, no split-K.  The tile shape (256 x 256 or 128 x 384) is chosen
+ *   per M, N from the device's compute-unit count; the environment variable
+ *   FP4Q_GEMM_TILE=256x256 or 128x384 forces one.  Both accumulate every
+ *   output over K in the same order, so they give bit-identical results.
  */
 fp4q_status_t fp4q_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                         const uint8_t* a_scales, const uint8_t* b_codes, const uint8_t* b_scales,

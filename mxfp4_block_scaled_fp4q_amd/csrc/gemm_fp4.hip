@@ -18,11 +18,14 @@
 // 32x32 fp32 result sits in 16 registers: register r of lane l holds row
 // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
 //
-// Tiling: a workgroup of 2 x WN waves computes a 256 x 256 tile of C; each
-// wave owns 128 rows x (256 / WN) columns as 4 x TN MFMA tiles.  With WN = 4
-// (8 waves, 128 accumulator registers each) two waves share every SIMD, so
-// one wave's MFMAs run while the other waits on LDS or the barrier.  The K
-// loop steps 64 bytes per operand row (128 FP4 or 32 bf16 elements).
+// Tiling: a workgroup of 8 waves (2 along M x 4 along N) computes a 256 x 256
+// tile of C, each wave 128 x 64 as 4 x 2 MFMA tiles (128 accumulator
+// registers), or a 128 x 384 tile, each wave 64 x 96 as 2 x 3 MFMA tiles,
+// where the latter saves a whole round of tiles (it is 3/4 of the work per
+// tile but measured 1.45x slower per flop, so the 256 x 256 tile is the
+// default).  Two waves share every SIMD, so one wave's MFMAs run while the
+// other waits on LDS or the barrier.  The K loop steps 64 bytes per operand
+// row (128 FP4 or 32 bf16 elements).
 //
 // Operands go global -> LDS directly (buffer loads with the LDS bit, so no
 // registers are spent on staging) through a 4-stage ring, issued three
@@ -40,6 +43,8 @@
 // writes 16 contiguous bytes.  Workgroups are remapped so that consecutive
 // tiles of a grouped (4 tile-rows) order run on the same XCD and share its
 // L2.
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "fp4q_device.h"
@@ -55,34 +60,44 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-static constexpr int BM = 256, BN = 256;
 static constexpr int BKB = 64;                  // operand bytes per row per K step
 static constexpr int REGION = 1024;             // 16 rows x 64 bytes
-static constexpr int OFF_B = 16 * REGION;       // B codes within a stage
 static constexpr int STAGE = 32 * REGION;       // one K step of A and B codes
 static constexpr int SG = 8;                    // K steps per scale group
 static constexpr int SGB = 4 * SG;              // scale bytes per row per group
-static constexpr int SCALE_BUF = 512 * SGB;     // A rows 0..255, then B rows
+static constexpr int SCALE_BUF = 512 * SGB;     // A rows, then B rows
 static constexpr int GROUP_M = 4;
 static constexpr int BUF_FLAGS = 0x00020000;    // buffer resource word 3: raw 32-bit data
-#ifndef FP4Q_GEMM_WN
-#define FP4Q_GEMM_WN 4
-#endif
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 at maximum).
 #define FP4Q_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
 
-template <int WN>
+// Tile configurations: eight waves, two along M and four along N, each
+// owning TM x TN MFMA tiles of 32 x 32.
+//   CFG 0: 256 x 256 tile, 128 x 64 per wave (4 x 2 MFMA tiles);
+//   CFG 1: 128 x 384 tile,  64 x 96 per wave (2 x 3 MFMA tiles), for shapes
+//          whose 256 x 256 tiles would leave part of the chip idle in the
+//          last round (three of its tiles cover the area of four of those).
+// Both stage 512 operand rows (32 KB) per K step and 512 scale rows.
+template <int CFG>
 struct Layout {
-    static constexpr int WAVES = 2 * WN;
-    static constexpr int THREADS = 64 * WAVES;
-    static constexpr int TN = 8 / WN;          // 32-column MFMA tiles per wave
-    static constexpr int WCOLS = 32 * TN;      // columns per wave
-    static constexpr int RPW = 16 / WAVES;     // 1 KB code regions per operand per wave per step
-    static constexpr int SROWS = 512 / WAVES;  // scale rows (A then B) fetched per wave
-    static constexpr int SPIECES = SROWS / 8;  // 8-row scale pieces per wave per group
-    static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
+    static constexpr int WAVES = 8, THREADS = 64 * WAVES;
+    static constexpr int WM = 2, WN = 4;
+    static constexpr int TM = CFG == 0 ? 4 : 2;  // 32-row MFMA tiles per wave
+    static constexpr int TN = CFG == 0 ? 2 : 3;  // 32-column MFMA tiles per wave
+    static constexpr int WROWS = 32 * TM, WCOLS = 32 * TN;
+    static constexpr int BM = WM * WROWS, BN = WN * WCOLS;
+    static constexpr int RA = BM / 16, RB = BN / 16;  // 1 KB code regions per step
+    static constexpr int RPW_A = RA / WAVES, RPW_B = RB / WAVES;
+    static constexpr int RPW = RPW_A > RPW_B ? RPW_A : RPW_B;
+    static constexpr int OFF_B = RA * REGION;         // B codes within a stage
+    static constexpr int SROWS = 64;                  // scale rows fetched per wave
+    static constexpr int SPIECES = SROWS / 8;         // 8-row scale pieces per wave per group
+    static constexpr int A_SWAVES = BM / SROWS;       // waves fetching A scale rows
+    static_assert(RA % WAVES == 0 && RB % WAVES == 0, "code regions divide among the waves");
+    static_assert((RA + RB) * REGION == STAGE, "one 32 KB stage per K step");
+    static_assert(BM + BN == WAVES * SROWS, "every wave fetches 64 scale rows");
 };
 
 // 16-byte slot of chunk c (bytes 16c .. 16c+15 of the step) of row j within
@@ -93,10 +108,10 @@ __device__ __forceinline__ int region_slot(int j, int c) { return 4 * j + (c ^ (
 // inside this tile (rows past M or N read as zero), 32-bit per-lane offsets
 // (they alone decide whether a row is in range), and the scalar byte offset
 // of the current K step.
-template <int WN>
+template <int CFG>
 struct Src {
     __amdgpu_buffer_rsrc_t ra, rb, rsc;  // rsc: scales of this wave's pieces (A or B)
-    uint32_t vrow[Layout<WN>::RPW];
+    uint32_t vrow[Layout<CFG>::RPW];     // region q of A and of B share the row offsets
     uint32_t vsc[4];  // scale piece offsets, by piece index % 4 (word swizzle)
     int soff;
 };
@@ -105,28 +120,32 @@ struct Src {
 // sources then advance to the next step if `advance` (past the end of K the
 // last step is re-issued into a stage nobody reads again, so every step
 // issues the same number of loads and the waits are compile-time).
-template <int WN, int BF16OPS>
-__device__ __forceinline__ void issue_codes(Src<WN>& src, uint8_t* stage, int wave, bool advance) {
-    using L = Layout<WN>;
+template <int CFG, int BF16OPS>
+__device__ __forceinline__ void issue_codes(Src<CFG>& src, uint8_t* stage, int wave,
+                                            bool advance) {
+    using L = Layout<CFG>;
 #pragma unroll
     for (int q = 0; q < L::RPW; ++q) {
         const int rho = q * L::WAVES + wave;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.ra, (lds_ptr_t)(stage + rho * REGION), 16,
-                                                 src.vrow[q], src.soff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rb, (lds_ptr_t)(stage + OFF_B + rho * REGION),
-                                                 16, src.vrow[q], src.soff, 0, 0);
+        if (q < L::RPW_A)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(src.ra, (lds_ptr_t)(stage + rho * REGION), 16,
+                                                     src.vrow[q], src.soff, 0, 0);
+        if (q < L::RPW_B)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                src.rb, (lds_ptr_t)(stage + L::OFF_B + rho * REGION), 16, src.vrow[q], src.soff, 0,
+                0);
     }
     src.soff += advance ? BKB : 0;
 }
 
 // Scale piece P (0 .. SPIECES-1) of this wave for group g: combined rows
-// wave*SROWS + P*8 .. +7 (A rows 0..255, then B rows), 32 bytes each; lane
+// wave*SROWS + P*8 .. +7 (A rows 0..BM-1, then B rows), 32 bytes each; lane
 // 8j + pos loads word pos ^ (P % 4) of the piece's row j, so that in LDS word
 // s of row R sits at R*32 + 4 (s ^ ((R / 8) % 4)) (SROWS / 8 is a multiple of
 // 4).  The group offset is part of the per-lane offset so the range check
 // covers it.
-template <int WN, int P>
-__device__ __forceinline__ void issue_scale_piece(const Src<WN>& src, uint8_t* sbuf, int wave,
+template <int CFG, int P>
+__device__ __forceinline__ void issue_scale_piece(const Src<CFG>& src, uint8_t* sbuf, int wave,
                                                   int kscale, int g) {
     // the uniform part as one scalar, so that the compiler does not keep a
     // hoisted per-piece vector offset live across the K loop
@@ -134,81 +153,84 @@ __device__ __forceinline__ void issue_scale_piece(const Src<WN>& src, uint8_t* s
     asm volatile("" : "+s"(soff));
     const uint32_t voff = src.vsc[P & 3] + soff;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        src.rsc, (lds_ptr_t)(sbuf + (wave * Layout<WN>::SROWS + P * 8) * SGB), 4, voff, 0, 0, 0);
+        src.rsc, (lds_ptr_t)(sbuf + (wave * Layout<CFG>::SROWS + P * 8) * SGB), 4, voff, 0, 0, 0);
 }
 
 // Pieces P0 .. P0+N-1.
-template <int WN, int P0, int N>
-__device__ __forceinline__ void issue_scale_pieces(const Src<WN>& src, uint8_t* sbuf, int wave,
+template <int CFG, int P0, int N>
+__device__ __forceinline__ void issue_scale_pieces(const Src<CFG>& src, uint8_t* sbuf, int wave,
                                                    int kscale, int g) {
     if constexpr (N > 0) {
-        issue_scale_piece<WN, P0>(src, sbuf, wave, kscale, g);
-        issue_scale_pieces<WN, P0 + 1, N - 1>(src, sbuf, wave, kscale, g);
+        issue_scale_piece<CFG, P0>(src, sbuf, wave, kscale, g);
+        issue_scale_pieces<CFG, P0 + 1, N - 1>(src, sbuf, wave, kscale, g);
     }
 }
 
-template <int WN>
+template <int CFG>
 struct Frags {
-    u32x4 a[4], b[Layout<WN>::TN];
+    u32x4 a[Layout<CFG>::TM], b[Layout<CFG>::TN];
 };
 
 // This wave's A and B fragments of one half of a staged step; `off` is this
 // lane's offset within a 32-row group for that half (row lane % 32, chunk
 // 2 kk + lane / 32).
-template <int WN>
+template <int CFG>
 __device__ __forceinline__ void read_frags(const uint8_t* base, int off, int wm, int wn,
-                                           Frags<WN>& F) {
-    using L = Layout<WN>;
+                                           Frags<CFG>& F) {
+    using L = Layout<CFG>;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) F.a[i] = *(const u32x4*)(base + (wm * 4 + i) * 2 * REGION + off);
+    for (int i = 0; i < L::TM; ++i)
+        F.a[i] = *(const u32x4*)(base + (wm * L::TM + i) * 2 * REGION + off);
 #pragma unroll
     for (int j = 0; j < L::TN; ++j)
-        F.b[j] = *(const u32x4*)(base + OFF_B + (wn * L::TN + j) * 2 * REGION + off);
+        F.b[j] = *(const u32x4*)(base + L::OFF_B + (wn * L::TN + j) * 2 * REGION + off);
 }
 
 // Scale words (4 K blocks of 32 elements each) of step word s of a group
 // for this lane's MFMA rows (A) and columns (B); `sx` is this lane's
 // swizzled byte offset 4 (s ^ ((lane % 32) / 8 % 4)) of that word.
-template <int WN>
+template <int CFG>
 __device__ __forceinline__ void read_scales(const uint8_t* sbuf, int sx, int wm, int wn, int lane,
-                                            uint32_t (&sa)[4], uint32_t (&sb)[Layout<WN>::TN]) {
-    using L = Layout<WN>;
+                                            uint32_t (&sa)[Layout<CFG>::TM],
+                                            uint32_t (&sb)[Layout<CFG>::TN]) {
+    using L = Layout<CFG>;
     const int l32 = lane & 31;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        sa[i] = *(const uint32_t*)(sbuf + (wm * 128 + i * 32 + l32) * SGB + sx);
+    for (int i = 0; i < L::TM; ++i)
+        sa[i] = *(const uint32_t*)(sbuf + (wm * L::WROWS + i * 32 + l32) * SGB + sx);
 #pragma unroll
     for (int j = 0; j < L::TN; ++j)
-        sb[j] = *(const uint32_t*)(sbuf + (256 + wn * L::WCOLS + j * 32 + l32) * SGB + sx);
+        sb[j] = *(const uint32_t*)(sbuf + (L::BM + wn * L::WCOLS + j * 32 + l32) * SGB + sx);
 }
 
 // Shifts raw scale words so that byte 2 kk is the K block of half kk for
 // this lane's 32-element K chunk (lanes 32..63 take the odd blocks).
-template <int WN>
-__device__ __forceinline__ void shift_scales(const uint32_t (&ra)[4],
-                                             const uint32_t (&rb)[Layout<WN>::TN], int sh,
-                                             uint32_t (&sa)[4], uint32_t (&sb)[Layout<WN>::TN]) {
+template <int CFG>
+__device__ __forceinline__ void shift_scales(const uint32_t (&ra)[Layout<CFG>::TM],
+                                             const uint32_t (&rb)[Layout<CFG>::TN], int sh,
+                                             uint32_t (&sa)[Layout<CFG>::TM],
+                                             uint32_t (&sb)[Layout<CFG>::TN]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = ra[i] >> sh;
+    for (int i = 0; i < Layout<CFG>::TM; ++i) sa[i] = ra[i] >> sh;
 #pragma unroll
-    for (int j = 0; j < Layout<WN>::TN; ++j) sb[j] = rb[j] >> sh;
+    for (int j = 0; j < Layout<CFG>::TN; ++j) sb[j] = rb[j] >> sh;
 }
 
-// The 4 x TN MFMAs of this wave on half KK of a K step.  FP4: the scaled
+// The TM x TN MFMAs of this wave on half KK of a K step.  FP4: the scaled
 // MFMA on E2M1 operands (64 K elements per half), its byte select picking
 // byte 2 KK of the lane's (pre-shifted) scale words; BF16: plain bf16 MFMAs
 // (16 K elements per half, the same 16 bytes per lane).  B is the MFMA's
 // first operand, so each accumulator holds the transposed tile: register r
 // of lane l is C[row l % 32][column 8 (r / 4) + 4 (l / 32) + r % 4], four
 // consecutive columns per register group, which the epilogue stores whole.
-template <int WN, int BF16OPS, int KK>
-__device__ __forceinline__ void mfma_half(const Frags<WN>& F, const uint32_t (&sa)[4],
-                                          const uint32_t (&sb)[Layout<WN>::TN],
-                                          v16f (&acc)[4][Layout<WN>::TN]) {
-    using L = Layout<WN>;
+template <int CFG, int BF16OPS, int KK>
+__device__ __forceinline__ void mfma_half(const Frags<CFG>& F, const uint32_t (&sa)[Layout<CFG>::TM],
+                                          const uint32_t (&sb)[Layout<CFG>::TN],
+                                          v16f (&acc)[Layout<CFG>::TM][Layout<CFG>::TN]) {
+    using L = Layout<CFG>;
     if (BF16OPS) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < L::TM; ++i)
 #pragma unroll
             for (int j = 0; j < L::TN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -217,7 +239,7 @@ __device__ __forceinline__ void mfma_half(const Frags<WN>& F, const uint32_t (&s
         return;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < L::TM; ++i) {
         const v8i fa = (v8i){(int)F.a[i].x, (int)F.a[i].y, (int)F.a[i].z, (int)F.a[i].w, 0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < L::TN; ++j) {
@@ -243,8 +265,8 @@ __shared__ __attribute__((aligned(16))) uint8_t sc1[SCALE_BUF];
 // elements deep; FP4 with scales as, bs, or bf16 without), accumulating into
 // acc.  Leaves no loads in flight; the caller synchronises before the stages
 // are reused.
-template <int WN, int BF16OPS>
-__device__ __forceinline__ void gemm_kloop(v16f (&acc)[4][Layout<WN>::TN],
+template <int CFG, int BF16OPS>
+__device__ __forceinline__ void gemm_kloop(v16f (&acc)[Layout<CFG>::TM][Layout<CFG>::TN],
                                            const uint8_t* __restrict__ ac,
                                            const uint8_t* __restrict__ as,
                                            const uint8_t* __restrict__ bc,
@@ -252,17 +274,17 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[4][Layout<WN>::TN],
                                            int m0, int n0, int wave, int lane, int wm, int wn,
                                            int half, int l32, int off0, int off1, int sxor) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot instantiate buffer resources
-    using L = Layout<WN>;
-    constexpr int TN = L::TN;
+    using L = Layout<CFG>;
+    constexpr int TM = L::TM, TN = L::TN;
     // bytes per operand row (< 2^23, checked by the caller); each K step
     // consumes 64 of them
     const int kbytes = BF16OPS ? K * 2 : K / 2;
     const int kscale = K / 32;
     const int ksteps = kbytes / BKB;
 
-    Src<WN> src;
+    Src<CFG> src;
     {
-        const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
+        const int rows_a = min(M - m0, L::BM), rows_b = min(N - n0, L::BN);
         src.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(ac + (int64_t)m0 * kbytes), (short)0,
                                                    rows_a * kbytes, BUF_FLAGS);
         src.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(bc + (int64_t)n0 * kbytes), (short)0,
@@ -273,22 +295,23 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[4][Layout<WN>::TN],
 #pragma unroll
         for (int q = 0; q < L::RPW; ++q)
             src.vrow[q] = (uint32_t)(((q * L::WAVES + wave) * 16 + j) * kbytes + c * 16);
-        // the first half of the waves fetch A scale rows, the second half B
-        constexpr int HW = L::WAVES / 2;
+        // waves 0 .. A_SWAVES-1 fetch A scale rows, the others B
+        constexpr int HW = L::A_SWAVES;
         src.rsc = wave < HW ? __builtin_amdgcn_make_buffer_rsrc((void*)(as + (int64_t)m0 * kscale),
                                                                 (short)0, rows_a * kscale, BUF_FLAGS)
                             : __builtin_amdgcn_make_buffer_rsrc((void*)(bs + (int64_t)n0 * kscale),
                                                                 (short)0, rows_b * kscale, BUF_FLAGS);
-        const int sbase = ((wave % HW) * L::SROWS + (lane >> 3)) * kscale;
+        const int sbase = ((wave < HW ? wave : wave - HW) * L::SROWS + (lane >> 3)) * kscale;
 #pragma unroll
         for (int q = 0; q < 4; ++q) src.vsc[q] = (uint32_t)(sbase + (((lane & 7) ^ q) << 2));
         src.soff = 0;
     }
-    Frags<WN> FA, FB;
+    Frags<CFG> FA, FB;
     // sa/sb: shifted scale words of the step being computed; ra/rb: raw
     // words of the next step, read after the barrier that publishes it.
-    uint32_t sa[4] = {0, 0, 0, 0}, ra[4] = {0, 0, 0, 0};
-    uint32_t sb[TN], rb[TN];
+    uint32_t sa[TM], ra[TM], sb[TN], rb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] = ra[i] = 0;
 #pragma unroll
     for (int j = 0; j < TN; ++j) sb[j] = rb[j] = 0;
     const int sh = 8 * half;
@@ -308,20 +331,20 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[4][Layout<WN>::TN],
     //   4. read the scales and (t + 1, 0) fragments; MFMAs of (t, 1).
     // The loop is unrolled by one scale group (8 steps, two turns of the
     // ring), so every load count and wait is a compile-time constant.
-    constexpr int LC = 2 * L::RPW;  // code loads per wave per step
+    constexpr int LC = L::RPW_A + L::RPW_B;  // code loads per wave per step
     // loads issued after the code loads of step t + 1, at the end of step t
     // with t % 8 == p: those of steps t - 1 and t plus the scale pieces
     // issued after the code loads in step t - 2
 #define FP4Q_PIECES(p) ((BF16OPS || ((p) & 7) >= 4) ? 0 : L::SPIECES / 4)
 #define FP4Q_BEHIND(p) (FP4Q_PIECES((p) + 6) + LC + FP4Q_PIECES((p) + 7) + LC + FP4Q_PIECES(p))
-    if (!BF16OPS) issue_scale_pieces<WN, 0, L::SPIECES>(src, sc0, wave, kscale, 0);
-    issue_codes<WN, BF16OPS>(src, st0, wave, 1 < ksteps);
-    issue_codes<WN, BF16OPS>(src, st1, wave, 2 < ksteps);
-    issue_codes<WN, BF16OPS>(src, st2, wave, 3 < ksteps);
+    if (!BF16OPS) issue_scale_pieces<CFG, 0, L::SPIECES>(src, sc0, wave, kscale, 0);
+    issue_codes<CFG, BF16OPS>(src, st0, wave, 1 < ksteps);
+    issue_codes<CFG, BF16OPS>(src, st1, wave, 2 < ksteps);
+    issue_codes<CFG, BF16OPS>(src, st2, wave, 3 < ksteps);
     FP4Q_WAIT_VMCNT(2 * LC);
     __builtin_amdgcn_s_barrier();
-    if (!BF16OPS) read_scales<WN>(sc0, sxor << 2, wm, wn, lane, ra, rb);
-    read_frags<WN>(st0, off0, wm, wn, FA);
+    if (!BF16OPS) read_scales<CFG>(sc0, sxor << 2, wm, wn, lane, ra, rb);
+    read_frags<CFG>(st0, off0, wm, wn, FA);
 
 // One K step t = kt + P (P = t % 16, compile-time; its position in the
 // scale group is P % 8).  SCUR / SNXT: scale buffers of this group and the
@@ -331,24 +354,24 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[4][Layout<WN>::TN],
     do {                                                                             \
         const int t_ = kt + (P);                                                     \
         __builtin_amdgcn_sched_barrier(0);                                           \
-        if (!BF16OPS) shift_scales<WN>(ra, rb, sh, sa, sb);                          \
-        read_frags<WN>(CUR, off1, wm, wn, FB);                                       \
-        issue_codes<WN, BF16OPS>(src, NEXTL, wave, t_ + 4 < ksteps);                 \
+        if (!BF16OPS) shift_scales<CFG>(ra, rb, sh, sa, sb);                          \
+        read_frags<CFG>(CUR, off1, wm, wn, FB);                                       \
+        issue_codes<CFG, BF16OPS>(src, NEXTL, wave, t_ + 4 < ksteps);                 \
         if (FP4Q_PIECES(P))                                                          \
-            issue_scale_pieces<WN, ((P) & 3) * (L::SPIECES / 4), L::SPIECES / 4>(        \
+            issue_scale_pieces<CFG, ((P) & 3) * (L::SPIECES / 4), L::SPIECES / 4>(        \
                 src, SNXT, wave, kscale, t_ / SG + 1);                                   \
         __builtin_amdgcn_sched_barrier(0);                                           \
-        mfma_half<WN, BF16OPS, 0>(FA, sa, sb, acc);                                  \
+        mfma_half<CFG, BF16OPS, 0>(FA, sa, sb, acc);                                  \
         __builtin_amdgcn_sched_barrier(0);                                           \
         FP4Q_WAIT_VMCNT(FP4Q_BEHIND(P));                                             \
         __builtin_amdgcn_s_waitcnt(0xC07F);                                          \
         __builtin_amdgcn_s_barrier();                                                \
         __builtin_amdgcn_sched_barrier(0);                                           \
         if (!BF16OPS)                                                                \
-            read_scales<WN>(((P) & 7) == 7 ? SNXT : SCUR, (((P) + 1) & 7 ^ sxor) << 2, wm, wn, \
+            read_scales<CFG>(((P) & 7) == 7 ? SNXT : SCUR, (((P) + 1) & 7 ^ sxor) << 2, wm, wn, \
                             lane, ra, rb);                                           \
-        read_frags<WN>(NEXT1, off0, wm, wn, FA);                                     \
-        mfma_half<WN, BF16OPS, 1>(FB, sa, sb, acc);                                  \
+        read_frags<CFG>(NEXT1, off0, wm, wn, FA);                                     \
+        mfma_half<CFG, BF16OPS, 1>(FB, sa, sb, acc);                                  \
     } while (0)
 
 // Eight steps of one scale group starting at t = kt + O; GUARD(P) says
@@ -393,15 +416,15 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[4][Layout<WN>::TN],
 // OPS: 0 = FP4 operands; 1 = bf16 operands (ac, bc hold bf16 rows, no
 // scales); 2 = FP4 over K, then bf16 over the kp-deep operands ha, hb into
 // the same accumulators (the single-kernel hot-channel compensation).
-template <int WN, int OUT_BF16, int ACCUM, int OPS>
-__global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
+template <int CFG, int OUT_BF16, int ACCUM, int OPS>
+__global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
     int M, int N, int K, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, void* __restrict__ cptr,
     int64_t ldc, int tiles_m, int tiles_n, const uint8_t* __restrict__ ha,
     const uint8_t* __restrict__ hb, int kp) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot instantiate buffer resources
-    using L = Layout<WN>;
-    constexpr int TN = L::TN;
+    using L = Layout<CFG>;
+    constexpr int TM = L::TM, TN = L::TN;
 
     // ---- tile index: XCD-contiguous, then grouped along M ----
     const int nwg = gridDim.x;
@@ -417,12 +440,12 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
     const int in_grp = wg - grp * per_group;
     const int tm = first_m + in_grp % gsize;
     const int tn = in_grp / gsize;
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int m0 = tm * L::BM, n0 = tn * L::BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
+    const int wm = wave / L::WN, wn = wave % L::WN;
     const int half = lane >> 5;
     const int l32 = lane & 31;
     // this lane's offsets within a 32-row group: row lane % 32, chunk
@@ -431,9 +454,9 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
     const int off1 = (l32 >> 4) * REGION + region_slot(l32 & 15, 2 + half) * 16;
     const int sxor = (l32 >> 3) & 3;  // scale word swizzle of this lane's rows
 
-    v16f acc[4][TN];
+    v16f acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -441,7 +464,7 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
 
 
 #define FP4Q_KLOOP(BF, A_, AS_, B_, BS_, KD_)                                              \
-    gemm_kloop<WN, BF>(acc, A_, AS_, B_, BS_, KD_, M, N, m0, n0, wave, lane, wm, wn, half, l32, \
+    gemm_kloop<CFG, BF>(acc, A_, AS_, B_, BS_, KD_, M, N, m0, n0, wave, lane, wm, wn, half, l32, \
                        off0, off1, sxor)
     if (OPS == 1) {
         FP4Q_KLOOP(1, ac, as, bc, bs, K);
@@ -470,14 +493,15 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
                     : wave / PER_STAGE == 2 ? st2
                                             : st3) +
                    (wave % PER_STAGE) * EREG;
-    const int row0 = m0 + wm * 128;
+    const int row0 = m0 + wm * L::WROWS;
     const int col0 = n0 + wn * L::WCOLS;
     const bool vec_ok = ((ldc * ESZ) % 16 == 0) && (((uintptr_t)cptr & 15) == 0);
     constexpr int CHUNK_ELEMS = 16 / ESZ;  // elements per 16-byte chunk
     constexpr int LANES_PER_ROW = L::WCOLS / CHUNK_ELEMS;
-    constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
+    constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;  // rows read back per pass
+    constexpr int PASSES = (32 + ROWS_PER_PASS - 1) / ROWS_PER_PASS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -501,9 +525,11 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
         __builtin_amdgcn_wave_barrier();
         const int rbase = row0 + i * 32;
 #pragma unroll
-        for (int p = 0; p < 32 / ROWS_PER_PASS; ++p) {
+        for (int p = 0; p < PASSES; ++p) {
             const int rl = p * ROWS_PER_PASS + lane / LANES_PER_ROW;
             const int ce = (lane % LANES_PER_ROW) * CHUNK_ELEMS;
+            // 96-column waves: lanes past the last whole row, and rows past 32
+            if (lane >= ROWS_PER_PASS * LANES_PER_ROW || rl >= 32) continue;
             const u32x4 v = *(const u32x4*)(reg + rl * PITCH + ce * ESZ);
             const int row = rbase + rl;
             const int col = col0 + ce;
@@ -547,17 +573,63 @@ __global__ __launch_bounds__(Layout<WN>::THREADS, 1) void gemm_fp4_kernel(
 #endif
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Tile configuration for an M x N output: one workgroup per compute unit at
+// a time, so the time goes as (rounds of workgroups) x (time per tile).  A
+// 128 x 384 tile holds 3/4 of a 256 x 256 tile's work but, measured on
+// MI355X, takes about 1.09x its time (its half-step of 6 MFMAs per wave hides
+// less of the LDS latency, and it loads 4/3 the operand bytes per flop), so
+// it is taken only where it saves a whole round (e.g. 257 tiles of 256 x 256
+// against at most 256 of 128 x 384).
+// FP4Q_GEMM_TILE=256x256 or 128x384 in the environment forces one (tests
+// cover both on the same shapes).
+static int pick_cfg(int64_t M, int64_t N) {
+    if (const char* e = getenv("FP4Q_GEMM_TILE")) {
+        if (!strcmp(e, "256x256")) return 0;
+        if (!strcmp(e, "128x384")) return 1;
+    }
+    const int64_t cus = device_cus();
+    const int64_t t0 = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t1 = ((M + 127) / 128) * ((N + 383) / 384);
+    const double e0 = (double)((t0 + cus - 1) / cus);
+    const double e1 = (double)((t1 + cus - 1) / cus) * 1.09;
+    return e1 < e0 ? 1 : 0;
+}
+
+template <int CFG, int OUT_BF16, int ACCUM, int OPS>
+static void launch_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
+                       const uint8_t* b, const uint8_t* bs, void* c, int64_t ldc, hipStream_t s,
+                       const uint8_t* ha, const uint8_t* hb, int64_t kp) {
+    using L = Layout<CFG>;
+    const int tiles_m = (int)((M + L::BM - 1) / L::BM);
+    const int tiles_n = (int)((N + L::BN - 1) / L::BN);
+    gemm_fp4_kernel<CFG, OUT_BF16, ACCUM, OPS><<<dim3((unsigned)(tiles_m * tiles_n)), L::THREADS, 0, s>>>(
+        (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m, tiles_n, ha, hb, (int)kp);
+}
+
 template <int OUT_BF16, int ACCUM, int OPS>
 static void launch_tiles(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                          const uint8_t* b, const uint8_t* bs, void* c, int64_t ldc,
                          hipStream_t s, const uint8_t* ha = nullptr, const uint8_t* hb = nullptr,
                          int64_t kp = 0) {
-    constexpr int WN = FP4Q_GEMM_WN;
-    const int tiles_m = (int)((M + BM - 1) / BM);
-    const int tiles_n = (int)((N + BN - 1) / BN);
-    gemm_fp4_kernel<WN, OUT_BF16, ACCUM, OPS>
-        <<<dim3((unsigned)(tiles_m * tiles_n)), Layout<WN>::THREADS, 0, s>>>(
-            (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m, tiles_n, ha, hb, (int)kp);
+    if (pick_cfg(M, N) == 1)
+        launch_cfg<1, OUT_BF16, ACCUM, OPS>(M, N, K, a, as, b, bs, c, ldc, s, ha, hb, kp);
+    else
+        launch_cfg<0, OUT_BF16, ACCUM, OPS>(M, N, K, a, as, b, bs, c, ldc, s, ha, hb, kp);
 }
 
 hipError_t launch_gemm_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,

@@ -55,15 +55,39 @@ def test_tiny_ref_gemm(orc):
     gemm_full_check(orc, A, B, torch.bfloat16)
 
 
+TILES = ["256x256", "128x384"]
+
+
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (300, 200, 256), (257, 129, 384),
-                                   (64, 520, 128), (513, 33, 1024)])
-def test_ragged_gemm(orc, M, N, K):
+                                   (64, 520, 128), (513, 33, 1024), (129, 769, 256)])
+def test_ragged_gemm(orc, M, N, K, tile, monkeypatch):
+    monkeypatch.setenv("FP4Q_GEMM_TILE", tile)
     a = inputs.with_outliers(inputs.normal((M, K), M), M + 1, max(1, M * K // 100), 50.0)
     b = inputs.with_outliers(inputs.normal((N, K), N + 7), N + 8, max(1, N * K // 100), 50.0)
     A, B = qpair(orc, a, b)
     gemm_full_check(orc, A, B, torch.float32, ldc_pad=4)
     gemm_full_check(orc, A, B, torch.bfloat16, ldc_pad=8)
     gemm_full_check(orc, A, B, torch.float32, accumulate=True, seed=M)
+
+
+@pytest.mark.parametrize("M,N,K", [(8192, 5632, 2048), (2048, 5632, 8192), (700, 1000, 512)])
+def test_gemm_tiles_bit_identical(M, N, K, monkeypatch):
+    """Both tile shapes accumulate each output over K in the same order: the
+    outputs agree bit for bit (bf16 and fp32 C), including ragged edges."""
+    rng = np.random.default_rng(M + N + K)
+    ac = torch.from_numpy(rng.integers(0, 256, (M, K // 2), dtype=np.uint8)).cuda()
+    bc = torch.from_numpy(rng.integers(0, 256, (N, K // 2), dtype=np.uint8)).cuda()
+    as_ = torch.from_numpy(rng.integers(118, 136, (M, K // 32), dtype=np.uint8)).cuda()
+    bs = torch.from_numpy(rng.integers(118, 136, (N, K // 32), dtype=np.uint8)).cuda()
+    for dt in (torch.bfloat16, torch.float32):
+        outs = []
+        for tile in TILES:
+            monkeypatch.setenv("FP4Q_GEMM_TILE", tile)
+            outs.append(fq.gemm(ac, as_, bc, bs, out_dtype=dt))
+        torch.cuda.synchronize()
+        a, b = host_bits(outs[0]), host_bits(outs[1])
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{M}x{N}x{K} {dt}"
 
 
 def test_gemm_nan_scale_and_zero(orc):
