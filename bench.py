@@ -9,8 +9,10 @@ through every kernel of the path:
             Q2(W): COL (forward operand) + ROW (dX operand), RNE, one pass
             Y = GEMM 8192x5632x2048 -> bf16;  DQ(Q(X)) -> bf16 (the QDQ output)
   backward  Q2(dY): ROW + COL, stochastic (one random stream, seed 1234)
-            dX = GEMM 8192x2048x5632 -> bf16;  dW = GEMM 2048x5632x8192 -> fp32
-            dW' = DGE(W, col blocks, k=5, clamp 3) applied to dW
+            dX = GEMM 8192x2048x5632 -> bf16
+            dW' = GEMM 2048x5632x8192 -> fp32 with DGE(W, col blocks, k=5,
+                  clamp 3) applied in its epilogue (one kernel; the unfused
+                  GEMM + DGE pair is timed aside)
   The 13B-shaped outlier layer's hot-channel residual has its own shape and
   is timed aside with --hcp.
 
@@ -170,6 +172,13 @@ def main():
          M * N * qb2, 0),
         ("gemm_dx", lambda: fq.gemm(*bufs["dyr"], *bufs["wr"], c=dX),
          (M + K) * N * (0.5 + 1 / 32) + M * K * 2, 2.0 * M * K * N),
+        # dW = X^T dY with W's DGE derivative applied in the GEMM's epilogue
+        # (the same bits as the GEMM into fp32 followed by fp4q_grad_estimate)
+        ("gemm_dw_dge", lambda: fq.gemm_dge(*bufs["xc"], *bufs["dyc"], W, 5.0, 3.0, out=dWo),
+         (K + N) * M * (0.5 + 1 / 32) + K * N * (2 + 4), 2.0 * K * N * M),
+    ]
+    # the unfused pair, timed aside (the DGE kernel's own HBM rate)
+    aside_ops = [
         ("gemm_dw", lambda: fq.gemm(*bufs["xc"], *bufs["dyc"], c=dW),
          (K + N) * M * (0.5 + 1 / 32) + K * N * 4, 2.0 * K * N * M),
         ("dge_dw", lambda: fq.grad_estimate(fq.DGE, W, dW, 32, fq.COL, 5.0, 3.0, out=dWo),
@@ -184,7 +193,7 @@ def main():
             b = torch.empty_like(a)
             fn = lambda: b.copy_(a)
         else:
-            fn = dict((o[0], o[1]) for o in ops)[args.profile_op]
+            fn = dict((o[0], o[1]) for o in ops + aside_ops)[args.profile_op]
         for _ in range(args.reps):
             fn()
         torch.cuda.synchronize()
@@ -233,9 +242,7 @@ def main():
         run_step(events[s])
     torch.cuda.synchronize()
 
-    per_op = {}
-    for i, (name, _, nbytes, nflops) in enumerate(ops):
-        ts = [hev.elapsed_us(events[s][i], events[s][i + 1]) for s in range(args.steps)]
+    def op_stats(ts, nbytes, nflops):
         us = float(np.mean(ts))
         d = {"us": round(us, 2), "us_min": round(float(np.min(ts)), 2)}
         if nflops:
@@ -243,7 +250,26 @@ def main():
             d["frac_fp4_peak"] = round(d["TFLOPS"] / PEAK_FP4_TFLOPS, 4)
         d["GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
         d["frac_hbm_peak"] = round(d["GBps"] / PEAK_HBM_GBPS, 4)
-        per_op[name] = d
+        return d
+
+    per_op = {}
+    for i, (name, _, nbytes, nflops) in enumerate(ops):
+        ts = [hev.elapsed_us(events[s][i], events[s][i + 1]) for s in range(args.steps)]
+        per_op[name] = op_stats(ts, nbytes, nflops)
+
+    # aside: the unfused dW GEMM and DGE kernel, each timed alone
+    aside = {}
+    for name, fn, nbytes, nflops in aside_ops:
+        fn()
+        torch.cuda.synchronize()
+        evs = [hev.create() for _ in range(2 * args.steps)]
+        for s_ in range(args.steps):
+            hev.record(evs[2 * s_])
+            fn()
+            hev.record(evs[2 * s_ + 1])
+        torch.cuda.synchronize()
+        ts = [hev.elapsed_us(evs[2 * s_], evs[2 * s_ + 1]) for s_ in range(args.steps)]
+        aside[name] = op_stats(ts, nbytes, nflops)
 
     hev.close()
     value = step_flops / (ms_per_step * 1e-3) / 1e12
@@ -291,6 +317,7 @@ def main():
         "roofline": roofline,
         "quantize": quant,
         "kernels": per_op,
+        "unfused_aside": aside,
         **extra,
     }
     if cpu is not None:

@@ -166,6 +166,25 @@ fp4q_status_t fp4q_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                         int32_t accumulate, void* stream);
 
 /*
+ * fp4q_gemm_dge -- the weight-gradient GEMM with the DGE gradient estimator
+ * applied in its epilogue (adjacent operations around a quantisation node
+ * merged, the optimisation the MXFP4 tutorial page, sec. 6.1, lists): exactly
+ *   G = fp4q_gemm(A, B) into fp32, then
+ *   out = fp4q_grad_estimate(FP4Q_DGE, x, G, block 32, FP4Q_BLOCK_COL, k, clamp)
+ * in one kernel, without writing or re-reading G (same bits as that pair of
+ * calls: the same accumulation order and the same per-element product).
+ *   A, B: as fp4q_gemm (block 32); x: bf16 [M, N] dense, the weight whose
+ *   estimator this is, with column blocks of 32 rows (M % 32 == 0);
+ *   out: fp32 [M, N], row stride ld_out >= N, written.
+ *   k >= 1, clamp_max > 0; K % 128 == 0, K < 2^24.  fp32 x:
+ *   FP4Q_ERR_UNSUPPORTED.  A block of x holding NaN/Inf gives NaN.
+ */
+fp4q_status_t fp4q_gemm_dge(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                            const uint8_t* a_scales, const uint8_t* b_codes,
+                            const uint8_t* b_scales, const void* x, fp4q_dtype_t x_dtype,
+                            float k, float clamp_max, float* out, int64_t ld_out, void* stream);
+
+/*
  * fp4q_hcp_workspace_bytes -- bytes of device workspace fp4q_hcp_residual_add
  * needs for these sizes.
  */

@@ -22,7 +22,8 @@ STATUS = {0: "FP4Q_OK", 1: "FP4Q_ERR_INVALID", 2: "FP4Q_ERR_UNSUPPORTED",
 
 EXPORTS = ["fp4q_quantize", "fp4q_quantize_dual", "fp4q_dequantize", "fp4q_grad_estimate",
            "fp4q_gemm",
-           "fp4q_hcp_workspace_bytes", "fp4q_hcp_residual_add", "fp4q_gemm_hcp",
+           "fp4q_gemm_dge", "fp4q_hcp_workspace_bytes", "fp4q_hcp_residual_add",
+           "fp4q_gemm_hcp",
            "fp4q_status_string",
            "fp4q_last_error", "fp4q_abi_version"]
 
@@ -57,6 +58,7 @@ def lib():
             "fp4q_hcp_workspace_bytes": (SZ, [I64, I64, I32]),
             "fp4q_hcp_residual_add": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, P, SZ,
                                             P]),
+            "fp4q_gemm_dge": (I32, [I64, I64, I64, P, P, P, P, P, I32, F, F, P, I64, P]),
             "fp4q_gemm_hcp": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, I64, P, SZ, P]),
             "fp4q_status_string": (_ct.c_char_p, [I32]),
             "fp4q_last_error": (_ct.c_char_p, []),
@@ -233,3 +235,22 @@ def gemm_hcp(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, y=None, wo
                                _ptr(wq_codes), _ptr(wq_scales), _ptr(hot_idx), n_hot, _ptr(y),
                                y.stride(0), _ptr(workspace), workspace.numel(), _stream(stream)))
     return y
+
+
+def gemm_dge(a_codes, a_scales, b_codes, b_scales, x, k=5.0, clamp_max=3.0, out=None,
+             stream=None):
+    """out[M,N] (fp32) = deq(A) deq(B)^T times the DGE derivative of x (bf16 [M,N],
+    column blocks of 32), in one kernel (fp4q_gemm_dge); returns out."""
+    torch = _torch()
+    _need_cuda(a_codes, a_scales, b_codes, b_scales, x)
+    M, N, K = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
+    if b_codes.shape[1] * 2 != K:
+        raise ValueError("A and B K dimensions differ")
+    if tuple(x.shape) != (M, N):
+        raise ValueError("x must be [M, N]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    _check(lib().fp4q_gemm_dge(M, N, K, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
+                               _ptr(b_scales), _ptr(x), _dt(x), k, clamp_max, _ptr(out),
+                               out.stride(0), _stream(stream)))
+    return out

@@ -239,6 +239,35 @@ fp4q_status_t fp4q_hcp_residual_add(int64_t M, int64_t N, int64_t K, const void*
                       "hcp launch");
 }
 
+fp4q_status_t fp4q_gemm_dge(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                            const uint8_t* a_scales, const uint8_t* b_codes,
+                            const uint8_t* b_scales, const void* x, fp4q_dtype_t x_dtype,
+                            float k, float clamp_max, float* out, int64_t ld_out, void* stream) {
+    if (!a_codes || !a_scales || !b_codes || !b_scales || !x || !out)
+        return fail(FP4Q_ERR_INVALID, "gemm_dge: null pointer");
+    if (M <= 0 || N <= 0 || K <= 0) return fail(FP4Q_ERR_INVALID, "gemm_dge: bad sizes");
+    if (!valid_dtype(x_dtype)) return fail(FP4Q_ERR_INVALID, "gemm_dge: bad x dtype");
+    if (x_dtype != FP4Q_BF16) return fail(FP4Q_ERR_UNSUPPORTED, "gemm_dge: x must be bf16");
+    if (K % 128) return fail(FP4Q_ERR_INVALID, "gemm_dge: K %% 128 != 0");
+    if (M % 32) return fail(FP4Q_ERR_INVALID, "gemm_dge: M %% 32 != 0 (column blocks of x)");
+    if (ld_out < N) return fail(FP4Q_ERR_INVALID, "gemm_dge: ld_out < N");
+    if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
+        return fail(FP4Q_ERR_INVALID, "gemm_dge: dimension too large");
+    if (M > kMaxElems / N) return fail(FP4Q_ERR_INVALID, "gemm_dge: tensor too large");
+    if (K >= ((int64_t)1 << 24))
+        return fail(FP4Q_ERR_UNSUPPORTED, "gemm_dge: K must be below 2^24");
+    if (!(k >= 1.0f) || !(k < 1e30f)) return fail(FP4Q_ERR_INVALID, "gemm_dge: k must be >= 1");
+    if (!(clamp_max > 0.0f)) return fail(FP4Q_ERR_INVALID, "gemm_dge: clamp_max must be > 0");
+    if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) ||
+        !aligned16(b_scales) || !aligned16(x) || ((uintptr_t)out % 4))
+        return fail(FP4Q_ERR_ALIGNMENT,
+                    "gemm_dge: operands and x must be 16-byte aligned, out 4-byte aligned");
+    return hip_status(fp4q::launch_gemm_fp4_dge(M, N, K, a_codes, a_scales, b_codes, b_scales,
+                                                (const uint16_t*)x, k, clamp_max, out, ld_out,
+                                                (hipStream_t)stream),
+                      "gemm_dge launch");
+}
+
 fp4q_status_t fp4q_gemm_hcp(int64_t M, int64_t N, int64_t K, const void* x,
                             const uint8_t* xq_codes, const uint8_t* xq_scales, const void* w,
                             const uint8_t* wq_codes, const uint8_t* wq_scales,

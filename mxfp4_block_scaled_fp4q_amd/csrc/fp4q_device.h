@@ -191,4 +191,31 @@ __device__ __forceinline__ uint32_t sr_pack8(const float x[8], float sc, const u
     return r;
 }
 
+// DGE derivative d(x) for one element with inverse block scale inv (the
+// MSRA FP4-training summary page, sec. 二): with m = |x| inv and
+// E = max(biased exponent(m), 127), q = m 2^(128 - E) puts every E2M1
+// interval at unit width, u = 2 (q - floor(q)) - 1 exactly, and
+// d = min((1/k) |u|^(1/k - 1), clamp_max) via the hardware log2/exp2;
+// m > 6 (saturated) gives 1.  Shared by the gradient-estimator kernels and the
+// GEMM epilogue that applies it, so both give the same bits.
+struct DgeParams {
+    float invk, p, clamp_max;
+    int k_one;
+};
+
+__device__ __forceinline__ float dge_factor(float x, float inv, DgeParams P) {
+    const float m = fabsf(x) * inv;
+    if (m > 6.0f) return 1.0f;
+    const uint32_t E = max(as_u32(m) >> 23, 127u);
+    const float q = m * as_f32((255u - E) << 23);
+    const float u = 2.0f * (q - floorf(q)) - 1.0f;
+    float d;
+    if (P.k_one) {
+        d = 1.0f;
+    } else {
+        d = P.invk * __builtin_amdgcn_exp2f(P.p * __builtin_amdgcn_logf(fabsf(u)));
+    }
+    return fminf(d, P.clamp_max);
+}
+
 }  // namespace fp4q

@@ -56,6 +56,12 @@ hipError_t launch_gemm_fp4_hot(int64_t M, int64_t N, int64_t K, const uint8_t* a
                                const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                                const uint16_t* ha, const uint16_t* hb, int64_t kp, float* c,
                                int64_t ldc, hipStream_t s);
+// C[M,N] (fp32, row stride ldc) = (A B^T) * DGE'(x), x bf16 [M, N] dense with
+// column blocks of 32 rows (M % 32 == 0, K % 128 == 0).
+hipError_t launch_gemm_fp4_dge(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
+                               const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                               const uint16_t* x, float k, float clamp_max, float* c,
+                               int64_t ldc, hipStream_t s);
 size_t hcp_workspace_bytes(int64_t M, int64_t N, int32_t n_hot);
 hipError_t launch_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
                       const uint8_t* xqs, const void* w, const uint8_t* wqc, const uint8_t* wqs,

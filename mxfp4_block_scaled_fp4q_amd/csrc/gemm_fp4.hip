@@ -416,15 +416,21 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[Layout<CFG>::TM][Layout<C
 // OPS: 0 = FP4 operands; 1 = bf16 operands (ac, bc hold bf16 rows, no
 // scales); 2 = FP4 over K, then bf16 over the kp-deep operands ha, hb into
 // the same accumulators (the single-kernel hot-channel compensation).
-template <int CFG, int OUT_BF16, int ACCUM, int OPS>
+// EPI = 1 (fp32 C, 256 x 256 tiles, M % 32 == 0): C is multiplied in the
+// epilogue by the DGE derivative of ex [M, N] (bf16, dense) with ex's column
+// blocks of 32 rows -- the weight gradient's estimator applied where the
+// weight gradient is produced.
+template <int CFG, int OUT_BF16, int ACCUM, int OPS, int EPI = 0>
 __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
     int M, int N, int K, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, void* __restrict__ cptr,
     int64_t ldc, int tiles_m, int tiles_n, const uint8_t* __restrict__ ha,
-    const uint8_t* __restrict__ hb, int kp) {
+    const uint8_t* __restrict__ hb, int kp, const uint16_t* __restrict__ ex, DgeParams dp) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot instantiate buffer resources
     using L = Layout<CFG>;
     constexpr int TM = L::TM, TN = L::TN;
+    static_assert(!EPI || (CFG == 0 && !OUT_BF16 && !ACCUM && OPS == 0),
+                  "the DGE epilogue is for fp32 C on 256 x 256 tiles");
 
     // ---- tile index: XCD-contiguous, then grouped along M ----
     const int nwg = gridDim.x;
@@ -524,13 +530,62 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
         __builtin_amdgcn_wave_barrier();
         const int rbase = row0 + i * 32;
+        // DGE epilogue: these 32 rows are one column block of ex.  Each lane
+        // reads ex at the 4 columns and PASSES rows it writes; lanes 16 apart
+        // share columns, so two exchanges give each column's block maximum.
+        uint2 xw[EPI ? PASSES : 1];
+        float inv4[4];
+        bool nf4[4];
+        if (EPI) {
+            const int cx = col0 + (lane % LANES_PER_ROW) * CHUNK_ELEMS;
+            const bool xvec = (N % 4) == 0 && cx + 4 <= N;
+            uint32_t m4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p) {
+                const int row = rbase + p * ROWS_PER_PASS + lane / LANES_PER_ROW;
+                uint2 w = make_uint2(0u, 0u);
+                if (row < M) {
+                    const uint16_t* xr = ex + (int64_t)row * N + cx;
+                    if (xvec) {
+                        w = *(const uint2*)xr;
+                    } else {
+                        uint32_t e4[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) e4[e] = cx + e < N ? (uint32_t)xr[e] : 0u;
+                        w = make_uint2(e4[0] | (e4[1] << 16), e4[2] | (e4[3] << 16));
+                    }
+                }
+                xw[p] = w;
+                m4[0] = max(m4[0], (w.x << 16) & 0x7FFFFFFFu);
+                m4[1] = max(m4[1], w.x & 0x7FFF0000u);
+                m4[2] = max(m4[2], (w.y << 16) & 0x7FFFFFFFu);
+                m4[3] = max(m4[3], w.y & 0x7FFF0000u);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                m4[e] = max(m4[e], (uint32_t)__shfl_xor((int)m4[e], 16));
+                m4[e] = max(m4[e], (uint32_t)__shfl_xor((int)m4[e], 32));
+                nf4[e] = m4[e] >= 0x7F800000u;
+                inv4[e] = e8m0_inv_scale_f32(nf4[e] ? 0u : e8m0_from_amax(m4[e]));
+            }
+        }
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) {
             const int rl = p * ROWS_PER_PASS + lane / LANES_PER_ROW;
             const int ce = (lane % LANES_PER_ROW) * CHUNK_ELEMS;
             // 96-column waves: lanes past the last whole row, and rows past 32
             if (lane >= ROWS_PER_PASS * LANES_PER_ROW || rl >= 32) continue;
-            const u32x4 v = *(const u32x4*)(reg + rl * PITCH + ce * ESZ);
+            u32x4 v = *(const u32x4*)(reg + rl * PITCH + ce * ESZ);
+            if (EPI) {
+                // the gradient estimator's product, as fp4q_grad_estimate forms it
+                const float xf[4] = {bf16_lo(xw[p].x), bf16_hi(xw[p].x), bf16_lo(xw[p].y),
+                                     bf16_hi(xw[p].y)};
+                float o[4] = {as_f32(v.x), as_f32(v.y), as_f32(v.z), as_f32(v.w)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = o[e] * (nf4[e] ? __builtin_nanf("") : dge_factor(xf[e], inv4[e], dp));
+                v = (u32x4){as_u32(o[0]), as_u32(o[1]), as_u32(o[2]), as_u32(o[3])};
+            }
             const int row = rbase + rl;
             const int col = col0 + ce;
             if (row >= M) continue;
@@ -610,15 +665,18 @@ static int pick_cfg(int64_t M, int64_t N) {
     return e1 < e0 ? 1 : 0;
 }
 
-template <int CFG, int OUT_BF16, int ACCUM, int OPS>
+template <int CFG, int OUT_BF16, int ACCUM, int OPS, int EPI = 0>
 static void launch_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                        const uint8_t* b, const uint8_t* bs, void* c, int64_t ldc, hipStream_t s,
-                       const uint8_t* ha, const uint8_t* hb, int64_t kp) {
+                       const uint8_t* ha, const uint8_t* hb, int64_t kp,
+                       const uint16_t* ex = nullptr, DgeParams dp = DgeParams{}) {
     using L = Layout<CFG>;
     const int tiles_m = (int)((M + L::BM - 1) / L::BM);
     const int tiles_n = (int)((N + L::BN - 1) / L::BN);
-    gemm_fp4_kernel<CFG, OUT_BF16, ACCUM, OPS><<<dim3((unsigned)(tiles_m * tiles_n)), L::THREADS, 0, s>>>(
-        (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m, tiles_n, ha, hb, (int)kp);
+    gemm_fp4_kernel<CFG, OUT_BF16, ACCUM, OPS, EPI>
+        <<<dim3((unsigned)(tiles_m * tiles_n)), L::THREADS, 0, s>>>(
+            (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m, tiles_n, ha, hb, (int)kp, ex,
+            dp);
 }
 
 template <int OUT_BF16, int ACCUM, int OPS>
@@ -657,6 +715,19 @@ hipError_t launch_gemm_fp4_hot(int64_t M, int64_t N, int64_t K, const uint8_t* a
                                int64_t ldc, hipStream_t s) {
     launch_tiles<0, 0, 2>(M, N, K, ac, as, bc, bs, c, ldc, s, (const uint8_t*)ha,
                           (const uint8_t*)hb, kp);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp4_dge(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
+                               const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                               const uint16_t* x, float k, float clamp_max, float* c,
+                               int64_t ldc, hipStream_t s) {
+    DgeParams P;
+    P.invk = 1.0f / k;
+    P.p = 1.0f / k - 1.0f;
+    P.clamp_max = clamp_max;
+    P.k_one = (k == 1.0f);
+    launch_cfg<0, 0, 0, 0, 1>(M, N, K, ac, as, bc, bs, c, ldc, s, nullptr, nullptr, 0, x, P);
     return hipGetLastError();
 }
 

@@ -27,26 +27,6 @@ namespace fp4q {
 
 static constexpr int kThreads = 256;
 
-struct DgeParams {
-    float invk, p, clamp_max;
-    int k_one;
-};
-
-__device__ __forceinline__ float dge_factor(float x, float inv, DgeParams P) {
-    const float m = fabsf(x) * inv;
-    if (m > 6.0f) return 1.0f;
-    const uint32_t E = max(as_u32(m) >> 23, 127u);
-    const float q = m * as_f32((255u - E) << 23);
-    const float u = 2.0f * (q - floorf(q)) - 1.0f;
-    float d;
-    if (P.k_one) {
-        d = 1.0f;
-    } else {
-        d = P.invk * __builtin_amdgcn_exp2f(P.p * __builtin_amdgcn_logf(fabsf(u)));
-    }
-    return fminf(d, P.clamp_max);
-}
-
 template <int BF16>
 __device__ __forceinline__ void load8(const void* p, int64_t e0, float (&f)[8]) {
     if (BF16) {

@@ -212,3 +212,39 @@ def test_gemm_hcp_validation(L):
     bad = list(args)
     bad[6] = FAKE_MIS    # W codes not 16-byte aligned
     assert h(*bad) == 3
+
+
+def test_gemm_dge_validation(L):
+    h = L.fp4q_gemm_dge
+    F = ct.c_float
+    args = [256, 64, 256, FAKE, FAKE, FAKE, FAKE, FAKE, 1, F(5.0), F(3.0), FAKE, 64, NUL]
+    bad = list(args)
+    bad[0] = 250         # M % 32 (column blocks of x)
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[2] = 192         # K % 128
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[8] = 0           # fp32 x
+    assert h(*bad) == 2
+    bad = list(args)
+    bad[8] = 7           # not a dtype
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[9] = F(0.5)      # k < 1
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[10] = F(0.0)     # clamp
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[12] = 63         # ld_out < N
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[7] = NUL         # x
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[7] = FAKE_MIS    # x alignment
+    assert h(*bad) == 3
+    bad = list(args)
+    bad[2] = 1 << 24
+    assert h(*bad) == 2

@@ -167,6 +167,44 @@ def test_ffn_backward_gemms_and_dge(orc):
     tol = dref * (GEMM_REL * S) * (1 + 2.0 ** -20) + np.abs(C) * dref * 2.0 ** -20 \
         + np.abs(C * dref) * 2.0 ** -23
     assert np.all(np.abs(got - C * dref) <= tol)
+    # the same product from the GEMM with the estimator in its epilogue
+    fused = fq.gemm_dge(dev(xc[0]), dev(xc[1]), dev(dyc[0]), dev(dyc[1]), dev_bf16(W), 5.0, 3.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(fused).view(np.uint32), host_bits(out).view(np.uint32)), \
+        "gemm_dge differs from gemm + grad_estimate"
+
+
+@pytest.mark.parametrize("M,N,K,k", [(32, 1, 128, 5.0), (96, 200, 256, 5.0), (320, 517, 384, 5.0),
+                                     (256, 256, 512, 1.0), (64, 388, 128, 3.0)])
+def test_gemm_dge_small(orc, M, N, K, k):
+    """fp4q_gemm_dge against the oracle (GEMM entries times the oracle's DGE
+    derivative of x, COL blocks of 32) over every output, and bit for bit
+    against fp4q_gemm + fp4q_grad_estimate; x carries a zero block, a block
+    with an Inf (its outputs are NaN) and outliers."""
+    a = inputs.normal((M, K), M + 3)
+    b = inputs.normal((N, K), N + 5)
+    A, B = qpair(orc, a, b)
+    x = inputs.with_outliers(inputs.normal((M, N), M + N, 0.02), 9, max(1, M * N // 100), 50.0)
+    x[0:32, 0] = 0.0
+    if N > 2:
+        x[5, 2] = np.inf
+    xb = inputs.to_bf16_bits(x)
+    out = fq.gemm_dge(dev(A[0]), dev(A[1]), dev(B[0]), dev(B[1]), dev_bf16(xb), k, 3.0)
+    g = fq.gemm(dev(A[0]), dev(A[1]), dev(B[0]), dev(B[1]), out_dtype=torch.float32)
+    two = fq.grad_estimate(fq.DGE, dev_bf16(xb), g, 32, fq.COL, k, 3.0, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = host_bits(out).astype(np.float64)
+    assert np.array_equal(host_bits(out).view(np.uint32), host_bits(two).view(np.uint32))
+    C, S = orc.gemm(A[0], A[1], B[0], B[1])
+    d_ref, _ = orc.grad_estimate(orc.DGE, xb, np.zeros((M, N), np.float32), 32, orc.COL, k, 3.0)
+    nan = np.isnan(d_ref)
+    assert np.isnan(got[nan]).all()
+    if N > 2:
+        assert nan[0:32, 2].all() and not nan[32:, 2].any()
+    ok = ~nan
+    tol = d_ref[ok] * (GEMM_REL * S[ok]) * (1 + 2.0 ** -20) + np.abs(C[ok]) * d_ref[ok] * 2.0 ** -20 \
+        + np.abs(C[ok] * d_ref[ok]) * 2.0 ** -23
+    assert np.all(np.abs(got[ok] - C[ok] * d_ref[ok]) <= tol)
 
 
 def test_outlier_layer_gemm_and_hcp(orc):
