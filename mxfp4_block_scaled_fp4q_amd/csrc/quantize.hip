@@ -457,6 +457,9 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
             if (ROW == 3) {
                 // the same words give rows 2p and 2p+1 their ROW codes
                 const int64_t rcodes = cols / 2, rscales = cols / BLOCK;
+                // this thread's first row's outputs, stepped by compile-time row counts
+                uint8_t* const crow0 = codes_r + (r0 + rg * RPT) * rcodes + c0 / 2;
+                uint8_t* const srow0 = scales_r + (r0 + rg * RPT) * rscales + c0 / BLOCK;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int i = 2 * p + h;
@@ -469,8 +472,8 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
                                                h ? w1 : w0);
                     if (rbyte == 0xFFu) packed = 0;
                     if (rows_ok && c0 < cols) {
-                        *(uint32_t*)(codes_r + (r + h) * rcodes + c0 / 2) = packed;
-                        if ((cg % RG) == 0) scales_r[(r + h) * rscales + c0 / BLOCK] = (uint8_t)rbyte;
+                        *(uint32_t*)(crow0 + (2 * p + h) * rcodes) = packed;
+                        if ((cg % RG) == 0) srow0[(2 * p + h) * rscales] = (uint8_t)rbyte;
                     }
                 }
             }
