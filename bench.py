@@ -177,8 +177,15 @@ def main():
         ("gemm_dw_dge", lambda: fq.gemm_dge(*bufs["xc"], *bufs["dyc"], W, 5.0, 3.0, out=dWo),
          (K + N) * M * (0.5 + 1 / 32) + K * N * (2 + 4), 2.0 * K * N * M),
     ]
-    # the unfused pair, timed aside (the DGE kernel's own HBM rate)
+    yq = (torch.empty((M, N // 2), **u8), torch.empty((M, N // 32), **u8))
+    # timed aside: the unfused dW GEMM and DGE (the DGE kernel's own HBM
+    # rate), and the forward GEMM that also quantises Y for a next layer
+    # against the same GEMM followed by the ROW quantiser
     aside_ops = [
+        ("gemm_fwd_quant_y", lambda: fq.gemm_quant(*bufs["xr"], *bufs["wc"], c=Y, out=yq),
+         (M + N) * K * (0.5 + 1 / 32) + M * N * (2 + 0.5 + 1 / 32), 2.0 * M * N * K),
+        ("quant_y_row", lambda: fq.quantize(Y, 32, fq.ROW, codes=yq[0], scales=yq[1]),
+         M * N * qb, 0),
         ("gemm_dw", lambda: fq.gemm(*bufs["xc"], *bufs["dyc"], c=dW),
          (K + N) * M * (0.5 + 1 / 32) + K * N * 4, 2.0 * K * N * M),
         ("dge_dw", lambda: fq.grad_estimate(fq.DGE, W, dW, 32, fq.COL, 5.0, 3.0, out=dWo),

@@ -185,6 +185,23 @@ fp4q_status_t fp4q_gemm_dge(int64_t M, int64_t N, int64_t K, const uint8_t* a_co
                             float k, float clamp_max, float* out, int64_t ld_out, void* stream);
 
 /*
+ * fp4q_gemm_quant -- a GEMM whose epilogue quantises its own bf16 output for
+ * the next layer (quantisation fused into the producing kernel, the merge of
+ * adjacent operations the MXFP4 tutorial page, sec. 6.1, lists): exactly
+ *   C = fp4q_gemm(A, B) as bf16, then
+ *   fp4q_quantize(C, bf16, block 32, FP4Q_BLOCK_ROW, FP4Q_ROUND_RNE)
+ * in one kernel, without re-reading C.
+ *   A, B: as fp4q_gemm (block 32; K % 128 == 0, K < 2^24).
+ *   c: bf16 [M, N] with row stride ld_c >= N, written; may be NULL (then only
+ *      the quantisation is written).
+ *   y_codes [M, N/2], y_scales [M, N/32]: written (N % 32 == 0).
+ */
+fp4q_status_t fp4q_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                              const uint8_t* a_scales, const uint8_t* b_codes,
+                              const uint8_t* b_scales, void* c, int64_t ld_c, uint8_t* y_codes,
+                              uint8_t* y_scales, void* stream);
+
+/*
  * fp4q_hcp_workspace_bytes -- bytes of device workspace fp4q_hcp_residual_add
  * needs for these sizes.
  */

@@ -22,7 +22,8 @@ STATUS = {0: "FP4Q_OK", 1: "FP4Q_ERR_INVALID", 2: "FP4Q_ERR_UNSUPPORTED",
 
 EXPORTS = ["fp4q_quantize", "fp4q_quantize_dual", "fp4q_dequantize", "fp4q_grad_estimate",
            "fp4q_gemm",
-           "fp4q_gemm_dge", "fp4q_hcp_workspace_bytes", "fp4q_hcp_residual_add",
+           "fp4q_gemm_dge", "fp4q_gemm_quant", "fp4q_hcp_workspace_bytes",
+           "fp4q_hcp_residual_add",
            "fp4q_gemm_hcp",
            "fp4q_status_string",
            "fp4q_last_error", "fp4q_abi_version"]
@@ -59,6 +60,7 @@ def lib():
             "fp4q_hcp_residual_add": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, P, SZ,
                                             P]),
             "fp4q_gemm_dge": (I32, [I64, I64, I64, P, P, P, P, P, I32, F, F, P, I64, P]),
+            "fp4q_gemm_quant": (I32, [I64, I64, I64, P, P, P, P, P, I64, P, P, P]),
             "fp4q_gemm_hcp": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, I64, P, SZ, P]),
             "fp4q_status_string": (_ct.c_char_p, [I32]),
             "fp4q_last_error": (_ct.c_char_p, []),
@@ -254,3 +256,26 @@ def gemm_dge(a_codes, a_scales, b_codes, b_scales, x, k=5.0, clamp_max=3.0, out=
                                _ptr(b_scales), _ptr(x), _dt(x), k, clamp_max, _ptr(out),
                                out.stride(0), _stream(stream)))
     return out
+
+
+def gemm_quant(a_codes, a_scales, b_codes, b_scales, c=None, write_c=True, out=None,
+               stream=None):
+    """C = deq(A) deq(B)^T in bf16 (written unless write_c is False) and C's ROW
+    block-32 nearest-even quantisation, in one kernel (fp4q_gemm_quant).
+    Returns (c or None, (codes, scales))."""
+    torch = _torch()
+    _need_cuda(a_codes, a_scales, b_codes, b_scales)
+    M, N, K = a_codes.shape[0], b_codes.shape[0], a_codes.shape[1] * 2
+    if b_codes.shape[1] * 2 != K:
+        raise ValueError("A and B K dimensions differ")
+    if write_c and c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a_codes.device)
+    if not write_c:
+        c = None
+    if out is None:
+        u8 = dict(dtype=torch.uint8, device=a_codes.device)
+        out = (torch.empty((M, N // 2), **u8), torch.empty((M, N // 32), **u8))
+    _check(lib().fp4q_gemm_quant(M, N, K, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
+                                 _ptr(b_scales), _ptr(c), c.stride(0) if c is not None else N,
+                                 _ptr(out[0]), _ptr(out[1]), _stream(stream)))
+    return c, out

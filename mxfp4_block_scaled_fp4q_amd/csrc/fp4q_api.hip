@@ -268,6 +268,30 @@ fp4q_status_t fp4q_gemm_dge(int64_t M, int64_t N, int64_t K, const uint8_t* a_co
                       "gemm_dge launch");
 }
 
+fp4q_status_t fp4q_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                              const uint8_t* a_scales, const uint8_t* b_codes,
+                              const uint8_t* b_scales, void* c, int64_t ld_c, uint8_t* y_codes,
+                              uint8_t* y_scales, void* stream) {
+    if (!a_codes || !a_scales || !b_codes || !b_scales || !y_codes || !y_scales)
+        return fail(FP4Q_ERR_INVALID, "gemm_quant: null pointer");
+    if (M <= 0 || N <= 0 || K <= 0) return fail(FP4Q_ERR_INVALID, "gemm_quant: bad sizes");
+    if (K % 128) return fail(FP4Q_ERR_INVALID, "gemm_quant: K %% 128 != 0");
+    if (N % 32) return fail(FP4Q_ERR_INVALID, "gemm_quant: N %% 32 != 0 (ROW blocks of C)");
+    if (c && ld_c < N) return fail(FP4Q_ERR_INVALID, "gemm_quant: ld_c < N");
+    if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
+        return fail(FP4Q_ERR_INVALID, "gemm_quant: dimension too large");
+    if (K >= ((int64_t)1 << 24))
+        return fail(FP4Q_ERR_UNSUPPORTED, "gemm_quant: K must be below 2^24");
+    if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(b_codes) ||
+        !aligned16(b_scales) || !aligned16(y_codes) || ((uintptr_t)c % 2))
+        return fail(FP4Q_ERR_ALIGNMENT,
+                    "gemm_quant: operands and codes 16-byte aligned, C element-aligned");
+    return hip_status(fp4q::launch_gemm_fp4_quant(M, N, K, a_codes, a_scales, b_codes, b_scales,
+                                                  (uint16_t*)c, ld_c, y_codes, y_scales,
+                                                  (hipStream_t)stream),
+                      "gemm_quant launch");
+}
+
 fp4q_status_t fp4q_gemm_hcp(int64_t M, int64_t N, int64_t K, const void* x,
                             const uint8_t* xq_codes, const uint8_t* xq_scales, const void* w,
                             const uint8_t* wq_codes, const uint8_t* wq_scales,

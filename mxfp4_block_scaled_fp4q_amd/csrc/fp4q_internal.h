@@ -62,6 +62,12 @@ hipError_t launch_gemm_fp4_dge(int64_t M, int64_t N, int64_t K, const uint8_t* a
                                const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
                                const uint16_t* x, float k, float clamp_max, float* c,
                                int64_t ldc, hipStream_t s);
+// C[M,N] = A B^T rounded to bf16 (stored if c is not null) and that bf16 C
+// quantised with ROW blocks of 32, nearest-even, into qc, qs (N % 32 == 0).
+hipError_t launch_gemm_fp4_quant(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
+                                 const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                                 uint16_t* c, int64_t ldc, uint8_t* qc, uint8_t* qs,
+                                 hipStream_t s);
 size_t hcp_workspace_bytes(int64_t M, int64_t N, int32_t n_hot);
 hipError_t launch_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
                       const uint8_t* xqs, const void* w, const uint8_t* wqc, const uint8_t* wqs,

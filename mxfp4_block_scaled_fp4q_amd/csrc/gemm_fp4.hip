@@ -420,17 +420,23 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[Layout<CFG>::TM][Layout<C
 // epilogue by the DGE derivative of ex [M, N] (bf16, dense) with ex's column
 // blocks of 32 rows -- the weight gradient's estimator applied where the
 // weight gradient is produced.
+// EPI = 2 (bf16 C, 256 x 256 tiles, N % 32 == 0): the bf16 C is also
+// quantised (ROW blocks of 32, nearest-even) into qc [M, N/2] and qs
+// [M, N/32], as fp4q_quantize would from the stored C; cptr may be null.
 template <int CFG, int OUT_BF16, int ACCUM, int OPS, int EPI = 0>
 __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
     int M, int N, int K, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, void* __restrict__ cptr,
     int64_t ldc, int tiles_m, int tiles_n, const uint8_t* __restrict__ ha,
-    const uint8_t* __restrict__ hb, int kp, const uint16_t* __restrict__ ex, DgeParams dp) {
+    const uint8_t* __restrict__ hb, int kp, const uint16_t* __restrict__ ex, DgeParams dp,
+    uint8_t* __restrict__ qc, uint8_t* __restrict__ qs) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot instantiate buffer resources
     using L = Layout<CFG>;
     constexpr int TM = L::TM, TN = L::TN;
-    static_assert(!EPI || (CFG == 0 && !OUT_BF16 && !ACCUM && OPS == 0),
+    static_assert(EPI != 1 || (CFG == 0 && !OUT_BF16 && !ACCUM && OPS == 0),
                   "the DGE epilogue is for fp32 C on 256 x 256 tiles");
+    static_assert(EPI != 2 || (CFG == 0 && OUT_BF16 && !ACCUM && OPS == 0),
+                  "the quantising epilogue is for bf16 C on 256 x 256 tiles");
 
     // ---- tile index: XCD-contiguous, then grouped along M ----
     const int nwg = gridDim.x;
@@ -533,10 +539,10 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
         // DGE epilogue: these 32 rows are one column block of ex.  Each lane
         // reads ex at the 4 columns and PASSES rows it writes; lanes 16 apart
         // share columns, so two exchanges give each column's block maximum.
-        uint2 xw[EPI ? PASSES : 1];
+        uint2 xw[EPI == 1 ? PASSES : 1];
         float inv4[4];
         bool nf4[4];
-        if (EPI) {
+        if (EPI == 1) {
             const int cx = col0 + (lane % LANES_PER_ROW) * CHUNK_ELEMS;
             const bool xvec = (N % 4) == 0 && cx + 4 <= N;
             uint32_t m4[4] = {0u, 0u, 0u, 0u};
@@ -576,7 +582,7 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
             // 96-column waves: lanes past the last whole row, and rows past 32
             if (lane >= ROWS_PER_PASS * LANES_PER_ROW || rl >= 32) continue;
             u32x4 v = *(const u32x4*)(reg + rl * PITCH + ce * ESZ);
-            if (EPI) {
+            if (EPI == 1) {
                 // the gradient estimator's product, as fp4q_grad_estimate forms it
                 const float xf[4] = {bf16_lo(xw[p].x), bf16_hi(xw[p].x), bf16_lo(xw[p].y),
                                      bf16_hi(xw[p].y)};
@@ -589,6 +595,40 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
             const int row = rbase + rl;
             const int col = col0 + ce;
             if (row >= M) continue;
+            if (EPI == 2) {
+                // 8 bf16 of one row; 4 adjacent lanes hold a 32-column block
+                // (the ROW quantiser's steps: bit amax, E8M0 byte, scaled
+                // nearest-even converts; a non-finite block: 0xFF and zero codes)
+                const u16x2_t m0 = __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu);
+                const u16x2_t m1 = __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu);
+                const u16x2_t m2 = __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu);
+                const u16x2_t m3 = __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu);
+                const u16x2_t mm = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1),
+                                                             __builtin_elementwise_max(m2, m3));
+                const uint32_t amax = group_max_u32<4>(((uint32_t)max(mm.x, mm.y)) << 16);
+                const bool nonfinite = amax >= 0x7F800000u;
+                const uint32_t byte = nonfinite ? 0xFFu : e8m0_from_amax(amax);
+                const float sc = e8m0_scale_f32(byte);
+                // the words go through scalars: this compiler, given a
+                // bit-cast of a vector element straight into the convert
+                // builtin, feeds element 0 to all four converts
+                const uint32_t w0 = v.x, w1 = v.y, w2 = v.z, w3 = v.w;
+                uint32_t packed = 0;
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                    packed, __builtin_bit_cast(bf16x2_t, w0), sc, 0);
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                    packed, __builtin_bit_cast(bf16x2_t, w1), sc, 1);
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                    packed, __builtin_bit_cast(bf16x2_t, w2), sc, 2);
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                    packed, __builtin_bit_cast(bf16x2_t, w3), sc, 3);
+                if (nonfinite) packed = 0;
+                if (col < N) {
+                    *(uint32_t*)(qc + (int64_t)row * (N / 2) + col / 2) = packed;
+                    if ((lane & 3) == 0) qs[(int64_t)row * (N / 32) + col / 32] = (uint8_t)byte;
+                }
+                if (!cptr) continue;
+            }
             const int64_t off = (int64_t)row * ldc + col;
             if (vec_ok && col + CHUNK_ELEMS <= N) {
                 // C is written once and not read again by this kernel:
@@ -669,14 +709,15 @@ template <int CFG, int OUT_BF16, int ACCUM, int OPS, int EPI = 0>
 static void launch_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                        const uint8_t* b, const uint8_t* bs, void* c, int64_t ldc, hipStream_t s,
                        const uint8_t* ha, const uint8_t* hb, int64_t kp,
-                       const uint16_t* ex = nullptr, DgeParams dp = DgeParams{}) {
+                       const uint16_t* ex = nullptr, DgeParams dp = DgeParams{},
+                       uint8_t* qc = nullptr, uint8_t* qs = nullptr) {
     using L = Layout<CFG>;
     const int tiles_m = (int)((M + L::BM - 1) / L::BM);
     const int tiles_n = (int)((N + L::BN - 1) / L::BN);
     gemm_fp4_kernel<CFG, OUT_BF16, ACCUM, OPS, EPI>
         <<<dim3((unsigned)(tiles_m * tiles_n)), L::THREADS, 0, s>>>(
             (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m, tiles_n, ha, hb, (int)kp, ex,
-            dp);
+            dp, qc, qs);
 }
 
 template <int OUT_BF16, int ACCUM, int OPS>
@@ -728,6 +769,15 @@ hipError_t launch_gemm_fp4_dge(int64_t M, int64_t N, int64_t K, const uint8_t* a
     P.clamp_max = clamp_max;
     P.k_one = (k == 1.0f);
     launch_cfg<0, 0, 0, 0, 1>(M, N, K, ac, as, bc, bs, c, ldc, s, nullptr, nullptr, 0, x, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp4_quant(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
+                                 const uint8_t* as, const uint8_t* bc, const uint8_t* bs,
+                                 uint16_t* c, int64_t ldc, uint8_t* qc, uint8_t* qs,
+                                 hipStream_t s) {
+    launch_cfg<0, 1, 0, 0, 2>(M, N, K, ac, as, bc, bs, c, ldc, s, nullptr, nullptr, 0, nullptr,
+                              DgeParams{}, qc, qs);
     return hipGetLastError();
 }
 

@@ -248,3 +248,29 @@ def test_gemm_dge_validation(L):
     bad = list(args)
     bad[2] = 1 << 24
     assert h(*bad) == 2
+
+
+def test_gemm_quant_validation(L):
+    h = L.fp4q_gemm_quant
+    args = [256, 64, 256, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, NUL]
+    bad = list(args)
+    bad[1] = 48          # N % 32 (ROW blocks of C)
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[2] = 192         # K % 128
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[8] = 63          # ld_c < N
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[9] = NUL         # codes
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[9] = FAKE_MIS    # codes alignment
+    assert h(*bad) == 3
+    bad = list(args)
+    bad[7] = ct.c_void_p(0x10001)   # C not element-aligned
+    assert h(*bad) == 3
+    bad = list(args)
+    bad[2] = 1 << 24
+    assert h(*bad) == 2

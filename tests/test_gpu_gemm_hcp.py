@@ -90,6 +90,34 @@ def test_gemm_tiles_bit_identical(M, N, K, monkeypatch):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{M}x{N}x{K} {dt}"
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 32, 128), (300, 288, 256), (513, 1056, 384),
+                                   (8192, 5632, 2048)])
+def test_gemm_quant_epilogue(orc, M, N, K):
+    """fp4q_gemm_quant: C (bf16) and its ROW block-32 RNE quantisation in one
+    kernel, bit for bit equal to fp4q_gemm then fp4q_quantize (which the
+    oracle pins elsewhere), with and without the C store, including a row of
+    A whose scale byte is 0xFF (a NaN row of C: scale 0xFF, codes 0)."""
+    a = inputs.normal((M, K), M + 11)
+    b = inputs.normal((N, K), N + 13)
+    A, B = qpair(orc, a, b) if M * K <= 1 << 22 else (None, None)
+    if A is None:
+        A = fq.quantize(torch.from_numpy(a).cuda(), 32)
+        B = fq.quantize(torch.from_numpy(b).cuda(), 32)
+        ac, as_, bc, bs = A[0], A[1].clone(), B[0], B[1]
+    else:
+        ac, as_, bc, bs = dev(A[0]), dev(A[1].copy()), dev(B[0]), dev(B[1])
+    as_[M // 2, 1] = 0xFF
+    c, (qc, qs) = fq.gemm_quant(ac, as_, bc, bs)
+    _, (qc2, qs2) = fq.gemm_quant(ac, as_, bc, bs, write_c=False)
+    c_ref = fq.gemm(ac, as_, bc, bs, out_dtype=torch.bfloat16)
+    qc_ref, qs_ref = fq.quantize(c_ref, 32, fq.ROW)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), c_ref.view(torch.int16))
+    for got_c, got_s in ((qc, qs), (qc2, qs2)):
+        assert torch.equal(got_c, qc_ref) and torch.equal(got_s, qs_ref)
+    assert (qs_ref[M // 2] == 0xFF).all() and (qc_ref[M // 2] == 0).all()
+
+
 def test_gemm_nan_scale_and_zero(orc):
     a = inputs.normal((64, 256), 1)
     b = inputs.normal((64, 256), 2)
