@@ -368,6 +368,9 @@ def bench_outlier_layer(torch, fq, inputs, dev):
     wq = fq.quantize(W, 32, fq.COL)
     Y = torch.empty((M, N), dtype=torch.float32, device=dev)
     Y2 = torch.empty((M, N), dtype=torch.float32, device=dev)
+    hmask = torch.empty(((K + 31) // 32,), dtype=torch.int32, device=dev)
+    xs = (torch.empty_like(xq[0]), torch.empty_like(xq[1]))
+    wsq = (torch.empty_like(wq[0]), torch.empty_like(wq[1]))
     ws = torch.empty(fq.hcp_workspace_bytes(M, N, hot.numel()), dtype=torch.uint8, device=dev)
     res = {}
     for name, fn in (("quant_x_row", lambda: fq.quantize(X, 32, fq.ROW, codes=xq[0], scales=xq[1])),
@@ -376,7 +379,13 @@ def bench_outlier_layer(torch, fq, inputs, dev):
                      ("hcp_residual", lambda: fq.hcp_residual_add(X, xq[0], xq[1], W, wq[0], wq[1],
                                                                   hot, Y, ws)),
                      ("gemm_hcp_single", lambda: fq.gemm_hcp(X, xq[0], xq[1], W, wq[0], wq[1], hot,
-                                                             y=Y2, workspace=ws))):
+                                                             y=Y2, workspace=ws)),
+                     ("hcp_split_masks_quant", lambda: (
+                         fq.channel_mask(hot, K, out=hmask),
+                         fq.quantize_masked(X, hmask, 32, fq.ROW, codes=xs[0], scales=xs[1]),
+                         fq.quantize_masked(W, hmask, 32, fq.COL, codes=wsq[0], scales=wsq[1]))),
+                     ("gemm_hcp_split", lambda: fq.gemm_hcp_split(X, xs[0], xs[1], W, wsq[0], wsq[1],
+                                                                 hot, y=Y2, workspace=ws))):
         fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)

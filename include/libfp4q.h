@@ -113,6 +113,30 @@ fp4q_status_t fp4q_quantize_dual(const void* x, fp4q_dtype_t x_dtype, int64_t ro
                                  uint8_t* col_codes, uint8_t* col_scales, void* stream);
 
 /*
+ * fp4q_channel_mask -- builds a zero mask for fp4q_quantize_masked: bit i of
+ *   mask (word i / 32, bit i % 32) is set for every i in idx[0 .. n) with
+ *   0 <= i < length; all other bits of the ceil(length / 32) words are
+ *   cleared.  Out-of-range indices are ignored (device data is not checked).
+ *   idx int32 [n] device (may be NULL if n = 0); mask uint32 device, written.
+ */
+fp4q_status_t fp4q_channel_mask(const int32_t* idx, int32_t n, int64_t length, uint32_t* mask,
+                                void* stream);
+
+/*
+ * fp4q_quantize_masked -- fp4q_quantize of x with the positions along the
+ * block axis whose zero_mask bit is set taken as zeros (ROW: columns, COL:
+ * rows; e.g. the hot channels of the outlier-dynamics page's hot-channel
+ * compensation, sec. 3.1, removed from the quantised product before it is
+ * formed).  Arguments and errors as fp4q_quantize, plus zero_mask: uint32
+ * device bit mask over that axis (fp4q_channel_mask writes one).
+ */
+fp4q_status_t fp4q_quantize_masked(const void* x, fp4q_dtype_t x_dtype, int64_t rows,
+                                   int64_t cols, int64_t ld_x, int32_t block, fp4q_axis_t axis,
+                                   fp4q_round_t round, uint64_t seed, uint64_t rng_offset,
+                                   const uint32_t* zero_mask, uint8_t* codes, uint8_t* scales,
+                                   void* stream);
+
+/*
  * fp4q_dequantize -- the QDQ partner (MXFP4 tutorial page, sec. 6.1): element
  * value(code) * 2^(byte-127), exact in fp32 and bf16 (results beyond the fp32
  * range become Inf; byte 0xFF gives NaN for the whole block).
@@ -255,6 +279,23 @@ fp4q_status_t fp4q_gemm_hcp(int64_t M, int64_t N, int64_t K, const void* x,
                             const uint8_t* wq_codes, const uint8_t* wq_scales,
                             const int32_t* hot_idx, int32_t n_hot, float* y, int64_t ld_y,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp4q_gemm_hcp_split -- hot-channel compensation, the "split" reading of
+ * the outlier-dynamics page, sec. 3.1-3.2: the hot channels H are removed
+ * from the quantised product (xq and wq come from fp4q_quantize_masked with
+ * H zeroed: X's columns, W's rows) and their bf16 product is added:
+ *   Y[i,j] = sum_k Xq'[i,k] Wq'[k,j] + sum_{c in H} X[i,c] W[c,j]
+ * in one GEMM kernel (FP4 K loop, then a bf16 K loop of depth |H| padded to
+ * 32).  Arguments and limits as fp4q_gemm_hcp; y fp32 [M, N] (row stride
+ * ld_y) is written.
+ */
+fp4q_status_t fp4q_gemm_hcp_split(int64_t M, int64_t N, int64_t K, const void* x,
+                                  const uint8_t* xq_codes, const uint8_t* xq_scales,
+                                  const void* w, const uint8_t* wq_codes,
+                                  const uint8_t* wq_scales, const int32_t* hot_idx,
+                                  int32_t n_hot, float* y, int64_t ld_y, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 const char* fp4q_status_string(fp4q_status_t s);
 const char* fp4q_last_error(void);

@@ -20,7 +20,8 @@ STE, DGE = 0, 1
 STATUS = {0: "FP4Q_OK", 1: "FP4Q_ERR_INVALID", 2: "FP4Q_ERR_UNSUPPORTED",
           3: "FP4Q_ERR_ALIGNMENT", 4: "FP4Q_ERR_WORKSPACE", 5: "FP4Q_ERR_HIP"}
 
-EXPORTS = ["fp4q_quantize", "fp4q_quantize_dual", "fp4q_dequantize", "fp4q_grad_estimate",
+EXPORTS = ["fp4q_channel_mask", "fp4q_quantize_masked", "fp4q_gemm_hcp_split",
+           "fp4q_quantize", "fp4q_quantize_dual", "fp4q_dequantize", "fp4q_grad_estimate",
            "fp4q_gemm",
            "fp4q_gemm_dge", "fp4q_gemm_quant", "fp4q_hcp_workspace_bytes",
            "fp4q_hcp_residual_add",
@@ -61,6 +62,11 @@ def lib():
                                             P]),
             "fp4q_gemm_dge": (I32, [I64, I64, I64, P, P, P, P, P, I32, F, F, P, I64, P]),
             "fp4q_gemm_quant": (I32, [I64, I64, I64, P, P, P, P, P, I64, P, P, P]),
+            "fp4q_channel_mask": (I32, [P, I32, I64, P, P]),
+            "fp4q_quantize_masked": (I32, [P, I32, I64, I64, I64, I32, I32, I32, U64, U64, P, P,
+                                           P, P]),
+            "fp4q_gemm_hcp_split": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, I64, P, SZ,
+                                          P]),
             "fp4q_gemm_hcp": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, I64, P, SZ, P]),
             "fp4q_status_string": (_ct.c_char_p, [I32]),
             "fp4q_last_error": (_ct.c_char_p, []),
@@ -279,3 +285,53 @@ def gemm_quant(a_codes, a_scales, b_codes, b_scales, c=None, write_c=True, out=N
                                  _ptr(b_scales), _ptr(c), c.stride(0) if c is not None else N,
                                  _ptr(out[0]), _ptr(out[1]), _stream(stream)))
     return c, out
+
+
+def channel_mask(idx, length, out=None, stream=None):
+    """uint32 bit mask over `length` positions with the bits of idx set
+    (fp4q_channel_mask); returns the mask tensor."""
+    torch = _torch()
+    _need_cuda(idx)
+    if out is None:
+        out = torch.empty(((length + 31) // 32,), dtype=torch.int32, device=idx.device)
+    _check(lib().fp4q_channel_mask(_ptr(idx), idx.numel(), length, _ptr(out), _stream(stream)))
+    return out
+
+
+def quantize_masked(x, zero_mask, block=32, axis=ROW, rounding=RNE, seed=0, rng_offset=0,
+                    codes=None, scales=None, stream=None):
+    """fp4q_quantize of x with the zero_mask positions along the block axis
+    taken as zeros (fp4q_quantize_masked); returns (codes, scales)."""
+    torch = _torch()
+    _need_cuda(x, zero_mask)
+    R, C = x.shape
+    if codes is None:
+        shape_c = (R, C // 2) if axis == ROW else (C, R // 2)
+        shape_s = (R, C // block) if axis == ROW else (C, R // block)
+        codes = torch.empty(shape_c, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(shape_s, dtype=torch.uint8, device=x.device)
+    _check(lib().fp4q_quantize_masked(_ptr(x), _dt(x), R, C, x.stride(0), block, axis, rounding,
+                                      seed, rng_offset, _ptr(zero_mask), _ptr(codes),
+                                      _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def gemm_hcp_split(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, y=None,
+                   workspace=None, stream=None):
+    """Y[M,N] (fp32) = Xq' Wq' + X[:, hot] W[hot, :] in one kernel
+    (fp4q_gemm_hcp_split; xq, wq quantised with the hot channels zeroed)."""
+    torch = _torch()
+    _need_cuda(x, w, hot_idx)
+    M, K = x.shape
+    N = w.shape[1]
+    n_hot = hot_idx.numel()
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    need = hcp_workspace_bytes(M, N, n_hot)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().fp4q_gemm_hcp_split(M, N, K, _ptr(x), _ptr(xq_codes), _ptr(xq_scales), _ptr(w),
+                                     _ptr(wq_codes), _ptr(wq_scales), _ptr(hot_idx), n_hot,
+                                     _ptr(y), y.stride(0), _ptr(workspace), workspace.numel(),
+                                     _stream(stream)))
+    return y

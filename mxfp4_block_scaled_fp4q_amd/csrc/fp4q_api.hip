@@ -87,6 +87,53 @@ fp4q_status_t fp4q_quantize(const void* x, fp4q_dtype_t x_dtype, int64_t rows, i
     return hip_status(e, "quantize launch");
 }
 
+fp4q_status_t fp4q_channel_mask(const int32_t* idx, int32_t n, int64_t length, uint32_t* mask,
+                                void* stream) {
+    if (!mask || (n > 0 && !idx)) return fail(FP4Q_ERR_INVALID, "channel_mask: null pointer");
+    if (n < 0 || length <= 0 || length >= ((int64_t)1 << 40))
+        return fail(FP4Q_ERR_INVALID, "channel_mask: bad sizes");
+    if (((uintptr_t)mask % 4) || (idx && ((uintptr_t)idx % 4)))
+        return fail(FP4Q_ERR_ALIGNMENT, "channel_mask: pointers must be 4-byte aligned");
+    return hip_status(fp4q::launch_channel_mask(idx, n, length, mask, (hipStream_t)stream),
+                      "channel_mask launch");
+}
+
+fp4q_status_t fp4q_quantize_masked(const void* x, fp4q_dtype_t x_dtype, int64_t rows,
+                                   int64_t cols, int64_t ld_x, int32_t block, fp4q_axis_t axis,
+                                   fp4q_round_t round, uint64_t seed, uint64_t rng_offset,
+                                   const uint32_t* zero_mask, uint8_t* codes, uint8_t* scales,
+                                   void* stream) {
+    if (!zero_mask) return fail(FP4Q_ERR_INVALID, "quantize_masked: null zero_mask");
+    if ((uintptr_t)zero_mask % 4)
+        return fail(FP4Q_ERR_ALIGNMENT, "quantize_masked: zero_mask must be 4-byte aligned");
+    if (!x || !codes || !scales) return fail(FP4Q_ERR_INVALID, "quantize_masked: null pointer");
+    if (!valid_dtype(x_dtype)) return fail(FP4Q_ERR_INVALID, "quantize_masked: bad x dtype");
+    if (rows <= 0 || cols <= 0) return fail(FP4Q_ERR_INVALID, "quantize_masked: bad sizes");
+    if (ld_x < cols) return fail(FP4Q_ERR_INVALID, "quantize_masked: ld_x < cols");
+    if (!valid_block(block)) return fail(FP4Q_ERR_INVALID, "quantize_masked: block %d", block);
+    if (axis != FP4Q_BLOCK_ROW && axis != FP4Q_BLOCK_COL)
+        return fail(FP4Q_ERR_INVALID, "quantize_masked: bad axis");
+    if (round != FP4Q_RNE && round != FP4Q_SR)
+        return fail(FP4Q_ERR_INVALID, "quantize_masked: bad round");
+    if (axis == FP4Q_BLOCK_ROW && cols % block)
+        return fail(FP4Q_ERR_INVALID, "quantize_masked: cols %% block != 0 for ROW blocks");
+    if (axis == FP4Q_BLOCK_COL && rows % block)
+        return fail(FP4Q_ERR_INVALID, "quantize_masked: rows %% block != 0 for COL blocks");
+    if (rows > kMaxElems / ld_x) return fail(FP4Q_ERR_INVALID, "quantize_masked: tensor too large");
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) ||
+        (ld_x * esize(x_dtype)) % 16)
+        return fail(FP4Q_ERR_ALIGNMENT,
+                    "quantize_masked: pointers and row stride must be 16-byte aligned");
+    hipError_t e;
+    if (axis == FP4Q_BLOCK_ROW)
+        e = fp4q::launch_quantize_row(x, x_dtype, rows, cols, ld_x, block, round == FP4Q_SR, seed,
+                                      rng_offset, codes, scales, (hipStream_t)stream, zero_mask);
+    else
+        e = fp4q::launch_quantize_col(x, x_dtype, rows, cols, ld_x, block, round == FP4Q_SR, seed,
+                                      rng_offset, codes, scales, (hipStream_t)stream, zero_mask);
+    return hip_status(e, "quantize_masked launch");
+}
+
 fp4q_status_t fp4q_quantize_dual(const void* x, fp4q_dtype_t x_dtype, int64_t rows, int64_t cols,
                                  int64_t ld_x, int32_t block, fp4q_round_t round_row,
                                  uint64_t seed_row, fp4q_round_t round_col, uint64_t seed_col,
@@ -290,6 +337,44 @@ fp4q_status_t fp4q_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_t* a_
                                                   (uint16_t*)c, ld_c, y_codes, y_scales,
                                                   (hipStream_t)stream),
                       "gemm_quant launch");
+}
+
+fp4q_status_t fp4q_gemm_hcp_split(int64_t M, int64_t N, int64_t K, const void* x,
+                                  const uint8_t* xq_codes, const uint8_t* xq_scales,
+                                  const void* w, const uint8_t* wq_codes,
+                                  const uint8_t* wq_scales, const int32_t* hot_idx,
+                                  int32_t n_hot, float* y, int64_t ld_y, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    if (M <= 0 || N <= 0 || K <= 0 || n_hot < 0)
+        return fail(FP4Q_ERR_INVALID, "gemm_hcp_split: bad sizes");
+    if (!xq_codes || !xq_scales || !wq_codes || !wq_scales || !y)
+        return fail(FP4Q_ERR_INVALID, "gemm_hcp_split: null pointer");
+    if (K % 128) return fail(FP4Q_ERR_INVALID, "gemm_hcp_split: K %% 128 != 0");
+    if (ld_y < N) return fail(FP4Q_ERR_INVALID, "gemm_hcp_split: ld_y < N");
+    if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
+        return fail(FP4Q_ERR_INVALID, "gemm_hcp_split: dimension too large");
+    if (K >= ((int64_t)1 << 24))
+        return fail(FP4Q_ERR_UNSUPPORTED, "gemm_hcp_split: K must be below 2^24");
+    if (n_hot > K) return fail(FP4Q_ERR_INVALID, "gemm_hcp_split: n_hot > K");
+    if (n_hot > (1 << 20)) return fail(FP4Q_ERR_UNSUPPORTED, "gemm_hcp_split: n_hot above 2^20");
+    if (!aligned16(xq_codes) || !aligned16(xq_scales) || !aligned16(wq_codes) ||
+        !aligned16(wq_scales) || ((uintptr_t)y % 4))
+        return fail(FP4Q_ERR_ALIGNMENT,
+                    "gemm_hcp_split: operand pointers must be 16-byte aligned, y 4-byte aligned");
+    if (n_hot > 0) {
+        if (!x || !w || !hot_idx || !workspace)
+            return fail(FP4Q_ERR_INVALID, "gemm_hcp_split: null pointer");
+        if (!aligned16(x) || !aligned16(w) || !aligned16(hot_idx) || !aligned16(workspace))
+            return fail(FP4Q_ERR_ALIGNMENT, "gemm_hcp_split: pointers must be 16-byte aligned");
+        const size_t need = fp4q::hcp_workspace_bytes(M, N, n_hot);
+        if (workspace_bytes < need)
+            return fail(FP4Q_ERR_WORKSPACE, "gemm_hcp_split: workspace %zu < %zu bytes",
+                        workspace_bytes, need);
+    }
+    return hip_status(fp4q::launch_gemm_hcp_split(M, N, K, x, xq_codes, xq_scales, w, wq_codes,
+                                                  wq_scales, hot_idx, n_hot, y, ld_y, workspace,
+                                                  (hipStream_t)stream),
+                      "gemm_hcp_split launch");
 }
 
 fp4q_status_t fp4q_gemm_hcp(int64_t M, int64_t N, int64_t K, const void* x,

@@ -27,12 +27,17 @@ __device__ __forceinline__ uint32_t fastdiv(uint32_t n, FastDiv f) {
 
 enum DType { F32 = 0, BF16 = 1 };
 
+// zmask (optional): one bit per position along the block axis (ROW: columns,
+// COL: rows); set positions are quantised as zeros.
 hipError_t launch_quantize_row(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                                int block, bool sr, uint64_t seed, uint64_t off, uint8_t* codes,
-                               uint8_t* scales, hipStream_t s);
+                               uint8_t* scales, hipStream_t s, const uint32_t* zmask = nullptr);
 hipError_t launch_quantize_col(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                                int block, bool sr, uint64_t seed, uint64_t off, uint8_t* codes,
-                               uint8_t* scales, hipStream_t s);
+                               uint8_t* scales, hipStream_t s, const uint32_t* zmask = nullptr);
+// mask[0 .. ceil(length/32)) = bit i set for every i in idx[0 .. n) (0 <= i < length).
+hipError_t launch_channel_mask(const int32_t* idx, int32_t n, int64_t length, uint32_t* mask,
+                               hipStream_t s);
 hipError_t launch_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ld, int block,
                                 bool sr_row, uint64_t seed_row, bool sr_col, uint64_t seed_col,
                                 uint64_t off, uint8_t* codes_r, uint8_t* scales_r,
@@ -69,6 +74,11 @@ hipError_t launch_gemm_fp4_quant(int64_t M, int64_t N, int64_t K, const uint8_t*
                                  uint16_t* c, int64_t ldc, uint8_t* qc, uint8_t* qs,
                                  hipStream_t s);
 size_t hcp_workspace_bytes(int64_t M, int64_t N, int32_t n_hot);
+// Split reading: Y = Xq' Wq' + X_H W_H (Xq', Wq' quantised with H zeroed).
+hipError_t launch_gemm_hcp_split(int64_t M, int64_t N, int64_t K, const void* x,
+                                 const uint8_t* xqc, const uint8_t* xqs, const void* w,
+                                 const uint8_t* wqc, const uint8_t* wqs, const int32_t* hot,
+                                 int32_t n_hot, float* y, int64_t ldy, void* ws, hipStream_t s);
 hipError_t launch_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
                       const uint8_t* xqs, const void* w, const uint8_t* wqc, const uint8_t* wqs,
                       const int32_t* hot, int32_t n_hot, float* y, void* ws, hipStream_t s);

@@ -24,6 +24,12 @@
 // same fp32 accumulators, so Y = Xq Wq + residual is written once and the
 // fp32 read-modify-write of Y disappears.
 //
+// Split reading (the alternative the outlier-dynamics page's wording
+// allows): the hot channels are taken out of the quantised product -- X's
+// hot columns and W's hot rows are zeroed before quantisation (the
+// quantisers' zero mask) -- and added back in bf16:
+//   Y = Xq' Wq' + X_H W_H,  one kernel, K' = |H| padded to 32.
+//
 // Kernels:
 //  * hcp_gather_x: one lane = 8 consecutive K' slots of one row of A'.
 //  * hcp_gather_w: one lane = one column j and 8 consecutive K' slots; lanes
@@ -55,6 +61,8 @@ __device__ __forceinline__ float deq_nibble(const uint8_t* codes_row, const uint
 static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 static int64_t padded_k(int32_t n_hot) { return (int64_t)round_up((size_t)(2 * n_hot), 32); }
+// split reading: the hot channels alone, unpaired with their quantised copies
+static int64_t padded_k_split(int32_t n_hot) { return (int64_t)round_up((size_t)n_hot, 32); }
 
 size_t hcp_workspace_bytes(int64_t M, int64_t N, int32_t n_hot) {
     if (n_hot <= 0) return 0;
@@ -67,7 +75,8 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_x(const uint16_t* __restr
                                                          const uint8_t* __restrict__ xqs,
                                                          const int32_t* __restrict__ hot,
                                                          int n_hot, int64_t M, int64_t K,
-                                                         int64_t kp, uint16_t* __restrict__ a) {
+                                                         int64_t kp, uint16_t* __restrict__ a,
+                                                         int with_q) {
     const int64_t chunks_per_row = kp / 8;
     const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (t >= M * chunks_per_row) return;
@@ -80,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_x(const uint16_t* __restr
         uint32_t bits = 0;
         if (h < n_hot) {
             bits = x[i * K + hot[h]];
-        } else if (h < 2 * n_hot) {
+        } else if (with_q && h < 2 * n_hot) {
             const int c = hot[h - n_hot];
             bits = f32_to_bf16_bits(deq_nibble(xqc + i * (K / 2), xqs + i * (K / 32), c));
         }
@@ -99,7 +108,8 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_w(const uint16_t* __restr
                                                          const uint8_t* __restrict__ wqs,
                                                          const int32_t* __restrict__ hot,
                                                          int n_hot, int64_t N, int64_t K,
-                                                         int64_t kp, uint16_t* __restrict__ b) {
+                                                         int64_t kp, uint16_t* __restrict__ b,
+                                                         int with_q) {
     const int64_t j = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
     const int64_t hc = (int64_t)blockIdx.y * (kThreads / 64) + (threadIdx.x >> 6);
     if (j >= N || hc >= kp / 8) return;
@@ -111,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_w(const uint16_t* __restr
         uint32_t bits = 0;
         if (h < n_hot) {
             bits = w[(int64_t)hot[h] * N + j];
-        } else if (h < 2 * n_hot) {
+        } else if (with_q && h < 2 * n_hot) {
             const int c = hot[h - n_hot];
             bits = f32_to_bf16_bits(-deq_nibble(wqc + j * (K / 2), wqs + j * (K / 32), c));
         }
@@ -125,24 +135,26 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_w(const uint16_t* __restr
     *(uint4*)(b + j * kp + h0) = o;
 }
 
-// Gathers the hot operands into the workspace: A' [M, kp] then B' [N, kp].
+// Gathers the hot operands into the workspace: A' [M, kp] then B' [N, kp]
+// (with_q: [X_H | Xq_H], [W_H ; -Wq_H]; else X_H, W_H alone).
 static hipError_t gather_hot(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
                              const uint8_t* xqs, const void* w, const uint8_t* wqc,
                              const uint8_t* wqs, const int32_t* hot, int32_t n_hot, void* ws,
-                             hipStream_t s, uint16_t** ap_out, uint16_t** bp_out) {
-    const int64_t kp = padded_k(n_hot);
+                             hipStream_t s, uint16_t** ap_out, uint16_t** bp_out,
+                             int with_q = 1) {
+    const int64_t kp = with_q ? padded_k(n_hot) : padded_k_split(n_hot);
     uint16_t* ap = (uint16_t*)ws;
     uint16_t* bp = (uint16_t*)((uint8_t*)ws + round_up((size_t)(M * kp * 2), 256));
     {
         const int64_t total = M * (kp / 8);
         dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
         hcp_gather_x<<<grid, kThreads, 0, s>>>((const uint16_t*)x, xqc, xqs, hot, n_hot, M, K, kp,
-                                               ap);
+                                               ap, with_q);
     }
     {
         dim3 grid((unsigned)((N + 63) / 64), (unsigned)((kp / 8 + 3) / 4));
         hcp_gather_w<<<grid, kThreads, 0, s>>>((const uint16_t*)w, wqc, wqs, hot, n_hot, N, K, kp,
-                                               bp);
+                                               bp, with_q);
     }
     *ap_out = ap;
     *bp_out = bp;
@@ -168,6 +180,19 @@ hipError_t launch_gemm_hcp(int64_t M, int64_t N, int64_t K, const void* x, const
     hipError_t e = gather_hot(M, N, K, x, xqc, xqs, w, wqc, wqs, hot, n_hot, ws, s, &ap, &bp);
     if (e != hipSuccess) return e;
     return launch_gemm_fp4_hot(M, N, K, xqc, xqs, wqc, wqs, ap, bp, padded_k(n_hot), y, ldy, s);
+}
+
+hipError_t launch_gemm_hcp_split(int64_t M, int64_t N, int64_t K, const void* x,
+                                 const uint8_t* xqc, const uint8_t* xqs, const void* w,
+                                 const uint8_t* wqc, const uint8_t* wqs, const int32_t* hot,
+                                 int32_t n_hot, float* y, int64_t ldy, void* ws, hipStream_t s) {
+    if (n_hot <= 0) return launch_gemm_fp4(M, N, K, xqc, xqs, wqc, wqs, y, F32, ldy, false, s);
+    uint16_t *ap, *bp;
+    hipError_t e =
+        gather_hot(M, N, K, x, xqc, xqs, w, wqc, wqs, hot, n_hot, ws, s, &ap, &bp, /*with_q=*/0);
+    if (e != hipSuccess) return e;
+    return launch_gemm_fp4_hot(M, N, K, xqc, xqs, wqc, wqs, ap, bp, padded_k_split(n_hot), y, ldy,
+                               s);
 }
 
 }  // namespace fp4q

@@ -31,11 +31,12 @@ static constexpr int kThreads = 256;
 // ---------------------------------------------------------------------------
 // ROW
 // ---------------------------------------------------------------------------
+// zmask (optional): one bit per column; set columns are quantised as zeros.
 template <int IN_BF16, int BLOCK, int SR, int UNROLL>
 __global__ __launch_bounds__(kThreads) void quantize_row_kernel(
     const void* __restrict__ xv, uint32_t total_chunks, FastDiv cpr, int64_t ld, int64_t cols,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t k0, uint32_t k1,
-    uint64_t rng_off) {
+    uint64_t rng_off, const uint32_t* __restrict__ zmask) {
     constexpr int G = BLOCK / 8;  // lanes per block
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = (blockIdx.x * (kThreads / 64)) + (threadIdx.x >> 6);
@@ -71,6 +72,18 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(
             w[u][5] = v1.y;
             w[u][6] = v1.z;
             w[u][7] = v1.w;
+        }
+        if (zmask) {
+            // the chunk's 8 columns are bits 8 (cc % 4) .. +7 of word cc / 4
+            const uint32_t mb = (zmask[cc >> 2] >> ((cc & 3) * 8)) & 0xFFu;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (!((mb >> j) & 1u)) continue;
+                if (IN_BF16)
+                    w[u][j >> 1] &= (j & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+                else
+                    w[u][j % (IN_BF16 ? 4 : 8)] = 0u;
+            }
         }
     }
 #pragma unroll
@@ -145,24 +158,25 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(
 template <int IN_BF16, int SR>
 static hipError_t row_dispatch(int block, dim3 grid, hipStream_t s, const void* x, uint32_t tc,
                                FastDiv cpr, int64_t ld, int64_t cols, uint8_t* codes,
-                               uint8_t* scales, uint32_t k0, uint32_t k1, uint64_t off) {
+                               uint8_t* scales, uint32_t k0, uint32_t k1, uint64_t off,
+                               const uint32_t* zmask) {
     constexpr int U = 4;
     switch (block) {
         case 16:
             quantize_row_kernel<IN_BF16, 16, SR, U><<<grid, kThreads, 0, s>>>(
-                x, tc, cpr, ld, cols, codes, scales, k0, k1, off);
+                x, tc, cpr, ld, cols, codes, scales, k0, k1, off, zmask);
             break;
         case 32:
             quantize_row_kernel<IN_BF16, 32, SR, U><<<grid, kThreads, 0, s>>>(
-                x, tc, cpr, ld, cols, codes, scales, k0, k1, off);
+                x, tc, cpr, ld, cols, codes, scales, k0, k1, off, zmask);
             break;
         case 64:
             quantize_row_kernel<IN_BF16, 64, SR, U><<<grid, kThreads, 0, s>>>(
-                x, tc, cpr, ld, cols, codes, scales, k0, k1, off);
+                x, tc, cpr, ld, cols, codes, scales, k0, k1, off, zmask);
             break;
         default:
             quantize_row_kernel<IN_BF16, 128, SR, U><<<grid, kThreads, 0, s>>>(
-                x, tc, cpr, ld, cols, codes, scales, k0, k1, off);
+                x, tc, cpr, ld, cols, codes, scales, k0, k1, off, zmask);
             break;
     }
     return hipGetLastError();
@@ -170,7 +184,7 @@ static hipError_t row_dispatch(int block, dim3 grid, hipStream_t s, const void* 
 
 hipError_t launch_quantize_row(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                                int block, bool sr, uint64_t seed, uint64_t off, uint8_t* codes,
-                               uint8_t* scales, hipStream_t s) {
+                               uint8_t* scales, hipStream_t s, const uint32_t* zmask) {
     const uint32_t cpr_n = (uint32_t)(cols / 8);
     const uint32_t tc = (uint32_t)(rows * (int64_t)cpr_n);
     const FastDiv cpr = make_fastdiv(cpr_n);
@@ -179,13 +193,13 @@ hipError_t launch_quantize_row(const void* x, int dtype, int64_t rows, int64_t c
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     if (dtype == BF16)
         return sr ? row_dispatch<1, 1>(block, grid, s, x, tc, cpr, ld, cols, codes, scales, k0,
-                                       k1, off)
+                                       k1, off, zmask)
                   : row_dispatch<1, 0>(block, grid, s, x, tc, cpr, ld, cols, codes, scales, k0,
-                                       k1, off);
+                                       k1, off, zmask);
     return sr ? row_dispatch<0, 1>(block, grid, s, x, tc, cpr, ld, cols, codes, scales, k0, k1,
-                                   off)
+                                   off, zmask)
               : row_dispatch<0, 0>(block, grid, s, x, tc, cpr, ld, cols, codes, scales, k0, k1,
-                                   off);
+                                   off, zmask);
 }
 
 // ---------------------------------------------------------------------------
@@ -217,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
     const void* __restrict__ xv, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t k0, uint32_t k1,
     uint64_t rng_off, int64_t nrb, int64_t n_ctiles, uint8_t* __restrict__ codes_r,
-    uint8_t* __restrict__ scales_r, uint32_t kr0, uint32_t kr1) {
+    uint8_t* __restrict__ scales_r, uint32_t kr0, uint32_t kr1, const uint32_t* __restrict__ zmask) {
     static_assert(ROW == 0 || IN_BF16, "the fused row pass is for bf16 input");
     static_assert(ROW != 3 || SR, "a shared random stream needs the stochastic column pass");
     constexpr int RG = BLOCK / 8;  // lanes per row block (fused row pass)
@@ -279,6 +293,17 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[i][j] = 0u;
         }
+    }
+    if (ROW == 0 && zmask && rows_ok) {
+        // one bit per row; set rows are quantised as zeros (the thread's
+        // RPT = 8 rows start at a multiple of 8: one byte of one word)
+        const int64_t rf = r0 + rg * RPT;
+        const uint32_t mb = (zmask[rf >> 5] >> (rf & 31)) & 0xFFu;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            if ((mb >> i) & 1u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[i][j] = 0u;
     }
     auto col_bits = [&](int i, int j) -> uint32_t {
         if (IN_BF16) return (j & 1) ? (v[i][j >> 1] & 0xFFFF0000u) : (v[i][j >> 1] << 16);
@@ -559,26 +584,31 @@ static hipError_t col_dispatch(int block, int64_t nct, hipStream_t s, const void
                                int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
                                uint32_t k0, uint32_t k1, uint64_t off, int64_t nrb,
                                uint8_t* codes_r = nullptr, uint8_t* scales_r = nullptr,
-                               uint32_t kr0 = 0, uint32_t kr1 = 0) {
+                               uint32_t kr0 = 0, uint32_t kr1 = 0,
+                               const uint32_t* zmask = nullptr) {
     constexpr int RPT = ColRows<SR, ROW>::value;
     const int64_t nrt = (rows + 16 * RPT - 1) / (16 * RPT);
     const dim3 grid((unsigned)(nrt * nct));
     switch (block) {
         case 16:
             quantize_col_kernel<IN_BF16, 16, SR, AL, ROW, RPT><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct, codes_r, scales_r, kr0, kr1);
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct, codes_r, scales_r, kr0, kr1,
+                zmask);
             break;
         case 32:
             quantize_col_kernel<IN_BF16, 32, SR, AL, ROW, RPT><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct, codes_r, scales_r, kr0, kr1);
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct, codes_r, scales_r, kr0, kr1,
+                zmask);
             break;
         case 64:
             quantize_col_kernel<IN_BF16, 64, SR, AL, ROW, RPT><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct, codes_r, scales_r, kr0, kr1);
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct, codes_r, scales_r, kr0, kr1,
+                zmask);
             break;
         default:
             quantize_col_kernel<IN_BF16, 128, SR, AL, ROW, RPT><<<grid, kThreads, 0, s>>>(
-                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct, codes_r, scales_r, kr0, kr1);
+                x, rows, cols, ld, codes, scales, k0, k1, off, nrb, nct, codes_r, scales_r, kr0, kr1,
+                zmask);
             break;
     }
     return hipGetLastError();
@@ -586,7 +616,7 @@ static hipError_t col_dispatch(int block, int64_t nct, hipStream_t s, const void
 
 hipError_t launch_quantize_col(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                                int block, bool sr, uint64_t seed, uint64_t off, uint8_t* codes,
-                               uint8_t* scales, hipStream_t s) {
+                               uint8_t* scales, hipStream_t s, const uint32_t* zmask) {
     const int64_t cols_per_tile = dtype == BF16 ? 128 : 64;
     const int64_t nct = (cols + cols_per_tile - 1) / cols_per_tile;
     const int64_t nrb = rows / block;
@@ -595,19 +625,19 @@ hipError_t launch_quantize_col(const void* x, int dtype, int64_t rows, int64_t c
     if (dtype == BF16) {
         if (!sr)
             return col_dispatch<1, 0, 1, 0>(block, nct, s, x, rows, cols, ld, codes, scales, k0,
-                                            k1, off, nrb);
+                                            k1, off, nrb, nullptr, nullptr, 0, 0, zmask);
         return al ? col_dispatch<1, 1, 1, 0>(block, nct, s, x, rows, cols, ld, codes, scales, k0,
-                                             k1, off, nrb)
+                                             k1, off, nrb, nullptr, nullptr, 0, 0, zmask)
                   : col_dispatch<1, 1, 0, 0>(block, nct, s, x, rows, cols, ld, codes, scales, k0,
-                                             k1, off, nrb);
+                                             k1, off, nrb, nullptr, nullptr, 0, 0, zmask);
     }
     if (!sr)
         return col_dispatch<0, 0, 1, 0>(block, nct, s, x, rows, cols, ld, codes, scales, k0, k1,
-                                        off, nrb);
+                                        off, nrb, nullptr, nullptr, 0, 0, zmask);
     return al ? col_dispatch<0, 1, 1, 0>(block, nct, s, x, rows, cols, ld, codes, scales, k0, k1,
-                                         off, nrb)
+                                         off, nrb, nullptr, nullptr, 0, 0, zmask)
               : col_dispatch<0, 1, 0, 0>(block, nct, s, x, rows, cols, ld, codes, scales, k0, k1,
-                                         off, nrb);
+                                         off, nrb, nullptr, nullptr, 0, 0, zmask);
 }
 
 // Both quantisations of a bf16 tensor in one pass (rows and cols multiples
@@ -643,6 +673,37 @@ hipError_t launch_quantize_dual(const void* x, int64_t rows, int64_t cols, int64
     if (sr_row) FP4Q_DUAL(0, 0, 2);
     FP4Q_DUAL(0, 0, 1);
 #undef FP4Q_DUAL
+}
+
+// ---------------------------------------------------------------------------
+// Channel masks for the quantisers' zero mask: a fill, then one atomic OR per
+// listed index (two launches on the stream, so the OR follows the fill).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void mask_fill_kernel(uint32_t* __restrict__ mask,
+                                                             int64_t words) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < words) mask[i] = 0u;
+}
+
+__global__ __launch_bounds__(kThreads) void mask_set_kernel(const int32_t* __restrict__ idx,
+                                                            int32_t n, int64_t length,
+                                                            uint32_t* __restrict__ mask) {
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t >= n) return;
+    const int64_t c = idx[t];
+    if (c < 0 || c >= length) return;  // outside the axis: ignored
+    atomicOr(mask + (c >> 5), 1u << (c & 31));
+}
+
+hipError_t launch_channel_mask(const int32_t* idx, int32_t n, int64_t length, uint32_t* mask,
+                               hipStream_t s) {
+    const int64_t words = (length + 31) / 32;
+    mask_fill_kernel<<<dim3((unsigned)((words + kThreads - 1) / kThreads)), kThreads, 0, s>>>(
+        mask, words);
+    if (n > 0)
+        mask_set_kernel<<<dim3((unsigned)((n + kThreads - 1) / kThreads)), kThreads, 0, s>>>(
+            idx, n, length, mask);
+    return hipGetLastError();
 }
 
 }  // namespace fp4q

@@ -259,3 +259,24 @@ def hcp_residual_entries(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx
     lib().orc_hcp_residual_entries(N, K, _p(x), _p(xqc), _p(xqs), _p(w), _p(wqc), _p(wqs),
                                    _p(hot), hot.size, ii.size, _p(ii), _p(jj), _p(R), _p(S))
     return R, S
+
+
+def hcp_split_entries(x, w, hot_idx, ii, jj):
+    """The split reading of the hot-channel compensation (outlier-dynamics
+    page, sec. 3.1-3.2): the hot channels' own bf16 product
+    sum_{c in H} X[i,c] W[c,j] at sampled (ii, jj), added to the product of the
+    operands quantised with H zeroed.  float64 (every bf16 x bf16 product is
+    exact; |H| terms), with the sum of |terms|.
+    x: bf16 bits [M, K]; w: bf16 bits [K, N]."""
+    xd = bf16_to_f64(_c(x, _np.uint16))
+    wd = bf16_to_f64(_c(w, _np.uint16))
+    hot = _c(hot_idx, _np.int64)
+    ii = _c(ii, _np.int64)
+    jj = _c(jj, _np.int64)
+    R = _np.zeros(ii.shape, _np.float64)
+    S = _np.zeros(ii.shape, _np.float64)
+    for c in hot:  # one hot channel at a time, in the list's order
+        t = xd[ii, c] * wd[c, jj]
+        R += t
+        S += _np.abs(t)
+    return R, S

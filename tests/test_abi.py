@@ -274,3 +274,34 @@ def test_gemm_quant_validation(L):
     bad = list(args)
     bad[2] = 1 << 24
     assert h(*bad) == 2
+
+
+def test_split_entry_points_validation(L):
+    assert L.fp4q_channel_mask(FAKE, 3, 0, FAKE, NUL) == 1          # length
+    assert L.fp4q_channel_mask(FAKE, -1, 10, FAKE, NUL) == 1        # n
+    assert L.fp4q_channel_mask(FAKE, 3, 10, NUL, NUL) == 1          # mask
+    assert L.fp4q_channel_mask(ct.c_void_p(0x10002), 3, 10, FAKE, NUL) == 3
+    q = L.fp4q_quantize_masked
+    args = [FAKE, 1, 64, 64, 64, 32, 0, 0, ct.c_uint64(0), ct.c_uint64(0), FAKE, FAKE, FAKE, NUL]
+    bad = list(args)
+    bad[10] = NUL        # zero mask
+    assert q(*bad) == 1
+    bad = list(args)
+    bad[10] = ct.c_void_p(0x10002)
+    assert q(*bad) == 3
+    bad = list(args)
+    bad[3] = 48          # cols % block for ROW
+    bad[4] = 48
+    assert q(*bad) == 1
+    h = L.fp4q_gemm_hcp_split
+    ws = L.fp4q_hcp_workspace_bytes(128, 64, 10)
+    args = [128, 64, 256, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, 64, FAKE, ws, NUL]
+    bad = list(args)
+    bad[14] = ws - 1
+    assert h(*bad) == 4
+    bad = list(args)
+    bad[2] = 160
+    assert h(*bad) == 1
+    bad = list(args)
+    bad[10] = 300
+    assert h(*bad) == 1

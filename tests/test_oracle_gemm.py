@@ -158,3 +158,33 @@ def test_hcp_on_grid_is_zero_and_linear(orc):
     Rab, S = orc.hcp_residual_entries(x, xqc, xqs, w, wqc, wqs, np.concatenate([h1, h2]),
                                       ii.ravel(), jj.ravel())
     assert np.all(np.abs(Ra + Rb - Rab) <= 1e-14 * S)
+
+
+def test_hcp_split_brute_force_and_identities(orc):
+    """Split reading: the residual equals a plain triple loop on a tiny case;
+    no hot channels gives zero; with every channel hot the quantised operands
+    are all zero and the residual alone is the exact bf16 product."""
+    M, K, N = 3, 64, 5
+    x, w, _, _, _, _ = _hcp_case(orc, M, K, N, 61)
+    hot = np.array([1, 5, 33, 62], np.int32)
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ii, jj = ii.ravel(), jj.ravel()
+    R, S = orc.hcp_split_entries(x, w, hot, ii, jj)
+    xd, wd = orc.bf16_to_f64(x), orc.bf16_to_f64(w)
+    for n, (i, j) in enumerate(zip(ii, jj)):
+        acc = 0.0
+        for c in hot:
+            acc += xd[i, c] * wd[c, j]
+        assert R[n] == acc
+    R0, S0 = orc.hcp_split_entries(x, w, np.zeros(0, np.int32), ii, jj)
+    assert np.all(R0 == 0) and np.all(S0 == 0)
+    allh = np.arange(K, dtype=np.int32)
+    xz, wz = x.copy(), w.copy()
+    xz[:, allh] = 0
+    wz[allh, :] = 0
+    xqc, xqs = orc.quantize(xz, 32)
+    wqc, wqs = orc.quantize(wz, 32, axis=orc.COL)
+    C, _ = orc.gemm(xqc, xqs, wqc, wqs)
+    assert np.all(C == 0)
+    R, S = orc.hcp_split_entries(x, w, allh, ii, jj)
+    assert np.all(np.abs(C.ravel() + R - (xd @ wd).ravel()) <= 1e-12 * S)
