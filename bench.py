@@ -402,6 +402,8 @@ def bench_outlier_layer(torch, fq, inputs, dev):
     xs = (torch.empty_like(xq[0]), torch.empty_like(xq[1]))
     wsq = (torch.empty_like(wq[0]), torch.empty_like(wq[1]))
     ws = torch.empty(fq.hcp_workspace_bytes(M, N, hot.numel()), dtype=torch.uint8, device=dev)
+    hsel = torch.empty_like(hot)
+    hws = torch.empty(fq.hot_channels_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
     res = {}
     for name, fn in (("quant_x_row", lambda: fq.quantize(X, 32, fq.ROW, codes=xq[0], scales=xq[1])),
                      ("quant_w_col", lambda: fq.quantize(W, 32, fq.COL, codes=wq[0], scales=wq[1])),
@@ -415,7 +417,9 @@ def bench_outlier_layer(torch, fq, inputs, dev):
                          fq.quantize_masked(X, hmask, 32, fq.ROW, codes=xs[0], scales=xs[1]),
                          fq.quantize_masked(W, hmask, 32, fq.COL, codes=wsq[0], scales=wsq[1]))),
                      ("gemm_hcp_split", lambda: fq.gemm_hcp_split(X, xs[0], xs[1], W, wsq[0], wsq[1],
-                                                                 hot, y=Y2, workspace=ws))):
+                                                                 hot, y=Y2, workspace=ws)),
+                     ("hot_channels", lambda: fq.hot_channels(X, hot.numel(), hot_idx=hsel,
+                                                              workspace=hws))):
         fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -432,6 +436,9 @@ def bench_outlier_layer(torch, fq, inputs, dev):
     res["quant_x_row_GBps"] = round(M * K * qb / (res["quant_x_row_us"] * 1e-6) / 1e9, 1)
     res["quant_w_col_GBps"] = round(K * N * qb / (res["quant_w_col_us"] * 1e-6) / 1e9, 1)
     res["hcp_n_hot"] = int(hot.numel())
+    # the choice reads X once (bf16); the partial-sum rows are small beside it
+    res["hot_channels_GBps"] = round(2.0 * M * K / (res["hot_channels_us"] * 1e-6) / 1e9, 1)
+    res["hot_channels_match_planted"] = bool(torch.equal(hsel, hot))
     res["hcp_y_rmw_GBps"] = round(8.0 * M * N / (res["hcp_residual_us"] * 1e-6) / 1e9, 1)
     # dual-kernel mode (base GEMM, then the residual's read-modify-write of Y)
     # against the single kernel that writes Y once

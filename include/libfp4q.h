@@ -297,6 +297,33 @@ fp4q_status_t fp4q_gemm_hcp_split(int64_t M, int64_t N, int64_t K, const void* x
                                   int32_t n_hot, float* y, int64_t ld_y, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/*
+ * fp4q_hot_channels -- the choice of the hot channels H (outlier-dynamics
+ * page, sec. 4.1: the top 9% of channels by quantisation error are kept in
+ * high precision, the choice refreshed every 1000 steps).  The error of
+ * channel c of X is
+ *   e_c = sum_i ( X[i,c] - deq(Q(X))[i,c] )^2
+ * with Q the ROW block-32 nearest-even quantisation that fp4q_quantize
+ * gives X (a block holding Inf or NaN dequantises to NaN, so e_c is NaN).
+ * The n_hot channels of largest e_c are written to hot_idx in ascending
+ * index order, ready for fp4q_quantize_masked / fp4q_channel_mask and the
+ * hot-channel GEMMs.  Ranking: NaN above every number, equal errors to the
+ * lower index.  e_c is summed in fp32 (squares rounded, a fixed order that
+ * does not depend on scheduling), so the choice is deterministic run to run.
+ *   x        bf16 [rows, cols], row stride ld_x >= cols (ld_x % 8 == 0),
+ *            16-byte aligned; read only.
+ *   cols % 32 == 0, cols <= 16384 (above: FP4Q_ERR_UNSUPPORTED);
+ *   0 <= n_hot <= cols.
+ *   hot_idx  int32 [n_hot], written (may be NULL when n_hot = 0).
+ *   err      fp32 [cols], e_c written; NULL to skip it.
+ *   workspace >= fp4q_hot_channels_workspace_bytes(rows, cols) device bytes,
+ *            16-byte aligned; caller-owned, contents not kept.
+ */
+size_t fp4q_hot_channels_workspace_bytes(int64_t rows, int64_t cols);
+fp4q_status_t fp4q_hot_channels(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                int32_t n_hot, int32_t* hot_idx, float* err, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 const char* fp4q_status_string(fp4q_status_t s);
 const char* fp4q_last_error(void);
 int32_t fp4q_abi_version(void);

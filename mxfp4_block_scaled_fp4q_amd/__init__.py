@@ -25,7 +25,7 @@ EXPORTS = ["fp4q_channel_mask", "fp4q_quantize_masked", "fp4q_gemm_hcp_split",
            "fp4q_gemm",
            "fp4q_gemm_dge", "fp4q_gemm_quant", "fp4q_hcp_workspace_bytes",
            "fp4q_hcp_residual_add",
-           "fp4q_gemm_hcp",
+           "fp4q_gemm_hcp", "fp4q_hot_channels_workspace_bytes", "fp4q_hot_channels",
            "fp4q_status_string",
            "fp4q_last_error", "fp4q_abi_version"]
 
@@ -68,6 +68,8 @@ def lib():
             "fp4q_gemm_hcp_split": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, I64, P, SZ,
                                           P]),
             "fp4q_gemm_hcp": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, I64, P, SZ, P]),
+            "fp4q_hot_channels_workspace_bytes": (SZ, [I64, I64]),
+            "fp4q_hot_channels": (I32, [P, I64, I64, I64, I32, P, P, P, SZ, P]),
             "fp4q_status_string": (_ct.c_char_p, [I32]),
             "fp4q_last_error": (_ct.c_char_p, []),
             "fp4q_abi_version": (I32, []),
@@ -335,3 +337,28 @@ def gemm_hcp_split(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, y=No
                                      _ptr(y), y.stride(0), _ptr(workspace), workspace.numel(),
                                      _stream(stream)))
     return y
+
+
+def hot_channels_workspace_bytes(rows, cols):
+    return int(lib().fp4q_hot_channels_workspace_bytes(rows, cols))
+
+
+def hot_channels(x, n_hot, hot_idx=None, err=None, want_err=False, workspace=None, stream=None):
+    """The n_hot channels (columns) of the bf16 x with the largest ROW block-32
+    quantisation error, ascending (fp4q_hot_channels).  Returns hot_idx, or
+    (hot_idx, err) when want_err (err: fp32 per-channel errors)."""
+    torch = _torch()
+    _need_cuda(x)
+    R, C = x.shape
+    if hot_idx is None:
+        hot_idx = torch.empty((max(n_hot, 0),), dtype=torch.int32, device=x.device)
+    if err is None and want_err:
+        err = torch.empty((C,), dtype=torch.float32, device=x.device)
+    need = hot_channels_workspace_bytes(R, C)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().fp4q_hot_channels(_ptr(x), R, C, x.stride(0), n_hot,
+                                   _ptr(hot_idx) if n_hot > 0 else None,
+                                   _ptr(err) if err is not None else None, _ptr(workspace),
+                                   workspace.numel(), _stream(stream)))
+    return (hot_idx, err) if want_err else hot_idx

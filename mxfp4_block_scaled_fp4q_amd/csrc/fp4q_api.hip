@@ -414,4 +414,38 @@ fp4q_status_t fp4q_gemm_hcp(int64_t M, int64_t N, int64_t K, const void* x,
                       "gemm_hcp launch");
 }
 
+size_t fp4q_hot_channels_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return fp4q::hot_channels_workspace_bytes(rows, cols);
+}
+
+fp4q_status_t fp4q_hot_channels(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                int32_t n_hot, int32_t* hot_idx, float* err, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (rows <= 0 || cols <= 0 || n_hot < 0)
+        return fail(FP4Q_ERR_INVALID, "hot_channels: rows=%lld cols=%lld n_hot=%d",
+                    (long long)rows, (long long)cols, (int)n_hot);
+    if (!x || !workspace || (n_hot > 0 && !hot_idx))
+        return fail(FP4Q_ERR_INVALID, "hot_channels: null pointer");
+    if (cols % 32) return fail(FP4Q_ERR_INVALID, "hot_channels: cols %% 32 != 0");
+    if (ld_x < cols || ld_x % 8)
+        return fail(FP4Q_ERR_INVALID, "hot_channels: ld_x must be >= cols and a multiple of 8");
+    if (n_hot > cols) return fail(FP4Q_ERR_INVALID, "hot_channels: n_hot > cols");
+    if (cols > fp4q::hot_channels_max_cols())
+        return fail(FP4Q_ERR_UNSUPPORTED, "hot_channels: cols above %lld",
+                    (long long)fp4q::hot_channels_max_cols());
+    if (rows > kMaxElems / ld_x) return fail(FP4Q_ERR_INVALID, "hot_channels: tensor too large");
+    if (!aligned16(x) || !aligned16(workspace) || ((uintptr_t)hot_idx % 4) ||
+        ((uintptr_t)err % 4))
+        return fail(FP4Q_ERR_ALIGNMENT,
+                    "hot_channels: x and workspace 16-byte aligned, hot_idx and err 4-byte");
+    const size_t need = fp4q::hot_channels_workspace_bytes(rows, cols);
+    if (workspace_bytes < need)
+        return fail(FP4Q_ERR_WORKSPACE, "hot_channels: workspace %zu < %zu bytes",
+                    workspace_bytes, need);
+    return hip_status(fp4q::launch_hot_channels((const uint16_t*)x, rows, cols, ld_x, n_hot,
+                                                workspace, hot_idx, err, (hipStream_t)stream),
+                      "hot_channels launch");
+}
+
 }  // extern "C"

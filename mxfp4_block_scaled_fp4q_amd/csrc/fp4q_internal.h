@@ -86,5 +86,12 @@ hipError_t launch_gemm_hcp(int64_t M, int64_t N, int64_t K, const void* x, const
                            const uint8_t* xqs, const void* w, const uint8_t* wqc,
                            const uint8_t* wqs, const int32_t* hot, int32_t n_hot, float* y,
                            int64_t ldy, void* ws, hipStream_t s);
+// Hot-channel choice: per-column ROW block-32 RNE quantisation error of the
+// bf16 X [rows, cols] and the n_hot columns of largest error, ascending.
+size_t hot_channels_workspace_bytes(int64_t rows, int64_t cols);
+int64_t hot_channels_max_cols();
+hipError_t launch_hot_channels(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                               int32_t n_hot, void* ws, int32_t* hot, float* err_out,
+                               hipStream_t s);
 
 }  // namespace fp4q

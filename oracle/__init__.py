@@ -280,3 +280,28 @@ def hcp_split_entries(x, w, hot_idx, ii, jj):
         R += t
         S += _np.abs(t)
     return R, S
+
+
+def channel_quant_error(x, block=32):
+    """Per-channel (per-column) quantisation error of X under the ROW
+    nearest-even MXFP4 quantisation: e_c = sum_i (x_ic - deq(Q(x))_ic)^2, in
+    float64 (the ranking quantity of the hot-channel choice, outlier-dynamics
+    page, sec. 4.1).  A block with a non-finite element dequantises to NaN, so
+    its channels' errors are NaN.  x: bf16 bits or float32 [rows, cols]."""
+    x = _np.ascontiguousarray(x)
+    codes, scales = quantize(x, block, ROW, RNE)
+    xd = bf16_to_f64(x) if x.dtype == _np.uint16 else x.astype(_np.float64)
+    d = xd - dequantize(codes, scales, block)
+    return (d * d).sum(axis=0)
+
+
+def hot_channels(x, n_hot, block=32):
+    """The n_hot channels of largest quantisation error (outlier-dynamics
+    page, sec. 4.1: the top 9% of channels by error are kept in high
+    precision), returned in ascending index order as int32.  Ranking: larger
+    error first, NaN above every number, equal errors to the lower index."""
+    e = channel_quant_error(x, block)
+    idx = _np.arange(e.size)
+    nan = _np.isnan(e)
+    order = _np.lexsort((idx, -_np.where(nan, 0.0, e), ~nan))
+    return _np.sort(order[:int(n_hot)]).astype(_np.int32), e

@@ -305,3 +305,29 @@ def test_split_entry_points_validation(L):
     bad = list(args)
     bad[10] = 300
     assert h(*bad) == 1
+
+
+def test_hot_channels_validation(L):
+    ws = L.fp4q_hot_channels_workspace_bytes(128, 64)
+    assert ws >= (2 + 1) * 64 * 4        # partial rows + the error row
+    assert L.fp4q_hot_channels_workspace_bytes(0, 64) == 0
+    h = L.fp4q_hot_channels
+    args = [FAKE, 128, 64, 64, 6, FAKE, NUL, FAKE, ws, NUL]
+    for i, v, st in [(2, 48, 1),          # cols % 32
+                     (3, 60, 1),          # ld_x < cols
+                     (3, 68, 1),          # ld_x % 8
+                     (4, 65, 1),          # n_hot > cols
+                     (4, -1, 1),          # n_hot < 0
+                     (1, 0, 1),           # rows
+                     (5, NUL, 1),         # hot_idx with n_hot > 0
+                     (7, NUL, 1),         # workspace
+                     (8, ws - 1, 4),      # workspace size
+                     (0, ct.c_void_p(0x10008), 3),   # x alignment
+                     (6, ct.c_void_p(0x10002), 3)]:  # err alignment
+        bad = list(args)
+        bad[i] = v
+        assert h(*bad) == st, (i, v)
+    bad = list(args)
+    bad[2] = bad[3] = 16384 + 32         # above the in-LDS selection limit
+    bad[8] = L.fp4q_hot_channels_workspace_bytes(128, 16384 + 32)
+    assert h(*bad) == 2

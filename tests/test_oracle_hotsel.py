@@ -1,0 +1,116 @@
+"""Pins of the oracle's hot-channel choice (outlier-dynamics page, sec. 4.1:
+the channels of largest quantisation error are kept in high precision): the
+per-channel error against a brute-force quantiser written here from the
+format definitions (frexp exponent, nearest E2M1 magnitude by exhaustive
+search, ties to the even code), and the ranking against closed cases (zero
+and on-grid inputs, a lone off-grid column, ties, non-finite blocks, exact
+power-of-two rescaling)."""
+import math
+
+import numpy as np
+import pytest
+
+from mxfp4_block_scaled_fp4q_amd import inputs
+
+MAGS = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # E2M1 magnitudes, codes 0..7
+
+
+def bf16_values(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def brute_channel_error(xv, block=32):
+    """sum over rows of (x - Q(x))^2 per column, Q by exhaustive search."""
+    rows, cols = xv.shape
+    err = [0.0] * cols
+    for r in range(rows):
+        for b0 in range(0, cols, block):
+            blk = [float(v) for v in xv[r, b0:b0 + block]]
+            amax = max(abs(v) for v in blk)
+            if amax == 0.0:
+                exp = -127
+            else:
+                exp = max(math.frexp(amax)[1] - 1 - 2, -127)
+            s = 2.0 ** exp
+            for j, v in enumerate(blk):
+                y = abs(v) / s
+                best = None
+                for code, m in enumerate(MAGS):
+                    d = abs(y - m)
+                    if best is None or d < best[0] or (d == best[0] and code % 2 == 0):
+                        best = (d, code)
+                q = math.copysign(MAGS[best[1]] * s, v)
+                err[b0 + j] += (v - q) ** 2
+    return np.array(err)
+
+
+def brute_top(err, n):
+    order = sorted(range(len(err)), key=lambda c: (-err[c], c))
+    return sorted(order[:n])
+
+
+def test_channel_error_brute_force(orc):
+    xf = inputs.with_outliers(inputs.normal((6, 96), 911), 912, 20, 40.0)
+    xb = inputs.to_bf16_bits(xf)
+    e = orc.channel_quant_error(xb)
+    ref = brute_channel_error(bf16_values(xb))
+    np.testing.assert_allclose(e, ref, rtol=1e-15, atol=0)
+    for n in (0, 1, 9, 50, 96):
+        hot, e2 = orc.hot_channels(xb, n)
+        assert hot.dtype == np.int32
+        assert hot.tolist() == brute_top(list(ref), n)
+        np.testing.assert_array_equal(e, e2)
+
+
+def test_zero_and_on_grid_inputs_have_no_error(orc):
+    z = np.zeros((4, 64), np.float32)
+    hot, e = orc.hot_channels(z, 5)
+    assert not e.any()
+    assert hot.tolist() == [0, 1, 2, 3, 4]                 # ties: lower index first
+    rng = np.random.default_rng(913)
+    g = rng.choice(np.array(MAGS + [-m for m in MAGS]), size=(5, 64)).astype(np.float32)
+    g[:, ::32] = 6.0                                       # block amax 6 -> scale 1
+    _, e = orc.hot_channels(g * np.float32(2.0 ** -9), 3)
+    assert not e.any()
+
+
+def test_lone_off_grid_column_and_ties(orc):
+    x = np.zeros((7, 64), np.float32)
+    x[:, 37] = 5.0          # amax 5 -> scale 1; 5 is a tie, to the even code (4): error 1
+    hot, e = orc.hot_channels(x, 1)
+    assert hot.tolist() == [37]
+    assert e[37] == 7.0 and e.sum() == 7.0
+    x[:, 5] = -5.0          # the same error, a lower index
+    assert orc.hot_channels(x, 1)[0].tolist() == [5]
+    assert orc.hot_channels(x, 2)[0].tolist() == [5, 37]
+    assert orc.hot_channels(x, 3)[0].tolist() == [0, 5, 37]
+
+
+def test_nonfinite_block_ranks_first(orc):
+    xb = inputs.to_bf16_bits(inputs.normal((4, 96), 914))
+    xb[2, 40] = 0x7F80                                     # +inf in block 1 of row 2
+    hot, e = orc.hot_channels(xb, 33)
+    assert np.isnan(e[32:64]).all() and np.isfinite(e[:32]).all() and np.isfinite(e[64:]).all()
+    fin = np.where(np.isnan(e), -1.0, e)
+    top_finite = int(np.argmax(fin))
+    assert hot.tolist() == sorted(list(range(32, 64)) + [top_finite])
+
+
+def test_power_of_two_rescale_is_equivariant(orc):
+    xf = inputs.student_t((16, 128), 915)
+    xb = inputs.to_bf16_bits(xf)
+    e1 = orc.channel_quant_error(xb)
+    xb2 = inputs.to_bf16_bits(bf16_values(xb).astype(np.float32) * np.float32(2.0 ** 6))
+    e2 = orc.channel_quant_error(xb2)
+    np.testing.assert_array_equal(e2, e1 * 4.0 ** 6)        # scales are powers of two
+    assert orc.hot_channels(xb, 12)[0].tolist() == orc.hot_channels(xb2, 12)[0].tolist()
+
+
+def test_planted_hot_columns_are_recovered(orc):
+    # the 13B-layer recipe at a reduced row count: 9% of the columns x100
+    k = 1024
+    hot = inputs.hot_channels(k, 502)
+    xf = inputs.normal((64, k), 501)
+    xf[:, hot] *= np.float32(100.0)
+    sel, e = orc.hot_channels(inputs.to_bf16_bits(xf), hot.size)
+    assert sel.tolist() == hot.tolist()
