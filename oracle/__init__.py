@@ -39,6 +39,7 @@ def lib():
             "orc_sr_bits": (_ct.c_uint32, [U64, U64]),
             "orc_quantize": (I32, [P, I32, I64, I64, I64, I32, I32, I32, U64, U64, P, P]),
             "orc_dequantize": (None, [P, P, I64, I64, I32, P]),
+            "orc_quantize_2d": (I32, [P, I32, I64, I64, I64, I32, I32, U64, U64, P, P, P, P]),
             "orc_round_f32": (None, [P, P, I64]),
             "orc_round_bf16": (None, [P, P, I64]),
             "orc_bf16_from_double": (_ct.c_uint16, [D]),
@@ -162,6 +163,26 @@ def quantize(x, block, axis=ROW, round=RNE, seed=0, rng_offset=0):
     if rc != 0:
         raise ValueError("oracle quantize: unsupported shape/block")
     return codes, scales
+
+
+def quantize_2d(x, tile=32, round=RNE, seed=0, rng_offset=0):
+    """Two-dimensional block scaling (outlier-dynamics page, sec. 4.1): one
+    scale per tile x tile square.  x: [rows, cols] float32 or bf16-as-uint16.
+    Returns (codes_r [rows, cols/2], scales_r [rows, cols/tile],
+             codes_c [cols, rows/2], scales_c [cols, rows/tile]): the same
+    quantised values in the ROW and the COL (K-major) layout."""
+    x = _np.ascontiguousarray(x)
+    dt = _dtype_of(x)
+    rows, cols = x.shape
+    cr = _np.empty((rows, cols // 2), _np.uint8)
+    sr = _np.empty((rows, cols // tile), _np.uint8)
+    cc = _np.empty((cols, rows // 2), _np.uint8)
+    sc = _np.empty((cols, rows // tile), _np.uint8)
+    rc = lib().orc_quantize_2d(_p(x), dt, rows, cols, cols, int(tile), int(round), int(seed),
+                               int(rng_offset), _p(cr), _p(sr), _p(cc), _p(sc))
+    if rc != 0:
+        raise ValueError("oracle quantize_2d: unsupported shape/tile")
+    return cr, sr, cc, sc
 
 
 def dequantize(codes, scales, block):

@@ -296,6 +296,54 @@ int orc_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
     return 0;
 }
 
+/* Two-dimensional block scaling ([P3] sec. 4.1: the backward pass of the
+ * recipe uses 2D block scales): every tile x tile square of X is one block
+ * (one shared scale from the square's amax, its tile*tile elements coded as
+ * any block), and the same codes are written in both layouts, so the ROW
+ * (blocks along columns) and the COL (blocks along rows, K-major) forms hold
+ * the same values and W and its transpose share one quantisation.
+ *   codes_r [rows, cols/2], scales_r [rows, cols/tile] (the square's scale
+ *   repeated on each of its rows); codes_c [cols, rows/2], scales_c
+ *   [cols, rows/tile].  SR draws element (r, c) from counter r*cols + c as
+ *   orc_quantize does.  Returns 0, or -1 on a shape the oracle does not take. */
+int orc_quantize_2d(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int tile,
+                    int round, uint64_t seed, uint64_t rng_offset, uint8_t* codes_r,
+                    uint8_t* scales_r, uint8_t* codes_c, uint8_t* scales_c) {
+    if (tile <= 0 || tile % 2 || rows % tile || cols % tile) return -1;
+    const int b = tile * tile;
+    uint32_t* v = (uint32_t*)malloc(sizeof(uint32_t) * b);
+    uint64_t* idx = (uint64_t*)malloc(sizeof(uint64_t) * b);
+    uint8_t* cd = (uint8_t*)malloc(b);
+    for (int64_t tr = 0; tr < rows / tile; ++tr)
+        for (int64_t tc = 0; tc < cols / tile; ++tc) {
+            for (int i = 0; i < tile; ++i)
+                for (int j = 0; j < tile; ++j) {
+                    int64_t r = tr * tile + i, c = tc * tile + j;
+                    v[i * tile + j] = src_bits(x, dtype, ld, r, c);
+                    idx[i * tile + j] = (uint64_t)(r * cols + c);
+                }
+            uint8_t byte = (uint8_t)quantize_block(v, idx, b, round, seed, rng_offset, cd);
+            for (int i = 0; i < tile; ++i) {
+                int64_t r = tr * tile + i;
+                scales_r[r * (cols / tile) + tc] = byte;
+                for (int j = 0; j < tile; j += 2)
+                    codes_r[r * (cols / 2) + (tc * tile + j) / 2] =
+                        (uint8_t)((cd[i * tile + j] & 0xF) | ((cd[i * tile + j + 1] & 0xF) << 4));
+            }
+            for (int j = 0; j < tile; ++j) {
+                int64_t c = tc * tile + j;
+                scales_c[c * (rows / tile) + tr] = byte;
+                for (int i = 0; i < tile; i += 2)
+                    codes_c[c * (rows / 2) + (tr * tile + i) / 2] =
+                        (uint8_t)((cd[i * tile + j] & 0xF) | ((cd[(i + 1) * tile + j] & 0xF) << 4));
+            }
+        }
+    free(v);
+    free(idx);
+    free(cd);
+    return 0;
+}
+
 /* Value of packed element (r, k) of a quantized [rows, kdim] operand. */
 static double deq_elem(const uint8_t* codes, const uint8_t* scales, int64_t kdim, int block,
                        int64_t r, int64_t k) {

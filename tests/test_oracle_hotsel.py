@@ -5,14 +5,10 @@ format definitions (frexp exponent, nearest E2M1 magnitude by exhaustive
 search, ties to the even code), and the ranking against closed cases (zero
 and on-grid inputs, a lone off-grid column, ties, non-finite blocks, exact
 power-of-two rescaling)."""
-import math
-
 import numpy as np
-import pytest
 
+from brute_quant import MAGS, code_value, nearest_code, scale_exp
 from mxfp4_block_scaled_fp4q_amd import inputs
-
-MAGS = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # E2M1 magnitudes, codes 0..7
 
 
 def bf16_values(bits):
@@ -26,21 +22,9 @@ def brute_channel_error(xv, block=32):
     for r in range(rows):
         for b0 in range(0, cols, block):
             blk = [float(v) for v in xv[r, b0:b0 + block]]
-            amax = max(abs(v) for v in blk)
-            if amax == 0.0:
-                exp = -127
-            else:
-                exp = max(math.frexp(amax)[1] - 1 - 2, -127)
-            s = 2.0 ** exp
+            e = scale_exp(max(abs(v) for v in blk))
             for j, v in enumerate(blk):
-                y = abs(v) / s
-                best = None
-                for code, m in enumerate(MAGS):
-                    d = abs(y - m)
-                    if best is None or d < best[0] or (d == best[0] and code % 2 == 0):
-                        best = (d, code)
-                q = math.copysign(MAGS[best[1]] * s, v)
-                err[b0 + j] += (v - q) ** 2
+                err[b0 + j] += (v - code_value(nearest_code(v, e), e)) ** 2
     return np.array(err)
 
 
