@@ -178,6 +178,8 @@ def main():
          (K + N) * M * (0.5 + 1 / 32) + K * N * (2 + 4), 2.0 * K * N * M),
     ]
     yq = (torch.empty((M, N // 2), **u8), torch.empty((M, N // 32), **u8))
+    w2d = (torch.empty((K, N // 2), **u8), torch.empty((K, N // 32), **u8),
+           torch.empty((N, K // 2), **u8), torch.empty((N, K // 32), **u8))
     # timed aside: the unfused dW GEMM and DGE (the DGE kernel's own HBM
     # rate), and the forward GEMM that also quantises Y for a next layer
     # against the same GEMM followed by the ROW quantiser
@@ -190,6 +192,9 @@ def main():
          (K + N) * M * (0.5 + 1 / 32) + K * N * 4, 2.0 * K * N * M),
         ("dge_dw", lambda: fq.grad_estimate(fq.DGE, W, dW, 32, fq.COL, 5.0, 3.0, out=dWo),
          K * N * (2 + 4 + 4), 0),
+        # W with one scale per 32 x 32 square: both layouts from one pass,
+        # one set of values for the forward and the data-gradient GEMM
+        ("quant_w_2d", lambda: fq.quantize_2d(W, fq.RNE, 0, 0, out=w2d), K * N * qb2, 0),
     ]
     step_flops = sum(o[3] for o in ops)
 

@@ -298,6 +298,33 @@ fp4q_status_t fp4q_gemm_hcp_split(int64_t M, int64_t N, int64_t K, const void* x
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * fp4q_quantize_2d -- two-dimensional block scaling: one E8M0 scale per
+ * 32 x 32 square of x (the outlier-dynamics page, sec. 4.1, scales the
+ * backward pass's operands in 2D blocks; MXFP4's 32-element block is used in
+ * both directions, the granularity at which the GEMM takes scales along K).
+ * Each square is quantised as one block (scale from the square's largest
+ * |x|, elements rounded as fp4q_quantize rounds them) and the same codes are
+ * written in both layouts:
+ *   row_codes [rows, cols/2], row_scales [rows, cols/32]: the ROW layout,
+ *       each square's scale repeated on its 32 rows (a GEMM operand that
+ *       contracts over columns);
+ *   col_codes [cols, rows/2], col_scales [cols, rows/32]: the COL (K-major)
+ *       layout, each square's scale repeated on its 32 columns (the operand
+ *       that contracts over rows).
+ * Dequantised, the two are one matrix and its transpose, so a weight enters
+ * the forward GEMM and the data-gradient GEMM with the same values.
+ *   x bf16 [rows, cols], row stride ld_x >= cols (multiple of 8 elements);
+ *   rows % 32 == 0, cols % 32 == 0; all pointers 16-byte aligned.
+ *   round FP4Q_RNE or FP4Q_SR; SR draws element (r, c) from counter
+ *   r*cols + c + rng_offset of seed's stream, as fp4q_quantize does.
+ *   A square holding Inf or NaN gets scale 0xFF and zero codes.
+ */
+fp4q_status_t fp4q_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                               fp4q_round_t round, uint64_t seed, uint64_t rng_offset,
+                               uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
+                               uint8_t* col_scales, void* stream);
+
+/*
  * fp4q_hot_channels -- the choice of the hot channels H (outlier-dynamics
  * page, sec. 4.1: the top 9% of channels by quantisation error are kept in
  * high precision, the choice refreshed every 1000 steps).  The error of

@@ -448,4 +448,30 @@ fp4q_status_t fp4q_hot_channels(const void* x, int64_t rows, int64_t cols, int64
                       "hot_channels launch");
 }
 
+fp4q_status_t fp4q_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                               fp4q_round_t round, uint64_t seed, uint64_t rng_offset,
+                               uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
+                               uint8_t* col_scales, void* stream) {
+    if (!x || !row_codes || !row_scales || !col_codes || !col_scales)
+        return fail(FP4Q_ERR_INVALID, "quantize_2d: null pointer");
+    if (rows <= 0 || cols <= 0)
+        return fail(FP4Q_ERR_INVALID, "quantize_2d: rows=%lld cols=%lld", (long long)rows,
+                    (long long)cols);
+    if (rows % 32 || cols % 32)
+        return fail(FP4Q_ERR_INVALID, "quantize_2d: rows and cols must be multiples of 32");
+    if (ld_x < cols) return fail(FP4Q_ERR_INVALID, "quantize_2d: ld_x < cols");
+    if (round != FP4Q_RNE && round != FP4Q_SR)
+        return fail(FP4Q_ERR_INVALID, "quantize_2d: bad round");
+    if (rows > kMaxElems / ld_x) return fail(FP4Q_ERR_INVALID, "quantize_2d: tensor too large");
+    if (rows / 128 >= 65535) return fail(FP4Q_ERR_UNSUPPORTED, "quantize_2d: too many rows");
+    if (!aligned16(x) || !aligned16(row_codes) || !aligned16(row_scales) ||
+        !aligned16(col_codes) || !aligned16(col_scales) || ld_x % 8)
+        return fail(FP4Q_ERR_ALIGNMENT,
+                    "quantize_2d: pointers and the row stride must be 16-byte aligned");
+    return hip_status(fp4q::launch_quantize_2d(x, rows, cols, ld_x, round == FP4Q_SR, seed,
+                                               rng_offset, row_codes, row_scales, col_codes,
+                                               col_scales, (hipStream_t)stream),
+                      "quantize_2d launch");
+}
+
 }  // extern "C"

@@ -93,5 +93,10 @@ int64_t hot_channels_max_cols();
 hipError_t launch_hot_channels(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                                int32_t n_hot, void* ws, int32_t* hot, float* err_out,
                                hipStream_t s);
+// 2D (32 x 32 square) block scaling of a bf16 [rows, cols]: the same codes
+// in the ROW and the COL layout.
+hipError_t launch_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_t ld, bool sr,
+                              uint64_t seed, uint64_t off, uint8_t* codes_r, uint8_t* scales_r,
+                              uint8_t* codes_c, uint8_t* scales_c, hipStream_t s);
 
 }  // namespace fp4q

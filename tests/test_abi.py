@@ -331,3 +331,20 @@ def test_hot_channels_validation(L):
     bad[2] = bad[3] = 16384 + 32         # above the in-LDS selection limit
     bad[8] = L.fp4q_hot_channels_workspace_bytes(128, 16384 + 32)
     assert h(*bad) == 2
+
+
+def test_quantize_2d_validation(L):
+    q = L.fp4q_quantize_2d
+    args = [FAKE, 64, 96, 96, 0, ct.c_uint64(0), ct.c_uint64(0), FAKE, FAKE, FAKE, FAKE, NUL]
+    for i, v, st in [(1, 48, 1),          # rows % 32
+                     (2, 80, 1),          # cols % 32
+                     (3, 64, 1),          # ld_x < cols
+                     (3, 100, 3),         # ld_x % 8
+                     (4, 2, 1),           # round
+                     (0, NUL, 1),
+                     (9, NUL, 1),
+                     (0, FAKE_MIS, 3),
+                     (10, ct.c_void_p(0x10001), 3)]:
+        bad = list(args)
+        bad[i] = v
+        assert q(*bad) == st, (i, v)
