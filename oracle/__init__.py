@@ -326,3 +326,48 @@ def hot_channels(x, n_hot, block=32):
     nan = _np.isnan(e)
     order = _np.lexsort((idx, -_np.where(nan, 0.0, e), ~nan))
     return _np.sort(order[:int(n_hot)]).astype(_np.int32), e
+
+
+# --- random Hadamard transform before quantisation ------------------------
+
+RHT_C = _np.float32(2.0 ** -2.5)   # 1/sqrt(32) rounded to fp32
+
+
+def rht_transform(x, axis, signs):
+    """The blockwise random Hadamard transform the recipe of the
+    outlier-dynamics page (sec. 4.1) applies before backward quantisation,
+    along the block axis in groups of 32: y = c * H32 * D * x per group, with
+    D = diag(+-1) from `signs` (bool per position along the axis, True =
+    negate), H32 the Sylvester (natural-order) Hadamard matrix, entries
+    (-1)^popcount(i & j), and c = fl32(2^-2.5), so c*H32 is orthogonal up to
+    rounding.  Evaluated in fp32, the precision the codes are decided in: the
+    butterflies (a, b) -> (a + b, a - b) on pairs (i, i + s), bit s of i
+    clear, for s = 1, 2, 4, 8, 16 in that order, then the product by c.
+    x: bf16 bits or float32 [rows, cols]; axis ROW = along columns,
+    COL = along rows.  Returns float32 [rows, cols]."""
+    x = _np.ascontiguousarray(x)
+    v = bf16_to_f64(x).astype(_np.float32) if x.dtype == _np.uint16 else x.astype(_np.float32)
+    if axis == COL:
+        v = _np.ascontiguousarray(v.T)
+    rows, n = v.shape
+    if n % 32:
+        raise ValueError("rht_transform: the block axis must be a multiple of 32")
+    sg = _np.asarray(signs, bool)
+    v = _np.where(sg[None, :], -v, v).astype(_np.float32)
+    v = v.reshape(rows, n // 32, 32)
+    s = 1
+    while s < 32:
+        w = v.reshape(rows, n // 32, 32 // (2 * s), 2, s)
+        a = w[:, :, :, 0, :]
+        b = w[:, :, :, 1, :]
+        v = _np.stack([a + b, a - b], axis=3).reshape(rows, n // 32, 32)
+        s *= 2
+    v = (v * RHT_C).astype(_np.float32).reshape(rows, n)
+    return _np.ascontiguousarray(v.T) if axis == COL else v
+
+
+def rht_quantize(x, axis, signs, round=RNE, seed=0, rng_offset=0):
+    """Block-32 quantisation of the transformed tensor: rht_transform(x) fed
+    to the quantiser (layouts, rounding and random counters as quantize)."""
+    y = rht_transform(x, axis, signs)
+    return quantize(y, 32, axis, round, seed, rng_offset)
