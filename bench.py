@@ -180,6 +180,12 @@ def main():
     yq = (torch.empty((M, N // 2), **u8), torch.empty((M, N // 32), **u8))
     w2d = (torch.empty((K, N // 2), **u8), torch.empty((K, N // 32), **u8),
            torch.empty((N, K // 2), **u8), torch.empty((N, K // 32), **u8))
+    # one sign mask over the token axis for both weight-gradient operands
+    gsm = torch.Generator().manual_seed(7)
+    msk = torch.randint(-2 ** 31, 2 ** 31 - 1, ((M + 31) // 32,), generator=gsm,
+                        dtype=torch.int64).to(torch.int32).to(dev)
+    xrht = (torch.empty((K, M // 2), **u8), torch.empty((K, M // 32), **u8))
+    dyrht = (torch.empty((N, M // 2), **u8), torch.empty((N, M // 32), **u8))
     # timed aside: the unfused dW GEMM and DGE (the DGE kernel's own HBM
     # rate), and the forward GEMM that also quantises Y for a next layer
     # against the same GEMM followed by the ROW quantiser
@@ -195,6 +201,13 @@ def main():
         # W with one scale per 32 x 32 square: both layouts from one pass,
         # one set of values for the forward and the data-gradient GEMM
         ("quant_w_2d", lambda: fq.quantize_2d(W, fq.RNE, 0, 0, out=w2d), K * N * qb2, 0),
+        # the weight-gradient operands with the random Hadamard transform
+        # along the token axis (COL groups), X nearest-even and dY stochastic
+        ("quant_x_col_rht", lambda: fq.quantize_rht(X, msk, fq.COL, fq.RNE, 0, 0, codes=xrht[0],
+                                                    scales=xrht[1]), M * K * qb, 0),
+        ("quant_dy_col_rht_sr", lambda: fq.quantize_rht(dY, msk, fq.COL, fq.SR, SR_SEED, 0,
+                                                        codes=dyrht[0], scales=dyrht[1]),
+         M * N * qb, 0),
     ]
     step_flops = sum(o[3] for o in ops)
 

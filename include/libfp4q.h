@@ -325,6 +325,40 @@ fp4q_status_t fp4q_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_
                                uint8_t* col_scales, void* stream);
 
 /*
+ * fp4q_quantize_rht -- random Hadamard transform, then block-32 quantisation
+ * (the recipe on the outlier-dynamics page, sec. 4.1, transforms the
+ * backward pass's operands before quantising them).  Along the block axis,
+ * each group of 32 values x (the group of one quantisation block) becomes
+ *   y = c * H32 * D * x,  c = 2^-2.5 rounded to fp32,
+ * with H32 the natural-order (Sylvester) Hadamard matrix, entries
+ * (-1)^popcount(i & j), and D = diag(-1 where the sign bit of the position is
+ * set, else +1).  y is evaluated in fp32 as butterflies (a, b) -> (a + b,
+ * a - b) on pairs (i, i + s) with bit s of i clear, for s = 1, 2, 4, 8, 16 in
+ * that order, then multiplied by c; y is then quantised exactly as
+ * fp4q_quantize quantises an fp32 tensor (block 32, same layouts, rounding
+ * and random counters r*cols + c + rng_offset).  c * H32 is orthogonal up to
+ * rounding: a GEMM whose two operands are transformed along their shared
+ * contraction axis with the same sign mask approximates the untransformed
+ * product (no correction factor).
+ *   x      bf16 [rows, cols], row stride ld_x >= cols (multiple of 8).
+ *   axis   FP4Q_BLOCK_ROW: groups along columns, cols % 32 == 0; codes
+ *            [rows, cols/2], scales [rows, cols/32].
+ *          FP4Q_BLOCK_COL: groups along rows, rows % 32 == 0, cols even;
+ *            codes [cols, rows/2], scales [cols, rows/32] (K-major).
+ *   signs  uint32 device bit mask over the block axis (bit i of word i/32
+ *          negates position i; cols bits for ROW, rows bits for COL),
+ *          4-byte aligned; the caller draws it (e.g. once per layer) and
+ *          passes the same mask for both operands of a GEMM.
+ *   round, seed, rng_offset as fp4q_quantize.  x, codes, scales 16-byte
+ *   aligned.  A group holding Inf or NaN (or overflowing fp32) gets scale
+ *   0xFF and zero codes.
+ */
+fp4q_status_t fp4q_quantize_rht(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                fp4q_axis_t axis, const uint32_t* signs, fp4q_round_t round,
+                                uint64_t seed, uint64_t rng_offset, uint8_t* codes,
+                                uint8_t* scales, void* stream);
+
+/*
  * fp4q_hot_channels -- the choice of the hot channels H (outlier-dynamics
  * page, sec. 4.1: the top 9% of channels by quantisation error are kept in
  * high precision, the choice refreshed every 1000 steps).  The error of

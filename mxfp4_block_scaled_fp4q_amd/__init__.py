@@ -26,7 +26,7 @@ EXPORTS = ["fp4q_channel_mask", "fp4q_quantize_masked", "fp4q_gemm_hcp_split",
            "fp4q_gemm_dge", "fp4q_gemm_quant", "fp4q_hcp_workspace_bytes",
            "fp4q_hcp_residual_add",
            "fp4q_gemm_hcp", "fp4q_hot_channels_workspace_bytes", "fp4q_hot_channels",
-           "fp4q_quantize_2d",
+           "fp4q_quantize_2d", "fp4q_quantize_rht",
            "fp4q_status_string",
            "fp4q_last_error", "fp4q_abi_version"]
 
@@ -71,6 +71,7 @@ def lib():
             "fp4q_gemm_hcp": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, I64, P, SZ, P]),
             "fp4q_hot_channels_workspace_bytes": (SZ, [I64, I64]),
             "fp4q_quantize_2d": (I32, [P, I64, I64, I64, I32, U64, U64, P, P, P, P, P]),
+            "fp4q_quantize_rht": (I32, [P, I64, I64, I64, I32, P, I32, U64, U64, P, P, P]),
             "fp4q_hot_channels": (I32, [P, I64, I64, I64, I32, P, P, P, SZ, P]),
             "fp4q_status_string": (_ct.c_char_p, [I32]),
             "fp4q_last_error": (_ct.c_char_p, []),
@@ -382,3 +383,21 @@ def quantize_2d(x, rounding=RNE, seed=0, rng_offset=0, out=None, stream=None):
     _check(lib().fp4q_quantize_2d(_ptr(x), R, C, x.stride(0), rounding, seed, rng_offset,
                                   *(_ptr(t) for t in out), _stream(stream)))
     return out
+
+
+def quantize_rht(x, signs, axis=ROW, rounding=RNE, seed=0, rng_offset=0, codes=None, scales=None,
+                 stream=None):
+    """Block-32 quantisation of c * H32 * D * x along the block axis
+    (fp4q_quantize_rht); signs: int32/uint32 device bit mask over that axis.
+    Returns (codes, scales) in the layout of quantize(x, 32, axis)."""
+    torch = _torch()
+    _need_cuda(x, signs)
+    R, C = x.shape
+    if codes is None:
+        shape_c = (R, C // 2) if axis == ROW else (C, R // 2)
+        shape_s = (R, C // 32) if axis == ROW else (C, R // 32)
+        codes = torch.empty(shape_c, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(shape_s, dtype=torch.uint8, device=x.device)
+    _check(lib().fp4q_quantize_rht(_ptr(x), R, C, x.stride(0), axis, _ptr(signs), rounding, seed,
+                                   rng_offset, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales

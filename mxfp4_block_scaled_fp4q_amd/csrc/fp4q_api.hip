@@ -474,4 +474,35 @@ fp4q_status_t fp4q_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_
                       "quantize_2d launch");
 }
 
+fp4q_status_t fp4q_quantize_rht(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                fp4q_axis_t axis, const uint32_t* signs, fp4q_round_t round,
+                                uint64_t seed, uint64_t rng_offset, uint8_t* codes,
+                                uint8_t* scales, void* stream) {
+    if (!x || !signs || !codes || !scales)
+        return fail(FP4Q_ERR_INVALID, "quantize_rht: null pointer");
+    if (rows <= 0 || cols <= 0)
+        return fail(FP4Q_ERR_INVALID, "quantize_rht: rows=%lld cols=%lld", (long long)rows,
+                    (long long)cols);
+    if (axis != FP4Q_BLOCK_ROW && axis != FP4Q_BLOCK_COL)
+        return fail(FP4Q_ERR_INVALID, "quantize_rht: bad axis");
+    if (round != FP4Q_RNE && round != FP4Q_SR)
+        return fail(FP4Q_ERR_INVALID, "quantize_rht: bad round");
+    if (axis == FP4Q_BLOCK_ROW && cols % 32)
+        return fail(FP4Q_ERR_INVALID, "quantize_rht: cols %% 32 != 0 for ROW groups");
+    if (axis == FP4Q_BLOCK_COL && (rows % 32 || cols % 2))
+        return fail(FP4Q_ERR_INVALID, "quantize_rht: COL groups need rows %% 32 == 0, even cols");
+    if (ld_x < cols) return fail(FP4Q_ERR_INVALID, "quantize_rht: ld_x < cols");
+    if (rows > kMaxElems / ld_x) return fail(FP4Q_ERR_INVALID, "quantize_rht: tensor too large");
+    if (axis == FP4Q_BLOCK_COL && rows / 128 >= 65535)
+        return fail(FP4Q_ERR_UNSUPPORTED, "quantize_rht: too many rows");
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || ((uintptr_t)signs % 4) ||
+        ld_x % 8)
+        return fail(FP4Q_ERR_ALIGNMENT,
+                    "quantize_rht: x, codes, scales and the row stride 16-byte aligned, signs 4");
+    return hip_status(fp4q::launch_quantize_rht(x, rows, cols, ld_x, axis == FP4Q_BLOCK_COL, signs,
+                                                round == FP4Q_SR, seed, rng_offset, codes, scales,
+                                                (hipStream_t)stream),
+                      "quantize_rht launch");
+}
+
 }  // extern "C"

@@ -356,13 +356,14 @@ def rht_transform(x, axis, signs):
     v = _np.where(sg[None, :], -v, v).astype(_np.float32)
     v = v.reshape(rows, n // 32, 32)
     s = 1
-    while s < 32:
-        w = v.reshape(rows, n // 32, 32 // (2 * s), 2, s)
-        a = w[:, :, :, 0, :]
-        b = w[:, :, :, 1, :]
-        v = _np.stack([a + b, a - b], axis=3).reshape(rows, n // 32, 32)
-        s *= 2
-    v = (v * RHT_C).astype(_np.float32).reshape(rows, n)
+    with _np.errstate(over="ignore", invalid="ignore"):  # fp32 overflow -> Inf/NaN, as defined
+        while s < 32:
+            w = v.reshape(rows, n // 32, 32 // (2 * s), 2, s)
+            a = w[:, :, :, 0, :]
+            b = w[:, :, :, 1, :]
+            v = _np.stack([a + b, a - b], axis=3).reshape(rows, n // 32, 32)
+            s *= 2
+        v = (v * RHT_C).astype(_np.float32).reshape(rows, n)
     return _np.ascontiguousarray(v.T) if axis == COL else v
 
 

@@ -348,3 +348,23 @@ def test_quantize_2d_validation(L):
         bad = list(args)
         bad[i] = v
         assert q(*bad) == st, (i, v)
+
+
+def test_quantize_rht_validation(L):
+    q = L.fp4q_quantize_rht
+    args = [FAKE, 64, 96, 96, 0, FAKE, 0, ct.c_uint64(0), ct.c_uint64(0), FAKE, FAKE, NUL]
+    for i, v, st in [(2, 80, 1),          # ROW: cols % 32
+                     (4, 2, 1),           # axis
+                     (6, 3, 1),           # round
+                     (5, NUL, 1),         # signs
+                     (3, 90, 1),          # ld_x < cols
+                     (3, 100, 3),         # ld_x % 8
+                     (5, ct.c_void_p(0x10002), 3),
+                     (9, FAKE_MIS, 3)]:
+        bad = list(args)
+        bad[i] = v
+        assert q(*bad) == st, (i, v)
+    bad = list(args)
+    bad[4] = 1                            # COL: rows % 32
+    bad[1] = 48
+    assert q(*bad) == 1

@@ -1,0 +1,94 @@
+"""GPU parity of the random Hadamard transform fused into quantisation
+(fp4q_quantize_rht): codes and scales bit for bit against the oracle (its
+fp32 butterflies in the same order, then its quantiser), both block axes,
+nearest-even and stochastic, over ragged sizes, a padded row stride,
+non-finite groups, and row slabs of the weight-gradient GEMM's operands at
+the LLaMA-1B FFN shape (X 8192 x 2048, dY 8192 x 5632, transformed along the
+token axis with one sign mask)."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_block_scaled_fp4q_amd as fq
+from mxfp4_block_scaled_fp4q_amd import inputs
+from gpu_helpers import assert_same_bits, dev, dev_bf16, host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def sign_mask(n, seed):
+    bits = np.random.default_rng(seed).random(n) < 0.5
+    words = np.zeros((n + 31) // 32, np.uint32)
+    for i in np.nonzero(bits)[0]:
+        words[i >> 5] |= np.uint32(1 << (i & 31))
+    return bits, words
+
+
+def check(orc, xb, xd, axis, rnd, bits, words, seed=0, off=0):
+    print(f"quantize_rht shape={xb.shape} ld={xd.stride(0)} axis={axis} round={rnd} "
+          f"seed={seed} off={off}", flush=True)
+    ax = fq.ROW if axis == "row" else fq.COL
+    r = fq.RNE if rnd == "rne" else fq.SR
+    codes, scales = fq.quantize_rht(xd, dev(words.view(np.int32)), ax, r, seed, off)
+    torch.cuda.synchronize()
+    wc, ws = orc.rht_quantize(xb, orc.ROW if axis == "row" else orc.COL, bits,
+                              orc.RNE if rnd == "rne" else orc.SR, seed, off)
+    assert_same_bits(host_bits(codes), wc, "codes")
+    assert_same_bits(host_bits(scales), ws, "scales")
+
+
+SHAPES = {"row": [(1, 32), (67, 96), (130, 416), (256, 2048)],
+          "col": [(32, 8), (96, 160), (288, 424), (2048, 512)]}
+
+
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("k", range(4))
+def test_quantize_rht_parity(orc, axis, rnd, k):
+    shape = SHAPES[axis][k]
+    xb = inputs.to_bf16_bits(inputs.with_outliers(inputs.student_t(shape, 31 + k), 32 + k,
+                                                  max(1, shape[0] * shape[1] // 250), 40.0))
+    n = shape[1] if axis == "row" else shape[0]
+    bits, words = sign_mask(n, 33 + k)
+    check(orc, xb, dev_bf16(xb), axis, rnd, bits, words, seed=4321 + k, off=3 * k)
+
+
+@pytest.mark.parametrize("axis", ["row", "col"])
+def test_quantize_rht_stride_and_nonfinite(orc, axis):
+    wide = inputs.to_bf16_bits(inputs.normal((96, 128 + 64), 971))
+    wide[40, 64 + 70] = 0x7F80        # +inf
+    wide[3, 64 + 5] = 0xFFC0          # NaN
+    wide[77, 64 + 100] = 0x7F7F       # two of the largest finite bf16 in one row group:
+    wide[77, 64 + 101] = 0x7F7F       # the butterflies overflow fp32 there (ROW)
+    xd = dev_bf16(wide)[:, 64:]
+    xb = np.ascontiguousarray(wide[:, 64:])
+    n = 128 if axis == "row" else 96
+    bits, words = sign_mask(n, 972)
+    for rnd in ("rne", "sr"):
+        check(orc, xb, xd, axis, rnd, bits, words, seed=5)
+
+
+@pytest.mark.parametrize("which", ["X", "dY"])
+def test_quantize_rht_wgrad_operands_slabs(orc, which):
+    # the weight-gradient GEMM contracts over the 8192 tokens: both operands
+    # transformed along rows (COL) with one mask; row slabs checked against
+    # the oracle with the slab's counter offset
+    if which == "X":
+        t, rnd, seed = inputs.ffn_forward()["X"], "rne", 0
+    else:
+        b = inputs.ffn_backward_grad()
+        t, rnd, seed = b["dY"], "sr", b["seed_col"]
+    M, C = t.shape
+    bits, words = sign_mask(M, 973)
+    td = dev_bf16(t)
+    codes, scales = fq.quantize_rht(td, dev(words.view(np.int32)), fq.COL,
+                                    fq.SR if rnd == "sr" else fq.RNE, seed, 0)
+    torch.cuda.synchronize()
+    hc, hs = host_bits(codes), host_bits(scales)
+    for r0 in (0, 4096, M - 128):
+        print(f"wgrad operand {which} slab rows {r0}..{r0 + 128}", flush=True)
+        wc, ws = orc.rht_quantize(np.ascontiguousarray(t[r0:r0 + 128]), orc.COL,
+                                  bits[r0:r0 + 128], orc.SR if rnd == "sr" else orc.RNE, seed,
+                                  r0 * C)
+        assert_same_bits(hc[:, r0 // 2:(r0 + 128) // 2], wc, f"{which} codes @{r0}")
+        assert_same_bits(hs[:, r0 // 32:(r0 + 128) // 32], ws, f"{which} scales @{r0}")
