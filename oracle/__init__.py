@@ -372,3 +372,64 @@ def rht_quantize(x, axis, signs, round=RNE, seed=0, rng_offset=0):
     to the quantiser (layouts, rounding and random counters as quantize)."""
     y = rht_transform(x, axis, signs)
     return quantize(y, 32, axis, round, seed, rng_offset)
+
+
+# --- outlier clamping and compensation (OCC) -------------------------------
+
+def occ_threshold(x, quantile=0.99):
+    """The clamp threshold of the outlier clamping and compensation on the
+    MSRA FP4-training summary page (sec. 三): the `quantile` quantile of |x|
+    over the whole tensor, as the order statistic T = a_j of the ascending
+    magnitudes a_1 <= ... <= a_n with j = ceil(quantile * n) (NaN ranks above
+    every number).  Returns (T as float64, nnz = #{|x| > T})."""
+    xd = bf16_to_f64(x) if _np.asarray(x).dtype == _np.uint16 else _np.asarray(x, _np.float64)
+    a = _np.sort(_np.abs(xd).reshape(-1))            # NaN sorts last
+    n = a.size
+    j = min(max(int(_np.ceil(quantile * n)), 1), n)
+    t = a[j - 1]
+    return t, int(_occ_outliers(xd, t).sum())
+
+
+def _occ_outliers(xd, t):
+    """|x| ranks above T, NaN ranking above every number (so with a finite T
+    the NaN elements are outliers; with a NaN T there are none)."""
+    if _np.isnan(t):
+        return _np.zeros(xd.shape, bool)
+    return (_np.abs(xd) > t) | _np.isnan(xd)
+
+
+def occ_split(x, t):
+    """Clamp and residual (same page, sec. 三 and 六): the outliers (|x| > T,
+    and NaN while T is finite) become sign(x) T (exact in bf16: T is one of x's magnitudes); the
+    residual R = x - clamp(x), nonzero only there, as CSR with columns
+    ascending in each row and fp32 values (the exact difference rounded once
+    to fp32).  x: bf16 bits [rows, cols].  Returns (clamped bf16 bits,
+    row_ptr int64 [rows + 1], col_idx int32, vals float32)."""
+    x = _c(x, _np.uint16)
+    xd = bf16_to_f64(x)
+    out = _occ_outliers(xd, t)
+    tb = _np.uint16(_np.float32(t).view(_np.uint32) >> 16)
+    clamped = _np.where(out, (x & _np.uint16(0x8000)) | tb, x).astype(_np.uint16)
+    resid = xd - bf16_to_f64(clamped)
+    rows, cols = x.shape
+    r_idx, c_idx = _np.nonzero(out)                  # row-major order: rows, then columns
+    row_ptr = _np.zeros(rows + 1, _np.int64)
+    _np.add.at(row_ptr, r_idx + 1, 1)
+    row_ptr = _np.cumsum(row_ptr)
+    vals = round_f32(resid[r_idx, c_idx])
+    return clamped, row_ptr, c_idx.astype(_np.int32), vals
+
+
+def occ_spmm(row_ptr, col_idx, vals, w):
+    """The sparse compensation product R W (float64, exact products; the
+    sum of |terms| alongside): R from occ_split [rows, K], w bf16 bits [K, N]."""
+    wd = bf16_to_f64(_c(w, _np.uint16))
+    rows = row_ptr.size - 1
+    out = _np.zeros((rows, wd.shape[1]), _np.float64)
+    mag = _np.zeros_like(out)
+    for i in range(rows):
+        for e in range(int(row_ptr[i]), int(row_ptr[i + 1])):
+            t = float(vals[e]) * wd[int(col_idx[e])]
+            out[i] += t
+            mag[i] += _np.abs(t)
+    return out, mag
