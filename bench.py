@@ -185,6 +185,23 @@ def main():
     msk = torch.randint(-2 ** 31, 2 ** 31 - 1, ((M + 31) // 32,), generator=gsm,
                         dtype=torch.int64).to(torch.int32).to(dev)
     xrht = (torch.empty((K, M // 2), **u8), torch.empty((K, M // 32), **u8))
+    # outlier clamping and compensation of X (1% clamped): buffers sized by
+    # the bound, the residual's product added into an fp32 output
+    occ_cap = fq.occ_max_nnz(M, K, 0.99)
+    occ = dict(codes=torch.empty((M, K // 2), **u8), scales=torch.empty((M, K // 32), **u8),
+               rp=torch.empty((M + 1,), dtype=torch.int64, device=dev),
+               ci=torch.empty((occ_cap,), dtype=torch.int32, device=dev),
+               v=torch.empty((occ_cap,), dtype=torch.float32, device=dev),
+               thr=torch.empty((8,), dtype=torch.int16, device=dev),
+               ws=torch.empty(fq.lib().fp4q_occ_workspace_bytes(M, K), **u8),
+               y=torch.zeros((M, N), dtype=torch.float32, device=dev))
+
+    def occ_quant():
+        fq._check(fq.lib().fp4q_occ_quantize(
+            fq._ptr(X), M, K, K, 0.99, fq.RNE, 0, 0, fq._ptr(occ["codes"]), fq._ptr(occ["scales"]),
+            fq._ptr(occ["rp"]), fq._ptr(occ["ci"]), fq._ptr(occ["v"]), occ_cap,
+            fq._ptr(occ["thr"]), fq._ptr(occ["ws"]), occ["ws"].numel(), fq._stream(None)))
+
     dyrht = (torch.empty((N, M // 2), **u8), torch.empty((N, M // 32), **u8))
     # timed aside: the unfused dW GEMM and DGE (the DGE kernel's own HBM
     # rate), and the forward GEMM that also quantises Y for a next layer
@@ -208,6 +225,11 @@ def main():
         ("quant_dy_col_rht_sr", lambda: fq.quantize_rht(dY, msk, fq.COL, fq.SR, SR_SEED, 0,
                                                         codes=dyrht[0], scales=dyrht[1]),
          M * N * qb, 0),
+        # six launches: histogram, threshold, clamp + quantise, scan, CSR fill
+        ("occ_quantize_x", occ_quant, M * K * qb, 0),
+        # Y[M, N] += R W: reads and writes the fp32 rows that hold outliers
+        ("occ_spmm", lambda: fq.occ_spmm(occ["rp"], occ["ci"], occ["v"], W, occ["y"]),
+         M * N * 8, 0),
     ]
     step_flops = sum(o[3] for o in ops)
 

@@ -359,6 +359,58 @@ fp4q_status_t fp4q_quantize_rht(const void* x, int64_t rows, int64_t cols, int64
                                 uint8_t* scales, void* stream);
 
 /*
+ * fp4q_occ_quantize -- outlier clamping and compensation (the MSRA
+ * FP4-training summary page, sec. 三: the largest 1% of activation values
+ * are clamped to the 99th-percentile threshold before quantisation, and what
+ * the clamp removes is kept in a sparse matrix handled in high precision;
+ * sec. 六: FP4 main path plus a higher-precision sparse path).  For the bf16
+ * x [rows, cols] with n = rows*cols elements:
+ *   T = the j-th smallest |x| over the whole tensor, j = ceil(quantile * n)
+ *       clamped to [1, n] (an order statistic of the bf16 magnitudes; NaN
+ *       ranks above every number), written to *threshold as bf16 magnitude
+ *       bits if threshold is not NULL;
+ *   outliers: the elements whose |x| ranks above T (with a finite T this
+ *       includes NaN; with a NaN T there are none);
+ *   clamp(x) = sign(x) * T on outliers, x elsewhere (exact in bf16);
+ *   codes, scales: fp4q_quantize(clamp(x), BF16, rows, cols, cols, 32,
+ *       FP4Q_BLOCK_ROW, round, seed, rng_offset) exactly (ROW layout);
+ *   the residual R = x - clamp(x) in CSR: row_ptr int64 [rows + 1],
+ *       col_idx int32 and vals fp32 [row_ptr[rows]], columns ascending within
+ *       a row, each value the fp32 rounding of the exact difference.
+ * The number of outliers is at most n - j = fp4q_occ_max_nnz(rows, cols,
+ * quantile); nnz_cap (the length of col_idx and vals) must be at least that.
+ *   quantile in (0, 1]; cols % 32 == 0; n < 2^32; ld_x >= cols, ld_x % 8 == 0.
+ *   workspace >= fp4q_occ_workspace_bytes(rows, cols) device bytes (16-byte
+ *   aligned; holds a 32768-bin histogram, row counts and a 1-bit outlier
+ *   mask; contents not kept).  x, codes, scales 16-byte aligned; row_ptr
+ *   8-byte, col_idx and vals 4-byte aligned.
+ */
+int64_t fp4q_occ_max_nnz(int64_t rows, int64_t cols, double quantile);
+size_t fp4q_occ_workspace_bytes(int64_t rows, int64_t cols);
+fp4q_status_t fp4q_occ_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                double quantile, fp4q_round_t round, uint64_t seed,
+                                uint64_t rng_offset, uint8_t* codes, uint8_t* scales,
+                                int64_t* row_ptr, int32_t* col_idx, float* vals, int64_t nnz_cap,
+                                uint16_t* threshold, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * fp4q_occ_spmm -- the compensation product of the same passage: for the
+ * residual R [M, K] in the CSR form fp4q_occ_quantize writes,
+ *   Y[i, :] += sum over row i's entries, in CSR order, of R[i,k] * W[k, :]
+ * in fp32 (fused multiply-adds from zero, then one add into Y); rows without
+ * entries leave Y untouched.  Y = Xq Wq (fp4q_gemm of the clamped
+ * activation, fp32 out) + R W is the compensated product.
+ *   w  bf16 [K, N], row stride ld_w >= N (ld_w % 8 == 0);
+ *   y  fp32 [M, N], row stride ld_y >= N (ld_y % 4 == 0), read and written;
+ *   N % 8 == 0; column indices must lie in [0, K) (device data, not checked).
+ *   w, y 16-byte aligned; row_ptr 8-byte, col_idx and vals 4-byte aligned.
+ */
+fp4q_status_t fp4q_occ_spmm(int64_t M, int64_t N, int64_t K, const int64_t* row_ptr,
+                            const int32_t* col_idx, const float* vals, const void* w,
+                            int64_t ld_w, float* y, int64_t ld_y, void* stream);
+
+/*
  * fp4q_hot_channels -- the choice of the hot channels H (outlier-dynamics
  * page, sec. 4.1: the top 9% of channels by quantisation error are kept in
  * high precision, the choice refreshed every 1000 steps).  The error of

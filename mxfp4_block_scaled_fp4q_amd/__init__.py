@@ -26,7 +26,8 @@ EXPORTS = ["fp4q_channel_mask", "fp4q_quantize_masked", "fp4q_gemm_hcp_split",
            "fp4q_gemm_dge", "fp4q_gemm_quant", "fp4q_hcp_workspace_bytes",
            "fp4q_hcp_residual_add",
            "fp4q_gemm_hcp", "fp4q_hot_channels_workspace_bytes", "fp4q_hot_channels",
-           "fp4q_quantize_2d", "fp4q_quantize_rht",
+           "fp4q_quantize_2d", "fp4q_quantize_rht", "fp4q_occ_max_nnz",
+           "fp4q_occ_workspace_bytes", "fp4q_occ_quantize", "fp4q_occ_spmm",
            "fp4q_status_string",
            "fp4q_last_error", "fp4q_abi_version"]
 
@@ -72,6 +73,11 @@ def lib():
             "fp4q_hot_channels_workspace_bytes": (SZ, [I64, I64]),
             "fp4q_quantize_2d": (I32, [P, I64, I64, I64, I32, U64, U64, P, P, P, P, P]),
             "fp4q_quantize_rht": (I32, [P, I64, I64, I64, I32, P, I32, U64, U64, P, P, P]),
+            "fp4q_occ_max_nnz": (I64, [I64, I64, _ct.c_double]),
+            "fp4q_occ_workspace_bytes": (SZ, [I64, I64]),
+            "fp4q_occ_quantize": (I32, [P, I64, I64, I64, _ct.c_double, I32, U64, U64, P, P, P, P,
+                                        P, I64, P, P, SZ, P]),
+            "fp4q_occ_spmm": (I32, [I64, I64, I64, P, P, P, P, I64, P, I64, P]),
             "fp4q_hot_channels": (I32, [P, I64, I64, I64, I32, P, P, P, SZ, P]),
             "fp4q_status_string": (_ct.c_char_p, [I32]),
             "fp4q_last_error": (_ct.c_char_p, []),
@@ -401,3 +407,44 @@ def quantize_rht(x, signs, axis=ROW, rounding=RNE, seed=0, rng_offset=0, codes=N
     _check(lib().fp4q_quantize_rht(_ptr(x), R, C, x.stride(0), axis, _ptr(signs), rounding, seed,
                                    rng_offset, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
+
+
+def occ_max_nnz(rows, cols, quantile=0.99):
+    return int(lib().fp4q_occ_max_nnz(rows, cols, quantile))
+
+
+def occ_quantize(x, quantile=0.99, rounding=RNE, seed=0, rng_offset=0, workspace=None,
+                 stream=None):
+    """Outlier clamping and compensation (fp4q_occ_quantize).  Returns
+    (codes, scales, row_ptr, col_idx, vals, threshold): the ROW block-32
+    quantisation of the clamped x, the residual in CSR (arrays sized by the
+    bound fp4q_occ_max_nnz; row_ptr[-1] entries are used) and T's bf16 bits."""
+    torch = _torch()
+    _need_cuda(x)
+    R, C = x.shape
+    dev = x.device
+    cap = occ_max_nnz(R, C, quantile)
+    codes = torch.empty((R, C // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty((R + 1,), dtype=torch.int64, device=dev)
+    col_idx = torch.empty((max(cap, 1),), dtype=torch.int32, device=dev)
+    vals = torch.empty((max(cap, 1),), dtype=torch.float32, device=dev)
+    thr = torch.empty((8,), dtype=torch.int16, device=dev)
+    if workspace is None:
+        workspace = torch.empty(int(lib().fp4q_occ_workspace_bytes(R, C)), dtype=torch.uint8,
+                                device=dev)
+    _check(lib().fp4q_occ_quantize(_ptr(x), R, C, x.stride(0), quantile, rounding, seed,
+                                   rng_offset, _ptr(codes), _ptr(scales), _ptr(row_ptr),
+                                   _ptr(col_idx), _ptr(vals), cap, _ptr(thr), _ptr(workspace),
+                                   workspace.numel(), _stream(stream)))
+    return codes, scales, row_ptr, col_idx, vals, thr[:1]
+
+
+def occ_spmm(row_ptr, col_idx, vals, w, y, stream=None):
+    """y[M, N] (fp32, in place) += R W for the CSR residual R (fp4q_occ_spmm)."""
+    _need_cuda(w, y)
+    M, N = y.shape
+    K = w.shape[0]
+    _check(lib().fp4q_occ_spmm(M, N, K, _ptr(row_ptr), _ptr(col_idx), _ptr(vals), _ptr(w),
+                               w.stride(0), _ptr(y), y.stride(0), _stream(stream)))
+    return y

@@ -14,7 +14,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp4q.so")
 SOURCES = ["fp4q_api.hip", "quantize.hip", "dequantize.hip", "grad.hip", "gemm_fp4.hip",
            "hcp.hip", "hotsel.hip",
-           "quant2d.hip", "rht.hip"]
+           "quant2d.hip", "rht.hip",
+           "occ.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -1,6 +1,7 @@
 // libfp4q C ABI: host-side validation, status reporting and kernel dispatch.
 // Every entry point checks its arguments before touching the device and
 // launches nothing when it returns an error other than FP4Q_ERR_HIP.
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -493,7 +494,7 @@ fp4q_status_t fp4q_quantize_rht(const void* x, int64_t rows, int64_t cols, int64
         return fail(FP4Q_ERR_INVALID, "quantize_rht: COL groups need rows %% 32 == 0, even cols");
     if (ld_x < cols) return fail(FP4Q_ERR_INVALID, "quantize_rht: ld_x < cols");
     if (rows > kMaxElems / ld_x) return fail(FP4Q_ERR_INVALID, "quantize_rht: tensor too large");
-    if (axis == FP4Q_BLOCK_COL && rows / 128 >= 65535)
+    if (axis == FP4Q_BLOCK_COL && rows / 32 > 65535)
         return fail(FP4Q_ERR_UNSUPPORTED, "quantize_rht: too many rows");
     if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || ((uintptr_t)signs % 4) ||
         ld_x % 8)
@@ -503,6 +504,87 @@ fp4q_status_t fp4q_quantize_rht(const void* x, int64_t rows, int64_t cols, int64
                                                 round == FP4Q_SR, seed, rng_offset, codes, scales,
                                                 (hipStream_t)stream),
                       "quantize_rht launch");
+}
+
+static bool occ_rank(int64_t rows, int64_t cols, double quantile, int64_t* j) {
+    if (rows <= 0 || cols <= 0 || !(quantile > 0.0 && quantile <= 1.0)) return false;
+    const int64_t n = rows * cols;
+    int64_t jj = (int64_t)ceil(quantile * (double)n);
+    if (jj < 1) jj = 1;
+    if (jj > n) jj = n;
+    *j = jj;
+    return true;
+}
+
+int64_t fp4q_occ_max_nnz(int64_t rows, int64_t cols, double quantile) {
+    int64_t j;
+    if (rows > ((int64_t)1 << 32) || cols > ((int64_t)1 << 32) || !occ_rank(rows, cols, quantile, &j))
+        return -1;
+    return rows * cols - j;
+}
+
+size_t fp4q_occ_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return 0;
+    return fp4q::occ_workspace_bytes(rows, cols);
+}
+
+fp4q_status_t fp4q_occ_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                double quantile, fp4q_round_t round, uint64_t seed,
+                                uint64_t rng_offset, uint8_t* codes, uint8_t* scales,
+                                int64_t* row_ptr, int32_t* col_idx, float* vals, int64_t nnz_cap,
+                                uint16_t* threshold, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    if (!x || !codes || !scales || !row_ptr || !workspace)
+        return fail(FP4Q_ERR_INVALID, "occ_quantize: null pointer");
+    if (rows <= 0 || cols <= 0 || cols % 32)
+        return fail(FP4Q_ERR_INVALID, "occ_quantize: rows > 0 and cols a positive multiple of 32");
+    if (rows * cols >= ((int64_t)1 << 32))
+        return fail(FP4Q_ERR_UNSUPPORTED, "occ_quantize: tensors of 2^32 elements or more");
+    int64_t j;
+    if (!occ_rank(rows, cols, quantile, &j))
+        return fail(FP4Q_ERR_INVALID, "occ_quantize: quantile must lie in (0, 1]");
+    if (round != FP4Q_RNE && round != FP4Q_SR) return fail(FP4Q_ERR_INVALID, "occ_quantize: bad round");
+    if (ld_x < cols) return fail(FP4Q_ERR_INVALID, "occ_quantize: ld_x < cols");
+    if (rows > kMaxElems / ld_x) return fail(FP4Q_ERR_INVALID, "occ_quantize: tensor too large");
+    const int64_t bound = rows * cols - j;
+    if (nnz_cap < bound)
+        return fail(FP4Q_ERR_INVALID, "occ_quantize: nnz_cap %lld < %lld (fp4q_occ_max_nnz)",
+                    (long long)nnz_cap, (long long)bound);
+    if (bound > 0 && (!col_idx || !vals))
+        return fail(FP4Q_ERR_INVALID, "occ_quantize: null residual arrays");
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(workspace) ||
+        ld_x % 8 || ((uintptr_t)row_ptr % 8) || ((uintptr_t)col_idx % 4) || ((uintptr_t)vals % 4))
+        return fail(FP4Q_ERR_ALIGNMENT, "occ_quantize: misaligned pointer or row stride");
+    const size_t need = fp4q::occ_workspace_bytes(rows, cols);
+    if (workspace_bytes < need)
+        return fail(FP4Q_ERR_WORKSPACE, "occ_quantize: workspace %zu < %zu bytes", workspace_bytes,
+                    need);
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return fail(FP4Q_ERR_HIP, "occ_quantize: device query failed");
+    return hip_status(fp4q::launch_occ_quantize(x, rows, cols, ld_x, (uint64_t)j, round == FP4Q_SR,
+                                                seed, rng_offset, codes, scales, row_ptr, col_idx,
+                                                vals, threshold, workspace, cus,
+                                                (hipStream_t)stream),
+                      "occ_quantize launch");
+}
+
+fp4q_status_t fp4q_occ_spmm(int64_t M, int64_t N, int64_t K, const int64_t* row_ptr,
+                            const int32_t* col_idx, const float* vals, const void* w,
+                            int64_t ld_w, float* y, int64_t ld_y, void* stream) {
+    if (M <= 0 || N <= 0 || K <= 0) return fail(FP4Q_ERR_INVALID, "occ_spmm: bad sizes");
+    if (!row_ptr || !w || !y) return fail(FP4Q_ERR_INVALID, "occ_spmm: null pointer");
+    if (N % 8) return fail(FP4Q_ERR_INVALID, "occ_spmm: N %% 8 != 0");
+    if (ld_w < N || ld_y < N) return fail(FP4Q_ERR_INVALID, "occ_spmm: ld_w or ld_y < N");
+    if (M > 2147483647LL || N / 2048 >= 65535)
+        return fail(FP4Q_ERR_UNSUPPORTED, "occ_spmm: M or N too large");
+    if (!aligned16(w) || !aligned16(y) || ld_w % 8 || ld_y % 4 || ((uintptr_t)row_ptr % 8) ||
+        ((uintptr_t)col_idx % 4) || ((uintptr_t)vals % 4))
+        return fail(FP4Q_ERR_ALIGNMENT, "occ_spmm: misaligned pointer or row stride");
+    return hip_status(fp4q::launch_occ_spmm(M, N, row_ptr, col_idx, vals, w, ld_w, y, ld_y,
+                                            (hipStream_t)stream),
+                      "occ_spmm launch");
 }
 
 }  // extern "C"

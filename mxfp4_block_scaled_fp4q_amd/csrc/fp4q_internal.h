@@ -103,5 +103,16 @@ hipError_t launch_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_t
 hipError_t launch_quantize_rht(const void* x, int64_t rows, int64_t cols, int64_t ld, bool col,
                                const uint32_t* signs, bool sr, uint64_t seed, uint64_t off,
                                uint8_t* codes, uint8_t* scales, hipStream_t s);
+// Outlier clamping and compensation: threshold (the j-th smallest |x|),
+// clamp + ROW block-32 quantisation, residual CSR; and the residual's
+// product with a bf16 weight added into an fp32 output.
+size_t occ_workspace_bytes(int64_t rows, int64_t cols);
+hipError_t launch_occ_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, uint64_t j,
+                               bool sr, uint64_t seed, uint64_t off, uint8_t* codes,
+                               uint8_t* scales, int64_t* row_ptr, int32_t* col_idx, float* vals,
+                               uint16_t* t_out, void* ws, int n_cus, hipStream_t s);
+hipError_t launch_occ_spmm(int64_t M, int64_t N, const int64_t* row_ptr, const int32_t* col_idx,
+                           const float* vals, const void* w, int64_t ldw, float* y, int64_t ldy,
+                           hipStream_t s);
 
 }  // namespace fp4q

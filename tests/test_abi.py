@@ -368,3 +368,32 @@ def test_quantize_rht_validation(L):
     bad[4] = 1                            # COL: rows % 32
     bad[1] = 48
     assert q(*bad) == 1
+
+
+def test_occ_validation(L):
+    assert L.fp4q_occ_max_nnz(100, 64, ct.c_double(0.99)) == 6400 - 6336
+    assert L.fp4q_occ_max_nnz(100, 64, ct.c_double(1.0)) == 0
+    assert L.fp4q_occ_max_nnz(100, 64, ct.c_double(0.0)) == -1
+    ws = L.fp4q_occ_workspace_bytes(100, 64)
+    q = L.fp4q_occ_quantize
+    args = [FAKE, 100, 64, 64, ct.c_double(0.99), 0, ct.c_uint64(0), ct.c_uint64(0), FAKE, FAKE,
+            FAKE, FAKE, FAKE, 64, NUL, FAKE, ws, NUL]
+    for i, v, st in [(2, 48, 1),                  # cols % 32
+                     (4, ct.c_double(1.5), 1),    # quantile
+                     (4, ct.c_double(0.0), 1),
+                     (5, 2, 1),                   # round
+                     (13, 63, 1),                 # nnz_cap below the bound
+                     (11, NUL, 1),                # col_idx
+                     (16, ws - 1, 4),             # workspace
+                     (3, 60, 1),                  # ld_x
+                     (10, ct.c_void_p(0x10004), 3)]:
+        bad = list(args)
+        bad[i] = v
+        assert q(*bad) == st, (i, v)
+    s = L.fp4q_occ_spmm
+    args = [16, 64, 128, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 64, NUL]
+    for i, v, st in [(1, 60, 1), (7, 32, 1), (9, 32, 1), (3, NUL, 1), (8, FAKE_MIS, 3),
+                     (9, 66, 3)]:
+        bad = list(args)
+        bad[i] = v
+        assert s(*bad) == st, (i, v)
