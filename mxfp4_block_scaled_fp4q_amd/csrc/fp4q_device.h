@@ -27,6 +27,15 @@ __device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
     __builtin_nontemporal_store((v4u){v.x, v.y, v.z, v.w}, (v4u*)p);
 }
 
+// 16-byte load with the non-temporal hint, for inputs a kernel reads once:
+// a streaming read of a tensor that is not in the caches runs faster with it
+// (the ROW quantiser on an 8192 x 5632 bf16 tensor: 6.0 against 5.5 TB/s).
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_nontemporal_load((const v4u*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f32(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f32(w & 0xFFFF0000u); }
 

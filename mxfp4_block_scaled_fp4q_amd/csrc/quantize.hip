@@ -32,7 +32,10 @@ static constexpr int kThreads = 256;
 // ROW
 // ---------------------------------------------------------------------------
 // zmask (optional): one bit per column; set columns are quantised as zeros.
-template <int IN_BF16, int BLOCK, int SR, int UNROLL>
+// MASK (compile-time, so that the unmasked kernel holds no mask loads: a mask
+// load among the data loads made the compiler wait for each data load before
+// issuing the next) says that zmask is given.
+template <int IN_BF16, int BLOCK, int SR, int UNROLL, int MASK>
 __global__ __launch_bounds__(kThreads) void quantize_row_kernel(
     const void* __restrict__ xv, uint32_t total_chunks, FastDiv cpr, int64_t ld, int64_t cols,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t k0, uint32_t k1,
@@ -45,17 +48,44 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(
     uint32_t w[UNROLL][IN_BF16 ? 4 : 8];
     uint32_t gidx[UNROLL];
     uint32_t rowi[UNROLL];
+    // dense rows (ld == cols) without a mask: chunk g starts at element 8 g,
+    // and nearest-even needs no row index, so no division
+    const bool flat = !SR && !MASK && ld == cols;
+    if (flat) {
+        // the input is read once: non-temporal loads, all in flight together
+        // (chunks past the end load chunk 0, unused; no branch around a load)
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const uint32_t g = base + (uint32_t)u * 64u + lane;
+            gidx[u] = g;
+            rowi[u] = 0;
+            const uint4* p = (const uint4*)xv + (IN_BF16 ? 1 : 2) * (g < total_chunks ? g : 0u);
+            const uint4 v0 = load_nt(p);
+            w[u][0] = v0.x;
+            w[u][1] = v0.y;
+            w[u][2] = v0.z;
+            w[u][3] = v0.w;
+            if (!IN_BF16) {
+                const uint4 v1 = load_nt(p + 1);
+                w[u][4 % (IN_BF16 ? 4 : 8)] = v1.x;
+                w[u][5 % (IN_BF16 ? 4 : 8)] = v1.y;
+                w[u][6 % (IN_BF16 ? 4 : 8)] = v1.z;
+                w[u][7 % (IN_BF16 ? 4 : 8)] = v1.w;
+            }
+        }
+    } else {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
         uint32_t g = base + (uint32_t)u * 64u + lane;
         gidx[u] = g;
         uint32_t gg = g < total_chunks ? g : 0u;
-        uint32_t r = fastdiv(gg, cpr);
-        uint32_t cc = gg - r * cpr.d;
+        const uint32_t r = fastdiv(gg, cpr);
+        const uint32_t cc = gg - r * cpr.d;
         rowi[u] = r;
+        // the input is read once: non-temporal loads
         if (IN_BF16) {
             const uint16_t* x = (const uint16_t*)xv;
-            uint4 v = *(const uint4*)(x + (int64_t)r * ld + (int64_t)cc * 8);
+            uint4 v = load_nt(x + (int64_t)r * ld + (int64_t)cc * 8);
             w[u][0] = v.x;
             w[u][1] = v.y;
             w[u][2] = v.z;
@@ -63,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(
         } else {
             const float* x = (const float*)xv;
             const uint4* p = (const uint4*)(x + (int64_t)r * ld + (int64_t)cc * 8);
-            uint4 v0 = p[0], v1 = p[1];
+            uint4 v0 = load_nt(p), v1 = load_nt(p + 1);
             w[u][0] = v0.x;
             w[u][1] = v0.y;
             w[u][2] = v0.z;
@@ -73,8 +103,15 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(
             w[u][6] = v1.z;
             w[u][7] = v1.w;
         }
-        if (zmask) {
-            // the chunk's 8 columns are bits 8 (cc % 4) .. +7 of word cc / 4
+    }
+    }
+    if (MASK) {
+        // after every data load is in flight: the chunk's 8 columns are bits
+        // 8 (cc % 4) .. +7 of word cc / 4
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const uint32_t gg = gidx[u] < total_chunks ? gidx[u] : 0u;
+            const uint32_t cc = gg - rowi[u] * cpr.d;
             const uint32_t mb = (zmask[cc >> 2] >> ((cc & 3) * 8)) & 0xFFu;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -155,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(
     }
 }
 
-template <int IN_BF16, int SR>
+template <int IN_BF16, int SR, int MASK>
 static hipError_t row_dispatch(int block, dim3 grid, hipStream_t s, const void* x, uint32_t tc,
                                FastDiv cpr, int64_t ld, int64_t cols, uint8_t* codes,
                                uint8_t* scales, uint32_t k0, uint32_t k1, uint64_t off,
@@ -163,23 +200,34 @@ static hipError_t row_dispatch(int block, dim3 grid, hipStream_t s, const void* 
     constexpr int U = 4;
     switch (block) {
         case 16:
-            quantize_row_kernel<IN_BF16, 16, SR, U><<<grid, kThreads, 0, s>>>(
+            quantize_row_kernel<IN_BF16, 16, SR, U, MASK><<<grid, kThreads, 0, s>>>(
                 x, tc, cpr, ld, cols, codes, scales, k0, k1, off, zmask);
             break;
         case 32:
-            quantize_row_kernel<IN_BF16, 32, SR, U><<<grid, kThreads, 0, s>>>(
+            quantize_row_kernel<IN_BF16, 32, SR, U, MASK><<<grid, kThreads, 0, s>>>(
                 x, tc, cpr, ld, cols, codes, scales, k0, k1, off, zmask);
             break;
         case 64:
-            quantize_row_kernel<IN_BF16, 64, SR, U><<<grid, kThreads, 0, s>>>(
+            quantize_row_kernel<IN_BF16, 64, SR, U, MASK><<<grid, kThreads, 0, s>>>(
                 x, tc, cpr, ld, cols, codes, scales, k0, k1, off, zmask);
             break;
         default:
-            quantize_row_kernel<IN_BF16, 128, SR, U><<<grid, kThreads, 0, s>>>(
+            quantize_row_kernel<IN_BF16, 128, SR, U, MASK><<<grid, kThreads, 0, s>>>(
                 x, tc, cpr, ld, cols, codes, scales, k0, k1, off, zmask);
             break;
     }
     return hipGetLastError();
+}
+
+template <int IN_BF16, int SR>
+static hipError_t row_dispatch_mask(int block, dim3 grid, hipStream_t s, const void* x,
+                                    uint32_t tc, FastDiv cpr, int64_t ld, int64_t cols,
+                                    uint8_t* codes, uint8_t* scales, uint32_t k0, uint32_t k1,
+                                    uint64_t off, const uint32_t* zmask) {
+    return zmask ? row_dispatch<IN_BF16, SR, 1>(block, grid, s, x, tc, cpr, ld, cols, codes,
+                                                scales, k0, k1, off, zmask)
+                 : row_dispatch<IN_BF16, SR, 0>(block, grid, s, x, tc, cpr, ld, cols, codes,
+                                                scales, k0, k1, off, zmask);
 }
 
 hipError_t launch_quantize_row(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
@@ -192,13 +240,13 @@ hipError_t launch_quantize_row(const void* x, int dtype, int64_t rows, int64_t c
     dim3 grid((tc + per_wg - 1) / per_wg);
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     if (dtype == BF16)
-        return sr ? row_dispatch<1, 1>(block, grid, s, x, tc, cpr, ld, cols, codes, scales, k0,
+        return sr ? row_dispatch_mask<1, 1>(block, grid, s, x, tc, cpr, ld, cols, codes, scales, k0,
                                        k1, off, zmask)
-                  : row_dispatch<1, 0>(block, grid, s, x, tc, cpr, ld, cols, codes, scales, k0,
+                  : row_dispatch_mask<1, 0>(block, grid, s, x, tc, cpr, ld, cols, codes, scales, k0,
                                        k1, off, zmask);
-    return sr ? row_dispatch<0, 1>(block, grid, s, x, tc, cpr, ld, cols, codes, scales, k0, k1,
+    return sr ? row_dispatch_mask<0, 1>(block, grid, s, x, tc, cpr, ld, cols, codes, scales, k0, k1,
                                    off, zmask)
-              : row_dispatch<0, 0>(block, grid, s, x, tc, cpr, ld, cols, codes, scales, k0, k1,
+              : row_dispatch_mask<0, 0>(block, grid, s, x, tc, cpr, ld, cols, codes, scales, k0, k1,
                                    off, zmask);
 }
 
@@ -268,17 +316,24 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
     const bool full = c0 + CPT <= cols;
 
     uint32_t v[RPT][4];
+    if (rows_ok && full) {
+        // all RPT loads in flight together (a per-row choice between this
+        // and the edge forms made the compiler wait between rows)
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int64_t r = r0 + rg * RPT + i;
-        if (rows_ok && full) {
+        for (int i = 0; i < RPT; ++i) {
+            const int64_t r = r0 + rg * RPT + i;
             const uint4 t = IN_BF16 ? *(const uint4*)((const uint16_t*)xv + r * ld + c0)
                                     : *(const uint4*)((const float*)xv + r * ld + c0);
             v[i][0] = t.x;
             v[i][1] = t.y;
             v[i][2] = t.z;
             v[i][3] = t.w;
-        } else if (rows_ok && IN_BF16) {
+        }
+    } else {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int64_t r = r0 + rg * RPT + i;
+        if (rows_ok && IN_BF16) {
             const uint16_t* x = (const uint16_t*)xv + r * ld;
             uint32_t e[8];
 #pragma unroll
@@ -293,6 +348,7 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[i][j] = 0u;
         }
+    }
     }
     if (ROW == 0 && zmask && rows_ok) {
         // one bit per row; set rows are quantised as zeros (the thread's
