@@ -82,10 +82,13 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(
         const uint32_t r = fastdiv(gg, cpr);
         const uint32_t cc = gg - r * cpr.d;
         rowi[u] = r;
-        // the input is read once: non-temporal loads
+        // the input is read once: non-temporal loads, except for the
+        // stochastic form, which is bound by its arithmetic and measured
+        // faster with plain loads (dY 8192 x 5632 cold: 27.4 against 28.6 us)
         if (IN_BF16) {
             const uint16_t* x = (const uint16_t*)xv;
-            uint4 v = load_nt(x + (int64_t)r * ld + (int64_t)cc * 8);
+            const uint4* p = (const uint4*)(x + (int64_t)r * ld + (int64_t)cc * 8);
+            uint4 v = SR ? *p : load_nt(p);
             w[u][0] = v.x;
             w[u][1] = v.y;
             w[u][2] = v.z;
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(
         } else {
             const float* x = (const float*)xv;
             const uint4* p = (const uint4*)(x + (int64_t)r * ld + (int64_t)cc * 8);
-            uint4 v0 = load_nt(p), v1 = load_nt(p + 1);
+            uint4 v0 = SR ? p[0] : load_nt(p), v1 = SR ? p[1] : load_nt(p + 1);
             w[u][0] = v0.x;
             w[u][1] = v0.y;
             w[u][2] = v0.z;
