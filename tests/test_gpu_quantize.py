@@ -130,3 +130,17 @@ def test_outlier_layer_operands(orc):
     d = inputs.outlier_layer()
     run_both(orc, d["X"], 32, fq.ROW)
     run_both(orc, d["W"], 32, fq.COL)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rnd", [fq.RNE, fq.SR])
+def test_row_partial_waves(orc, dtype, rnd):
+    """Dense ROW inputs whose 8-element chunk count leaves a partial wave
+    (and a single chunk): the loads past the last chunk are clamped and
+    their lanes write nothing."""
+    for shape, block in (((1, 16), 16), ((5, 48), 16), ((3, 96), 32), ((7, 128), 64),
+                         ((2, 128), 128)):
+        x = inputs.with_outliers(inputs.normal(shape, 31), 32, 1, 40.0)
+        if dtype == "bf16":
+            x = inputs.to_bf16_bits(x)
+        run_both(orc, x, block, fq.ROW, rnd, 77)
