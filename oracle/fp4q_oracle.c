@@ -28,8 +28,8 @@
  *
  * Readings of points the pages leave open (E8M0 bias, exponent rule, tie rule,
  * saturation, sign of zero, SR in magnitude form, RNG, DGE beyond the grid,
- * HCP residual content) are listed in the design doc's readings table; the code
- * below states each where it is used.
+ * HCP residual content) are fixed by readings of this implementation, and
+ * the code below states each where it is used.
  *
  * Philox4x32 follows Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers:
  * As Easy as 1, 2, 3" (SC'11), written from that paper's description.
