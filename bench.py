@@ -291,7 +291,9 @@ def main():
 
     def op_stats(ts, nbytes, nflops):
         us = float(np.mean(ts))
-        d = {"us": round(us, 2), "us_min": round(float(np.min(ts)), 2)}
+        d = {"us": round(us, 2), "us_min": round(float(np.min(ts)), 2),
+             "us_median": round(float(np.median(ts)), 2),
+             "us_p10": round(float(np.percentile(ts, 10)), 2)}
         if nflops:
             d["TFLOPS"] = round(nflops / (us * 1e-6) / 1e12, 1)
             d["frac_fp4_peak"] = round(d["TFLOPS"] / PEAK_FP4_TFLOPS, 4)
@@ -329,7 +331,9 @@ def main():
                 "traffic": measured_traffic(),
                 "kernel": "gemm_fp4_kernel 8192x5632x2048 bf16 out",
                 "per_launch_flops": fwd_flops, "launch_us_mean": round(fwd_mean_us, 2),
-                "launch_us_min": round(float(np.min(fwd_us)), 2)}
+                "launch_us_min": round(float(np.min(fwd_us)), 2),
+                "launch_us_median": round(float(np.median(fwd_us)), 2),
+                "launch_us_p10": round(float(np.percentile(fwd_us, 10)), 2)}
     q = per_op["quant_dy_dual_sr"]
     qr = per_op["quant_x_dual"]
     quant = {"quant_bf16_dual_rne_GBps": qr["GBps"], "quant_bf16_dual_rne_frac": qr["frac_hbm_peak"],
