@@ -173,6 +173,12 @@ __global__ __launch_bounds__(kRhtThreads) void rht_col_kernel(
         const int64_t b = (int64_t)blockIdx.y * rb_per + t;
         if (b >= nb) break;  // uniform over the workgroup
         const int64_t r0 = b * 32;
+        // this group's 32 rows are loaded first, so their latency passes
+        // while the stochastic bits are filled
+        uint32_t xw[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            xw[i] = cok ? *(const uint32_t*)(x + (r0 + i) * ld + c) : 0u;
         if (SR) {
             __syncthreads();  // the previous group row's bits are consumed
 #pragma unroll
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(kRhtThreads) void rht_col_kernel(
         const uint32_t sg = signs[b];
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-            const uint32_t w = *(const uint32_t*)(x + (r0 + i) * ld + c);
+            const uint32_t w = xw[i];
             const float lo = bf16_lo(w), hi = bf16_hi(w);
             const bool neg = (sg >> i) & 1u;
             v0[i] = neg ? -lo : lo;
