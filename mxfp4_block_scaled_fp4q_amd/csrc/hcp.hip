@@ -31,13 +31,22 @@
 //   Y = Xq' Wq' + X_H W_H,  one kernel, K' = |H| padded to 32.
 //
 // Kernels:
-//  * hcp_gather_x: one lane = 8 consecutive K' slots of one row of A'.
+//  * hcp_gather_x_rows: a workgroup stages a few whole rows of X (and of its
+//    codes and scales) in LDS with coalesced 16-byte loads, then each lane
+//    forms 8 consecutive K' slots of a row of A' from LDS.  The hot columns
+//    are scattered over each row, so gathering them straight from HBM costs
+//    one address per element (the load path, not HBM, was the limit); a row
+//    read whole costs a few full-line loads.
+//  * hcp_gather_x: one lane = 8 consecutive K' slots of one row of A', read
+//    straight from global memory (rows too long to stage in LDS).
 //  * hcp_gather_w: one lane = one column j and 8 consecutive K' slots; lanes
 //    of a wave take consecutive j, so the reads of W's hot rows coalesce.
 //  * the residual GEMM runs on the FP4 GEMM's kernel instantiated for bf16
 //    operands (v_mfma_f32_32x32x16_bf16: lane l supplies row l % 32, K
 //    elements [8 (l / 32), 8 (l / 32) + 8) -- the same 16 bytes per lane as
 //    an FP4 fragment), adding into the fp32 Y in its epilogue.
+#include <algorithm>
+
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -103,6 +112,68 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_x(const uint16_t* __restr
     *(uint4*)(a + i * kp + h0) = o;
 }
 
+// Row-staged gather: dynamic LDS holds the hot list (n_hot int32, rounded
+// to 16 bytes), then RPW rows of row_bytes each: K bf16 of X, and with_q
+// also K/2 code bytes and K/32 scale bytes.  K % 32 == 0, so the X and code
+// rows are whole 16-byte words (the scale bytes are copied one by one).  A
+// hot index outside [0, K) (a broken caller precondition) reads as zero.
+__global__ __launch_bounds__(kThreads) void hcp_gather_x_rows(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ xqc,
+    const uint8_t* __restrict__ xqs, const int32_t* __restrict__ hot, int n_hot, int64_t M,
+    int64_t K, int64_t kp, uint16_t* __restrict__ a, int with_q, int rpw, int hot_bytes,
+    int row_bytes) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    int32_t* hs = (int32_t*)smem;
+    const int tid = threadIdx.x;
+    const int64_t i0 = (int64_t)blockIdx.x * rpw;
+    for (int h = tid; h < n_hot; h += kThreads) hs[h] = hot[h];
+    const int xw = (int)(K * 2 / 16), cw = (int)(K / 2 / 16), sw = (int)(K / 32);
+    for (int r = 0; r < rpw; ++r) {
+        const int64_t i = i0 + r;
+        if (i >= M) break;
+        uint8_t* row = smem + hot_bytes + r * row_bytes;
+        const uint4* xs = (const uint4*)(x + i * K);
+        for (int c = tid; c < xw; c += kThreads) ((uint4*)row)[c] = xs[c];
+        if (with_q) {
+            const uint4* cs = (const uint4*)(xqc + i * (K / 2));
+            for (int c = tid; c < cw; c += kThreads) ((uint4*)(row + K * 2))[c] = cs[c];
+            const uint8_t* ss = xqs + i * (K / 32);
+            for (int c = tid; c < sw; c += kThreads) row[K * 2 + K / 2 + c] = ss[c];
+        }
+    }
+    __syncthreads();
+    const int cpr = (int)(kp / 8);
+    for (int t = tid; t < rpw * cpr; t += kThreads) {
+        const int r = t / cpr;
+        const int64_t i = i0 + r;
+        if (i >= M) break;
+        const int h0 = (t - r * cpr) * 8;
+        const uint8_t* row = smem + hot_bytes + r * row_bytes;
+        const uint16_t* xr = (const uint16_t*)row;
+        uint32_t v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int h = h0 + q;
+            uint32_t bits = 0;
+            if (h < n_hot) {
+                const uint32_t c = (uint32_t)hs[h];
+                bits = c < (uint64_t)K ? xr[c] : 0u;
+            } else if (with_q && h < 2 * n_hot) {
+                const uint32_t c = (uint32_t)hs[h - n_hot];
+                if (c < (uint64_t)K)
+                    bits = f32_to_bf16_bits(deq_nibble(row + K * 2, row + K * 2 + K / 2, (int)c));
+            }
+            v[q] = bits;
+        }
+        uint4 o;
+        o.x = v[0] | (v[1] << 16);
+        o.y = v[2] | (v[3] << 16);
+        o.z = v[4] | (v[5] << 16);
+        o.w = v[6] | (v[7] << 16);
+        *(uint4*)(a + i * kp + h0) = o;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void hcp_gather_w(const uint16_t* __restrict__ w,
                                                          const uint8_t* __restrict__ wqc,
                                                          const uint8_t* __restrict__ wqs,
@@ -146,10 +217,23 @@ static hipError_t gather_hot(int64_t M, int64_t N, int64_t K, const void* x, con
     uint16_t* ap = (uint16_t*)ws;
     uint16_t* bp = (uint16_t*)((uint8_t*)ws + round_up((size_t)(M * kp * 2), 256));
     {
-        const int64_t total = M * (kp / 8);
-        dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
-        hcp_gather_x<<<grid, kThreads, 0, s>>>((const uint16_t*)x, xqc, xqs, hot, n_hot, M, K, kp,
-                                               ap, with_q);
+        // rows staged whole in LDS when a row and the hot list fit in 40 KB
+        const int64_t hot_bytes = (int64_t)round_up((size_t)n_hot * 4, 16);
+        const int64_t row_bytes = (int64_t)round_up((size_t)(K * 2 + (with_q ? K / 2 + K / 32 : 0)), 16);
+        constexpr int64_t kLdsBudget = 40 * 1024;
+        if (hot_bytes + row_bytes <= kLdsBudget) {
+            const int rpw = (int)std::min<int64_t>(4, (kLdsBudget - hot_bytes) / row_bytes);
+            const size_t lds = (size_t)(hot_bytes + rpw * row_bytes);
+            dim3 grid((unsigned)((M + rpw - 1) / rpw));
+            hcp_gather_x_rows<<<grid, kThreads, lds, s>>>((const uint16_t*)x, xqc, xqs, hot, n_hot,
+                                                          M, K, kp, ap, with_q, rpw, (int)hot_bytes,
+                                                          (int)row_bytes);
+        } else {
+            const int64_t total = M * (kp / 8);
+            dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
+            hcp_gather_x<<<grid, kThreads, 0, s>>>((const uint16_t*)x, xqc, xqs, hot, n_hot, M, K,
+                                                   kp, ap, with_q);
+        }
     }
     {
         dim3 grid((unsigned)((N + 63) / 64), (unsigned)((kp / 8 + 3) / 4));
