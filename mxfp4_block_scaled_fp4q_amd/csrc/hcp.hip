@@ -39,8 +39,12 @@
 //    read whole costs a few full-line loads.
 //  * hcp_gather_x: one lane = 8 consecutive K' slots of one row of A', read
 //    straight from global memory (rows too long to stage in LDS).
+//  * hcp_gather_w_rows: a workgroup forms 8 rows of B' from LDS-staged
+//    pieces (the hot rows' values at those 8 columns, and Wq's 8 K-major code
+//    and scale rows read whole).
 //  * hcp_gather_w: one lane = one column j and 8 consecutive K' slots; lanes
-//    of a wave take consecutive j, so the reads of W's hot rows coalesce.
+//    of a wave take consecutive j, so the reads of W's hot rows coalesce
+//    (used where the staged pieces do not fit in LDS).
 //  * the residual GEMM runs on the FP4 GEMM's kernel instantiated for bf16
 //    operands (v_mfma_f32_32x32x16_bf16: lane l supplies row l % 32, K
 //    elements [8 (l / 32), 8 (l / 32) + 8) -- the same 16 bytes per lane as
@@ -112,9 +116,22 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_x(const uint16_t* __restr
     *(uint4*)(a + i * kp + h0) = o;
 }
 
-// Row-staged gather: dynamic LDS holds the hot list (n_hot int32, rounded
-// to 16 bytes), then RPW rows of row_bytes each: K bf16 of X, and with_q
-// also K/2 code bytes and K/32 scale bytes.  K % 32 == 0, so the X and code
+// LDS table of the column each of the kp slots of a gathered row takes:
+// slot h < n_hot the hot column hot[h], slot n_hot + h (with_q) the same
+// column's quantised copy, -1 (zero) for the padding and for an index outside
+// [0, K) (a broken caller precondition).  The caller synchronises.
+__device__ __forceinline__ void fill_slot_columns(int32_t* hs, const int32_t* __restrict__ hot,
+                                                  int n_hot, int64_t kp, int with_q, int64_t K) {
+    for (int h = threadIdx.x; h < kp; h += kThreads) {
+        int src = h < n_hot ? h : (with_q && h < 2 * n_hot ? h - n_hot : -1);
+        int c = src >= 0 ? hot[src] : -1;
+        hs[h] = (c >= 0 && c < K) ? c : -1;
+    }
+}
+
+// Row-staged gather: dynamic LDS holds the slot -> column table (kp int32),
+// then RPW rows of row_bytes each: K bf16 of X, and with_q also K/2 code
+// bytes and K/32 scale bytes.  K % 32 == 0, so the X and code
 // rows are whole 16-byte words (the scale bytes are copied one by one).  A
 // hot index outside [0, K) (a broken caller precondition) reads as zero.
 __global__ __launch_bounds__(kThreads) void hcp_gather_x_rows(
@@ -123,10 +140,10 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_x_rows(
     int64_t K, int64_t kp, uint16_t* __restrict__ a, int with_q, int rpw, int hot_bytes,
     int row_bytes) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    int32_t* hs = (int32_t*)smem;
+    int32_t* hs = (int32_t*)smem;  // slot -> column of X (-1: zero), kp entries
     const int tid = threadIdx.x;
     const int64_t i0 = (int64_t)blockIdx.x * rpw;
-    for (int h = tid; h < n_hot; h += kThreads) hs[h] = hot[h];
+    fill_slot_columns(hs, hot, n_hot, kp, with_q, K);
     const int xw = (int)(K * 2 / 16), cw = (int)(K / 2 / 16), sw = (int)(K / 32);
     for (int r = 0; r < rpw; ++r) {
         const int64_t i = i0 + r;
@@ -150,18 +167,20 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_x_rows(
         const int h0 = (t - r * cpr) * 8;
         const uint8_t* row = smem + hot_bytes + r * row_bytes;
         const uint16_t* xr = (const uint16_t*)row;
+        // the chunk's 8 slot columns as two 16-byte reads
+        const int4 c0 = *(const int4*)(hs + h0), c1 = *(const int4*)(hs + h0 + 4);
+        const int cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
         uint32_t v[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int h = h0 + q;
+            const int c = cs[q];
             uint32_t bits = 0;
-            if (h < n_hot) {
-                const uint32_t c = (uint32_t)hs[h];
-                bits = c < (uint64_t)K ? xr[c] : 0u;
-            } else if (with_q && h < 2 * n_hot) {
-                const uint32_t c = (uint32_t)hs[h - n_hot];
-                if (c < (uint64_t)K)
-                    bits = f32_to_bf16_bits(deq_nibble(row + K * 2, row + K * 2 + K / 2, (int)c));
+            if (c >= 0) {
+                if (h < n_hot)
+                    bits = xr[c];
+                else
+                    bits = f32_to_bf16_bits(deq_nibble(row + K * 2, row + K * 2 + K / 2, c));
             }
             v[q] = bits;
         }
@@ -206,6 +225,96 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_w(const uint16_t* __restr
     *(uint4*)(b + j * kp + h0) = o;
 }
 
+// Row-staged gather of B' = [W_H ; -Wq_H]^T (with_q): a workgroup forms
+// JB = 8 consecutive rows j of B'.  Dynamic LDS holds the slot -> column
+// table (kp int32), the hot rows' values W[hot[h], j0 .. j0+7] transposed to
+// [8][n_hot rounded up to 8] (read 16 bytes per hot row when the rows allow)
+// and the 8 K-major code rows (K/2 bytes each) and scale rows (K/32 bytes
+// each) of Wq; the output rows then leave as consecutive 16-byte chunks.
+// K % 32 == 0.  A hot index outside [0, K) reads as zero.
+__global__ __launch_bounds__(kThreads) void hcp_gather_w_rows(
+    const uint16_t* __restrict__ w, const uint8_t* __restrict__ wqc,
+    const uint8_t* __restrict__ wqs, const int32_t* __restrict__ hot, int n_hot, int64_t N,
+    int64_t K, int64_t kp, uint16_t* __restrict__ b, int with_q, int hot_bytes, int wh_bytes) {
+    constexpr int JB = 8;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    int32_t* hs = (int32_t*)smem;                  // slot -> column (kp entries)
+    uint16_t* wh = (uint16_t*)(smem + hot_bytes);  // [JB][hp]: W[hot[h], j0 + jj]
+    const int hp = wh_bytes / (2 * JB);            // n_hot rounded up to 8
+    uint8_t* cr = smem + hot_bytes + wh_bytes;      // [JB][K/2] codes, then [JB][K/32] scales
+    uint8_t* sr = cr + JB * (K / 2);
+    const int tid = threadIdx.x;
+    const int64_t j0 = (int64_t)blockIdx.x * JB;
+    const int nj = (int)std::min<int64_t>(JB, N - j0);
+    fill_slot_columns(hs, hot, n_hot, kp, 1, K);
+    __syncthreads();
+    const bool vec = (N % 8) == 0 && nj == JB;  // 16-byte aligned, whole
+    for (int h = tid; h < hp; h += kThreads) {
+        const int c = h < n_hot ? hs[h] : -1;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (c >= 0) {
+            const uint16_t* src = w + (int64_t)c * N + j0;
+            if (vec) {
+                v = *(const uint4*)src;
+            } else {
+                uint32_t e[JB];
+#pragma unroll
+                for (int q = 0; q < JB; ++q) e[q] = q < nj ? (uint32_t)src[q] : 0u;
+                v = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                               e[6] | (e[7] << 16));
+            }
+        }
+        const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < JB; ++q) wh[q * hp + h] = (uint16_t)(e[q >> 1] >> (16 * (q & 1)));
+    }
+    if (with_q) {
+        const int cw = (int)(K / 2 / 16);
+        for (int t = tid; t < nj * cw; t += kThreads) {
+            const int jj = t / cw, c = t - jj * cw;
+            ((uint4*)(cr + jj * (K / 2)))[c] = ((const uint4*)(wqc + (j0 + jj) * (K / 2)))[c];
+        }
+        const int sw = (int)(K / 32);
+        for (int t = tid; t < nj * sw; t += kThreads) {
+            const int jj = t / sw, c = t - jj * sw;
+            sr[jj * sw + c] = wqs[(j0 + jj) * sw + c];
+        }
+    }
+    __syncthreads();
+    const int cpr = (int)(kp / 8);
+    for (int t = tid; t < nj * cpr; t += kThreads) {
+        const int jj = t / cpr;
+        const int h0 = (t - jj * cpr) * 8;
+        const int4 c0 = *(const int4*)(hs + h0), c1 = *(const int4*)(hs + h0 + 4);
+        const int cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        // this row's W values of slots h0 .. h0+7 (read whole when all of
+        // them are hot slots)
+        uint4 wv = make_uint4(0u, 0u, 0u, 0u);
+        if (h0 + 8 <= hp) wv = *(const uint4*)(wh + jj * hp + h0);
+        const uint32_t we[4] = {wv.x, wv.y, wv.z, wv.w};
+        uint32_t v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int h = h0 + q;
+            const int c = cs[q];
+            uint32_t bits = 0;
+            if (c >= 0) {
+                if (h < n_hot)
+                    bits = (we[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
+                else
+                    bits = f32_to_bf16_bits(-deq_nibble(cr + jj * (K / 2), sr + jj * (K / 32), c));
+            }
+            v[q] = bits;
+        }
+        uint4 o;
+        o.x = v[0] | (v[1] << 16);
+        o.y = v[2] | (v[3] << 16);
+        o.z = v[4] | (v[5] << 16);
+        o.w = v[6] | (v[7] << 16);
+        *(uint4*)(b + (j0 + jj) * kp + h0) = o;
+    }
+}
+
 // Gathers the hot operands into the workspace: A' [M, kp] then B' [N, kp]
 // (with_q: [X_H | Xq_H], [W_H ; -Wq_H]; else X_H, W_H alone).
 static hipError_t gather_hot(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,
@@ -218,7 +327,7 @@ static hipError_t gather_hot(int64_t M, int64_t N, int64_t K, const void* x, con
     uint16_t* bp = (uint16_t*)((uint8_t*)ws + round_up((size_t)(M * kp * 2), 256));
     {
         // rows staged whole in LDS when a row and the hot list fit in 40 KB
-        const int64_t hot_bytes = (int64_t)round_up((size_t)n_hot * 4, 16);
+        const int64_t hot_bytes = kp * 4;  // the slot -> column table
         const int64_t row_bytes = (int64_t)round_up((size_t)(K * 2 + (with_q ? K / 2 + K / 32 : 0)), 16);
         constexpr int64_t kLdsBudget = 40 * 1024;
         if (hot_bytes + row_bytes <= kLdsBudget) {
@@ -236,9 +345,21 @@ static hipError_t gather_hot(int64_t M, int64_t N, int64_t K, const void* x, con
         }
     }
     {
-        dim3 grid((unsigned)((N + 63) / 64), (unsigned)((kp / 8 + 3) / 4));
-        hcp_gather_w<<<grid, kThreads, 0, s>>>((const uint16_t*)w, wqc, wqs, hot, n_hot, N, K, kp,
-                                               bp, with_q);
+        // eight rows of B' per workgroup, staged in LDS, when they fit in 40 KB
+        // (with_q only: W's hot rows alone are read coalesced by the kernel below)
+        const int64_t hot_bytes = kp * 4;
+        const int64_t wh_bytes = (int64_t)round_up((size_t)n_hot, 8) * 16;
+        const int64_t q_bytes = 8 * (K / 2 + K / 32);
+        if (with_q && hot_bytes + wh_bytes + q_bytes <= 40 * 1024) {
+            dim3 grid((unsigned)((N + 7) / 8));
+            hcp_gather_w_rows<<<grid, kThreads, (size_t)(hot_bytes + wh_bytes + q_bytes), s>>>(
+                (const uint16_t*)w, wqc, wqs, hot, n_hot, N, K, kp, bp, with_q, (int)hot_bytes,
+                (int)wh_bytes);
+        } else {
+            dim3 grid((unsigned)((N + 63) / 64), (unsigned)((kp / 8 + 3) / 4));
+            hcp_gather_w<<<grid, kThreads, 0, s>>>((const uint16_t*)w, wqc, wqs, hot, n_hot, N, K,
+                                                   kp, bp, with_q);
+        }
     }
     *ap_out = ap;
     *bp_out = bp;
