@@ -354,10 +354,10 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
     }
     }
     if (ROW == 0 && zmask && rows_ok) {
-        // one bit per row; set rows are quantised as zeros (the thread's
-        // RPT = 8 rows start at a multiple of 8: one byte of one word)
+        // one bit per row; set rows are quantised as zeros (the thread's RPT
+        // rows start at a multiple of RPT, so their bits lie in one word)
         const int64_t rf = r0 + rg * RPT;
-        const uint32_t mb = (zmask[rf >> 5] >> (rf & 31)) & 0xFFu;
+        const uint32_t mb = (zmask[rf >> 5] >> (rf & 31)) & ((1u << RPT) - 1u);
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
             if ((mb >> i) & 1u)
@@ -629,13 +629,17 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
     }
 }
 
-// Rows per thread of the column-pass tile: 8, so a 128-row tile.  The
-// stochastic passes need the registers; the nearest-even ones measured
-// 10-20% faster at the layer's X and W sizes (twice the workgroups overlap
-// their load, convert and store phases) and equal at dY's.
+// Rows per thread of the column-pass tile: 8 (a 128-row tile) for the fused
+// passes and the stochastic ones, 16 (a 256-row tile, whole 128-byte lines
+// of codes per column) for the nearest-even column pass alone.  The
+// stochastic passes need the registers; the fused nearest-even ones measured
+// 10-20% faster with 8 at the layer's X and W sizes (twice the workgroups
+// overlap their load, convert and store phases); the column pass alone on
+// the 13B-shaped weight (5120 x 13824) measured 35.6 us with 8 and 34.2 us
+// with 16.
 template <int SR, int ROW>
 struct ColRows {
-    static constexpr int value = 8;
+    static constexpr int value = (SR == 0 && ROW == 0) ? 16 : 8;
 };
 
 template <int IN_BF16, int SR, int AL, int ROW>
