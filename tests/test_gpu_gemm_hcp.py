@@ -255,7 +255,12 @@ def test_outlier_layer_gemm_and_hcp(orc):
 
 
 @pytest.mark.parametrize("M,N,K,n_hot", [(64, 96, 256, 23), (300, 257, 512, 46),
-                                         (1, 33, 128, 1), (128, 128, 256, 256)])
+                                         (1, 33, 128, 1), (128, 128, 256, 256),
+                                         # rows too long to stage in LDS: both gathers
+                                         # read global memory directly
+                                         (64, 40, 16384, 37),
+                                         # X's rows staged, W's pieces too large
+                                         (48, 40, 8192, 500)])
 def test_hcp_small(orc, M, N, K, n_hot):
     x = inputs.to_bf16_bits(inputs.normal((M, K), M + K))
     w = inputs.to_bf16_bits(inputs.normal((K, N), N + K, 0.02))
@@ -291,7 +296,8 @@ def test_hcp_empty_is_noop(orc):
 
 @pytest.mark.parametrize("M,N,K,n_hot,ld_pad", [(64, 96, 256, 23, 0), (300, 257, 512, 46, 3),
                                                 (1, 33, 128, 1, 0), (128, 128, 256, 256, 0),
-                                                (513, 260, 384, 0, 1)])
+                                                (513, 260, 384, 0, 1), (64, 40, 16384, 37, 0),
+                                                (48, 40, 8192, 500, 2)])
 def test_gemm_hcp_single_kernel(orc, M, N, K, n_hot, ld_pad):
     """fp4q_gemm_hcp: Y = Xq Wq + residual in one kernel, against the oracle's
     base GEMM plus its residual entries, over the sum of both bounds; columns
