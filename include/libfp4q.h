@@ -72,14 +72,25 @@ typedef enum { FP4Q_STE = 0, FP4Q_DGE = 1 } fp4q_grad_t;
  *            FP4Q_BLOCK_COL: block j of column c = rows [j*block, (j+1)*block);
  *              codes [cols, rows/2] and scales [cols, rows/block], i.e. the
  *              K-major quantisation of x^T; needs rows % block == 0.
- *   round    FP4Q_RNE: nearest, ties to the even code; FP4Q_SR: stochastic
- *            rounding floor + (u < frac) (low-precision overview page,
- *            sec. 3.2) between the two neighbouring E2M1 values, with
- *            u = 16 random bits from Philox4x32-10 (Salmon et al., SC'11):
- *            key = seed, counter = (pos >> 3), bits (pos & 7) of the output
- *            as 16-bit lanes, pos = r*cols + c + rng_offset (the element's
- *            logical row-major index in x plus the offset).  A row shard
- *            starting at row r0 reproduces the unsharded result with
+ *   round    FP4Q_RNE: nearest, ties to the even code.
+ *            FP4Q_SR: stochastic rounding (low-precision overview page,
+ *            sec. 3.2: round up with probability equal to the fractional
+ *            distance) between the two neighbouring E2M1 magnitudes
+ *            lo <= m < hi of m = |x/s|, at 16-bit resolution.  With
+ *            frac = (m - lo) / (hi - lo), F = floor(frac * 2^16) and u the
+ *            element's 16 random bits, the magnitude becomes hi iff
+ *              u + F >= 2^16        (a carry out of 16 bits),
+ *            equivalently (0xFFFF - u) < F: the page's "rand < frac" with
+ *            rand = (0xFFFF - u) / 2^16 and frac truncated to 16 bits, so
+ *            P(hi) = F / 2^16.  This is NOT the rule u < frac * 2^16: for a
+ *            given u the two disagree on up to ~90% of the u values (their
+ *            probabilities agree within 2^-16).  m >= 6 gives 6; the sign is
+ *            kept.  u: Philox4x32-10 (Salmon et al., SC'11) with key = seed,
+ *            counter = (pos >> 3) in words 0-1 (words 2-3 zero), and 16-bit
+ *            lane (pos & 7) of the output (word lane/2, low half for even
+ *            lanes), pos = r*cols + c + rng_offset (the element's logical
+ *            row-major index in x plus the offset).  A row shard starting at
+ *            row r0 reproduces the unsharded result with
  *            rng_offset = r0*cols.  Ignored for RNE.
  *   |x/s| > 6 saturates to 6.  A block holding NaN or Inf gets scale 0xFF and
  *   all-zero codes.  The sign bit is kept (negative values that round to 0
@@ -329,17 +340,21 @@ fp4q_status_t fp4q_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_
  * (the recipe on the outlier-dynamics page, sec. 4.1, transforms the
  * backward pass's operands before quantising them).  Along the block axis,
  * each group of 32 values x (the group of one quantisation block) becomes
- *   y = c * H32 * D * x,  c = 2^-2.5 rounded to fp32,
+ *   y = 2^-2.5 * H32 * D * x,
  * with H32 the natural-order (Sylvester) Hadamard matrix, entries
  * (-1)^popcount(i & j), and D = diag(-1 where the sign bit of the position is
- * set, else +1).  y is evaluated in fp32 as butterflies (a, b) -> (a + b,
- * a - b) on pairs (i, i + s) with bit s of i clear, for s = 1, 2, 4, 8, 16 in
- * that order, then multiplied by c; y is then quantised exactly as
- * fp4q_quantize quantises an fp32 tensor (block 32, same layouts, rounding
- * and random counters r*cols + c + rng_offset).  c * H32 is orthogonal up to
- * rounding: a GEMM whose two operands are transformed along their shared
- * contraction axis with the same sign mask approximates the untransformed
- * product (no correction factor).
+ * set, else +1), so 2^-2.5 * H32 is orthogonal: a GEMM whose two operands are
+ * transformed along their shared contraction axis with the same sign mask
+ * approximates the untransformed product (no correction factor).  y is
+ * evaluated in fp32 (five levels of butterflies (a, b) -> (a + b, a - b),
+ * then the product by 2^-2.5 rounded to fp32), so each value is within
+ * 8 * 2^-24 * 2^-2.5 * sum|x| (+ 2^-149) of the exact y; the fp32 values are
+ * then quantised exactly as fp4q_quantize quantises an fp32 tensor (block
+ * 32, same layouts, rounding and random counters r*cols + c + rng_offset).
+ * The codes and scales are therefore those of the exact y wherever that
+ * bound crosses no rounding or scale boundary (nearly every element), and
+ * one of the two neighbouring results elsewhere; the evaluation order is
+ * fixed, so results are deterministic.
  *   x      bf16 [rows, cols], row stride ld_x >= cols (multiple of 8).
  *   axis   FP4Q_BLOCK_ROW: groups along columns, cols % 32 == 0; codes
  *            [rows, cols/2], scales [rows, cols/32].

@@ -5,8 +5,10 @@
 // 16..128 elements (MXFP4 tutorial page, sec. 2.1 and 4.1); E2M1 elements on
 // [-6, 6] (outlier-dynamics page, sec. 1.1; MSRA FP4-training summary page,
 // sec. 一); 8-bit exponent-only scale (low-precision overview page, sec. 1.1);
-// stochastic rounding floor + (rand < frac) (same page, sec. 3.2) with a
-// counter-based Philox4x32-10 stream indexed by the element's logical position.
+// stochastic rounding (same page, sec. 3.2: up with probability equal to the
+// fractional distance) at 16-bit resolution: up iff u + floor(frac * 2^16)
+// carries out of 16 bits, u from a counter-based Philox4x32-10 stream indexed
+// by the element's logical position.
 //
 // Two kernels, both HBM-streaming:
 //  * quantize_row_kernel: blocks along the contiguous dim.  Each lane owns 8

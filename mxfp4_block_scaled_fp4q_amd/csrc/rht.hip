@@ -2,16 +2,17 @@
 // the outlier-dynamics page, sec. 4.1, transforms backward operands before
 // quantising them).  Along the block axis, each group of 32 values becomes
 //
-//   y = c * H32 * D * x,   c = fl32(2^-2.5),
+//   y = 2^-2.5 * H32 * D * x,
 //
 // D = diag(+-1) from a caller-given sign mask over the axis, H32 the natural
-// (Sylvester) order Hadamard matrix.  c * H32 is orthogonal up to rounding,
-// so a GEMM whose two operands are transformed along their shared
-// contraction axis with the same signs keeps its product.  The transform is
-// evaluated in fp32 as butterflies (a, b) -> (a + b, a - b) on pairs
-// (i, i + s) with bit s of i clear, s = 1, 2, 4, 8, 16 in that order, then
-// the product by c: a fixed sequence of correctly rounded operations, so the
-// values the codes are decided on are reproducible bit for bit.  The block's
+// (Sylvester) order Hadamard matrix.  2^-2.5 * H32 is orthogonal, so a GEMM
+// whose two operands are transformed along their shared contraction axis
+// with the same signs keeps its product.  The transform is evaluated in fp32
+// as butterflies (a, b) -> (a + b, a - b) on pairs (i, i + s) with bit s of i
+// clear, s = 1, 2, 4, 8, 16, then the product by fl32(2^-2.5): five rounded
+// levels of additions and two roundings for the constant, so every value is
+// within 8 * 2^-24 * 2^-2.5 * sum|x| of the exact y, and the fixed order makes
+// the values the codes are decided on deterministic run to run.  The block's
 // scale and codes then follow the ordinary quantiser (nearest-even or
 // stochastic with counter r*cols + c + offset).
 //

@@ -329,49 +329,172 @@ def hot_channels(x, n_hot, block=32):
 
 
 # --- random Hadamard transform before quantisation ------------------------
+#
+# The recipe of the outlier-dynamics page (sec. 4.1) transforms the backward
+# pass's operands with a random Hadamard transform before quantising them.
+# Read as the usual blockwise form: along the block axis every group of 32
+# values x becomes y = 2^-2.5 * H32 * D * x, H32 the Sylvester
+# (natural-order) Hadamard matrix with entries (-1)^popcount(i & j) and
+# D = diag(+-1) from a sign mask, so that 2^-2.5 * H32 is orthogonal.  The
+# oracle computes that definition in float64 (a matrix product, no
+# evaluation order).  A device evaluates y in fp32; any evaluation as five
+# levels of pairwise additions (a butterfly network, in any stride order),
+# then a product by the rounded constant, lies within RHT_BOUND_ULPS fp32
+# rounding units of 2^-2.5 * sum|x| of the exact value (each level adds at
+# most one unit of the group's sum|x|; the constant and the product add two
+# more), so
+# the quantised result is checked for being one that some value within that
+# bound gives (rht_check), and is exact wherever the bound crosses no
+# rounding or scale boundary.
 
-RHT_C = _np.float32(2.0 ** -2.5)   # 1/sqrt(32) rounded to fp32
+RHT_BOUND_ULPS = 8.0
+_FLT_MAX = float(_np.finfo(_np.float32).max)
 
 
-def rht_transform(x, axis, signs):
-    """The blockwise random Hadamard transform the recipe of the
-    outlier-dynamics page (sec. 4.1) applies before backward quantisation,
-    along the block axis in groups of 32: y = c * H32 * D * x per group, with
-    D = diag(+-1) from `signs` (bool per position along the axis, True =
-    negate), H32 the Sylvester (natural-order) Hadamard matrix, entries
-    (-1)^popcount(i & j), and c = fl32(2^-2.5), so c*H32 is orthogonal up to
-    rounding.  Evaluated in fp32, the precision the codes are decided in: the
-    butterflies (a, b) -> (a + b, a - b) on pairs (i, i + s), bit s of i
-    clear, for s = 1, 2, 4, 8, 16 in that order, then the product by c.
-    x: bf16 bits or float32 [rows, cols]; axis ROW = along columns,
-    COL = along rows.  Returns float32 [rows, cols]."""
+def hadamard32():
+    """H32 of the definition: entry (i, j) = (-1)^popcount(i & j)."""
+    i = _np.arange(32)
+    pc = _np.array([bin(v).count("1") for v in range(32)])
+    return _np.where(pc[i[:, None] & i[None, :]] % 2 == 1, -1.0, 1.0)
+
+
+def _block_last(x, axis):
+    """float64 view of x with the block axis last (COL: the transpose)."""
     x = _np.ascontiguousarray(x)
-    v = bf16_to_f64(x).astype(_np.float32) if x.dtype == _np.uint16 else x.astype(_np.float32)
-    if axis == COL:
-        v = _np.ascontiguousarray(v.T)
-    rows, n = v.shape
-    if n % 32:
-        raise ValueError("rht_transform: the block axis must be a multiple of 32")
-    sg = _np.asarray(signs, bool)
-    v = _np.where(sg[None, :], -v, v).astype(_np.float32)
-    v = v.reshape(rows, n // 32, 32)
-    s = 1
-    with _np.errstate(over="ignore", invalid="ignore"):  # fp32 overflow -> Inf/NaN, as defined
-        while s < 32:
-            w = v.reshape(rows, n // 32, 32 // (2 * s), 2, s)
-            a = w[:, :, :, 0, :]
-            b = w[:, :, :, 1, :]
-            v = _np.stack([a + b, a - b], axis=3).reshape(rows, n // 32, 32)
-            s *= 2
-        v = (v * RHT_C).astype(_np.float32).reshape(rows, n)
+    v = bf16_to_f64(x) if x.dtype == _np.uint16 else x.astype(_np.float64)
     return _np.ascontiguousarray(v.T) if axis == COL else v
 
 
+def _rht_groups(v, signs):
+    """v float64 [R, n] (block axis last) -> exact y, the fp32 bound per
+    element, and per group (R, n/32) the flags must_ff / may_ff: the group
+    holds a non-finite input or its fp32 evaluation must overflow / may
+    overflow."""
+    R, n = v.shape
+    if n % 32:
+        raise ValueError("rht: the block axis must be a multiple of 32")
+    d = _np.where(_np.asarray(signs, bool), -1.0, 1.0)
+    g = (v * d[None, :]).reshape(R, n // 32, 32)
+    fin = _np.isfinite(g).all(axis=2)
+    gz = _np.where(fin[:, :, None], g, 0.0)
+    s = gz @ hadamard32().T                 # H32 * D * x per group (H32 is symmetric)
+    c = 2.0 ** -2.5
+    sabs = _np.abs(gz).sum(axis=2)          # sum |x| per group
+    u = 2.0 ** -24
+    bound = RHT_BOUND_ULPS * u * c * sabs + 2.0 ** -149
+    must_ff = ~fin | (_np.abs(s).max(axis=2) - 6 * u * sabs > 2.0 ** 128)
+    may_ff = must_ff | (sabs * (1 + RHT_BOUND_ULPS * u) >= _FLT_MAX)
+    y = (s * c).reshape(R, n)
+    return y, _np.repeat(bound, 32, axis=1), must_ff, may_ff
+
+
+def rht_exact(x, axis, signs):
+    """The transform's definition y = 2^-2.5 * H32 * D * x per group of 32
+    along the block axis, in float64.  x: bf16 bits or float32 [rows, cols];
+    axis ROW = groups along columns, COL = along rows; signs: bool per
+    position of the block axis (True = negate).  Returns (y float64 in x's
+    orientation, bound float64: the largest distance of a correct fp32
+    evaluation from y, element by element).  Groups holding a non-finite
+    value give y = 0 there (see rht_check for how they are judged)."""
+    y, b, _, _ = _rht_groups(_block_last(x, axis), signs)
+    if axis == COL:
+        return _np.ascontiguousarray(y.T), _np.ascontiguousarray(b.T)
+    return y, b
+
+
 def rht_quantize(x, axis, signs, round=RNE, seed=0, rng_offset=0):
-    """Block-32 quantisation of the transformed tensor: rht_transform(x) fed
-    to the quantiser (layouts, rounding and random counters as quantize)."""
-    y = rht_transform(x, axis, signs)
-    return quantize(y, 32, axis, round, seed, rng_offset)
+    """A nominal quantisation of the transformed tensor: the exact transform
+    rounded once to fp32 (one admissible evaluation), then the block-32
+    quantiser (layouts, rounding and random counters as quantize); groups
+    holding a non-finite input or overflowing fp32 get scale 0xFF."""
+    v = _block_last(x, axis)
+    y, _, must_ff, may_ff = _rht_groups(v, signs)
+    with _np.errstate(over="ignore"):
+        y32 = y.astype(_np.float32)
+    ff = _np.repeat(must_ff, 32, axis=1)
+    y32[ff] = _np.nan                       # the quantiser writes 0xFF for such groups
+    src = _np.ascontiguousarray(y32.T) if axis == COL else y32
+    return quantize(src, 32, axis, round, seed, rng_offset)
+
+
+def _signed_val(codes):
+    grid = _np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    v = grid[codes & 7]
+    return _np.where(codes & 8, -v, v)
+
+
+def _unpack(codes):
+    c = _np.ascontiguousarray(codes, _np.uint8)
+    out = _np.empty((c.shape[0], 2 * c.shape[1]), _np.uint8)
+    out[:, 0::2] = c & 0xF
+    out[:, 1::2] = c >> 4
+    return out
+
+
+def _byte_of(a):
+    """E8M0 byte of amax values a >= 0 given in float64: floor(log2 a) - 2
+    clamped to [-127, 127], biased by 127; a = 0 gives 0."""
+    a = _np.asarray(a, _np.float64)
+    _, ex = _np.frexp(_np.where(a > 0, a, 1.0))
+    e = _np.clip(ex - 1 - 2, -127, 127)
+    return _np.where(a > 0, e + 127, 0).astype(_np.int64)
+
+
+def rht_check(x, axis, signs, codes, scales, round=RNE, seed=0, rng_offset=0):
+    """Is (codes, scales) the quantisation of some fp32 evaluation of the
+    transform within the bound of the exact value?  For each group: the scale
+    byte must be one that an amax within the bounds admits (0xFF only where
+    the group holds a non-finite value or may overflow fp32; required where
+    it must); under the byte given, each element's code must lie between the
+    codes of y - bound and y + bound (nearest-even, or stochastic with the
+    element's own random bits; both are monotone in y), a signed zero only
+    where that sign is reachable.  Returns a dict with the counts of bad
+    scale bytes and bad codes, the first bad position, and how many groups
+    and elements were fixed uniquely by the bound (the exact ones) out of the
+    groups and the elements of groups with a finite scale."""
+    v = _block_last(x, axis)
+    R, n = v.shape
+    y, b, must_ff, may_ff = _rht_groups(v, signs)
+    sc = _np.ascontiguousarray(scales, _np.uint8).astype(_np.int64)
+    cd = _unpack(codes)
+    if sc.shape != (R, n // 32) or cd.shape != (R, n):
+        raise ValueError("rht_check: codes/scales do not have the quantised layout")
+    ay = _np.abs(y).reshape(R, n // 32, 32)
+    bb = b.reshape(R, n // 32, 32)
+    blo = _byte_of(_np.maximum(ay - bb, 0.0).max(axis=2))
+    bhi = _byte_of((ay + bb).max(axis=2))
+    is_ff = sc == 0xFF
+    ok_byte = _np.where(is_ff, may_ff, ~must_ff & (sc >= blo) & (sc <= bhi))
+    # codes under the byte given (groups with 0xFF: all codes zero)
+    e = _np.repeat(_np.where(is_ff, 127, sc) - 127, 32, axis=1)
+    lo = _np.ldexp(y - b, -e)
+    hi = _np.ldexp(y + b, -e)
+    if round == RNE:
+        c_lo, c_hi = rne_codes(lo), rne_codes(hi)
+    else:
+        u = sr_bits(seed, rng_offset, R * n).reshape((n, R) if axis == COL else (R, n))
+        u = _np.ascontiguousarray(u.T) if axis == COL else u
+        c_lo, c_hi = sr_codes(lo, u), sr_codes(hi, u)
+    vg, vl, vh = _signed_val(cd), _signed_val(c_lo), _signed_val(c_hi)
+    ok_code = (vg >= vl) & (vg <= vh)
+    zero = (cd & 7) == 0
+    ok_code &= ~zero | _np.where(cd & 8, (y - b) < 0, (y + b) > 0)
+    ffe = _np.repeat(is_ff, 32, axis=1)
+    ok_code = _np.where(ffe, cd == 0, ok_code)
+    exact_groups = int(((blo == bhi) & ~may_ff).sum())
+    exact_elems = int(((c_lo == c_hi) & ~ffe).sum())
+    bad_s = _np.argwhere(~ok_byte)
+    bad_c = _np.argwhere(~ok_code)
+    first = None
+    if bad_s.size:
+        i, j = bad_s[0]
+        first = ("scale", (int(i), int(j)), int(sc[i, j]), (int(blo[i, j]), int(bhi[i, j])))
+    elif bad_c.size:
+        i, j = bad_c[0]
+        first = ("code", (int(i), int(j)), int(cd[i, j]), (int(c_lo[i, j]), int(c_hi[i, j])))
+    return {"bad_scales": int(bad_s.shape[0]), "bad_codes": int(bad_c.shape[0]),
+            "exact_groups": exact_groups, "groups": int(sc.size),
+            "exact_elems": exact_elems, "elems": int((~ffe).sum()), "first_bad": first}
 
 
 # --- outlier clamping and compensation (OCC) -------------------------------

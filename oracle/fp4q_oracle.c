@@ -17,7 +17,10 @@
  *        sec. 4.1 block-structured shared scale over 16..128 elements.
  *   [P2] framerc.cn overview of low-precision training ("低精度训练技术概述"):
  *        sec. 1.1 E8M0 = 8 exponent bits, 0 mantissa bits;
- *        sec. 3.2 stochastic rounding floor + (rand < frac).
+ *        sec. 3.2 stochastic rounding: round up with probability equal to
+ *        the fractional distance (read here at 16-bit resolution as the
+ *        carry rule of orc_sr_code, which is rand < frac with rand the
+ *        complement of the 16 random bits and frac truncated to 16 bits).
  *   [P3] devpress.csdn.net "大模型4位训练中的异常值动态分析与优化实践":
  *        sec. 1.1 E2M1 covers [-6, 6]; sec. 3.1 HCP error decomposition and
  *        the dual-kernel (D) mode; sec. 3.2 hcp_gemm sketch; sec. 4.1 top 9%.
@@ -140,7 +143,11 @@ int orc_rne_code(double y) {
  * 16 random bits are added, and a carry out of 16 bits rounds up:
  * round up iff u16 + floor(frac * 2^16) >= 2^16, so P(up) =
  * floor(frac * 2^16) / 2^16, within 2^-16 of frac (every quantity is exact in
- * double).  |y| >= 6 gives 6. */
+ * double).  Written as the page's comparison this is rand < frac with
+ * rand = (0xFFFF - u16) / 2^16 and frac truncated to 16 bits; it is not
+ * u16 < frac * 2^16, which rounds a given u16 differently on up to ~90% of
+ * the 2^16 values (the two draws are complements of each other).
+ * |y| >= 6 gives 6. */
 int orc_sr_code(double y, uint32_t u16) {
     int sign = signbit(y) ? 8 : 0;
     double m = fabs(y);

@@ -142,3 +142,33 @@ def test_sr_uses_logical_index_and_offset(orc):
     assert np.array_equal(c[4:], c2) and np.array_equal(s[4:], s2)
     c3, _ = orc.quantize(x[4:], 32, round=orc.SR, seed=7)
     assert not np.array_equal(c3, c2)
+
+
+def test_sr_documented_rule_every_u16(orc):
+    """The rule as the header and the design state it, written here with exact
+    rationals: with frac = (m - lo)/(hi - lo) and F = floor(frac * 2^16), the
+    magnitude rounds up iff (0xFFFF - u) < F (the page's rand < frac with
+    rand the complement of the 16 random bits and frac truncated to 16 bits),
+    the same as a carry out of u + F.  Checked against the oracle for every
+    u in [0, 2^16) at fractions of every E2M1 interval, both signs; and the
+    literal u < frac * 2^16 is shown to round differently for a large share
+    of the u values (the counts the design quotes)."""
+    from fractions import Fraction
+    u = np.arange(65536, dtype=np.int64)
+    ys = [1.1, 0.625, 2.7, 4.9, 0.01, 0.49, 1.75, 3.999, 5.0, 2.0 ** -30]
+    differ = {}
+    for y in ys:
+        y32 = float(np.float32(y))
+        lo, hi = (Fraction(float(t)) for t in _lo_hi(y32))
+        frac = (Fraction(y32) - lo) / (hi - lo)
+        F = (frac * 65536).numerator // (frac * 65536).denominator
+        up = (65535 - u) < F
+        assert np.array_equal(up, u + F >= 65536)
+        for s in (1.0, -1.0):
+            codes = orc.sr_codes(np.full(65536, s * y32), u.astype(np.uint32))
+            mags = GRID[codes & 7]
+            assert np.array_equal(mags == float(hi), up), (y, s)
+            assert np.all((codes >> 3) == (1 if s < 0 else 0))
+        literal = u < float(frac * 65536)
+        differ[y] = int(np.sum(literal != up))
+    assert [differ[y] for y in (1.1, 0.625, 2.7, 4.9)] == [26215, 32768, 39321, 58983]
