@@ -126,6 +126,49 @@ def _need_cuda(*ts):
             raise ValueError("libfp4q takes device (cuda) tensors")
 
 
+def _need(t, name, dtype, shape=None, dense=True):
+    """Raise unless t has the dtype (and shape) the C call reads it as and,
+    with dense, is contiguous (the C call takes no strides for it)."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dense and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _scratch(nbytes, device, stream):
+    """Caller-less workspace for one call: allocated from torch's pool and,
+    when the kernels run on a stream other than the current one, recorded on
+    that stream so the pool does not hand the block to other work before
+    those kernels finish."""
+    torch = _torch()
+    ws = torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+    if stream is not None:
+        ws.record_stream(stream)
+    return ws
+
+
+def _hcp_operands(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx):
+    """Shapes and dtypes of the hot-channel calls' operands; returns M, N, K."""
+    torch = _torch()
+    _need_cuda(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx)
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x and w must be 2-D")
+    M, K = x.shape
+    N = w.shape[1]
+    _need(x, "x", torch.bfloat16)
+    _need(w, "w", torch.bfloat16, (K, N))
+    _need(xq_codes, "xq_codes", torch.uint8, (M, K // 2))
+    _need(xq_scales, "xq_scales", torch.uint8, (M, K // 32))
+    _need(wq_codes, "wq_codes", torch.uint8, (N, K // 2))
+    _need(wq_scales, "wq_scales", torch.uint8, (N, K // 32))
+    _need(hot_idx, "hot_idx", torch.int32)
+    if hot_idx.dim() != 1:
+        raise ValueError("hot_idx must be 1-D")
+    return M, N, K
+
+
 def quantize(x, block=32, axis=ROW, rounding=RNE, seed=0, rng_offset=0, codes=None, scales=None,
              stream=None):
     """Fused MXFP4 quantisation of a 2-D bf16/fp32 tensor (row stride from x).
@@ -222,13 +265,12 @@ def hcp_residual_add(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, y,
                      stream=None):
     """y[M,N] (fp32, in place) += sum_{c in hot} X[:,c] W[c,:] - Xq[:,c] Wq[c,:]."""
     torch = _torch()
-    _need_cuda(x, w, y, hot_idx)
-    M, K = x.shape
-    N = w.shape[1]
+    M, N, K = _hcp_operands(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx)
+    _need_cuda(y)
+    _need(y, "y", torch.float32, (M, N))
     n_hot = hot_idx.numel()
-    need = hcp_workspace_bytes(M, N, n_hot)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        workspace = _scratch(hcp_workspace_bytes(M, N, n_hot), x.device, stream)
     _check(lib().fp4q_hcp_residual_add(M, N, K, _ptr(x), _ptr(xq_codes), _ptr(xq_scales), _ptr(w),
                                        _ptr(wq_codes), _ptr(wq_scales), _ptr(hot_idx), n_hot,
                                        _ptr(y), _ptr(workspace), workspace.numel(),
@@ -241,15 +283,16 @@ def gemm_hcp(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, y=None, wo
     """Y[M,N] (fp32) = Xq Wq + sum_{c in hot} X[:,c] W[c,:] - Xq[:,c] Wq[c,:], in one GEMM
     kernel (fp4q_gemm_hcp); returns y."""
     torch = _torch()
-    _need_cuda(x, w, hot_idx)
-    M, K = x.shape
-    N = w.shape[1]
+    M, N, K = _hcp_operands(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx)
     n_hot = hot_idx.numel()
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    need = hcp_workspace_bytes(M, N, n_hot)
+    _need_cuda(y)
+    _need(y, "y", torch.float32, (M, N), dense=False)
+    if y.stride(1) != 1:
+        raise ValueError("y must have unit column stride")
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        workspace = _scratch(hcp_workspace_bytes(M, N, n_hot), x.device, stream)
     _check(lib().fp4q_gemm_hcp(M, N, K, _ptr(x), _ptr(xq_codes), _ptr(xq_scales), _ptr(w),
                                _ptr(wq_codes), _ptr(wq_scales), _ptr(hot_idx), n_hot, _ptr(y),
                                y.stride(0), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -332,15 +375,16 @@ def gemm_hcp_split(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, y=No
     """Y[M,N] (fp32) = Xq' Wq' + X[:, hot] W[hot, :] in one kernel
     (fp4q_gemm_hcp_split; xq, wq quantised with the hot channels zeroed)."""
     torch = _torch()
-    _need_cuda(x, w, hot_idx)
-    M, K = x.shape
-    N = w.shape[1]
+    M, N, K = _hcp_operands(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx)
     n_hot = hot_idx.numel()
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    need = hcp_workspace_bytes(M, N, n_hot)
+    _need_cuda(y)
+    _need(y, "y", torch.float32, (M, N), dense=False)
+    if y.stride(1) != 1:
+        raise ValueError("y must have unit column stride")
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        workspace = _scratch(hcp_workspace_bytes(M, N, n_hot), x.device, stream)
     _check(lib().fp4q_gemm_hcp_split(M, N, K, _ptr(x), _ptr(xq_codes), _ptr(xq_scales), _ptr(w),
                                      _ptr(wq_codes), _ptr(wq_scales), _ptr(hot_idx), n_hot,
                                      _ptr(y), y.stride(0), _ptr(workspace), workspace.numel(),
@@ -358,14 +402,21 @@ def hot_channels(x, n_hot, hot_idx=None, err=None, want_err=False, workspace=Non
     (hot_idx, err) when want_err (err: fp32 per-channel errors)."""
     torch = _torch()
     _need_cuda(x)
+    _need(x, "x", torch.bfloat16, dense=False)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
     R, C = x.shape
     if hot_idx is None:
         hot_idx = torch.empty((max(n_hot, 0),), dtype=torch.int32, device=x.device)
+    _need_cuda(hot_idx)
+    _need(hot_idx, "hot_idx", torch.int32)
     if err is None and want_err:
         err = torch.empty((C,), dtype=torch.float32, device=x.device)
-    need = hot_channels_workspace_bytes(R, C)
+    if err is not None:
+        _need_cuda(err)
+        _need(err, "err", torch.float32, (C,))
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        workspace = _scratch(hot_channels_workspace_bytes(R, C), x.device, stream)
     _check(lib().fp4q_hot_channels(_ptr(x), R, C, x.stride(0), n_hot,
                                    _ptr(hot_idx) if n_hot > 0 else None,
                                    _ptr(err) if err is not None else None, _ptr(workspace),
@@ -421,6 +472,9 @@ def occ_quantize(x, quantile=0.99, rounding=RNE, seed=0, rng_offset=0, workspace
     bound fp4q_occ_max_nnz; row_ptr[-1] entries are used) and T's bf16 bits."""
     torch = _torch()
     _need_cuda(x)
+    _need(x, "x", torch.bfloat16, dense=False)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
     R, C = x.shape
     dev = x.device
     cap = occ_max_nnz(R, C, quantile)
@@ -431,8 +485,7 @@ def occ_quantize(x, quantile=0.99, rounding=RNE, seed=0, rng_offset=0, workspace
     vals = torch.empty((max(cap, 1),), dtype=torch.float32, device=dev)
     thr = torch.empty((8,), dtype=torch.int16, device=dev)
     if workspace is None:
-        workspace = torch.empty(int(lib().fp4q_occ_workspace_bytes(R, C)), dtype=torch.uint8,
-                                device=dev)
+        workspace = _scratch(lib().fp4q_occ_workspace_bytes(R, C), dev, stream)
     _check(lib().fp4q_occ_quantize(_ptr(x), R, C, x.stride(0), quantile, rounding, seed,
                                    rng_offset, _ptr(codes), _ptr(scales), _ptr(row_ptr),
                                    _ptr(col_idx), _ptr(vals), cap, _ptr(thr), _ptr(workspace),
@@ -442,7 +495,15 @@ def occ_quantize(x, quantile=0.99, rounding=RNE, seed=0, rng_offset=0, workspace
 
 def occ_spmm(row_ptr, col_idx, vals, w, y, stream=None):
     """y[M, N] (fp32, in place) += R W for the CSR residual R (fp4q_occ_spmm)."""
-    _need_cuda(w, y)
+    torch = _torch()
+    _need_cuda(row_ptr, col_idx, vals, w, y)
+    _need(row_ptr, "row_ptr", torch.int64)
+    _need(col_idx, "col_idx", torch.int32)
+    _need(vals, "vals", torch.float32)
+    _need(w, "w", torch.bfloat16, dense=False)
+    _need(y, "y", torch.float32, dense=False)
+    if w.stride(1) != 1 or y.stride(1) != 1:
+        raise ValueError("w and y must have unit column stride")
     M, N = y.shape
     K = w.shape[0]
     _check(lib().fp4q_occ_spmm(M, N, K, _ptr(row_ptr), _ptr(col_idx), _ptr(vals), _ptr(w),

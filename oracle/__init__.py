@@ -245,6 +245,24 @@ def gemm(a_codes, a_scales, b_codes, b_scales, block=32):
     return C, S
 
 
+def gemm_dense(a_codes, a_scales, b_codes, b_scales, block=32, rows=None, cols=None):
+    """The same C = deq(A) deq(B)^T and S = sum |products| as gemm(), with
+    the contraction done by a float64 matrix product of the exactly
+    dequantised operands (a library primitive standing in for the sum; its
+    rounding is K * 2^-53 * S at most, far below any tolerance used here).
+    rows / cols: optional index arrays selecting rows of A / rows of B, so
+    whole output rows or columns of a large product can be formed alone."""
+    A = dequantize(a_codes if rows is None else _np.asarray(a_codes)[rows],
+                   a_scales if rows is None else _np.asarray(a_scales)[rows], block)
+    B = dequantize(b_codes if cols is None else _np.asarray(b_codes)[cols],
+                   b_scales if cols is None else _np.asarray(b_scales)[cols], block)
+    C = A @ B.T
+    _np.abs(A, out=A)
+    _np.abs(B, out=B)
+    S = A @ B.T
+    return C, S
+
+
 def gemm_intblock(a_codes, a_scales, b_codes, b_scales, block=32):
     ac, as_, bc, bs = (_c(t, _np.uint8) for t in (a_codes, a_scales, b_codes, b_scales))
     M, N, K = ac.shape[0], bc.shape[0], 2 * ac.shape[1]
@@ -282,6 +300,27 @@ def hcp_residual_entries(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx
     return R, S
 
 
+def hcp_residual_dense(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, rows=None,
+                       cols=None):
+    """The residual of hcp_residual_entries for whole blocks of outputs:
+    R = X_H W_H - Xq_H Wq_H over the hot channels H (float64 matrix products
+    of the exact operand values), with S = |X_H| |W_H| + |Xq_H| |Wq_H|.
+    x: bf16 bits [M, K]; w: bf16 bits [K, N]; wq K-major [N, K/2].
+    rows / cols: optional index arrays of the outputs wanted."""
+    hot = _np.asarray(hot_idx, _np.int64)
+    xs = _c(x, _np.uint16) if rows is None else _np.asarray(x)[rows]
+    ws = _c(w, _np.uint16) if cols is None else _np.asarray(w)[:, cols]
+    xh = bf16_to_f64(_np.ascontiguousarray(xs[:, hot]))
+    wh = bf16_to_f64(_np.ascontiguousarray(ws[hot, :]))
+    xq = dequantize(xq_codes if rows is None else _np.asarray(xq_codes)[rows],
+                    xq_scales if rows is None else _np.asarray(xq_scales)[rows], 32)[:, hot]
+    wq = dequantize(wq_codes if cols is None else _np.asarray(wq_codes)[cols],
+                    wq_scales if cols is None else _np.asarray(wq_scales)[cols], 32)[:, hot].T
+    R = xh @ wh - xq @ wq
+    S = _np.abs(xh) @ _np.abs(wh) + _np.abs(xq) @ _np.abs(wq)
+    return R, S
+
+
 def hcp_split_entries(x, w, hot_idx, ii, jj):
     """The split reading of the hot-channel compensation (outlier-dynamics
     page, sec. 3.1-3.2): the hot channels' own bf16 product
@@ -301,6 +340,19 @@ def hcp_split_entries(x, w, hot_idx, ii, jj):
         R += t
         S += _np.abs(t)
     return R, S
+
+
+def hcp_split_dense(x, w, hot_idx, rows=None, cols=None):
+    """hcp_split_entries for whole blocks of outputs: X_H W_H over the hot
+    channels (a float64 matrix product of the exact bf16 values) with the
+    sum of |terms|.  x: bf16 bits [M, K]; w: bf16 bits [K, N]; rows / cols:
+    optional index arrays of the outputs wanted."""
+    hot = _np.asarray(hot_idx, _np.int64)
+    xs = _np.asarray(x) if rows is None else _np.asarray(x)[rows]
+    ws = _np.asarray(w) if cols is None else _np.asarray(w)[:, cols]
+    xh = bf16_to_f64(_np.ascontiguousarray(xs[:, hot]))
+    wh = bf16_to_f64(_np.ascontiguousarray(ws[hot, :]))
+    return xh @ wh, _np.abs(xh) @ _np.abs(wh)
 
 
 def channel_quant_error(x, block=32):

@@ -102,9 +102,20 @@ def check_dge(out: torch.Tensor, d_ref: np.ndarray, g_f64: np.ndarray, orc, clam
     assert not bad.any(), f"{what}: {int(bad.sum())} clamped/unit entries not bit-exact"
 
 
+def edge_lines(n, k, seed):
+    """k distinct indices of [0, n), always including 0 and n - 1 (all of
+    them when n <= k), ascending."""
+    if n <= k:
+        return np.arange(n)
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(np.arange(1, n - 1), k - 2, replace=False)
+    return np.sort(np.concatenate([[0, n - 1], pick])).astype(np.int64)
+
+
 def sample_positions(M, N, seed, per_tile=4, tile=128, full_rows=2, full_cols=2):
-    """>= per_tile random entries in every tile x tile output tile, plus a few
-    full rows and columns (edges included)."""
+    """>= per_tile random entries in every tile x tile output tile, plus
+    full_rows whole rows and full_cols whole columns that always include the
+    first and the last (edge_lines)."""
     rng = np.random.default_rng(seed)
     ii, jj = [], []
     for t0 in range(0, M, tile):
@@ -113,12 +124,19 @@ def sample_positions(M, N, seed, per_tile=4, tile=128, full_rows=2, full_cols=2)
             w = min(tile, N - u0)
             ii.append(t0 + rng.integers(0, h, per_tile))
             jj.append(u0 + rng.integers(0, w, per_tile))
-    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, full_rows)]))
-    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, full_cols)]))
-    for r in rows[:full_rows]:
+    for r in edge_lines(M, max(full_rows, 2), seed + 1):
         ii.append(np.full(N, r))
         jj.append(np.arange(N))
-    for c in cols[:full_cols]:
+    for c in edge_lines(N, max(full_cols, 2), seed + 2):
         ii.append(np.arange(M))
         jj.append(np.full(M, c))
     return np.concatenate(ii).astype(np.int64), np.concatenate(jj).astype(np.int64)
+
+
+def check_lines_f32(orc, got, rows, cols, ref, what=""):
+    """Whole rows `rows` and whole columns `cols` of an fp32 output `got`
+    [M, N] against ref(rows=..., cols=...) -> (C, S) of those lines."""
+    C, S = ref(rows=rows, cols=None)
+    check_gemm_f32(got[rows], C, S, f"{what} rows")
+    C, S = ref(rows=None, cols=cols)
+    check_gemm_f32(got[:, cols], C, S, f"{what} cols")

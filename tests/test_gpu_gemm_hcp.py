@@ -1,16 +1,18 @@
 """GPU parity of fp4q_gemm (|c - C_ref| <= 1e-5 * sum|a_i b_i|; bf16 outputs
 inside the rounded bracket) and fp4q_hcp_residual_add (same bound over the
-extended sum), at small/ragged sizes in full and at the layer workloads'
-full sizes on sampled outputs (>= 4 per 128x128 tile, plus full rows and
-columns)."""
+extended sum): small/ragged sizes in full; the LLaMA-1B FFN GEMMs (forward
+8192 x 5632 x 2048, dX 8192 x 2048 x 5632, dW 2048 x 5632 x 8192 with the DGE
+estimator) over every output; the 13B-shaped outlier layer on >= 4 sampled
+outputs per 128 x 128 tile plus 64 whole rows and 64 whole columns (the
+first and last included)."""
 import numpy as np
 import pytest
 import torch
 
 import mxfp4_block_scaled_fp4q_amd as fq
 from mxfp4_block_scaled_fp4q_amd import inputs
-from gpu_helpers import (GEMM_REL, check_gemm_bf16, check_gemm_f32, dev, dev_bf16, host_bits,
-                         sample_positions, to_dev_input)
+from gpu_helpers import (GEMM_REL, check_gemm_bf16, check_gemm_f32, check_lines_f32, dev,
+                         dev_bf16, edge_lines, host_bits, sample_positions, to_dev_input)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,29 +95,37 @@ def test_gemm_tiles_bit_identical(M, N, K, monkeypatch):
 @pytest.mark.parametrize("M,N,K", [(64, 32, 128), (300, 288, 256), (513, 1056, 384),
                                    (8192, 5632, 2048)])
 def test_gemm_quant_epilogue(orc, M, N, K):
-    """fp4q_gemm_quant: C (bf16) and its ROW block-32 RNE quantisation in one
-    kernel, bit for bit equal to fp4q_gemm then fp4q_quantize (which the
-    oracle pins elsewhere), with and without the C store, including a row of
-    A whose scale byte is 0xFF (a NaN row of C: scale 0xFF, codes 0)."""
+    """fp4q_gemm_quant against the oracle: its bf16 C inside the rounded
+    bracket of the oracle's product (every output), and its codes and scales
+    equal to the oracle's ROW block-32 nearest-even quantisation of that C;
+    with and without the C store; bit for bit equal to fp4q_gemm then
+    fp4q_quantize; a row of A whose scale byte is 0xFF gives a NaN row of C
+    (scale 0xFF, codes 0).  Operands are the oracle's quantisations."""
+    print(f"gemm_quant {M}x{N}x{K}", flush=True)
     a = inputs.normal((M, K), M + 11)
     b = inputs.normal((N, K), N + 13)
-    A, B = qpair(orc, a, b) if M * K <= 1 << 22 else (None, None)
-    if A is None:
-        A = fq.quantize(torch.from_numpy(a).cuda(), 32)
-        B = fq.quantize(torch.from_numpy(b).cuda(), 32)
-        ac, as_, bc, bs = A[0], A[1].clone(), B[0], B[1]
-    else:
-        ac, as_, bc, bs = dev(A[0]), dev(A[1].copy()), dev(B[0]), dev(B[1])
+    (ac, as_), (bc, bs) = qpair(orc, a, b)
+    as_ = as_.copy()
     as_[M // 2, 1] = 0xFF
-    c, (qc, qs) = fq.gemm_quant(ac, as_, bc, bs)
-    _, (qc2, qs2) = fq.gemm_quant(ac, as_, bc, bs, write_c=False)
-    c_ref = fq.gemm(ac, as_, bc, bs, out_dtype=torch.bfloat16)
+    acd, asd, bcd, bsd = dev(ac), dev(as_), dev(bc), dev(bs)
+    c, (qc, qs) = fq.gemm_quant(acd, asd, bcd, bsd)
+    _, (qc2, qs2) = fq.gemm_quant(acd, asd, bcd, bsd, write_c=False)
+    c_ref = fq.gemm(acd, asd, bcd, bsd, out_dtype=torch.bfloat16)
     qc_ref, qs_ref = fq.quantize(c_ref, 32, fq.ROW)
     torch.cuda.synchronize()
-    assert torch.equal(c.view(torch.int16), c_ref.view(torch.int16))
+    cb = host_bits(c)
+    C, S = orc.gemm_dense(ac, as_, bc, bs)
+    nan = np.isnan(C)
+    assert nan[M // 2].all() and nan.sum() == N
+    assert ((cb[M // 2] & 0x7FFF) > 0x7F80).all()
+    ok = ~nan.any(axis=1)
+    check_gemm_bf16(cb[ok], C[ok], S[ok], orc, f"gemm_quant C {M}x{N}x{K}")
+    oc, os_ = orc.quantize(cb, 32)
     for got_c, got_s in ((qc, qs), (qc2, qs2)):
-        assert torch.equal(got_c, qc_ref) and torch.equal(got_s, qs_ref)
-    assert (qs_ref[M // 2] == 0xFF).all() and (qc_ref[M // 2] == 0).all()
+        assert np.array_equal(host_bits(got_c), oc) and np.array_equal(host_bits(got_s), os_)
+    assert (os_[M // 2] == 0xFF).all() and (oc[M // 2] == 0).all()
+    assert torch.equal(c.view(torch.int16), c_ref.view(torch.int16))
+    assert torch.equal(qc, qc_ref) and torch.equal(qs, qs_ref)
 
 
 def test_gemm_nan_scale_and_zero(orc):
@@ -149,8 +159,9 @@ def sampled_gemm_check(orc, A, B, c_gpu, seed, what):
 
 
 def test_ffn_forward_gemm(orc):
-    """8192 x 5632 x 2048, bf16 out, operands quantised on the GPU and
-    checked bit-exact against the oracle's first."""
+    """8192 x 5632 x 2048, bf16 and fp32 out, every output against the
+    oracle; operands quantised on the GPU and checked bit-exact against the
+    oracle's first."""
     d = inputs.ffn_forward()
     X, W = d["X"], d["W"]
     A = orc.quantize(X, 32)
@@ -158,18 +169,19 @@ def test_ffn_forward_gemm(orc):
     xq = fq.quantize(dev_bf16(X), 32, fq.ROW)
     wq = fq.quantize(dev_bf16(W), 32, fq.COL)
     y = fq.gemm(xq[0], xq[1], wq[0], wq[1], out_dtype=torch.bfloat16)
+    y32 = fq.gemm(xq[0], xq[1], wq[0], wq[1], out_dtype=torch.float32)
     torch.cuda.synchronize()
     for g, o in zip(xq + wq, A + B):
         assert np.array_equal(host_bits(g), o)
-    sampled_gemm_check(orc, A, B, y, 3, "ffn fwd")
-    y32 = fq.gemm(xq[0], xq[1], wq[0], wq[1], out_dtype=torch.float32)
-    torch.cuda.synchronize()
-    sampled_gemm_check(orc, A, B, y32, 4, "ffn fwd f32")
+    C, S = orc.gemm_dense(*A, *B)
+    check_gemm_bf16(host_bits(y), C, S, orc, "ffn fwd bf16")
+    check_gemm_f32(host_bits(y32), C, S, "ffn fwd f32")
 
 
 def test_ffn_backward_gemms_and_dge(orc):
     """dX = dY W^T (K = 5632, bf16) and dW = X^T dY (K = 8192, fp32) with dY
-    stochastically rounded, then the DGE mask of W applied to dW."""
+    stochastically rounded, then the DGE mask of W applied to dW (separately
+    and in the GEMM's epilogue): every output against the oracle."""
     f = inputs.ffn_forward()
     b = inputs.ffn_backward_grad()
     X, W, dY = f["X"], f["W"], b["dY"]
@@ -177,24 +189,25 @@ def test_ffn_backward_gemms_and_dge(orc):
     wr = orc.quantize(W, 32)
     dx = fq.gemm(dev(dyr[0]), dev(dyr[1]), dev(wr[0]), dev(wr[1]), out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    sampled_gemm_check(orc, dyr, wr, dx, 5, "dX")
-    del dx
+    C, S = orc.gemm_dense(*dyr, *wr)
+    check_gemm_bf16(host_bits(dx), C, S, orc, "dX")
+    del dx, C, S
     xc = orc.quantize(X, 32, axis=orc.COL)
     dyc = orc.quantize(dY, 32, axis=orc.COL, round=orc.SR, seed=b["seed_col"])
     dw = fq.gemm(dev(xc[0]), dev(xc[1]), dev(dyc[0]), dev(dyc[1]), out_dtype=torch.float32)
     torch.cuda.synchronize()
-    ii, jj, C, S = sampled_gemm_check(orc, xc, dyc, dw, 6, "dW")
+    C, S = orc.gemm_dense(*xc, *dyc)
+    check_gemm_f32(host_bits(dw), C, S, "dW")
     # DGE mask of W (COL blocks of 32) on the GPU's dW: out = dW * d, checked
     # against d_ref * C_ref with the GEMM bound and the DGE bound combined
     out = fq.grad_estimate(fq.DGE, dev_bf16(W), dw, 32, fq.COL, 5.0, 3.0,
                            out_dtype=torch.float32)
     torch.cuda.synchronize()
     d_ref, _ = orc.grad_estimate(orc.DGE, W, np.zeros(W.shape, np.float32), 32, orc.COL)
-    dref = d_ref[ii, jj]
-    got = host_bits(out)[ii, jj].astype(np.float64)
-    tol = dref * (GEMM_REL * S) * (1 + 2.0 ** -20) + np.abs(C) * dref * 2.0 ** -20 \
-        + np.abs(C * dref) * 2.0 ** -23
-    assert np.all(np.abs(got - C * dref) <= tol)
+    got = host_bits(out).astype(np.float64)
+    tol = d_ref * (GEMM_REL * S) * (1 + 2.0 ** -20) + np.abs(C) * d_ref * 2.0 ** -20 \
+        + np.abs(C * d_ref) * 2.0 ** -23
+    assert np.all(np.abs(got - C * d_ref) <= tol)
     # the same product from the GEMM with the estimator in its epilogue
     fused = fq.gemm_dge(dev(xc[0]), dev(xc[1]), dev(dyc[0]), dev(dyc[1]), dev_bf16(W), 5.0, 3.0)
     torch.cuda.synchronize()
@@ -235,9 +248,24 @@ def test_gemm_dge_small(orc, M, N, K, k):
     assert np.all(np.abs(got[ok] - C[ok] * d_ref[ok]) <= tol)
 
 
+def _outlier_refs(orc, X, A, W, B, hot):
+    """Oracle references of the 13B-shaped layer for whole lines: the base
+    product, and the base product plus the hot-channel residual."""
+    def base(rows=None, cols=None):
+        return orc.gemm_dense(*A, *B, rows=rows, cols=cols)
+
+    def with_hcp(rows=None, cols=None):
+        C, S = orc.gemm_dense(*A, *B, rows=rows, cols=cols)
+        R, SR = orc.hcp_residual_dense(X, A[0], A[1], W, B[0], B[1], hot, rows=rows, cols=cols)
+        return C + R, S + SR
+    return base, with_hcp
+
+
 def test_outlier_layer_gemm_and_hcp(orc):
     """16384 x 13824 x 5120 fp32 base GEMM plus the dual-mode hot-channel
-    residual over 9% persistent hot channels."""
+    residual over 9% persistent hot channels: >= 4 sampled outputs per
+    128 x 128 tile and 64 whole rows and columns (first and last included),
+    before and after the residual add."""
     d = inputs.outlier_layer()
     X, W, hot = d["X"], d["W"], d["hot"]
     A = orc.quantize(X, 32)
@@ -246,12 +274,21 @@ def test_outlier_layer_gemm_and_hcp(orc):
     Bd = (dev(B[0]), dev(B[1]))
     y = fq.gemm(Ad[0], Ad[1], Bd[0], Bd[1], out_dtype=torch.float32)
     torch.cuda.synchronize()
-    ii, jj, C, S = sampled_gemm_check(orc, A, B, y, 7, "13B base")
+    M, N = y.shape
+    yh = host_bits(y)
+    ii, jj = sample_positions(M, N, 7)
+    C, S = orc.gemm_entries(A[0], A[1], B[0], B[1], ii, jj)
+    check_gemm_f32(yh[ii, jj], C, S, "13B base")
+    rows, cols = edge_lines(M, 64, 71), edge_lines(N, 64, 72)
+    base, with_hcp = _outlier_refs(orc, X, A, W, B, hot)
+    check_lines_f32(orc, yh, rows, cols, base, "13B base")
     xd, wd = dev_bf16(X), dev_bf16(W)
     fq.hcp_residual_add(xd, Ad[0], Ad[1], wd, Bd[0], Bd[1], dev(hot), y)
     torch.cuda.synchronize()
+    yh = host_bits(y)
     R, SR = orc.hcp_residual_entries(X, A[0], A[1], W, B[0], B[1], hot, ii, jj)
-    check_gemm_f32(host_bits(y)[ii, jj], C + R, S + SR, "13B base + hcp")
+    check_gemm_f32(yh[ii, jj], C + R, S + SR, "13B base + hcp")
+    check_lines_f32(orc, yh, rows, cols, with_hcp, "13B base + hcp")
 
 
 @pytest.mark.parametrize("M,N,K,n_hot", [(64, 96, 256, 23), (300, 257, 512, 46),
@@ -327,8 +364,9 @@ def test_gemm_hcp_single_kernel(orc, M, N, K, n_hot, ld_pad):
 
 
 def test_outlier_layer_single_kernel_hcp(orc):
-    """16384 x 13824 x 5120 with 461 hot channels in one kernel, on sampled
-    outputs, and equal to the two-call form within the same bound."""
+    """16384 x 13824 x 5120 with 461 hot channels in one kernel: >= 4 sampled
+    outputs per 128 x 128 tile and 64 whole rows and columns (first and last
+    included), and equal to the two-call form within the same bound."""
     d = inputs.outlier_layer()
     X, W, hot = d["X"], d["W"], d["hot"]
     A = orc.quantize(X, 32)
@@ -339,12 +377,16 @@ def test_outlier_layer_single_kernel_hcp(orc):
     y = fq.gemm_hcp(xd, Ad[0], Ad[1], wd, Bd[0], Bd[1], hd)
     torch.cuda.synchronize()
     M, N = y.shape
+    yh = host_bits(y)
     ii, jj = sample_positions(M, N, 7)
     C, S = orc.gemm_entries(A[0], A[1], B[0], B[1], ii, jj)
     R, SR = orc.hcp_residual_entries(X, A[0], A[1], W, B[0], B[1], hot, ii, jj)
-    check_gemm_f32(host_bits(y)[ii, jj], C + R, S + SR, "13B single-kernel hcp")
+    check_gemm_f32(yh[ii, jj], C + R, S + SR, "13B single-kernel hcp")
+    _, with_hcp = _outlier_refs(orc, X, A, W, B, hot)
+    check_lines_f32(orc, yh, edge_lines(M, 64, 73), edge_lines(N, 64, 74), with_hcp,
+                    "13B single-kernel hcp")
     y2 = fq.gemm(Ad[0], Ad[1], Bd[0], Bd[1], out_dtype=torch.float32)
     fq.hcp_residual_add(xd, Ad[0], Ad[1], wd, Bd[0], Bd[1], hd, y2)
     torch.cuda.synchronize()
-    a, b = host_bits(y)[ii, jj].astype(np.float64), host_bits(y2)[ii, jj].astype(np.float64)
+    a, b = yh[ii, jj].astype(np.float64), host_bits(y2)[ii, jj].astype(np.float64)
     assert np.all(np.abs(a - b) <= 2 * GEMM_REL * (S + SR)), "single-kernel vs two-call"

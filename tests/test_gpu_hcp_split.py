@@ -10,7 +10,8 @@ import torch
 
 import mxfp4_block_scaled_fp4q_amd as fq
 from mxfp4_block_scaled_fp4q_amd import inputs
-from gpu_helpers import check_gemm_f32, dev, dev_bf16, host_bits, sample_positions
+from gpu_helpers import (check_gemm_f32, check_lines_f32, dev, dev_bf16, edge_lines,
+                         host_bits, sample_positions)
 
 pytestmark = pytest.mark.gpu
 
@@ -89,23 +90,38 @@ def test_gemm_hcp_split(orc, M, N, K, n_hot):
 
 
 def test_outlier_layer_split(orc):
-    """16384 x 13824 x 5120 with 461 hot channels, split reading, sampled."""
+    """16384 x 13824 x 5120 with 461 hot channels, split reading: the masked
+    quantisations of X and W bit for bit against the oracle's quantisations
+    of the zeroed tensors (whole tensors), then the product on >= 4 sampled
+    outputs per 128 x 128 tile and 64 whole rows and columns (first and last
+    included)."""
     d = inputs.outlier_layer()
     X, W, hot = d["X"], d["W"], d["hot"]
     M, K = X.shape
     N = W.shape[1]
+    xz = X.copy()
+    xz[:, hot] = 0
+    wz = W.copy()
+    wz[hot, :] = 0
+    A = orc.quantize(xz, 32)
+    B = orc.quantize(wz, 32, axis=orc.COL)
+    del xz, wz
     xd, wd, hd = dev_bf16(X), dev_bf16(W), dev(hot)
     mask = fq.channel_mask(hd, K)
     xq = fq.quantize_masked(xd, mask, 32, fq.ROW)
     wq = fq.quantize_masked(wd, mask, 32, fq.COL)
     y = fq.gemm_hcp_split(xd, xq[0], xq[1], wd, wq[0], wq[1], hd)
     torch.cuda.synchronize()
+    for g, o, what in zip(xq + wq, A + B, ("X codes", "X scales", "W codes", "W scales")):
+        assert np.array_equal(host_bits(g), o), what
+    yh = host_bits(y)
     ii, jj = sample_positions(M, N, 8)
-    C, S = orc.gemm_entries(xq[0].cpu().numpy(), xq[1].cpu().numpy(), wq[0].cpu().numpy(),
-                            wq[1].cpu().numpy(), ii, jj)
+    C, S = orc.gemm_entries(A[0], A[1], B[0], B[1], ii, jj)
     R, SR = orc.hcp_split_entries(X, W, hot, ii, jj)
-    check_gemm_f32(host_bits(y)[ii, jj], C + R, S + SR, "13B split hcp")
-    # the masked quantisations themselves, on a slab of rows / columns
-    xz = X[:64].copy()
-    xz[:, hot] = 0
-    assert np.array_equal(xq[0][:64].cpu().numpy(), orc.quantize(xz, 32)[0])
+    check_gemm_f32(yh[ii, jj], C + R, S + SR, "13B split hcp")
+
+    def ref(rows=None, cols=None):
+        C, S = orc.gemm_dense(*A, *B, rows=rows, cols=cols)
+        R, SR = orc.hcp_split_dense(X, W, hot, rows=rows, cols=cols)
+        return C + R, S + SR
+    check_lines_f32(orc, yh, edge_lines(M, 64, 81), edge_lines(N, 64, 82), ref, "13B split hcp")

@@ -188,3 +188,64 @@ def test_hcp_split_brute_force_and_identities(orc):
     assert np.all(C == 0)
     R, S = orc.hcp_split_entries(x, w, allh, ii, jj)
     assert np.all(np.abs(C.ravel() + R - (xd @ wd).ravel()) <= 1e-12 * S)
+
+
+def test_gemm_dense_equals_loop_form(orc):
+    """gemm_dense (matrix product of the dequantised operands, with row and
+    column selections) against the plain loop and the integer-block sum,
+    including a NaN scale and ragged sizes."""
+    (ac, as_), (bc, bs) = _qpair(orc, (37, 192), (29, 192), 23)
+    as_ = as_.copy()
+    as_[3, 2] = 0xFF
+    C, S = orc.gemm(ac, as_, bc, bs)
+    Cd, Sd = orc.gemm_dense(ac, as_, bc, bs)
+    nan = np.isnan(C)
+    assert np.array_equal(nan, np.isnan(Cd)) and nan[3].all() and nan.sum() == 29
+    ok = ~nan
+    assert np.all(np.abs(C[ok] - Cd[ok]) <= 1e-13 * S[ok])
+    assert np.allclose(S[ok], Sd[ok], rtol=1e-13, atol=0)
+    Ci = orc.gemm_intblock(ac, as_, bc, bs)
+    assert np.all(np.abs(Ci[ok] - Cd[ok]) <= 1e-13 * S[ok])
+    rows, cols = np.array([0, 36, 5]), np.array([28, 0, 7, 7])
+    Cr, Sr = orc.gemm_dense(ac, as_, bc, bs, rows=rows)
+    Cc, Sc = orc.gemm_dense(ac, as_, bc, bs, cols=cols)
+    for got, want, sw in ((Cr, Cd[rows], Sd[rows]), (Cc, Cd[:, cols], Sd[:, cols])):
+        assert np.array_equal(np.isnan(got), np.isnan(want))
+        f = ~np.isnan(want)
+        assert np.all(np.abs(got[f] - want[f]) <= 1e-13 * sw[f])
+
+
+def test_hcp_residual_dense_equals_entries(orc):
+    M, N, K = 24, 20, 256
+    x = inputs.to_bf16_bits(inputs.normal((M, K), 31))
+    w = inputs.to_bf16_bits(inputs.normal((K, N), 32, 0.02))
+    hot = inputs.hot_channels(K, 33, 0.09)
+    xq = orc.quantize(x, 32)
+    wq = orc.quantize(w, 32, axis=orc.COL)
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    R, S = orc.hcp_residual_entries(x, xq[0], xq[1], w, wq[0], wq[1], hot, ii.ravel(),
+                                    jj.ravel())
+    Rd, Sd = orc.hcp_residual_dense(x, xq[0], xq[1], w, wq[0], wq[1], hot)
+    assert np.all(np.abs(R.reshape(M, N) - Rd) <= 1e-13 * Sd)
+    assert np.allclose(S.reshape(M, N), Sd, rtol=1e-13, atol=0)
+    rows, cols = np.array([23, 0, 4]), np.array([19, 3])
+    Rr, Sr = orc.hcp_residual_dense(x, xq[0], xq[1], w, wq[0], wq[1], hot, rows=rows)
+    Rc, Sc = orc.hcp_residual_dense(x, xq[0], xq[1], w, wq[0], wq[1], hot, cols=cols)
+    assert np.allclose(Rr, Rd[rows], rtol=0, atol=1e-13 * Sd.max())
+    assert np.allclose(Rc, Rd[:, cols], rtol=0, atol=1e-13 * Sd.max())
+
+
+def test_hcp_split_dense_equals_entries(orc):
+    M, N, K = 16, 12, 128
+    x = inputs.to_bf16_bits(inputs.normal((M, K), 41))
+    w = inputs.to_bf16_bits(inputs.normal((K, N), 42, 0.02))
+    hot = inputs.hot_channels(K, 43, 0.1)
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    R, S = orc.hcp_split_entries(x, w, hot, ii.ravel(), jj.ravel())
+    Rd, Sd = orc.hcp_split_dense(x, w, hot)
+    assert np.allclose(R.reshape(M, N), Rd, rtol=0, atol=1e-13 * Sd.max())
+    assert np.allclose(S.reshape(M, N), Sd, rtol=1e-13, atol=0)
+    Rr, _ = orc.hcp_split_dense(x, w, hot, rows=np.array([15, 2]))
+    Rc, _ = orc.hcp_split_dense(x, w, hot, cols=np.array([0, 11]))
+    assert np.allclose(Rr, Rd[[15, 2]], rtol=0, atol=1e-13 * Sd.max())
+    assert np.allclose(Rc, Rd[:, [0, 11]], rtol=0, atol=1e-13 * Sd.max())
