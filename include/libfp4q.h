@@ -268,6 +268,30 @@ fp4q_status_t fp4q_hcp_residual_add(int64_t M, int64_t N, int64_t K, const void*
                                     size_t workspace_bytes, void* stream);
 
 /*
+ * fp4q_hcp_residual_add_noalloc -- fp4q_hcp_residual_add without a caller
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * same kernels and results as fp4q_hcp_residual_add (bit for bit); the
+ * gathered hot operands go to a library-owned device array of
+ * FP4Q_HCP_NOALLOC_MAX_BYTES (64 MiB) instead, which each GPU the library
+ * runs on holds until the process ends.  This call allocates nothing.
+ *   Arguments and limits as fp4q_hcp_residual_add (minus the workspace).
+ *   fp4q_hcp_workspace_bytes(M, N, n_hot) must not exceed
+ *   FP4Q_HCP_NOALLOC_MAX_BYTES, else FP4Q_ERR_WORKSPACE (nothing launched);
+ *   the 16384 x 13824 layer with 461 hot channels needs 56 MB.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (two streams, two threads) race and may corrupt each other's results;
+ *   calls ordered on one stream are safe.  The array's contents are not kept
+ *   between calls (every call writes what it reads).
+ */
+#define FP4Q_HCP_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+fp4q_status_t fp4q_hcp_residual_add_noalloc(int64_t M, int64_t N, int64_t K, const void* x,
+                                            const uint8_t* xq_codes, const uint8_t* xq_scales,
+                                            const void* w, const uint8_t* wq_codes,
+                                            const uint8_t* wq_scales, const int32_t* hot_idx,
+                                            int32_t n_hot, float* y, void* stream);
+
+/*
  * fp4q_gemm_hcp -- hot-channel compensation in the single-kernel mode of the
  * outlier-dynamics page, sec. 3.1 (the hot-channel terms are computed inside
  * the main GEMM instead of by a second kernel):

@@ -24,7 +24,7 @@ EXPORTS = ["fp4q_channel_mask", "fp4q_quantize_masked", "fp4q_gemm_hcp_split",
            "fp4q_quantize", "fp4q_quantize_dual", "fp4q_dequantize", "fp4q_grad_estimate",
            "fp4q_gemm",
            "fp4q_gemm_dge", "fp4q_gemm_quant", "fp4q_hcp_workspace_bytes",
-           "fp4q_hcp_residual_add",
+           "fp4q_hcp_residual_add", "fp4q_hcp_residual_add_noalloc",
            "fp4q_gemm_hcp", "fp4q_hot_channels_workspace_bytes", "fp4q_hot_channels",
            "fp4q_quantize_2d", "fp4q_quantize_rht", "fp4q_occ_max_nnz",
            "fp4q_occ_workspace_bytes", "fp4q_occ_quantize", "fp4q_occ_spmm",
@@ -62,6 +62,8 @@ def lib():
             "fp4q_hcp_workspace_bytes": (SZ, [I64, I64, I32]),
             "fp4q_hcp_residual_add": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, P, SZ,
                                             P]),
+            "fp4q_hcp_residual_add_noalloc": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P,
+                                                    P]),
             "fp4q_gemm_dge": (I32, [I64, I64, I64, P, P, P, P, P, I32, F, F, P, I64, P]),
             "fp4q_gemm_quant": (I32, [I64, I64, I64, P, P, P, P, P, I64, P, P, P]),
             "fp4q_channel_mask": (I32, [P, I32, I64, P, P]),
@@ -275,6 +277,25 @@ def hcp_residual_add(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, y,
                                        _ptr(wq_codes), _ptr(wq_scales), _ptr(hot_idx), n_hot,
                                        _ptr(y), _ptr(workspace), workspace.numel(),
                                        _stream(stream)))
+    return y
+
+
+HCP_NOALLOC_MAX_BYTES = 64 << 20
+
+
+def hcp_residual_add_noalloc(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, y,
+                             stream=None):
+    """hcp_residual_add without a workspace (fp4q_hcp_residual_add_noalloc):
+    the library's own 64 MiB device scratch holds the gathered operands;
+    nothing is allocated.  Calls overlapping on one GPU race."""
+    torch = _torch()
+    M, N, K = _hcp_operands(x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx)
+    _need_cuda(y)
+    _need(y, "y", torch.float32, (M, N))
+    _check(lib().fp4q_hcp_residual_add_noalloc(M, N, K, _ptr(x), _ptr(xq_codes), _ptr(xq_scales),
+                                               _ptr(w), _ptr(wq_codes), _ptr(wq_scales),
+                                               _ptr(hot_idx), hot_idx.numel(), _ptr(y),
+                                               _stream(stream)))
     return y
 
 

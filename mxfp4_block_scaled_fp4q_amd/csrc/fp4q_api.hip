@@ -32,6 +32,9 @@ bool valid_block(int32_t b) { return b == 16 || b == 32 || b == 64 || b == 128; 
 bool valid_dtype(int d) { return d == FP4Q_F32 || d == FP4Q_BF16; }
 int64_t esize(int d) { return d == FP4Q_BF16 ? 2 : 4; }
 
+static_assert(fp4q::kHcpStaticScratchBytes == FP4Q_HCP_NOALLOC_MAX_BYTES,
+              "the header states the size of the library-owned hot-channel scratch");
+
 // Index arithmetic inside the streaming kernels is 32-bit over 8-element
 // chunks; element counts up to 2^33 are accepted.
 constexpr int64_t kMaxElems = (int64_t)1 << 33;
@@ -285,6 +288,38 @@ fp4q_status_t fp4q_hcp_residual_add(int64_t M, int64_t N, int64_t K, const void*
     return hip_status(fp4q::launch_hcp(M, N, K, x, xq_codes, xq_scales, w, wq_codes, wq_scales,
                                        hot_idx, n_hot, y, workspace, (hipStream_t)stream),
                       "hcp launch");
+}
+
+fp4q_status_t fp4q_hcp_residual_add_noalloc(int64_t M, int64_t N, int64_t K, const void* x,
+                                            const uint8_t* xq_codes, const uint8_t* xq_scales,
+                                            const void* w, const uint8_t* wq_codes,
+                                            const uint8_t* wq_scales, const int32_t* hot_idx,
+                                            int32_t n_hot, float* y, void* stream) {
+    if (M <= 0 || N <= 0 || K <= 0 || n_hot < 0)
+        return fail(FP4Q_ERR_INVALID, "hcp_noalloc: bad sizes");
+    if (n_hot > K) return fail(FP4Q_ERR_INVALID, "hcp_noalloc: n_hot > K");
+    if (K % 32) return fail(FP4Q_ERR_INVALID, "hcp_noalloc: K %% 32 != 0");
+    if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
+        return fail(FP4Q_ERR_INVALID, "hcp_noalloc: dimension too large");
+    if (n_hot > (1 << 20)) return fail(FP4Q_ERR_UNSUPPORTED, "hcp_noalloc: n_hot above 2^20");
+    if (n_hot == 0) return FP4Q_OK;
+    if (!x || !xq_codes || !xq_scales || !w || !wq_codes || !wq_scales || !hot_idx || !y)
+        return fail(FP4Q_ERR_INVALID, "hcp_noalloc: null pointer");
+    if (!aligned16(x) || !aligned16(xq_codes) || !aligned16(xq_scales) || !aligned16(w) ||
+        !aligned16(wq_codes) || !aligned16(wq_scales) || !aligned16(hot_idx) || !aligned16(y))
+        return fail(FP4Q_ERR_ALIGNMENT, "hcp_noalloc: pointers must be 16-byte aligned");
+    const size_t need = fp4q::hcp_workspace_bytes(M, N, n_hot);
+    if (need > fp4q::kHcpStaticScratchBytes)
+        return fail(FP4Q_ERR_WORKSPACE,
+                    "hcp_noalloc: these sizes need %zu bytes of scratch, above the library's "
+                    "static maximum of %zu (use fp4q_hcp_residual_add with a workspace)",
+                    need, fp4q::kHcpStaticScratchBytes);
+    void* ws = nullptr;
+    fp4q_status_t st = hip_status(fp4q::hcp_static_scratch(&ws), "hcp_noalloc scratch address");
+    if (st != FP4Q_OK) return st;
+    return hip_status(fp4q::launch_hcp(M, N, K, x, xq_codes, xq_scales, w, wq_codes, wq_scales,
+                                       hot_idx, n_hot, y, ws, (hipStream_t)stream),
+                      "hcp_noalloc launch");
 }
 
 fp4q_status_t fp4q_gemm_dge(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,

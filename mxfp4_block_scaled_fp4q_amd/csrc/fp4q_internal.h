@@ -74,6 +74,12 @@ hipError_t launch_gemm_fp4_quant(int64_t M, int64_t N, int64_t K, const uint8_t*
                                  uint16_t* c, int64_t ldc, uint8_t* qc, uint8_t* qs,
                                  hipStream_t s);
 size_t hcp_workspace_bytes(int64_t M, int64_t N, int32_t n_hot);
+// Size of the library-owned scratch array fp4q_hcp_residual_add_noalloc uses
+// instead of a caller workspace, and the device address of the current
+// device's copy (taken once per device).
+constexpr size_t kHcpStaticScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t hcp_static_scratch(void** out);
 // Split reading: Y = Xq' Wq' + X_H W_H (Xq', Wq' quantised with H zeroed).
 hipError_t launch_gemm_hcp_split(int64_t M, int64_t N, int64_t K, const void* x,
                                  const uint8_t* xqc, const uint8_t* xqs, const void* w,

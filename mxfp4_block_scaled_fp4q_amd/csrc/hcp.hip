@@ -51,6 +51,8 @@
 //    an FP4 fragment), adding into the fp32 Y in its epilogue.
 #include <algorithm>
 
+#include <mutex>
+
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -364,6 +366,37 @@ static hipError_t gather_hot(int64_t M, int64_t N, int64_t K, const void* x, con
     *ap_out = ap;
     *bp_out = bp;
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned scratch for fp4q_hcp_residual_add_noalloc (callers that
+// cannot allocate): the gathered hot operands A' [M, kp] and B' [N, kp] live
+// in this file-scope device array instead of a caller workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code `scratch` is only a stand-in for the symbol: its device address is
+// taken once per device with hipGetSymbolAddress and only that address is
+// ever passed to kernels.  The gathers write every element of A' and B'
+// (padding included), so nothing has to be cleared between calls; calls
+// that overlap on one GPU share the array and race.
+static __device__ __align__(256) uint8_t scratch[kHcpStaticScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxDevices];  // device address of `scratch`, per device
+
+hipError_t hcp_static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current
+        if (e != hipSuccess) return e;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_hcp(int64_t M, int64_t N, int64_t K, const void* x, const uint8_t* xqc,

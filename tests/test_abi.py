@@ -397,3 +397,18 @@ def test_occ_validation(L):
         bad = list(args)
         bad[i] = v
         assert s(*bad) == st, (i, v)
+
+
+def test_hcp_noalloc_validation(L):
+    """The workspace-free hot-channel call refuses, on the host, sizes whose
+    gathered operands exceed its static scratch (nothing is launched)."""
+    h = L.fp4q_hcp_residual_add_noalloc
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert h(64, 64, 1024, *args, 0, FAKE, NUL) == 0                      # no hot channels: no-op
+    assert h(64, 64, 1000, *args, 8, FAKE, NUL) == 1                      # K % 32
+    assert h(64, 64, 1024, *args, 2000, FAKE, NUL) == 1                   # n_hot > K
+    assert h(64, 64, 1024, NUL, *args[1:], 8, FAKE, NUL) == 1             # null x
+    assert h(64, 64, 1024, FAKE_MIS, *args[1:], 8, FAKE, NUL) == 3        # misaligned x
+    assert h(1 << 20, 1 << 16, 1024, *args, 64, FAKE, NUL) == 4           # > 64 MiB of scratch
+    assert b"static maximum" in L.fp4q_last_error()
+    assert fq.hcp_workspace_bytes(1 << 20, 1 << 16, 64) > fq.HCP_NOALLOC_MAX_BYTES
