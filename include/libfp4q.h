@@ -185,7 +185,7 @@ fp4q_status_t fp4q_grad_estimate(fp4q_grad_t mode, const void* x, fp4q_dtype_t x
  *   b_scales [N, K/32] (both K-major, block 32, as fp4q_quantize writes them);
  *   C: [M, N] row-major with row stride ld_c elements, bf16 or fp32 (bf16 is
  *   the round-to-nearest-even of the fp32 accumulator).
- *   block must be 32 (FP4Q_ERR_UNSUPPORTED otherwise); K % 128 == 0 and
+ *   block must be 32 (FP4Q_ERR_UNSUPPORTED otherwise); K % 64 == 0 and
  *   K < 2^24 (larger K: FP4Q_ERR_UNSUPPORTED, since 256 rows of codes are
  *   addressed with 32-bit offsets); M, N < 2^31.
  *   accumulate = 1 adds into an fp32 C (bf16 C: FP4Q_ERR_UNSUPPORTED).
@@ -211,7 +211,7 @@ fp4q_status_t fp4q_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
  *   A, B: as fp4q_gemm (block 32); x: bf16 [M, N] dense, the weight whose
  *   estimator this is, with column blocks of 32 rows (M % 32 == 0);
  *   out: fp32 [M, N], row stride ld_out >= N, written.
- *   k >= 1, clamp_max > 0; K % 128 == 0, K < 2^24.  fp32 x:
+ *   k >= 1, clamp_max > 0; K % 64 == 0, K < 2^24.  fp32 x:
  *   FP4Q_ERR_UNSUPPORTED.  A block of x holding NaN/Inf gives NaN.
  */
 fp4q_status_t fp4q_gemm_dge(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
@@ -226,7 +226,7 @@ fp4q_status_t fp4q_gemm_dge(int64_t M, int64_t N, int64_t K, const uint8_t* a_co
  *   C = fp4q_gemm(A, B) as bf16, then
  *   fp4q_quantize(C, bf16, block 32, FP4Q_BLOCK_ROW, FP4Q_ROUND_RNE)
  * in one kernel, without re-reading C.
- *   A, B: as fp4q_gemm (block 32; K % 128 == 0, K < 2^24).
+ *   A, B: as fp4q_gemm (block 32; K % 64 == 0, K < 2^24).
  *   c: bf16 [M, N] with row stride ld_c >= N, written; may be NULL (then only
  *      the quantisation is written).
  *   y_codes [M, N/2], y_scales [M, N/32]: written (N % 32 == 0).
@@ -304,7 +304,7 @@ fp4q_status_t fp4q_hcp_residual_add_noalloc(int64_t M, int64_t N, int64_t K, con
  *   x, xq_codes, xq_scales, w, wq_codes, wq_scales, hot_idx, n_hot, workspace:
  *       as fp4q_hcp_residual_add (block 32 quantisations: X ROW, W COL).
  *   y   fp32 [M, N], row stride ld_y >= N elements, written.
- *   K % 128 == 0 and K < 2^24 as fp4q_gemm; n_hot <= min(K, 2^20).
+ *   K % 64 == 0 and K < 2^24 as fp4q_gemm; n_hot <= min(K, 2^20).
  *   n_hot = 0: Y is the plain FP4 GEMM (x, w, hot_idx, workspace may be NULL).
  *   Summation order differs from the two-call form (one accumulator), so
  *   results agree with it to fp32 rounding, not bit for bit.

@@ -239,7 +239,7 @@ fp4q_status_t fp4q_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
     if (!valid_block(block)) return fail(FP4Q_ERR_INVALID, "gemm: block %d", block);
     if (block != 32)
         return fail(FP4Q_ERR_UNSUPPORTED, "gemm: only block 32 (the MX hardware block)");
-    if (K % 128) return fail(FP4Q_ERR_INVALID, "gemm: K %% 128 != 0");
+    if (K % 64) return fail(FP4Q_ERR_INVALID, "gemm: K %% 64 != 0");
     if (ld_c < N) return fail(FP4Q_ERR_INVALID, "gemm: ld_c < N");
     if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
         return fail(FP4Q_ERR_INVALID, "gemm: dimension too large");
@@ -331,7 +331,7 @@ fp4q_status_t fp4q_gemm_dge(int64_t M, int64_t N, int64_t K, const uint8_t* a_co
     if (M <= 0 || N <= 0 || K <= 0) return fail(FP4Q_ERR_INVALID, "gemm_dge: bad sizes");
     if (!valid_dtype(x_dtype)) return fail(FP4Q_ERR_INVALID, "gemm_dge: bad x dtype");
     if (x_dtype != FP4Q_BF16) return fail(FP4Q_ERR_UNSUPPORTED, "gemm_dge: x must be bf16");
-    if (K % 128) return fail(FP4Q_ERR_INVALID, "gemm_dge: K %% 128 != 0");
+    if (K % 64) return fail(FP4Q_ERR_INVALID, "gemm_dge: K %% 64 != 0");
     if (M % 32) return fail(FP4Q_ERR_INVALID, "gemm_dge: M %% 32 != 0 (column blocks of x)");
     if (ld_out < N) return fail(FP4Q_ERR_INVALID, "gemm_dge: ld_out < N");
     if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
@@ -358,7 +358,7 @@ fp4q_status_t fp4q_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_t* a_
     if (!a_codes || !a_scales || !b_codes || !b_scales || !y_codes || !y_scales)
         return fail(FP4Q_ERR_INVALID, "gemm_quant: null pointer");
     if (M <= 0 || N <= 0 || K <= 0) return fail(FP4Q_ERR_INVALID, "gemm_quant: bad sizes");
-    if (K % 128) return fail(FP4Q_ERR_INVALID, "gemm_quant: K %% 128 != 0");
+    if (K % 64) return fail(FP4Q_ERR_INVALID, "gemm_quant: K %% 64 != 0");
     if (N % 32) return fail(FP4Q_ERR_INVALID, "gemm_quant: N %% 32 != 0 (ROW blocks of C)");
     if (c && ld_c < N) return fail(FP4Q_ERR_INVALID, "gemm_quant: ld_c < N");
     if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
@@ -385,7 +385,7 @@ fp4q_status_t fp4q_gemm_hcp_split(int64_t M, int64_t N, int64_t K, const void* x
         return fail(FP4Q_ERR_INVALID, "gemm_hcp_split: bad sizes");
     if (!xq_codes || !xq_scales || !wq_codes || !wq_scales || !y)
         return fail(FP4Q_ERR_INVALID, "gemm_hcp_split: null pointer");
-    if (K % 128) return fail(FP4Q_ERR_INVALID, "gemm_hcp_split: K %% 128 != 0");
+    if (K % 64) return fail(FP4Q_ERR_INVALID, "gemm_hcp_split: K %% 64 != 0");
     if (ld_y < N) return fail(FP4Q_ERR_INVALID, "gemm_hcp_split: ld_y < N");
     if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
         return fail(FP4Q_ERR_INVALID, "gemm_hcp_split: dimension too large");
@@ -422,7 +422,7 @@ fp4q_status_t fp4q_gemm_hcp(int64_t M, int64_t N, int64_t K, const void* x,
         return fail(FP4Q_ERR_INVALID, "gemm_hcp: bad sizes");
     if (!xq_codes || !xq_scales || !wq_codes || !wq_scales || !y)
         return fail(FP4Q_ERR_INVALID, "gemm_hcp: null pointer");
-    if (K % 128) return fail(FP4Q_ERR_INVALID, "gemm_hcp: K %% 128 != 0");
+    if (K % 64) return fail(FP4Q_ERR_INVALID, "gemm_hcp: K %% 64 != 0");
     if (ld_y < N) return fail(FP4Q_ERR_INVALID, "gemm_hcp: ld_y < N");
     if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31))
         return fail(FP4Q_ERR_INVALID, "gemm_hcp: dimension too large");

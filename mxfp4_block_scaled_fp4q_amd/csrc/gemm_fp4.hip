@@ -63,9 +63,17 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 static constexpr int BKB = 64;                  // operand bytes per row per K step
 static constexpr int REGION = 1024;             // 16 rows x 64 bytes
 static constexpr int STAGE = 32 * REGION;       // one K step of A and B codes
-static constexpr int SG = 8;                    // K steps per scale group
-static constexpr int SGB = 4 * SG;              // scale bytes per row per group
-static constexpr int SCALE_BUF = 512 * SGB;     // A rows, then B rows
+static constexpr int SROW = 32;                 // LDS bytes per scale row per group
+static constexpr int SCALE_BUF = 512 * SROW;    // A rows, then B rows
+// K steps per scale group: 8 (32 scale bytes per row) when every scale row
+// starts on a 4-byte boundary (K % 128 == 0); 4 when K % 128 == 64, where the
+// rows are only 2-byte aligned and are fetched with 2-byte loads, each of
+// which fills a whole LDS dword (low half data, high half zero), so a group
+// of 16 data bytes still takes 32 bytes of LDS per row.
+template <int TAIL> struct Groups {
+    static constexpr int SG = TAIL ? 4 : 8;
+    static constexpr int SGB = 4 * SG;          // scale bytes per row per group in memory
+};
 static constexpr int GROUP_M = 4;
 static constexpr int BUF_FLAGS = 0x00020000;    // buffer resource word 3: raw 32-bit data
 
@@ -139,30 +147,36 @@ __device__ __forceinline__ void issue_codes(Src<CFG>& src, uint8_t* stage, int w
 }
 
 // Scale piece P (0 .. SPIECES-1) of this wave for group g: combined rows
-// wave*SROWS + P*8 .. +7 (A rows 0..BM-1, then B rows), 32 bytes each; lane
-// 8j + pos loads word pos ^ (P % 4) of the piece's row j, so that in LDS word
-// s of row R sits at R*32 + 4 (s ^ ((R / 8) % 4)) (SROWS / 8 is a multiple of
-// 4).  The group offset is part of the per-lane offset so the range check
-// covers it.
-template <int CFG, int P>
+// wave*SROWS + P*8 .. +7 (A rows 0..BM-1, then B rows), 32 LDS bytes each.
+// Whole words (TAIL = 0): lane 8j + pos loads word pos ^ (P % 4) of the
+// piece's row j, so that in LDS word s of row R sits at R*32 + 4 (s ^ ((R / 8)
+// % 4)) (SROWS / 8 is a multiple of 4).  Half words (TAIL = 1): lane 8j + pos
+// loads half (pos % 2) of word (pos / 2) ^ (P % 4) into LDS dword pos of row
+// j, so that word s of row R is the low halves of the dwords at R*32 +
+// 8 (s ^ ((R / 8) % 4)) and the next one.  The group offset is part of the
+// per-lane offset so the range check covers it.
+template <int CFG, int P, int TAIL>
 __device__ __forceinline__ void issue_scale_piece(const Src<CFG>& src, uint8_t* sbuf, int wave,
                                                   int kscale, int g) {
     // the uniform part as one scalar, so that the compiler does not keep a
     // hoisted per-piece vector offset live across the K loop
-    uint32_t soff = (uint32_t)(P * 8 * kscale + g * SGB);
+    uint32_t soff = (uint32_t)(P * 8 * kscale + g * Groups<TAIL>::SGB);
     asm volatile("" : "+s"(soff));
     const uint32_t voff = src.vsc[P & 3] + soff;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        src.rsc, (lds_ptr_t)(sbuf + (wave * Layout<CFG>::SROWS + P * 8) * SGB), 4, voff, 0, 0, 0);
+    lds_ptr_t dst = (lds_ptr_t)(sbuf + (wave * Layout<CFG>::SROWS + P * 8) * SROW);
+    if constexpr (TAIL)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rsc, dst, 2, voff, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rsc, dst, 4, voff, 0, 0, 0);
 }
 
 // Pieces P0 .. P0+N-1.
-template <int CFG, int P0, int N>
+template <int CFG, int P0, int N, int TAIL>
 __device__ __forceinline__ void issue_scale_pieces(const Src<CFG>& src, uint8_t* sbuf, int wave,
                                                    int kscale, int g) {
     if constexpr (N > 0) {
-        issue_scale_piece<CFG, P0>(src, sbuf, wave, kscale, g);
-        issue_scale_pieces<CFG, P0 + 1, N - 1>(src, sbuf, wave, kscale, g);
+        issue_scale_piece<CFG, P0, TAIL>(src, sbuf, wave, kscale, g);
+        issue_scale_pieces<CFG, P0 + 1, N - 1, TAIL>(src, sbuf, wave, kscale, g);
     }
 }
 
@@ -188,8 +202,20 @@ __device__ __forceinline__ void read_frags(const uint8_t* base, int off, int wm,
 
 // Scale words (4 K blocks of 32 elements each) of step word s of a group
 // for this lane's MFMA rows (A) and columns (B); `sx` is this lane's
-// swizzled byte offset 4 (s ^ ((lane % 32) / 8 % 4)) of that word.
-template <int CFG>
+// swizzled byte offset of that word: 4 (s ^ ((lane % 32) / 8 % 4)) for whole
+// words, 8 (s ^ ...) for the half-word layout (TAIL), whose two dwords carry
+// the word's low and high halves.
+template <int CFG, int TAIL>
+__device__ __forceinline__ uint32_t scale_word(const uint8_t* p) {
+    if constexpr (TAIL) {
+        const uint2 d = *(const uint2*)p;
+        return (d.x & 0xFFFFu) | (d.y << 16);
+    } else {
+        return *(const uint32_t*)p;
+    }
+}
+
+template <int CFG, int TAIL>
 __device__ __forceinline__ void read_scales(const uint8_t* sbuf, int sx, int wm, int wn, int lane,
                                             uint32_t (&sa)[Layout<CFG>::TM],
                                             uint32_t (&sb)[Layout<CFG>::TN]) {
@@ -197,10 +223,10 @@ __device__ __forceinline__ void read_scales(const uint8_t* sbuf, int sx, int wm,
     const int l32 = lane & 31;
 #pragma unroll
     for (int i = 0; i < L::TM; ++i)
-        sa[i] = *(const uint32_t*)(sbuf + (wm * L::WROWS + i * 32 + l32) * SGB + sx);
+        sa[i] = scale_word<CFG, TAIL>(sbuf + (wm * L::WROWS + i * 32 + l32) * SROW + sx);
 #pragma unroll
     for (int j = 0; j < L::TN; ++j)
-        sb[j] = *(const uint32_t*)(sbuf + (L::BM + wn * L::WCOLS + j * 32 + l32) * SGB + sx);
+        sb[j] = scale_word<CFG, TAIL>(sbuf + (L::BM + wn * L::WCOLS + j * 32 + l32) * SROW + sx);
 }
 
 // Shifts raw scale words so that byte 2 kk is the K block of half kk for
@@ -264,8 +290,11 @@ __shared__ __attribute__((aligned(16))) uint8_t sc1[SCALE_BUF];
 // One K loop of the workgroup's tile over operands ac / bc (K-major rows, K
 // elements deep; FP4 with scales as, bs, or bf16 without), accumulating into
 // acc.  Leaves no loads in flight; the caller synchronises before the stages
-// are reused.
-template <int CFG, int BF16OPS>
+// are reused.  TAIL (FP4 only, K % 128 == 64): the last K step holds one half
+// (its second half's MFMAs are skipped; what its loads fetch past the row is
+// never used) and the scale rows, only 2-byte aligned, go through the
+// half-word layout in groups of 4 steps.
+template <int CFG, int BF16OPS, int TAIL>
 __device__ __forceinline__ void gemm_kloop(v16f (&acc)[Layout<CFG>::TM][Layout<CFG>::TN],
                                            const uint8_t* __restrict__ ac,
                                            const uint8_t* __restrict__ as,
@@ -276,11 +305,13 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[Layout<CFG>::TM][Layout<C
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot instantiate buffer resources
     using L = Layout<CFG>;
     constexpr int TM = L::TM, TN = L::TN;
+    static_assert(!(TAIL && BF16OPS), "bf16 K loops are whole steps");
+    constexpr int SG = Groups<TAIL>::SG;
     // bytes per operand row (< 2^23, checked by the caller); each K step
-    // consumes 64 of them
+    // consumes 64 of them (the last one 32 with TAIL)
     const int kbytes = BF16OPS ? K * 2 : K / 2;
     const int kscale = K / 32;
-    const int ksteps = kbytes / BKB;
+    const int ksteps = (kbytes + BKB - 1) / BKB;
 
     Src<CFG> src;
     {
@@ -303,7 +334,9 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[Layout<CFG>::TM][Layout<C
                                                                 (short)0, rows_b * kscale, BUF_FLAGS);
         const int sbase = ((wave < HW ? wave : wave - HW) * L::SROWS + (lane >> 3)) * kscale;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) src.vsc[q] = (uint32_t)(sbase + (((lane & 7) ^ q) << 2));
+        for (int q = 0; q < 4; ++q)
+            src.vsc[q] = TAIL ? (uint32_t)(sbase + ((((lane & 7) >> 1) ^ q) << 2) + ((lane & 1) << 1))
+                              : (uint32_t)(sbase + (((lane & 7) ^ q) << 2));
         src.soff = 0;
     }
     Frags<CFG> FA, FB;
@@ -319,8 +352,10 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[Layout<CFG>::TM][Layout<C
     // Software pipeline over K steps t with a 4-stage code ring: step t
     // issues the code loads of step t + 3 into the stage step t - 1 used
     // (every wave finished reading it before the previous barrier), and, in
-    // the first half of each scale group, two scale pieces of the next group
-    // into the other scale buffer (its previous group ended before).  Each
+    // the first half of each 8-step scale group, two scale pieces of the next
+    // group into the other scale buffer (its previous group ended before);
+    // with TAIL's 4-step groups, all eight pieces in the group's first step
+    // (so that they have landed by the wait at the end of its last step).  Each
     // step computes two halves (K bytes 0..31 and 32..63 of the step); order
     // within a step, fenced against the compiler's scheduler:
     //   1. shift the step's scale words; read the fragments of (t, 1); issue
@@ -329,28 +364,34 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[Layout<CFG>::TM][Layout<C
     //   3. wait for this wave's loads of step t + 1 (later loads stay in
     //      flight) and its LDS reads, then one workgroup barrier;
     //   4. read the scales and (t + 1, 0) fragments; MFMAs of (t, 1).
-    // The loop is unrolled by one scale group (8 steps, two turns of the
-    // ring), so every load count and wait is a compile-time constant.
+    // The loop is unrolled by 16 steps (two or four scale groups, four turns
+    // of the ring), so every load count, wait and LDS buffer is a
+    // compile-time constant.
     constexpr int LC = L::RPW_A + L::RPW_B;  // code loads per wave per step
     // loads issued after the code loads of step t + 1, at the end of step t
     // with t % 8 == p: those of steps t - 1 and t plus the scale pieces
     // issued after the code loads in step t - 2
-#define FP4Q_PIECES(p) ((BF16OPS || ((p) & 7) >= 4) ? 0 : L::SPIECES / 4)
+#define FP4Q_PIECES(p)                                                              \
+    (BF16OPS ? 0 : TAIL ? ((((p) & 3) == 0) ? L::SPIECES : 0)                          \
+                        : ((((p) & 7) >= 4) ? 0 : L::SPIECES / 4))
 #define FP4Q_BEHIND(p) (FP4Q_PIECES((p) + 6) + LC + FP4Q_PIECES((p) + 7) + LC + FP4Q_PIECES(p))
-    if (!BF16OPS) issue_scale_pieces<CFG, 0, L::SPIECES>(src, sc0, wave, kscale, 0);
+    if (!BF16OPS) issue_scale_pieces<CFG, 0, L::SPIECES, TAIL>(src, sc0, wave, kscale, 0);
     issue_codes<CFG, BF16OPS>(src, st0, wave, 1 < ksteps);
     issue_codes<CFG, BF16OPS>(src, st1, wave, 2 < ksteps);
     issue_codes<CFG, BF16OPS>(src, st2, wave, 3 < ksteps);
     FP4Q_WAIT_VMCNT(2 * LC);
     __builtin_amdgcn_s_barrier();
-    if (!BF16OPS) read_scales<CFG>(sc0, sxor << 2, wm, wn, lane, ra, rb);
+    if (!BF16OPS) read_scales<CFG, TAIL>(sc0, TAIL ? sxor << 3 : sxor << 2, wm, wn, lane, ra, rb);
     read_frags<CFG>(st0, off0, wm, wn, FA);
 
-// One K step t = kt + P (P = t % 16, compile-time; its position in the
-// scale group is P % 8).  SCUR / SNXT: scale buffers of this group and the
-// next.  The final step's reads of a next step are harmless (in-bounds,
-// unused), so no step is special.
-#define FP4Q_GEMM_STEP(P, CUR, NEXT1, NEXTL, SCUR, SNXT)                             \
+// One K step t = kt + P (P = t % 16, compile-time; its position in its
+// scale group is P % SG).  The scale buffer of step P's group and of the
+// next group alternate with the group's parity.  The final step's reads of
+// a next step are harmless (in-bounds, unused), so no step is special, except
+// that with TAIL the last step's second half has no data.
+#define FP4Q_SCUR(P) ((((P) / SG) & 1) ? sc1 : sc0)
+#define FP4Q_SNXT(P) ((((P) / SG) & 1) ? sc0 : sc1)
+#define FP4Q_GEMM_STEP(P, CUR, NEXT1, NEXTL)                                         \
     do {                                                                             \
         const int t_ = kt + (P);                                                     \
         __builtin_amdgcn_sched_barrier(0);                                           \
@@ -358,8 +399,9 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[Layout<CFG>::TM][Layout<C
         read_frags<CFG>(CUR, off1, wm, wn, FB);                                       \
         issue_codes<CFG, BF16OPS>(src, NEXTL, wave, t_ + 4 < ksteps);                 \
         if (FP4Q_PIECES(P))                                                          \
-            issue_scale_pieces<CFG, ((P) & 3) * (L::SPIECES / 4), L::SPIECES / 4>(        \
-                src, SNXT, wave, kscale, t_ / SG + 1);                                   \
+            issue_scale_pieces<CFG, TAIL ? 0 : ((P) & 3) * (L::SPIECES / 4),             \
+                               FP4Q_PIECES(P), TAIL>(src, FP4Q_SNXT(P), wave, kscale,      \
+                                                     t_ / SG + 1);                       \
         __builtin_amdgcn_sched_barrier(0);                                           \
         mfma_half<CFG, BF16OPS, 0>(FA, sa, sb, acc);                                  \
         __builtin_amdgcn_sched_barrier(0);                                           \
@@ -368,43 +410,47 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[Layout<CFG>::TM][Layout<C
         __builtin_amdgcn_s_barrier();                                                \
         __builtin_amdgcn_sched_barrier(0);                                           \
         if (!BF16OPS)                                                                \
-            read_scales<CFG>(((P) & 7) == 7 ? SNXT : SCUR, (((P) + 1) & 7 ^ sxor) << 2, wm, wn, \
-                            lane, ra, rb);                                           \
+            read_scales<CFG, TAIL>(((P) % SG) == SG - 1 ? FP4Q_SNXT(P) : FP4Q_SCUR(P),       \
+                                   TAIL ? (((P) + 1) & 3 ^ sxor) << 3                       \
+                                        : (((P) + 1) & 7 ^ sxor) << 2,                      \
+                                   wm, wn, lane, ra, rb);                                \
         read_frags<CFG>(NEXT1, off0, wm, wn, FA);                                     \
-        mfma_half<CFG, BF16OPS, 1>(FB, sa, sb, acc);                                  \
+        if (!TAIL || t_ != ksteps - 1) mfma_half<CFG, BF16OPS, 1>(FB, sa, sb, acc);   \
     } while (0)
 
-// Eight steps of one scale group starting at t = kt + O; GUARD(P) says
-// whether step kt + P exists (compile-time true in full turns).
-#define FP4Q_GEMM_GROUP(O, SCUR, SNXT, GUARD)                                        \
+// Eight steps starting at t = kt + O (two turns of the code ring); GUARD(P)
+// says whether step kt + P exists (compile-time true in full turns).
+#define FP4Q_GEMM_GROUP(O, GUARD)                                                    \
     do {                                                                             \
-        if (GUARD(O + 0)) FP4Q_GEMM_STEP(O + 0, st0, st1, st3, SCUR, SNXT);          \
-        if (GUARD(O + 1)) FP4Q_GEMM_STEP(O + 1, st1, st2, st0, SCUR, SNXT);          \
-        if (GUARD(O + 2)) FP4Q_GEMM_STEP(O + 2, st2, st3, st1, SCUR, SNXT);          \
-        if (GUARD(O + 3)) FP4Q_GEMM_STEP(O + 3, st3, st0, st2, SCUR, SNXT);          \
-        if (GUARD(O + 4)) FP4Q_GEMM_STEP(O + 4, st0, st1, st3, SCUR, SNXT);          \
-        if (GUARD(O + 5)) FP4Q_GEMM_STEP(O + 5, st1, st2, st0, SCUR, SNXT);          \
-        if (GUARD(O + 6)) FP4Q_GEMM_STEP(O + 6, st2, st3, st1, SCUR, SNXT);          \
-        if (GUARD(O + 7)) FP4Q_GEMM_STEP(O + 7, st3, st0, st2, SCUR, SNXT);          \
+        if (GUARD(O + 0)) FP4Q_GEMM_STEP(O + 0, st0, st1, st3);                       \
+        if (GUARD(O + 1)) FP4Q_GEMM_STEP(O + 1, st1, st2, st0);                       \
+        if (GUARD(O + 2)) FP4Q_GEMM_STEP(O + 2, st2, st3, st1);                       \
+        if (GUARD(O + 3)) FP4Q_GEMM_STEP(O + 3, st3, st0, st2);                       \
+        if (GUARD(O + 4)) FP4Q_GEMM_STEP(O + 4, st0, st1, st3);                       \
+        if (GUARD(O + 5)) FP4Q_GEMM_STEP(O + 5, st1, st2, st0);                       \
+        if (GUARD(O + 6)) FP4Q_GEMM_STEP(O + 6, st2, st3, st1);                       \
+        if (GUARD(O + 7)) FP4Q_GEMM_STEP(O + 7, st3, st0, st2);                       \
     } while (0)
 #define FP4Q_ALL(P) true
 #define FP4Q_EXISTS(P) (kt + (P) < ksteps)
 
-    // Step t uses code stage t % 4 and scale buffer (t / 8) % 2; a turn of
-    // the loops covers two groups so both buffers are named at compile time
-    // (the compiler then sees that scale reads and the loads in flight touch
+    // Step t uses code stage t % 4 and scale buffer (t / SG) % 2; a turn of
+    // the loop covers 16 steps so every buffer is named at compile time (the
+    // compiler then sees that scale reads and the loads in flight touch
     // different LDS objects).
     int kt = 0;
-    for (; kt + 2 * SG <= ksteps; kt += 2 * SG) {
-        FP4Q_GEMM_GROUP(0, sc0, sc1, FP4Q_ALL);
-        FP4Q_GEMM_GROUP(8, sc1, sc0, FP4Q_ALL);
+    for (; kt + 16 <= ksteps; kt += 16) {
+        FP4Q_GEMM_GROUP(0, FP4Q_ALL);
+        FP4Q_GEMM_GROUP(8, FP4Q_ALL);
     }
     if (kt < ksteps) {
-        FP4Q_GEMM_GROUP(0, sc0, sc1, FP4Q_EXISTS);
-        FP4Q_GEMM_GROUP(8, sc1, sc0, FP4Q_EXISTS);
+        FP4Q_GEMM_GROUP(0, FP4Q_EXISTS);
+        FP4Q_GEMM_GROUP(8, FP4Q_EXISTS);
     }
 #undef FP4Q_GEMM_GROUP
 #undef FP4Q_GEMM_STEP
+#undef FP4Q_SCUR
+#undef FP4Q_SNXT
 #undef FP4Q_ALL
 #undef FP4Q_EXISTS
 #undef FP4Q_PIECES
@@ -423,7 +469,8 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[Layout<CFG>::TM][Layout<C
 // EPI = 2 (bf16 C, 256 x 256 tiles, N % 32 == 0): the bf16 C is also
 // quantised (ROW blocks of 32, nearest-even) into qc [M, N/2] and qs
 // [M, N/32], as fp4q_quantize would from the stored C; cptr may be null.
-template <int CFG, int OUT_BF16, int ACCUM, int OPS, int EPI = 0>
+// TAIL: K % 128 == 64 (the FP4 K loop ends on a half step; see gemm_kloop).
+template <int CFG, int OUT_BF16, int ACCUM, int OPS, int EPI = 0, int TAIL = 0>
 __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
     int M, int N, int K, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, void* __restrict__ cptr,
@@ -476,7 +523,7 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
 
 
 #define FP4Q_KLOOP(BF, A_, AS_, B_, BS_, KD_)                                              \
-    gemm_kloop<CFG, BF>(acc, A_, AS_, B_, BS_, KD_, M, N, m0, n0, wave, lane, wm, wn, half, l32, \
+    gemm_kloop<CFG, BF, BF ? 0 : TAIL>(acc, A_, AS_, B_, BS_, KD_, M, N, m0, n0, wave, lane, wm, wn, half, l32, \
                        off0, off1, sxor)
     if (OPS == 1) {
         FP4Q_KLOOP(1, ac, as, bc, bs, K);
@@ -714,10 +761,19 @@ static void launch_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
     using L = Layout<CFG>;
     const int tiles_m = (int)((M + L::BM - 1) / L::BM);
     const int tiles_n = (int)((N + L::BN - 1) / L::BN);
-    gemm_fp4_kernel<CFG, OUT_BF16, ACCUM, OPS, EPI>
-        <<<dim3((unsigned)(tiles_m * tiles_n)), L::THREADS, 0, s>>>(
-            (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m, tiles_n, ha, hb, (int)kp, ex,
-            dp, qc, qs);
+    const dim3 grid((unsigned)(tiles_m * tiles_n));
+    // an FP4 K loop that ends on a half step (K % 128 == 64) takes the TAIL form
+    if constexpr (OPS != 1) {
+        if (K % 128) {
+            gemm_fp4_kernel<CFG, OUT_BF16, ACCUM, OPS, EPI, 1><<<grid, L::THREADS, 0, s>>>(
+                (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m, tiles_n, ha, hb, (int)kp,
+                ex, dp, qc, qs);
+            return;
+        }
+    }
+    gemm_fp4_kernel<CFG, OUT_BF16, ACCUM, OPS, EPI, 0><<<grid, L::THREADS, 0, s>>>(
+        (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m, tiles_n, ha, hb, (int)kp, ex, dp,
+        qc, qs);
 }
 
 template <int OUT_BF16, int ACCUM, int OPS>

@@ -100,7 +100,8 @@ def test_gemm_validation(L):
     assert call(M=0) == 1
     assert call(blk=16) == 2            # valid block, not the MX hardware block
     assert call(blk=12) == 1
-    assert call(K=192) == 1             # K % 128
+    assert call(K=160) == 1             # K % 64
+    assert call(K=96) == 1
     assert call(K=1 << 24) == 2         # 256 rows of codes exceed 32-bit offsets
     assert call(ldc=32) == 1
     assert call(acc=1, cdt=1) == 2      # accumulate into bf16
@@ -192,7 +193,7 @@ def test_gemm_hcp_validation(L):
     bad[10] = (1 << 20) + 1
     assert h(*bad) == 2
     bad = list(args)
-    bad[2] = 160         # K % 128 (the FP4 GEMM's K step)
+    bad[2] = 160         # K % 64 (the FP4 GEMM's half step)
     assert h(*bad) == 1
     bad = list(args)
     bad[2] = 1 << 24     # K beyond the GEMM's 32-bit row offsets
@@ -222,7 +223,7 @@ def test_gemm_dge_validation(L):
     bad[0] = 250         # M % 32 (column blocks of x)
     assert h(*bad) == 1
     bad = list(args)
-    bad[2] = 192         # K % 128
+    bad[2] = 160         # K % 64
     assert h(*bad) == 1
     bad = list(args)
     bad[8] = 0           # fp32 x
@@ -257,7 +258,7 @@ def test_gemm_quant_validation(L):
     bad[1] = 48          # N % 32 (ROW blocks of C)
     assert h(*bad) == 1
     bad = list(args)
-    bad[2] = 192         # K % 128
+    bad[2] = 160         # K % 64
     assert h(*bad) == 1
     bad = list(args)
     bad[8] = 63          # ld_c < N

@@ -62,7 +62,11 @@ TILES = ["256x256", "128x384"]
 
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (300, 200, 256), (257, 129, 384),
-                                   (64, 520, 128), (513, 33, 1024), (129, 769, 256)])
+                                   (64, 520, 128), (513, 33, 1024), (129, 769, 256),
+                                   # K % 128 == 64: the K loop ends on a half step and the
+                                   # scale rows are only 2-byte aligned
+                                   (1, 1, 64), (300, 200, 192), (257, 129, 320),
+                                   (129, 769, 64), (520, 300, 2112)])
 def test_ragged_gemm(orc, M, N, K, tile, monkeypatch):
     monkeypatch.setenv("FP4Q_GEMM_TILE", tile)
     a = inputs.with_outliers(inputs.normal((M, K), M), M + 1, max(1, M * K // 100), 50.0)
@@ -73,7 +77,8 @@ def test_ragged_gemm(orc, M, N, K, tile, monkeypatch):
     gemm_full_check(orc, A, B, torch.float32, accumulate=True, seed=M)
 
 
-@pytest.mark.parametrize("M,N,K", [(8192, 5632, 2048), (2048, 5632, 8192), (700, 1000, 512)])
+@pytest.mark.parametrize("M,N,K", [(8192, 5632, 2048), (2048, 5632, 8192), (700, 1000, 512),
+                                   (700, 1000, 576)])
 def test_gemm_tiles_bit_identical(M, N, K, monkeypatch):
     """Both tile shapes accumulate each output over K in the same order: the
     outputs agree bit for bit (bf16 and fp32 C), including ragged edges."""
@@ -93,7 +98,7 @@ def test_gemm_tiles_bit_identical(M, N, K, monkeypatch):
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 32, 128), (300, 288, 256), (513, 1056, 384),
-                                   (8192, 5632, 2048)])
+                                   (300, 288, 320), (8192, 5632, 2048)])
 def test_gemm_quant_epilogue(orc, M, N, K):
     """fp4q_gemm_quant against the oracle: its bf16 C inside the rounded
     bracket of the oracle's product (every output), and its codes and scales
@@ -216,6 +221,7 @@ def test_ffn_backward_gemms_and_dge(orc):
 
 
 @pytest.mark.parametrize("M,N,K,k", [(32, 1, 128, 5.0), (96, 200, 256, 5.0), (320, 517, 384, 5.0),
+                                     (96, 200, 192, 5.0), (64, 70, 64, 3.0),
                                      (256, 256, 512, 1.0), (64, 388, 128, 3.0)])
 def test_gemm_dge_small(orc, M, N, K, k):
     """fp4q_gemm_dge against the oracle (GEMM entries times the oracle's DGE
@@ -332,6 +338,7 @@ def test_hcp_empty_is_noop(orc):
 
 
 @pytest.mark.parametrize("M,N,K,n_hot,ld_pad", [(64, 96, 256, 23, 0), (300, 257, 512, 46, 3),
+                                                (64, 96, 320, 29, 1), (33, 65, 64, 6, 0),
                                                 (1, 33, 128, 1, 0), (128, 128, 256, 256, 0),
                                                 (513, 260, 384, 0, 1), (64, 40, 16384, 37, 0),
                                                 (48, 40, 8192, 500, 2)])

@@ -63,7 +63,7 @@ def test_quantize_masked(orc, dtype, axis, rounding):
 
 
 # N a multiple of 8: the GPU quantiser takes 16-byte-aligned rows of W
-@pytest.mark.parametrize("M,N,K,n_hot", [(64, 96, 256, 23), (300, 264, 512, 46),
+@pytest.mark.parametrize("M,N,K,n_hot", [(64, 96, 256, 23), (300, 264, 512, 46), (64, 96, 192, 17),
                                          (1, 40, 128, 1), (128, 128, 256, 256),
                                          (96, 64, 128, 0)])
 def test_gemm_hcp_split(orc, M, N, K, n_hot):
