@@ -49,7 +49,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--hcp", action="store_true",
-                   help="also time the 13B-shaped GEMM + hot-channel residual (reported aside)")
+                   help="(kept for compatibility: the 13B-shaped layer is part of the default run)")
+    p.add_argument("--skip-configs", action="store_true",
+                   help="skip the activation-sweep and 13B-shaped outlier-layer measurements")
     p.add_argument("--profile-op", default=None,
                    help="run only this step kernel (or 'copy', a plain 256 MiB device copy) "
                         "--reps times and exit: the target of rocprofv3 counter runs")
@@ -342,7 +344,10 @@ def main():
     quant.update(qhead)
 
     extra = {"copy_ceiling_GBps": copy_ceiling(torch, dev)}
-    if args.hcp:
+    if not args.skip_configs:
+        # the other workloads: the activation sweep (every block size, both
+        # roundings, dequantize, STE and DGE) and the 13B-shaped outlier layer
+        extra["activation_sweep"] = bench_activation_sweep(torch, fq, inputs, dev)
         extra["outlier_layer"] = bench_outlier_layer(torch, fq, inputs, dev)
 
     cpu = None
@@ -455,8 +460,66 @@ def copy_ceiling(torch, dev):
     return round(2 * 4 * n / secs / 1e9, 1)
 
 
+def _stream_us(torch, fn, n=50):
+    """Mean time per launch of n back-to-back launches between one pair of
+    events (the per-launch event turnaround is not counted)."""
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def _rate(nbytes, us):
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
+def bench_activation_sweep(torch, fq, inputs, dev):
+    """Activation sweep: bf16 4096x2048 = 0.5 * Student-t(3), ROW blocks of
+    16/32/64/128, nearest-even and stochastic (seed 1234); dequantize of each
+    back to bf16; STE and DGE(k=5, clamp 3, blocks of 32) on a bf16 N(0,1)
+    gradient.  Each kernel is launched 50 times back to back (inputs stay in
+    the caches: 16.8 MB tensors; a launch lasts a few microseconds, so these
+    rates include each launch's ramp-up and drain)."""
+    d = inputs.activation_sweep()
+    R, C = d["X"].shape
+
+    def to_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, G = to_bf16(d["X"]), to_bf16(d["G"])
+    n = R * C
+    out = {"shape": [R, C]}
+    y = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+    for b in (16, 32, 64, 128):
+        codes = torch.empty((R, C // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((R, C // b), dtype=torch.uint8, device=dev)
+        qbytes = n * (2 + 0.5 + 1.0 / b)
+        for name, rnd in (("rne", fq.RNE), ("sr", fq.SR)):
+            us = _stream_us(torch, lambda: fq.quantize(X, b, fq.ROW, rnd, d["sr_seed"], codes=codes,
+                                                       scales=scales))
+            out[f"quant_b{b}_{name}"] = _rate(qbytes, us)
+        us = _stream_us(torch, lambda: fq.dequantize(codes, scales, b, out=y))
+        out[f"dequant_b{b}"] = _rate(qbytes, us)
+    us = _stream_us(torch, lambda: fq.grad_estimate(fq.STE, None, G, 32, fq.ROW, out=y))
+    out["ste"] = _rate(n * 4, us)
+    us = _stream_us(torch, lambda: fq.grad_estimate(fq.DGE, X, G, 32, fq.ROW, 5.0, 3.0, out=y))
+    out["dge"] = _rate(n * 6, us)
+    return out
+
+
 def bench_outlier_layer(torch, fq, inputs, dev):
-    """13B-shaped layer: fp32 base GEMM 16384x13824x5120 + hot-channel residual."""
+    """13B-shaped outlier layer (X 16384x5120 with 461 hot channels x100, W
+    5120x13824): X ROW and W COL quantisation, the fp32 base GEMM, the
+    dual-kernel hot-channel residual, the single-kernel and split forms and
+    the on-device hot-channel choice; 5 back-to-back launches each between
+    one pair of events."""
     d = inputs.outlier_layer()
     M, K = d["X"].shape
     N = d["W"].shape[1]
@@ -504,18 +567,26 @@ def bench_outlier_layer(torch, fq, inputs, dev):
         torch.cuda.synchronize()
         res[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 1)
     res["gemm_TFLOPS"] = round(2.0 * M * N * K / (res["gemm_fp32_us"] * 1e-6) / 1e12, 1)
+    res["gemm_frac_fp4_peak"] = round(res["gemm_TFLOPS"] / PEAK_FP4_TFLOPS, 4)
     qb = 2.53125
     res["quant_x_row_GBps"] = round(M * K * qb / (res["quant_x_row_us"] * 1e-6) / 1e9, 1)
     res["quant_w_col_GBps"] = round(K * N * qb / (res["quant_w_col_us"] * 1e-6) / 1e9, 1)
+    res["quant_x_row_frac_hbm_peak"] = round(res["quant_x_row_GBps"] / PEAK_HBM_GBPS, 4)
+    res["quant_w_col_frac_hbm_peak"] = round(res["quant_w_col_GBps"] / PEAK_HBM_GBPS, 4)
     res["hcp_n_hot"] = int(hot.numel())
     # the choice reads X once (bf16); the partial-sum rows are small beside it
     res["hot_channels_GBps"] = round(2.0 * M * K / (res["hot_channels_us"] * 1e-6) / 1e9, 1)
     res["hot_channels_match_planted"] = bool(torch.equal(hsel, hot))
+    # D mode: the residual's floor is the fp32 read-modify-write of Y (8 B per
+    # output) plus the gathered operands written and read once
+    kp = (2 * int(hot.numel()) + 31) // 32 * 32
+    hcp_bytes = 8.0 * M * N + 2.0 * 2.0 * (M + N) * kp
+    res["hcp_residual_GBps"] = round(hcp_bytes / (res["hcp_residual_us"] * 1e-6) / 1e9, 1)
+    res["hcp_residual_frac_hbm_peak"] = round(res["hcp_residual_GBps"] / PEAK_HBM_GBPS, 4)
     res["hcp_y_rmw_GBps"] = round(8.0 * M * N / (res["hcp_residual_us"] * 1e-6) / 1e9, 1)
     # dual-kernel mode (base GEMM, then the residual's read-modify-write of Y)
     # against the single kernel that writes Y once
     res["hcp_two_kernel_total_us"] = round(res["gemm_fp32_us"] + res["hcp_residual_us"], 1)
-    kp = (2 * int(hot.numel()) + 31) // 32 * 32
     res["gemm_hcp_single_flops"] = 2.0 * M * N * K + 2.0 * M * N * kp
     res["gemm_hcp_single_TFLOPS"] = round(res["gemm_hcp_single_flops"] /
                                           (res["gemm_hcp_single_us"] * 1e-6) / 1e12, 1)

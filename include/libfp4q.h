@@ -360,6 +360,26 @@ fp4q_status_t fp4q_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_
                                uint8_t* col_scales, void* stream);
 
 /*
+ * fp4q_quantize_2d_tile -- fp4q_quantize_2d with the square side as an
+ * argument: tile = 32 is fp4q_quantize_2d; tile = 16 gives the 16 x 16
+ * backward blocks that the outlier-dynamics page's configuration names
+ * (sec. 4.2), one E8M0 scale per 16 x 16 square (scale from the square's
+ * largest |x|, elements rounded as fp4q_quantize rounds them, SR counters
+ * r*cols + c + rng_offset), written in the same two layouts with block 16:
+ *   row_codes [rows, cols/2], row_scales [rows, cols/16];
+ *   col_codes [cols, rows/2], col_scales [cols, rows/16].
+ * Each layout dequantises with fp4q_dequantize(..., block = 16).  The
+ * hardware GEMM takes one scale per 32 elements, so the 16 x 16 form is a
+ * quantise/dequantise form; 32 x 32 is the GEMM-feeding one.
+ *   tile 16 or 32 (else FP4Q_ERR_INVALID); other arguments, limits and errors
+ *   as fp4q_quantize_2d (rows % 32 == 0, cols % 32 == 0 for both tiles).
+ */
+fp4q_status_t fp4q_quantize_2d_tile(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                    int32_t tile, fp4q_round_t round, uint64_t seed,
+                                    uint64_t rng_offset, uint8_t* row_codes, uint8_t* row_scales,
+                                    uint8_t* col_codes, uint8_t* col_scales, void* stream);
+
+/*
  * fp4q_quantize_rht -- random Hadamard transform, then block-32 quantisation
  * (the recipe on the outlier-dynamics page, sec. 4.1, transforms the
  * backward pass's operands before quantising them).  Along the block axis,

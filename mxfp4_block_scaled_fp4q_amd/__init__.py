@@ -26,7 +26,7 @@ EXPORTS = ["fp4q_channel_mask", "fp4q_quantize_masked", "fp4q_gemm_hcp_split",
            "fp4q_gemm_dge", "fp4q_gemm_quant", "fp4q_hcp_workspace_bytes",
            "fp4q_hcp_residual_add", "fp4q_hcp_residual_add_noalloc",
            "fp4q_gemm_hcp", "fp4q_hot_channels_workspace_bytes", "fp4q_hot_channels",
-           "fp4q_quantize_2d", "fp4q_quantize_rht", "fp4q_occ_max_nnz",
+           "fp4q_quantize_2d", "fp4q_quantize_2d_tile", "fp4q_quantize_rht", "fp4q_occ_max_nnz",
            "fp4q_occ_workspace_bytes", "fp4q_occ_quantize", "fp4q_occ_spmm",
            "fp4q_status_string",
            "fp4q_last_error", "fp4q_abi_version"]
@@ -74,6 +74,7 @@ def lib():
             "fp4q_gemm_hcp": (I32, [I64, I64, I64, P, P, P, P, P, P, P, I32, P, I64, P, SZ, P]),
             "fp4q_hot_channels_workspace_bytes": (SZ, [I64, I64]),
             "fp4q_quantize_2d": (I32, [P, I64, I64, I64, I32, U64, U64, P, P, P, P, P]),
+            "fp4q_quantize_2d_tile": (I32, [P, I64, I64, I64, I32, I32, U64, U64, P, P, P, P, P]),
             "fp4q_quantize_rht": (I32, [P, I64, I64, I64, I32, P, I32, U64, U64, P, P, P]),
             "fp4q_occ_max_nnz": (I64, [I64, I64, _ct.c_double]),
             "fp4q_occ_workspace_bytes": (SZ, [I64, I64]),
@@ -445,21 +446,26 @@ def hot_channels(x, n_hot, hot_idx=None, err=None, want_err=False, workspace=Non
     return (hot_idx, err) if want_err else hot_idx
 
 
-def quantize_2d(x, rounding=RNE, seed=0, rng_offset=0, out=None, stream=None):
-    """One E8M0 scale per 32 x 32 square of the bf16 x (fp4q_quantize_2d).
-    Returns (row_codes, row_scales, col_codes, col_scales): the same codes in
-    the ROW layout [R, C/2], [R, C/32] and the COL layout [C, R/2], [C, R/32]."""
+def quantize_2d(x, rounding=RNE, seed=0, rng_offset=0, out=None, stream=None, tile=32):
+    """One E8M0 scale per tile x tile square of the bf16 x (fp4q_quantize_2d,
+    or fp4q_quantize_2d_tile for tile 16).  Returns (row_codes, row_scales,
+    col_codes, col_scales): the same codes in the ROW layout [R, C/2],
+    [R, C/tile] and the COL layout [C, R/2], [C, R/tile]."""
     torch = _torch()
     _need_cuda(x)
     R, C = x.shape
     if out is None:
         dev = x.device
         out = (torch.empty((R, C // 2), dtype=torch.uint8, device=dev),
-               torch.empty((R, C // 32), dtype=torch.uint8, device=dev),
+               torch.empty((R, C // tile), dtype=torch.uint8, device=dev),
                torch.empty((C, R // 2), dtype=torch.uint8, device=dev),
-               torch.empty((C, R // 32), dtype=torch.uint8, device=dev))
-    _check(lib().fp4q_quantize_2d(_ptr(x), R, C, x.stride(0), rounding, seed, rng_offset,
-                                  *(_ptr(t) for t in out), _stream(stream)))
+               torch.empty((C, R // tile), dtype=torch.uint8, device=dev))
+    if tile == 32:
+        _check(lib().fp4q_quantize_2d(_ptr(x), R, C, x.stride(0), rounding, seed, rng_offset,
+                                      *(_ptr(t) for t in out), _stream(stream)))
+    else:
+        _check(lib().fp4q_quantize_2d_tile(_ptr(x), R, C, x.stride(0), tile, rounding, seed,
+                                           rng_offset, *(_ptr(t) for t in out), _stream(stream)))
     return out
 
 

@@ -484,12 +484,13 @@ fp4q_status_t fp4q_hot_channels(const void* x, int64_t rows, int64_t cols, int64
                       "hot_channels launch");
 }
 
-fp4q_status_t fp4q_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
-                               fp4q_round_t round, uint64_t seed, uint64_t rng_offset,
-                               uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
-                               uint8_t* col_scales, void* stream) {
+fp4q_status_t fp4q_quantize_2d_tile(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                    int32_t tile, fp4q_round_t round, uint64_t seed,
+                                    uint64_t rng_offset, uint8_t* row_codes, uint8_t* row_scales,
+                                    uint8_t* col_codes, uint8_t* col_scales, void* stream) {
     if (!x || !row_codes || !row_scales || !col_codes || !col_scales)
         return fail(FP4Q_ERR_INVALID, "quantize_2d: null pointer");
+    if (tile != 16 && tile != 32) return fail(FP4Q_ERR_INVALID, "quantize_2d: tile must be 16 or 32");
     if (rows <= 0 || cols <= 0)
         return fail(FP4Q_ERR_INVALID, "quantize_2d: rows=%lld cols=%lld", (long long)rows,
                     (long long)cols);
@@ -504,10 +505,18 @@ fp4q_status_t fp4q_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_
         !aligned16(col_codes) || !aligned16(col_scales) || ld_x % 8)
         return fail(FP4Q_ERR_ALIGNMENT,
                     "quantize_2d: pointers and the row stride must be 16-byte aligned");
-    return hip_status(fp4q::launch_quantize_2d(x, rows, cols, ld_x, round == FP4Q_SR, seed,
+    return hip_status(fp4q::launch_quantize_2d(x, rows, cols, ld_x, tile, round == FP4Q_SR, seed,
                                                rng_offset, row_codes, row_scales, col_codes,
                                                col_scales, (hipStream_t)stream),
                       "quantize_2d launch");
+}
+
+fp4q_status_t fp4q_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_t ld_x,
+                               fp4q_round_t round, uint64_t seed, uint64_t rng_offset,
+                               uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
+                               uint8_t* col_scales, void* stream) {
+    return fp4q_quantize_2d_tile(x, rows, cols, ld_x, 32, round, seed, rng_offset, row_codes,
+                                 row_scales, col_codes, col_scales, stream);
 }
 
 fp4q_status_t fp4q_quantize_rht(const void* x, int64_t rows, int64_t cols, int64_t ld_x,

@@ -101,9 +101,10 @@ hipError_t launch_hot_channels(const uint16_t* x, int64_t rows, int64_t cols, in
                                hipStream_t s);
 // 2D (32 x 32 square) block scaling of a bf16 [rows, cols]: the same codes
 // in the ROW and the COL layout.
-hipError_t launch_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_t ld, bool sr,
-                              uint64_t seed, uint64_t off, uint8_t* codes_r, uint8_t* scales_r,
-                              uint8_t* codes_c, uint8_t* scales_c, hipStream_t s);
+hipError_t launch_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_t ld, int tile,
+                              bool sr, uint64_t seed, uint64_t off, uint8_t* codes_r,
+                              uint8_t* scales_r, uint8_t* codes_c, uint8_t* scales_c,
+                              hipStream_t s);
 // Block-32 quantisation of c * H32 * D * x along the block axis (ROW: along
 // columns; COL: along rows, K-major output), D from the sign mask.
 hipError_t launch_quantize_rht(const void* x, int64_t rows, int64_t cols, int64_t ld, bool col,

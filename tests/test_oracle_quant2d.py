@@ -1,5 +1,5 @@
 """Pins of the oracle's two-dimensional block scaling (one scale per 32 x 32
-square, outlier-dynamics page, sec. 4.1): codes and scales against the
+or 16 x 16 square, outlier-dynamics page, sec. 4.1-4.2): codes and scales against the
 brute-force quantiser applied square by square; the COL form equal to the
 ROW form of the transpose; both forms dequantising to the same matrix (W and
 W^T share one quantisation); reduction to the pinned 1D quantiser where every
@@ -21,37 +21,39 @@ def pack_rows(codes):
     return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
 
 
-def test_brute_force_squares(orc):
+@pytest.mark.parametrize("t", [32, 16])
+def test_brute_force_squares(orc, t):
     xf = inputs.with_outliers(inputs.normal((64, 96), 921), 922, 30, 50.0)
     xb = inputs.to_bf16_bits(xf)
     xv = bf16_values(xb)
-    cr, sr, cc, sc = orc.quantize_2d(xb)
+    cr, sr, cc, sc = orc.quantize_2d(xb, tile=t)
     codes = np.zeros(xv.shape, np.int64)
-    scl = np.zeros((2, 3), np.int64)
-    for tr in range(2):
-        for tc in range(3):
-            sq = xv[32 * tr:32 * tr + 32, 32 * tc:32 * tc + 32]
+    scl = np.zeros((64 // t, 96 // t), np.int64)
+    for tr in range(64 // t):
+        for tc in range(96 // t):
+            sq = xv[t * tr:t * tr + t, t * tc:t * tc + t]
             e = scale_exp(float(np.abs(sq).max()))
             scl[tr, tc] = e + 127
-            for i in range(32):
-                for j in range(32):
-                    codes[32 * tr + i, 32 * tc + j] = nearest_code(float(sq[i, j]), e)
+            for i in range(t):
+                for j in range(t):
+                    codes[t * tr + i, t * tc + j] = nearest_code(float(sq[i, j]), e)
     np.testing.assert_array_equal(cr, pack_rows(codes))
     np.testing.assert_array_equal(cc, pack_rows(codes.T))
-    np.testing.assert_array_equal(sr, np.repeat(scl, 32, axis=0))
-    np.testing.assert_array_equal(sc, np.repeat(scl.T, 32, axis=0))
+    np.testing.assert_array_equal(sr, np.repeat(scl, t, axis=0))
+    np.testing.assert_array_equal(sc, np.repeat(scl.T, t, axis=0))
 
 
+@pytest.mark.parametrize("t", [32, 16])
 @pytest.mark.parametrize("rnd", ["rne", "sr"])
-def test_both_forms_hold_one_matrix(orc, rnd):
+def test_both_forms_hold_one_matrix(orc, rnd, t):
     xb = inputs.to_bf16_bits(inputs.student_t((96, 160), 923))
     r = orc.RNE if rnd == "rne" else orc.SR
-    cr, sr, cc, sc = orc.quantize_2d(xb, round=r, seed=77, rng_offset=5)
-    a = orc.dequantize(cr, sr, 32)
-    b = orc.dequantize(cc, sc, 32)
+    cr, sr, cc, sc = orc.quantize_2d(xb, tile=t, round=r, seed=77, rng_offset=5)
+    a = orc.dequantize(cr, sr, t)
+    b = orc.dequantize(cc, sc, t)
     np.testing.assert_array_equal(a, b.T)
     if rnd == "rne":
-        cr2, sr2, cc2, sc2 = orc.quantize_2d(np.ascontiguousarray(xb.T))
+        cr2, sr2, cc2, sc2 = orc.quantize_2d(np.ascontiguousarray(xb.T), tile=t)
         np.testing.assert_array_equal(cc, cr2)
         np.testing.assert_array_equal(sc, sr2)
         np.testing.assert_array_equal(cr, cc2)
