@@ -42,7 +42,11 @@
 // buffer ranges).  The epilogue stages each wave's tile in LDS so every lane
 // writes 16 contiguous bytes.  Workgroups are remapped so that consecutive
 // tiles of a grouped (4 tile-rows) order run on the same XCD and share its
-// L2.
+// L2.  Where there are more 256 x 256 tiles than compute units and K is a
+// multiple of 2048, a persistent form runs instead (one workgroup per compute
+// unit walking its tiles with the operand ring running on across tiles; see
+// gemm_fp4_persistent_kernel).
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -100,12 +104,13 @@ struct Layout {
     static constexpr int RPW_A = RA / WAVES, RPW_B = RB / WAVES;
     static constexpr int RPW = RPW_A > RPW_B ? RPW_A : RPW_B;
     static constexpr int OFF_B = RA * REGION;         // B codes within a stage
-    static constexpr int SROWS = 64;                  // scale rows fetched per wave
+    static constexpr int SROWS = 512 / WAVES;         // scale rows fetched per wave
     static constexpr int SPIECES = SROWS / 8;         // 8-row scale pieces per wave per group
     static constexpr int A_SWAVES = BM / SROWS;       // waves fetching A scale rows
     static_assert(RA % WAVES == 0 && RB % WAVES == 0, "code regions divide among the waves");
     static_assert((RA + RB) * REGION == STAGE, "one 32 KB stage per K step");
-    static_assert(BM + BN == WAVES * SROWS, "every wave fetches 64 scale rows");
+    static_assert(BM + BN == WAVES * SROWS, "the waves fetch all scale rows");
+    static_assert(SPIECES % 4 == 0, "scale pieces spread over four steps");
 };
 
 // 16-byte slot of chunk c (bytes 16c .. 16c+15 of the step) of row j within
@@ -715,6 +720,328 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
 #endif
 }
 
+// ---------------------------------------------------------------------------
+// Persistent form: one workgroup per compute unit walks tiles blockIdx.x,
+// blockIdx.x + gridDim.x, ... and the operand ring runs on across tile
+// boundaries: the last three K steps of a tile issue the next tile's first
+// three steps (and its first scale group), so those loads are in flight
+// while the tile's epilogue stores C, and the next tile starts without a
+// relaunch or a cold first load.  For K % 2048 == 0 (the K steps of a tile a
+// multiple of 16, so each tile starts at step 0 of the unrolled turn and on
+// scale buffer 0) and plain C; the epilogue stages each wave's rows in the
+// stage and the scale buffer the tile's last step and last group used
+// (st3 and sc1), which the next tile does not touch before the barrier that
+// ends the epilogue.  Every output is summed over K in the same order as the
+// one-tile-per-workgroup kernel, so the two agree bit for bit.
+struct TileRsrc {
+    __amdgpu_buffer_rsrc_t ra, rb, rsc;
+};
+
+// Origin of tile number t (XCD-contiguous, then grouped along M, as the
+// one-tile kernel maps its workgroups).
+__device__ __forceinline__ void tile_origin(int t, int ntiles, int tiles_m, int tiles_n, int& m0,
+                                            int& n0) {
+    using L = Layout<0>;
+    int wg = t;
+    const int full = (ntiles / 8) * 8;
+    if (wg < full) wg = (wg % 8) * (full / 8) + wg / 8;
+    const int per_group = GROUP_M * tiles_n;
+    const int grp = wg / per_group;
+    const int first_m = grp * GROUP_M;
+    const int gsize = min(GROUP_M, tiles_m - first_m);
+    const int in_grp = wg - grp * per_group;
+    m0 = (first_m + in_grp % gsize) * L::BM;
+    n0 = (in_grp / gsize) * L::BN;
+}
+
+__device__ __forceinline__ TileRsrc tile_rsrc(const uint8_t* ac, const uint8_t* as,
+                                              const uint8_t* bc, const uint8_t* bs, int M, int N,
+                                              int m0, int n0, int kbytes, int kscale, int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using L = Layout<0>;
+    const int rows_a = min(M - m0, L::BM), rows_b = min(N - n0, L::BN);
+    TileRsrc r;
+    r.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(ac + (int64_t)m0 * kbytes), (short)0,
+                                             rows_a * kbytes, BUF_FLAGS);
+    r.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(bc + (int64_t)n0 * kbytes), (short)0,
+                                             rows_b * kbytes, BUF_FLAGS);
+    r.rsc = wave < L::A_SWAVES
+                ? __builtin_amdgcn_make_buffer_rsrc((void*)(as + (int64_t)m0 * kscale), (short)0,
+                                                    rows_a * kscale, BUF_FLAGS)
+                : __builtin_amdgcn_make_buffer_rsrc((void*)(bs + (int64_t)n0 * kscale), (short)0,
+                                                    rows_b * kscale, BUF_FLAGS);
+    return r;
+#else
+    return TileRsrc{};
+#endif
+}
+
+// Epilogue of the persistent form: C rows of this wave's tile, staged CW
+// columns at a time in `reg` (32 rows x (CW * ESZ + 16) bytes), then written
+// as 16-byte chunks with non-temporal stores (or added into an fp32 C).
+template <int OUT_BF16, int ACCUM>
+__device__ __forceinline__ void persist_epilogue(v16f (&acc)[4][2], uint8_t* reg, void* cptr,
+                                                 int64_t ldc, int M, int N, int row0, int col0,
+                                                 int lane) {
+    using L = Layout<0>;
+    constexpr int ESZ = OUT_BF16 ? 2 : 4;
+    constexpr int CW = OUT_BF16 ? 64 : 32;  // columns staged per pass
+    constexpr int JPC = CW / 32;            // MFMA tiles per pass
+    constexpr int PITCH = CW * ESZ + 16;
+    constexpr int CHUNK_ELEMS = 16 / ESZ;
+    constexpr int LANES_PER_ROW = CW / CHUNK_ELEMS;
+    constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
+    constexpr int PASSES = 32 / ROWS_PER_PASS;
+    const int half = lane >> 5, l32 = lane & 31;
+    const bool vec_ok = ((ldc * ESZ) % 16 == 0) && (((uintptr_t)cptr & 15) == 0);
+#pragma unroll
+    for (int i = 0; i < L::TM; ++i) {
+#pragma unroll
+        for (int jc = 0; jc < L::TN / JPC; ++jc) {
+#pragma unroll
+            for (int jj = 0; jj < JPC; ++jj)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int j = jc * JPC + jj;
+                    const int cl = jj * 32 + 8 * g + 4 * half;
+                    uint8_t* dst = reg + l32 * PITCH + cl * ESZ;
+                    const v16f& a = acc[i][j];
+                    if (OUT_BF16) {
+                        const bf16x2_t p0 = {(__bf16)a[4 * g], (__bf16)a[4 * g + 1]};
+                        const bf16x2_t p1 = {(__bf16)a[4 * g + 2], (__bf16)a[4 * g + 3]};
+                        *(uint2*)dst = make_uint2(__builtin_bit_cast(uint32_t, p0),
+                                                  __builtin_bit_cast(uint32_t, p1));
+                    } else {
+                        *(u32x4*)dst = (u32x4){as_u32(a[4 * g]), as_u32(a[4 * g + 1]),
+                                               as_u32(a[4 * g + 2]), as_u32(a[4 * g + 3])};
+                    }
+                }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int p = 0; p < PASSES; ++p) {
+                const int rl = p * ROWS_PER_PASS + lane / LANES_PER_ROW;
+                const int ce = (lane % LANES_PER_ROW) * CHUNK_ELEMS;
+                const u32x4 v = *(const u32x4*)(reg + rl * PITCH + ce * ESZ);
+                const int row = row0 + i * 32 + rl;
+                const int col = col0 + jc * CW + ce;
+                if (row >= M) continue;
+                const int64_t off = (int64_t)row * ldc + col;
+                if (vec_ok && col + CHUNK_ELEMS <= N) {
+                    if (ACCUM) {
+                        float4 o = *(const float4*)((const float*)cptr + off);
+                        o.x += as_f32(v.x);
+                        o.y += as_f32(v.y);
+                        o.z += as_f32(v.z);
+                        o.w += as_f32(v.w);
+                        __builtin_nontemporal_store(
+                            (u32x4){as_u32(o.x), as_u32(o.y), as_u32(o.z), as_u32(o.w)},
+                            (u32x4*)((float*)cptr + off));
+                    } else if (OUT_BF16) {
+                        __builtin_nontemporal_store(v, (u32x4*)((uint16_t*)cptr + off));
+                    } else {
+                        __builtin_nontemporal_store(v, (u32x4*)((float*)cptr + off));
+                    }
+                } else {
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < CHUNK_ELEMS; ++e) {
+                        if (col + e >= N) break;
+                        if (OUT_BF16) {
+                            ((uint16_t*)cptr)[off + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                        } else if (ACCUM) {
+                            ((float*)cptr)[off + e] += as_f32(w[e]);
+                        } else {
+                            ((float*)cptr)[off + e] = as_f32(w[e]);
+                        }
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+template <int OUT_BF16, int ACCUM>
+__global__ __launch_bounds__(Layout<0>::THREADS, 1) void gemm_fp4_persistent_kernel(
+    int M, int N, int K, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
+    const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, void* __restrict__ cptr,
+    int64_t ldc, int tiles_m, int tiles_n) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using L = Layout<0>;
+    constexpr int CFG = 0, BF16OPS = 0, TAIL = 0, SG = 8;
+    constexpr int TM = L::TM, TN = L::TN;
+    const int ntiles = tiles_m * tiles_n;
+    const int G = gridDim.x;
+    int tseq = blockIdx.x;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / L::WN, wn = wave % L::WN;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    const int off0 = (l32 >> 4) * REGION + region_slot(l32 & 15, half) * 16;
+    const int off1 = (l32 >> 4) * REGION + region_slot(l32 & 15, 2 + half) * 16;
+    const int sxor = (l32 >> 3) & 3;
+    const int kbytes = K / 2;
+    const int kscale = K / 32;
+    const int ksteps = kbytes / BKB;  // a multiple of 16
+
+    // per-lane offsets, the same for every tile
+    Src<CFG> src;
+    {
+        const int j = lane >> 2;
+        const int c = (lane & 3) ^ ((j >> 2) & 3);
+#pragma unroll
+        for (int q = 0; q < L::RPW; ++q)
+            src.vrow[q] = (uint32_t)(((q * L::WAVES + wave) * 16 + j) * kbytes + c * 16);
+        constexpr int HW = L::A_SWAVES;
+        const int sbase = ((wave < HW ? wave : wave - HW) * L::SROWS + (lane >> 3)) * kscale;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) src.vsc[q] = (uint32_t)(sbase + (((lane & 7) ^ q) << 2));
+        src.soff = 0;
+    }
+    int m0, n0, m1 = 0, n1 = 0;
+    tile_origin(tseq, ntiles, tiles_m, tiles_n, m0, n0);
+    TileRsrc cur = tile_rsrc(ac, as, bc, bs, M, N, m0, n0, kbytes, kscale, wave), nxt = cur;
+    bool has_next = tseq + G < ntiles;
+    if (has_next) {
+        tile_origin(tseq + G, ntiles, tiles_m, tiles_n, m1, n1);
+        nxt = tile_rsrc(ac, as, bc, bs, M, N, m1, n1, kbytes, kscale, wave);
+    }
+
+    Frags<CFG> FA, FB;
+    uint32_t sa[TM], ra[TM], sb[TN], rb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] = ra[i] = 0;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb[j] = rb[j] = 0;
+    const int sh = 8 * half;
+    constexpr int LC = L::RPW_A + L::RPW_B;
+
+    // first tile: scale group 0 and code steps 0..2
+    src.ra = cur.ra;
+    src.rb = cur.rb;
+    src.rsc = cur.rsc;
+    issue_scale_pieces<CFG, 0, L::SPIECES, 0>(src, sc0, wave, kscale, 0);
+    src.soff = 0;
+    issue_codes<CFG, 0>(src, st0, wave, true);
+    issue_codes<CFG, 0>(src, st1, wave, true);
+    issue_codes<CFG, 0>(src, st2, wave, true);
+    FP4Q_WAIT_VMCNT(2 * LC);
+    __builtin_amdgcn_s_barrier();
+    read_scales<CFG, 0>(sc0, sxor << 2, wm, wn, lane, ra, rb);
+    read_frags<CFG>(st0, off0, wm, wn, FA);
+
+#define FP4Q_PIECES(p) ((((p) & 7) >= 4) ? 0 : L::SPIECES / 4)
+#define FP4Q_BEHIND(p) (FP4Q_PIECES((p) + 6) + LC + FP4Q_PIECES((p) + 7) + LC + FP4Q_PIECES(p))
+#define FP4Q_SCUR(P) ((((P) / SG) & 1) ? sc1 : sc0)
+#define FP4Q_SNXT(P) ((((P) / SG) & 1) ? sc0 : sc1)
+    // one K step; the loads it issues (step t_ + 3 and, early in a scale
+    // group, the next group's pieces) come from this tile or, past its end,
+    // from the next one (or repeat this tile's last step when there is none)
+#define FP4Q_PSTEP(P, CUR, NEXT1, NEXTL)                                             \
+    do {                                                                             \
+        const int t_ = kt + (P);                                                     \
+        __builtin_amdgcn_sched_barrier(0);                                           \
+        shift_scales<CFG>(ra, rb, sh, sa, sb);                                       \
+        read_frags<CFG>(CUR, off1, wm, wn, FB);                                       \
+        {                                                                            \
+            const int tl_ = t_ + 3;                                                  \
+            const bool into_next_ = tl_ >= ksteps && has_next;                       \
+            const TileRsrc& r_ = into_next_ ? nxt : cur;                             \
+            src.ra = r_.ra;                                                          \
+            src.rb = r_.rb;                                                          \
+            src.soff = (into_next_ ? tl_ - ksteps : min(tl_, ksteps - 1)) * BKB;     \
+            issue_codes<CFG, 0>(src, NEXTL, wave, false);                            \
+        }                                                                            \
+        if (FP4Q_PIECES(P)) {                                                        \
+            const int g_ = t_ / SG + 1;                                              \
+            const bool into_next_ = g_ * SG >= ksteps && has_next;                   \
+            src.rsc = into_next_ ? nxt.rsc : cur.rsc;                                \
+            issue_scale_pieces<CFG, ((P) & 3) * (L::SPIECES / 4), L::SPIECES / 4, 0>(     \
+                src, FP4Q_SNXT(P), wave, kscale, into_next_ ? 0 : g_);               \
+        }                                                                            \
+        __builtin_amdgcn_sched_barrier(0);                                           \
+        mfma_half<CFG, 0, 0>(FA, sa, sb, acc);                                       \
+        __builtin_amdgcn_sched_barrier(0);                                           \
+        FP4Q_WAIT_VMCNT(FP4Q_BEHIND(P));                                             \
+        __builtin_amdgcn_s_waitcnt(0xC07F);                                          \
+        __builtin_amdgcn_s_barrier();                                                \
+        __builtin_amdgcn_sched_barrier(0);                                           \
+        read_scales<CFG, 0>(((P) % SG) == SG - 1 ? FP4Q_SNXT(P) : FP4Q_SCUR(P),      \
+                            (((P) + 1) & 7 ^ sxor) << 2, wm, wn, lane, ra, rb);      \
+        read_frags<CFG>(NEXT1, off0, wm, wn, FA);                                     \
+        mfma_half<CFG, 0, 1>(FB, sa, sb, acc);                                       \
+    } while (0)
+
+    for (;;) {
+        v16f acc[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+        for (int kt = 0; kt < ksteps; kt += 16) {
+            FP4Q_PSTEP(0, st0, st1, st3);
+            FP4Q_PSTEP(1, st1, st2, st0);
+            FP4Q_PSTEP(2, st2, st3, st1);
+            FP4Q_PSTEP(3, st3, st0, st2);
+            FP4Q_PSTEP(4, st0, st1, st3);
+            FP4Q_PSTEP(5, st1, st2, st0);
+            FP4Q_PSTEP(6, st2, st3, st1);
+            FP4Q_PSTEP(7, st3, st0, st2);
+            FP4Q_PSTEP(8, st0, st1, st3);
+            FP4Q_PSTEP(9, st1, st2, st0);
+            FP4Q_PSTEP(10, st2, st3, st1);
+            FP4Q_PSTEP(11, st3, st0, st2);
+            FP4Q_PSTEP(12, st0, st1, st3);
+            FP4Q_PSTEP(13, st1, st2, st0);
+            FP4Q_PSTEP(14, st2, st3, st1);
+            FP4Q_PSTEP(15, st3, st0, st2);
+        }
+
+        // epilogue through the stage and scale buffer the tile's last step and
+        // last group used (six waves' regions in st3, two in sc1)
+        {
+            constexpr int ESZ = OUT_BF16 ? 2 : 4;
+            constexpr int CW = OUT_BF16 ? 64 : 32;
+            constexpr int EREG = 32 * (CW * ESZ + 16);
+            static_assert(6 * EREG <= STAGE && 2 * EREG <= SCALE_BUF, "staging fits");
+            uint8_t* reg = wave < 6 ? st3 + wave * EREG : sc1 + (wave - 6) * EREG;
+            persist_epilogue<OUT_BF16, ACCUM>(acc, reg, cptr, ldc, M, N, m0 + wm * L::WROWS,
+                                              n0 + wn * L::WCOLS, lane);
+        }
+        __syncthreads();  // st3 and sc1 are free again before the next tile refills them
+        if (!has_next) break;
+        tseq += G;
+        m0 = m1;
+        n0 = n1;
+        cur = nxt;
+        has_next = tseq + G < ntiles;
+        if (has_next) {
+            tile_origin(tseq + G, ntiles, tiles_m, tiles_n, m1, n1);
+            nxt = tile_rsrc(ac, as, bc, bs, M, N, m1, n1, kbytes, kscale, wave);
+        }
+        // the next tile's step 0 and scale group 0 landed before the last
+        // step's barrier; read them again (nothing was kept across the epilogue)
+        read_scales<CFG, 0>(sc0, sxor << 2, wm, wn, lane, ra, rb);
+        read_frags<CFG>(st0, off0, wm, wn, FA);
+    }
+#undef FP4Q_PSTEP
+#undef FP4Q_PIECES
+#undef FP4Q_BEHIND
+#undef FP4Q_SCUR
+#undef FP4Q_SNXT
+    FP4Q_WAIT_VMCNT(0);  // the repeated loads of the last step have landed
+    (void)TAIL;
+    (void)BF16OPS;
+#endif
+}
+
 // Compute units of the current device (cached per device).
 static int device_cus() {
     static int cache[64] = {0};
@@ -743,6 +1070,7 @@ static int pick_cfg(int64_t M, int64_t N) {
     if (const char* e = getenv("FP4Q_GEMM_TILE")) {
         if (!strcmp(e, "256x256")) return 0;
         if (!strcmp(e, "128x384")) return 1;
+
     }
     const int64_t cus = device_cus();
     const int64_t t0 = ((M + 255) / 256) * ((N + 255) / 256);
@@ -776,11 +1104,39 @@ static void launch_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
         qc, qs);
 }
 
+// Whether the persistent form runs: plain FP4 GEMMs on 256 x 256 tiles with
+// K % 2048 == 0 and more tiles than compute units (FP4Q_GEMM_PERSIST=0
+// disables it, =1 forces it wherever it applies).
+static bool use_persistent(int64_t M, int64_t N, int64_t K) {
+    if (K % 2048) return false;
+    const char* e = getenv("FP4Q_GEMM_PERSIST");
+    if (e && !strcmp(e, "0")) return false;
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    if (e && !strcmp(e, "1")) return true;
+    return tiles > device_cus();
+}
+
 template <int OUT_BF16, int ACCUM, int OPS>
 static void launch_tiles(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                          const uint8_t* b, const uint8_t* bs, void* c, int64_t ldc,
                          hipStream_t s, const uint8_t* ha = nullptr, const uint8_t* hb = nullptr,
                          int64_t kp = 0) {
+    if constexpr (OPS == 0) {
+        if (pick_cfg(M, N) == 0 && use_persistent(M, N, K)) {
+            const int tiles_m = (int)((M + 255) / 256), tiles_n = (int)((N + 255) / 256);
+            const int ntiles = tiles_m * tiles_n;
+            int64_t grid = std::min<int64_t>(ntiles, device_cus());
+            // FP4Q_GEMM_PERSIST_GRID=g caps the number of workgroups (so that
+            // tests can chain several tiles per workgroup at small sizes)
+            if (const char* g = getenv("FP4Q_GEMM_PERSIST_GRID")) {
+                const long v = strtol(g, nullptr, 10);
+                if (v > 0) grid = std::min<int64_t>(grid, v);
+            }
+            gemm_fp4_persistent_kernel<OUT_BF16, ACCUM><<<dim3((unsigned)grid), 512, 0, s>>>(
+                (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m, tiles_n);
+            return;
+        }
+    }
     if (pick_cfg(M, N) == 1)
         launch_cfg<1, OUT_BF16, ACCUM, OPS>(M, N, K, a, as, b, bs, c, ldc, s, ha, hb, kp);
     else

@@ -93,8 +93,10 @@ def test_gemm_tiles_bit_identical(M, N, K, monkeypatch):
             monkeypatch.setenv("FP4Q_GEMM_TILE", tile)
             outs.append(fq.gemm(ac, as_, bc, bs, out_dtype=dt))
         torch.cuda.synchronize()
-        a, b = host_bits(outs[0]), host_bits(outs[1])
-        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{M}x{N}x{K} {dt}"
+        a = host_bits(outs[0])
+        for t, o in zip(TILES[1:], outs[1:]):
+            assert np.array_equal(a.view(np.uint8), host_bits(o).view(np.uint8)), \
+                f"{M}x{N}x{K} {dt} {t}"
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 32, 128), (300, 288, 256), (513, 1056, 384),
@@ -397,3 +399,30 @@ def test_outlier_layer_single_kernel_hcp(orc):
     torch.cuda.synchronize()
     a, b = yh[ii, jj].astype(np.float64), host_bits(y2)[ii, jj].astype(np.float64)
     assert np.all(np.abs(a - b) <= 2 * GEMM_REL * (S + SR)), "single-kernel vs two-call"
+
+
+@pytest.mark.parametrize("M,N,K,grid", [(700, 1000, 2048, 5), (257, 513, 4096, 2),
+                                        (1024, 1024, 2048, 7), (300, 260, 2048, 1)])
+def test_persistent_gemm_chains_tiles(orc, M, N, K, grid, monkeypatch):
+    """The persistent form (one workgroup walking several tiles, the operand
+    ring running on across tile boundaries) against the oracle over every
+    output, bf16, fp32 and accumulated fp32, with fewer workgroups than tiles
+    so that each chains several; and bit for bit equal to the
+    one-tile-per-workgroup kernel."""
+    a = inputs.with_outliers(inputs.normal((M, K), M + 31), M + 32, M * K // 100, 50.0)
+    b = inputs.with_outliers(inputs.normal((N, K), N + 33), N + 34, N * K // 100, 50.0)
+    A, B = qpair(orc, a, b)
+    monkeypatch.setenv("FP4Q_GEMM_TILE", "256x256")
+    monkeypatch.setenv("FP4Q_GEMM_PERSIST", "1")
+    monkeypatch.setenv("FP4Q_GEMM_PERSIST_GRID", str(grid))
+    gemm_full_check(orc, A, B, torch.float32, ldc_pad=4)
+    gemm_full_check(orc, A, B, torch.bfloat16, ldc_pad=8)
+    gemm_full_check(orc, A, B, torch.float32, accumulate=True, seed=M)
+    ad, asd, bd, bsd = dev(A[0]), dev(A[1]), dev(B[0]), dev(B[1])
+    for dt in (torch.bfloat16, torch.float32):
+        monkeypatch.setenv("FP4Q_GEMM_PERSIST", "1")
+        p = fq.gemm(ad, asd, bd, bsd, out_dtype=dt)
+        monkeypatch.setenv("FP4Q_GEMM_PERSIST", "0")
+        q = fq.gemm(ad, asd, bd, bsd, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(p).view(np.uint8), host_bits(q).view(np.uint8)), dt
