@@ -65,6 +65,23 @@ def test_ragged_and_offsets(orc, dtype, axis, rnd):
     run_both(orc, x, 16, axis, rnd, 99, 1, ld_pad=pad)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_col_aligned_edges(orc, dtype):
+    """COL pass with columns a multiple of 8 (unconditional loads; lanes
+    wholly outside the matrix read its first rows and columns, which reach no
+    stored output): partial row and column tiles, 32-bit tile offsets, and
+    columns that are not a multiple of 8 (element loads at the edge)."""
+    x = inputs.with_outliers(inputs.normal((640, 1192), 61), 12, 60, 90.0)
+    if dtype == "bf16":
+        x = inputs.to_bf16_bits(x)
+    run_both(orc, x, 32, fq.COL, fq.RNE)
+    run_both(orc, x, 16, fq.COL, fq.SR, 77)
+    run_both(orc, x, 64, fq.COL, fq.SR, 78, 8 * 55, ld_pad=8)
+    run_both(orc, x, 32, fq.COL, fq.SR, 79, 3)
+    run_both(orc, x[:, :1190], 32, fq.COL, fq.RNE, ld_pad=2)
+    run_both(orc, x[:, :1190], 32, fq.COL, fq.SR, 80, ld_pad=2)
+
+
 @pytest.mark.parametrize("axis", [fq.ROW, fq.COL])
 def test_strided_rows(orc, axis):
     x = inputs.to_bf16_bits(inputs.normal((64, 256), 8))

@@ -61,6 +61,19 @@ def test_dual_ragged_tiles_and_offsets(orc, rounds):
     run_dual(orc, x, 16, rounds[0], 9, rounds[1], 10, 1)
 
 
+def test_dual_aligned_edges(orc):
+    """640 x 1184 is 5 x 10 tiles of 128 x 128 with a partial last column
+    tile: lanes wholly outside the matrix read its first rows and columns,
+    which reach no stored output; offsets 5 (not a multiple of 8) take the
+    element-load form."""
+    x = inputs.to_bf16_bits(inputs.with_outliers(inputs.normal((640, 1184), 51), 32, 60, 90.0))
+    run_dual(orc, x, 32, fq.RNE, 0, fq.RNE, 0)
+    run_dual(orc, x, 32, fq.SR, 7, fq.SR, 7)
+    run_dual(orc, x, 16, fq.SR, 7, fq.SR, 8, 16)
+    run_dual(orc, x, 32, fq.RNE, 0, fq.SR, 9, 5)
+    run_dual(orc, x, 32, fq.SR, 10, fq.RNE, 0, ld_pad=8)
+
+
 def test_dual_strided_rows_and_fp32(orc):
     x = inputs.to_bf16_bits(inputs.normal((128, 256), 41))
     run_dual(orc, x, 32, fq.SR, 3, fq.SR, 4, ld_pad=8)
