@@ -475,18 +475,52 @@ def _stream_us(torch, fn, n=50):
     return e0.elapsed_time(e1) * 1e3 / n
 
 
-def _rate(nbytes, us):
-    gbps = nbytes / (us * 1e-6) / 1e9
-    return {"us": round(us, 2), "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+def _graph_us(torch, fns, replays=5):
+    """Mean time per launch of the launches fns[0](), fns[1](), ... captured
+    in order in one HIP graph, the graph replayed `replays` times (no
+    host-side launch cost between kernels)."""
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / (len(fns) * replays)
 
 
-def bench_activation_sweep(torch, fq, inputs, dev):
+def _rate(nbytes, us, us_graph=None):
+    """Rates by the graph-replay time when given (else the stream time)."""
+    t = us_graph if us_graph is not None else us
+    gbps = nbytes / (t * 1e-6) / 1e9
+    d = {"us": round(us, 2)}
+    if us_graph is not None:
+        d["us_graph"] = round(us_graph, 2)
+    d.update({"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)})
+    return d
+
+
+def bench_activation_sweep(torch, fq, inputs, dev, ncopies=32):
     """Activation sweep: bf16 4096x2048 = 0.5 * Student-t(3), ROW blocks of
     16/32/64/128, nearest-even and stochastic (seed 1234); dequantize of each
     back to bf16; STE and DGE(k=5, clamp 3, blocks of 32) on a bf16 N(0,1)
-    gradient.  Each kernel is launched 50 times back to back (inputs stay in
-    the caches: 16.8 MB tensors; a launch lasts a few microseconds, so these
-    rates include each launch's ramp-up and drain)."""
+    gradient.  `us`: one launch on one set of buffers, 50 times back to back
+    (the 16.8 MB tensors stay in the caches).  `us_graph`, which the rates
+    use: one launch on each of `ncopies` copies of the inputs and outputs
+    (about 0.7 GB in all, so each launch finds its data evicted from the 256 MB
+    Infinity Cache by the others), captured in one HIP graph and replayed:
+    no host launch cost between kernels, inputs from HBM; a launch lasts a
+    few microseconds, so its ramp-up and drain are still counted."""
     d = inputs.activation_sweep()
     R, C = d["X"].shape
 
@@ -494,23 +528,35 @@ def bench_activation_sweep(torch, fq, inputs, dev):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
     X, G = to_bf16(d["X"]), to_bf16(d["G"])
+    Xs = [X] + [X.clone() for _ in range(ncopies - 1)]
+    Gs = [G] + [G.clone() for _ in range(ncopies - 1)]
+    ys = [torch.empty((R, C), dtype=torch.bfloat16, device=dev) for _ in range(ncopies)]
+    cs = [torch.empty((R, C // 2), dtype=torch.uint8, device=dev) for _ in range(ncopies)]
     n = R * C
-    out = {"shape": [R, C]}
-    y = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+    out = {"shape": [R, C], "copies": ncopies}
+    seed = d["sr_seed"]
     for b in (16, 32, 64, 128):
-        codes = torch.empty((R, C // 2), dtype=torch.uint8, device=dev)
-        scales = torch.empty((R, C // b), dtype=torch.uint8, device=dev)
+        ss = [torch.empty((R, C // b), dtype=torch.uint8, device=dev) for _ in range(ncopies)]
         qbytes = n * (2 + 0.5 + 1.0 / b)
         for name, rnd in (("rne", fq.RNE), ("sr", fq.SR)):
-            us = _stream_us(torch, lambda: fq.quantize(X, b, fq.ROW, rnd, d["sr_seed"], codes=codes,
-                                                       scales=scales))
-            out[f"quant_b{b}_{name}"] = _rate(qbytes, us)
-        us = _stream_us(torch, lambda: fq.dequantize(codes, scales, b, out=y))
-        out[f"dequant_b{b}"] = _rate(qbytes, us)
-    us = _stream_us(torch, lambda: fq.grad_estimate(fq.STE, None, G, 32, fq.ROW, out=y))
-    out["ste"] = _rate(n * 4, us)
-    us = _stream_us(torch, lambda: fq.grad_estimate(fq.DGE, X, G, 32, fq.ROW, 5.0, 3.0, out=y))
-    out["dge"] = _rate(n * 6, us)
+            fns = [lambda i=i: fq.quantize(Xs[i], b, fq.ROW, rnd, seed, codes=cs[i], scales=ss[i])
+                   for i in range(ncopies)]
+            out[f"quant_b{b}_{name}"] = _rate(qbytes, _stream_us(torch, fns[0]),
+                                              _graph_us(torch, fns))
+        fns = [lambda i=i: fq.dequantize(cs[i], ss[i], b, out=ys[i]) for i in range(ncopies)]
+        out[f"dequant_b{b}"] = _rate(qbytes, _stream_us(torch, fns[0]), _graph_us(torch, fns))
+        del ss
+    # the attainable rate at this size: torch's device copy of one bf16
+    # tensor to another (16.8 MB read, 16.8 MB written), timed the same way
+    fns = [lambda i=i: ys[i].copy_(Gs[i]) for i in range(ncopies)]
+    out["copy_same_size"] = _rate(n * 4, _stream_us(torch, fns[0]), _graph_us(torch, fns))
+    fns = [lambda i=i: fq.grad_estimate(fq.STE, None, Gs[i], 32, fq.ROW, out=ys[i])
+           for i in range(ncopies)]
+    out["ste"] = _rate(n * 4, _stream_us(torch, fns[0]), _graph_us(torch, fns))
+    fns = [lambda i=i: fq.grad_estimate(fq.DGE, Xs[i], Gs[i], 32, fq.ROW, 5.0, 3.0, out=ys[i])
+           for i in range(ncopies)]
+    out["dge"] = _rate(n * 6, _stream_us(torch, fns[0]), _graph_us(torch, fns))
+    del Xs, Gs, ys, cs
     return out
 
 
