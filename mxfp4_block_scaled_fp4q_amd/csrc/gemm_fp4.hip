@@ -550,13 +550,6 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
     constexpr int ESZ = OUT_BF16 ? 2 : 4;
     constexpr int PITCH = L::WCOLS * ESZ + 16;
     constexpr int EREG = 32 * PITCH;
-    constexpr int PER_STAGE = STAGE / EREG;  // wave regions that fit in one stage
-    static_assert(L::WAVES <= 4 * PER_STAGE, "epilogue regions fit in the four stages");
-    uint8_t* reg = (wave / PER_STAGE == 0   ? st0
-                    : wave / PER_STAGE == 1 ? st1
-                    : wave / PER_STAGE == 2 ? st2
-                                            : st3) +
-                   (wave % PER_STAGE) * EREG;
     const int row0 = m0 + wm * L::WROWS;
     const int col0 = n0 + wn * L::WCOLS;
     const bool vec_ok = ((ldc * ESZ) % 16 == 0) && (((uintptr_t)cptr & 15) == 0);
@@ -564,8 +557,41 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
     constexpr int LANES_PER_ROW = L::WCOLS / CHUNK_ELEMS;
     constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;  // rows read back per pass
     constexpr int PASSES = (32 + ROWS_PER_PASS - 1) / ROWS_PER_PASS;
+    // Accumulating into an fp32 C (C += A B): each 32-row group's C chunks
+    // are read ahead of their use, two groups in flight (each group's while
+    // the group before it is added and stored), instead of one
+    // read-then-write round trip per chunk.  (256 x 256 tiles: 8 chunks per
+    // lane per group.  Reading the first group before the K loop would keep
+    // 32 more registers live through it, which spills.)
+    constexpr bool YPF = ACCUM && !OUT_BF16 && EPI == 0 && PASSES <= 8 && L::TM == 4;
+    auto c_chunk = [&](int i, int p, int64_t& off) __attribute__((always_inline)) -> bool {
+        const int rl = p * ROWS_PER_PASS + lane / LANES_PER_ROW;
+        const int row = row0 + i * 32 + rl;
+        const int col = col0 + (lane % LANES_PER_ROW) * CHUNK_ELEMS;
+        off = (int64_t)row * ldc + col;
+        return lane < ROWS_PER_PASS * LANES_PER_ROW && rl < 32 && row < M && vec_ok &&
+               col + CHUNK_ELEMS <= N;
+    };
+    auto c_prefetch = [&](int i, float4 (&y)[YPF ? PASSES : 1]) __attribute__((always_inline)) {
+        if constexpr (YPF) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+            for (int p = 0; p < PASSES; ++p) {
+                int64_t off;
+                if (c_chunk(i, p, off)) y[p] = *(const float4*)((const float*)cptr + off);
+            }
+        }
+    };
+    float4 ya[YPF ? PASSES : 1], yb[YPF ? PASSES : 1];
+    constexpr int PER_STAGE = STAGE / EREG;  // wave regions that fit in one stage
+    static_assert(L::WAVES <= 4 * PER_STAGE, "epilogue regions fit in the four stages");
+    uint8_t* reg = (wave / PER_STAGE == 0   ? st0
+                    : wave / PER_STAGE == 1 ? st1
+                    : wave / PER_STAGE == 2 ? st2
+                                            : st3) +
+                   (wave % PER_STAGE) * EREG;
+    // group i of the wave's rows; yv: its C chunks read ahead (YPF)
+    auto epi_group = [&](const int i, const float4 (&yv)[YPF ? PASSES : 1])
+                         __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -687,7 +713,7 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
                 // non-temporal stores keep it from displacing the operands in
                 // the caches (worth 10% on a 906 MB fp32 C)
                 if (ACCUM) {
-                    float4 o = *(const float4*)((const float*)cptr + off);
+                    float4 o = YPF ? yv[YPF ? p : 0] : *(const float4*)((const float*)cptr + off);
                     o.x += as_f32(v.x);
                     o.y += as_f32(v.y);
                     o.z += as_f32(v.z);
@@ -716,6 +742,19 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
             }
         }
         __builtin_amdgcn_wave_barrier();
+    };
+    if constexpr (YPF) {
+        c_prefetch(0, ya);
+        c_prefetch(1, yb);
+        epi_group(0, ya);
+        c_prefetch(2, ya);
+        epi_group(1, yb);
+        c_prefetch(3, yb);
+        epi_group(2, ya);
+        epi_group(3, yb);
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) epi_group(i, ya);
     }
 #endif
 }
