@@ -53,8 +53,11 @@ def parse():
     p.add_argument("--skip-configs", action="store_true",
                    help="skip the activation-sweep and 13B-shaped outlier-layer measurements")
     p.add_argument("--profile-op", default=None,
-                   help="run only this step kernel (or 'copy', a plain 256 MiB device copy) "
-                        "--reps times and exit: the target of rocprofv3 counter runs")
+                   help="run only this step kernel (or 'copy', a plain 256 MiB device copy, "
+                        "or 'hcp_residual', the 13B layer's D-mode residual) --reps times "
+                        "and exit: the target of rocprofv3 counter runs")
+    p.add_argument("--hot-channels", type=int, default=None,
+                   help="with --profile-op hcp_residual: use only the first N hot channels")
     p.add_argument("--reps", type=int, default=10)
     return p.parse_args()
 
@@ -235,6 +238,9 @@ def main():
     ]
     step_flops = sum(o[3] for o in ops)
 
+    if args.profile_op == "hcp_residual":
+        profile_hcp_residual(torch, fq, inputs, dev, args.reps, args.hot_channels)
+        return
     if args.profile_op is not None:
         if args.profile_op == "copy":
             n = 64 << 20
@@ -331,7 +337,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4_TFLOPS, 4),
                 "traffic": measured_traffic(),
-                "kernel": "gemm_fp4_kernel 8192x5632x2048 bf16 out",
+                "kernel": "gemm_fp4_persistent_kernel<1, 0> 8192x5632x2048 bf16 out",
                 "per_launch_flops": fwd_flops, "launch_us_mean": round(fwd_mean_us, 2),
                 "launch_us_min": round(float(np.min(fwd_us)), 2),
                 "launch_us_median": round(float(np.median(fwd_us)), 2),
@@ -345,8 +351,10 @@ def main():
 
     extra = {"copy_ceiling_GBps": copy_ceiling(torch, dev)}
     if not args.skip_configs:
-        # the other workloads: the activation sweep (every block size, both
-        # roundings, dequantize, STE and DGE) and the 13B-shaped outlier layer
+        # the other workloads: the tiny reference case, the activation sweep
+        # (every block size, both roundings, dequantize, STE and DGE) and the
+        # 13B-shaped outlier layer
+        extra["tiny_ref"] = bench_tiny_ref(torch, fq, inputs, dev)
         extra["activation_sweep"] = bench_activation_sweep(torch, fq, inputs, dev)
         extra["outlier_layer"] = bench_outlier_layer(torch, fq, inputs, dev)
 
@@ -560,6 +568,63 @@ def bench_activation_sweep(torch, fq, inputs, dev, ncopies=32):
     return out
 
 
+def profile_hcp_residual(torch, fq, inputs, dev, reps, n_hot=None):
+    """The 13B layer's D-mode residual (fp4q_hcp_residual_add) `reps` times on
+    a zero fp32 Y, with the first n_hot of its hot channels (all 461 by
+    default): the target of counter and trace runs."""
+    d = inputs.outlier_layer()
+
+    def to_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, W = to_bf16(d["X"]), to_bf16(d["W"])
+    hot = torch.from_numpy(d["hot"]).to(dev)
+    if n_hot is not None:
+        hot = hot[:n_hot].contiguous()
+    M, K = X.shape
+    N = W.shape[1]
+    xq = fq.quantize(X, 32, fq.ROW)
+    wq = fq.quantize(W, 32, fq.COL)
+    y = torch.zeros((M, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(fq.hcp_workspace_bytes(M, N, hot.numel()), dtype=torch.uint8, device=dev)
+    for _ in range(reps):
+        fq.hcp_residual_add(X, xq[0], xq[1], W, wq[0], wq[1], hot, y, workspace=ws)
+    torch.cuda.synchronize()
+
+
+def bench_tiny_ref(torch, fq, inputs, dev):
+    """Tiny reference case: fp32 256x256 N(0,1) with 1% of entries x50, ROW
+    blocks of 32, nearest-even; dequantize; DGE(k=5, clamp 3) backward on an
+    N(0,1) gradient; the FP4 GEMM 256x256x256 of two such quantised
+    matrices into fp32.  Each launch is a few microseconds of launch-bound
+    work: timed as 20 launches captured in a HIP graph and replayed."""
+    d = inputs.tiny_ref()
+    A = torch.from_numpy(d["A"]).to(dev)
+    B = torch.from_numpy(d["B"]).to(dev)
+    G = torch.from_numpy(d["G"]).to(dev)
+    aq = fq.quantize(A, 32)
+    bq = fq.quantize(B, 32)
+    y = torch.empty_like(A)
+    c = torch.empty((256, 256), dtype=torch.float32, device=dev)
+    out = {"shape": [256, 256, 256]}
+    rep = 20
+    ops = (("quant_row_rne", lambda: fq.quantize(A, 32, codes=aq[0], scales=aq[1]),
+            256 * 256 * (4 + 0.5 + 1 / 32), 0),
+           ("dequant", lambda: fq.dequantize(aq[0], aq[1], 32, out=y),
+            256 * 256 * (4 + 0.5 + 1 / 32), 0),
+           ("dge", lambda: fq.grad_estimate(fq.DGE, A, G, 32, fq.ROW, 5.0, 3.0, out=y),
+            256 * 256 * 12, 0),
+           ("gemm", lambda: fq.gemm(aq[0], aq[1], bq[0], bq[1], c=c),
+            2 * 256 * 256 * (0.5 + 1 / 32) + 256 * 256 * 4, 2.0 * 256 ** 3))
+    for name, fn, nbytes, nflops in ops:
+        us = _graph_us(torch, [fn] * rep)
+        d_ = {"us_graph": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        if nflops:
+            d_["TFLOPS"] = round(nflops / (us * 1e-6) / 1e12, 2)
+        out[name] = d_
+    return out
+
+
 def bench_outlier_layer(torch, fq, inputs, dev):
     """13B-shaped outlier layer (X 16384x5120 with 461 hot channels x100, W
     5120x13824): X ROW and W COL quantisation, the fp32 base GEMM, the
@@ -600,7 +665,10 @@ def bench_outlier_layer(torch, fq, inputs, dev):
                      ("gemm_hcp_split", lambda: fq.gemm_hcp_split(X, xs[0], xs[1], W, wsq[0], wsq[1],
                                                                  hot, y=Y2, workspace=ws)),
                      ("hot_channels", lambda: fq.hot_channels(X, hot.numel(), hot_idx=hsel,
-                                                              workspace=hws))):
+                                                              workspace=hws)),
+                     # the floor of the residual's C traffic: a plain
+                     # elementwise read-modify-write of the same fp32 Y
+                     ("y_plain_rmw", lambda: Y2.add_(1.0))):
         fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -630,6 +698,7 @@ def bench_outlier_layer(torch, fq, inputs, dev):
     res["hcp_residual_GBps"] = round(hcp_bytes / (res["hcp_residual_us"] * 1e-6) / 1e9, 1)
     res["hcp_residual_frac_hbm_peak"] = round(res["hcp_residual_GBps"] / PEAK_HBM_GBPS, 4)
     res["hcp_y_rmw_GBps"] = round(8.0 * M * N / (res["hcp_residual_us"] * 1e-6) / 1e9, 1)
+    res["y_plain_rmw_GBps"] = round(8.0 * M * N / (res["y_plain_rmw_us"] * 1e-6) / 1e9, 1)
     # dual-kernel mode (base GEMM, then the residual's read-modify-write of Y)
     # against the single kernel that writes Y once
     res["hcp_two_kernel_total_us"] = round(res["gemm_fp32_us"] + res["hcp_residual_us"], 1)
@@ -683,6 +752,7 @@ def cpu_baseline(f, b, step_flops, budget_s):
                       f"rows/cols per GEMM), extrapolated linearly to one full step; "
                       f"est. step {total:.1f} s",
             "est_step_s": round(total, 2),
+            "per_kernel_est_s": {k: round(v, 3) for k, v in t.items()},
             "host_cpus": os.cpu_count()}
 
 
