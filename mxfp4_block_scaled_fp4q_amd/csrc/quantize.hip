@@ -691,14 +691,29 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // stage: column cg*CPT + j, bytes rg*RPT/2 .. of its tile segment
+        // stage: column cg*CPT + j, bytes rg*RPT/2 .. of its tile segment.
+        // Every column's staged bytes start on the same LDS bank (the pitch
+        // times CPT columns is a multiple of 128 bytes), so the 16-byte
+        // chunks of column c sit rotated by (c / CPT) chunks: the lanes of
+        // one write (16 column groups) then spread over the banks instead of
+        // all hitting one; the reads below undo the rotation.
+        constexpr int NCH = TR / 32;  // 16-byte chunks per staged column
+        auto staged = [&](int col, int byte) -> uint8_t* {
+            const int ch = ((byte >> 4) + col / CPT) & (NCH - 1);
+            return cst + col * PITCH + ch * 16 + (byte & 15);
+        };
+        {
+            // this thread's columns all have the rotation cg
+            const int byte = rg * (RPT / 2);
+            uint8_t* const w0 =
+                cst + cg * CPT * PITCH + (((byte >> 4) + cg) & (NCH - 1)) * 16 + (byte & 15);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            if (WPT == 2)
-                *(uint2*)(cst + (cg * CPT + j) * PITCH + rg * 8) =
-                    make_uint2(out[j][0], out[j][WPT - 1]);
-            else
-                *(uint32_t*)(cst + (cg * CPT + j) * PITCH + rg * 4) = out[j][0];
+            for (int j = 0; j < CPT; ++j) {
+                if (WPT == 2)
+                    *(uint2*)(w0 + j * PITCH) = make_uint2(out[j][0], out[j][WPT - 1]);
+                else
+                    *(uint32_t*)(w0 + j * PITCH) = out[j][0];
+            }
         }
         __syncthreads();
 
@@ -721,7 +736,7 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
             for (int k = 0; k < TC * CH16 / kThreads; ++k) {
                 const int col = col0 + k * (kThreads / CH16);
                 if (interior || (cbase + col < cols && ch * 16 < vbytes))
-                    *(uint4*)ccode_at(col, ch * 16) = *(const uint4*)(cst + col * PITCH + ch * 16);
+                    *(uint4*)ccode_at(col, ch * 16) = *(const uint4*)staged(col, ch * 16);
             }
         } else {
             const int col0 = tid / (2 * CH16), ch = tid % (2 * CH16);
@@ -729,7 +744,7 @@ __global__ __launch_bounds__(kThreads) void quantize_col_kernel(
             for (int k = 0; k < TC * 2 * CH16 / kThreads; ++k) {
                 const int col = col0 + k * (kThreads / (2 * CH16));
                 if (interior || (cbase + col < cols && ch * 8 < vbytes))
-                    *(uint2*)ccode_at(col, ch * 8) = *(const uint2*)(cst + col * PITCH + ch * 8);
+                    *(uint2*)ccode_at(col, ch * 8) = *(const uint2*)staged(col, ch * 8);
             }
         }
         // scales: each column's vrows/BLOCK bytes
