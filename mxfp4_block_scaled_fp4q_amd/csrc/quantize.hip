@@ -72,24 +72,27 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(
     uint32_t gidx[UNROLL];
     uint32_t rowi[UNROLL];
     // dense rows (ld == cols) without a mask: chunk g starts at element 8 g,
-    // and nearest-even needs no row index, so no division
-    const bool flat = !SR && !MASK && ld == cols;
+    // and neither rounding needs the row index (the stochastic one's position
+    // is 8 g + offset), so no division
+    const bool flat = !MASK && ld == cols;
     if (flat) {
-        // the input is read once: non-temporal loads, all in flight together
-        // (chunks past the end load chunk 0, unused; no branch around a load)
+        // the input is read once: non-temporal loads (plain ones for the
+        // stochastic form, which is bound by its arithmetic), all in flight
+        // together (chunks past the end load chunk 0, unused; no branch
+        // around a load)
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const uint32_t g = base + (uint32_t)u * 64u + lane;
             gidx[u] = g;
             rowi[u] = 0;
             const uint4* p = (const uint4*)xv + (IN_BF16 ? 1 : 2) * (g < total_chunks ? g : 0u);
-            const uint4 v0 = load_nt(p);
+            const uint4 v0 = SR ? *p : load_nt(p);
             w[u][0] = v0.x;
             w[u][1] = v0.y;
             w[u][2] = v0.z;
             w[u][3] = v0.w;
             if (!IN_BF16) {
-                const uint4 v1 = load_nt(p + 1);
+                const uint4 v1 = SR ? p[1] : load_nt(p + 1);
                 w[u][4 % (IN_BF16 ? 4 : 8)] = v1.x;
                 w[u][5 % (IN_BF16 ? 4 : 8)] = v1.y;
                 w[u][6 % (IN_BF16 ? 4 : 8)] = v1.z;
@@ -195,11 +198,18 @@ __global__ __launch_bounds__(kThreads) void quantize_row_kernel(
             }
         } else {
             const float sc = e8m0_scale_f32(byte);
-            const uint32_t r = rowi[u];
-            const uint32_t cc = (valid ? g : 0u) - r * cpr.d;
-            const uint64_t p0 = (uint64_t)r * (uint64_t)cols + (uint64_t)cc * 8u + rng_off;
+            // position of the chunk's first element: r * cols + 8 cc = 8 g
+            const uint64_t p0 = (uint64_t)(valid ? g : 0u) * 8u + rng_off;
             uint32_t wr[4];
-            sr_words8(p0, k0, k1, wr);
+            if ((rng_off & 7) == 0) {
+                // (a workgroup-uniform test) the chunk is one Philox counter
+                const uint64_t n = p0 >> 3;
+                const Philox4 a = philox4x32_10((uint32_t)n, (uint32_t)(n >> 32), 0u, 0u, k0, k1);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) wr[k] = a.v[k];
+            } else {
+                sr_words8(p0, k0, k1, wr);
+            }
             float xf[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
