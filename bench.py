@@ -158,6 +158,7 @@ def main():
     dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     dW = torch.empty((K, N), dtype=torch.float32, device=dev)
     dWo = torch.empty((K, N), dtype=torch.float32, device=dev)
+    dYg = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
     # (name, callable, algorithmic bytes, algorithmic flops)
     qb = 2 + 0.5 + 1 / 32  # bf16 in, codes + E8M0 bytes out, per element
@@ -235,6 +236,11 @@ def main():
         # Y[M, N] += R W: reads and writes the fp32 rows that hold outliers
         ("occ_spmm", lambda: fq.occ_spmm(occ["rp"], occ["ci"], occ["v"], W, occ["y"]),
          M * N * 8, 0),
+        # the straight-through estimator on a gradient of dY's size (bf16 in,
+        # bf16 out, 4 B per element), and torch's device copy of the same
+        # tensor as the attainable rate for that traffic
+        ("ste_dy", lambda: fq.grad_estimate(fq.STE, None, dY, 32, fq.ROW, out=dYg), M * N * 4, 0),
+        ("copy_dy", lambda: dYg.copy_(dY), M * N * 4, 0),
     ]
     step_flops = sum(o[3] for o in ops)
 
