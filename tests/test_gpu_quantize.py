@@ -82,6 +82,31 @@ def test_col_aligned_edges(orc, dtype):
     run_both(orc, x[:, :1190], 32, fq.COL, fq.SR, 80, ld_pad=2)
 
 
+def test_col_huge_row_stride(orc):
+    """A row stride so long that a column tile's extent reaches 2^31 bytes:
+    the host takes the element-load form (64-bit addressing) instead of the
+    32-bit tile offsets; results are the same bits."""
+    x = inputs.to_bf16_bits(inputs.with_outliers(inputs.normal((64, 1024), 81), 9, 40, 60.0))
+    ld = 8_500_000  # 128 rows x ld x 2 bytes > 2^31
+    big = torch.zeros((64, ld), dtype=torch.bfloat16, device="cuda")
+    big[:, :1024] = to_dev_input(x)
+    xd = big[:, :1024]
+    for rnd, seed in ((fq.RNE, 0), (fq.SR, 5)):
+        c, s_ = fq.quantize(xd, 32, fq.COL, rnd, seed)
+        (rc, rs), (cc, cs) = fq.quantize_dual(xd, 32, rnd, seed, rnd, seed)
+        torch.cuda.synchronize()
+        co, so = orc.quantize(x, 32, fq.COL, rnd, seed)
+        ro, rso = orc.quantize(x, 32, fq.ROW, rnd, seed)
+        what = f"ld={ld} round={rnd}"
+        assert_same_bits(host_bits(s_), so, "col scales " + what)
+        assert_same_bits(host_bits(c), co, "col codes " + what)
+        assert_same_bits(host_bits(cs), so, "dual col scales " + what)
+        assert_same_bits(host_bits(cc), co, "dual col codes " + what)
+        assert_same_bits(host_bits(rs), rso, "dual row scales " + what)
+        assert_same_bits(host_bits(rc), ro, "dual row codes " + what)
+    del big
+
+
 @pytest.mark.parametrize("axis", [fq.ROW, fq.COL])
 def test_strided_rows(orc, axis):
     x = inputs.to_bf16_bits(inputs.normal((64, 256), 8))
