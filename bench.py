@@ -270,10 +270,8 @@ def main():
             if evs is not None:
                 hev.record(evs[i])
             if fwd_evs is not None and i == i_fwd:
-                hev.record(fwd_evs[0])
+                fq.set_gemm_events(fwd_evs[0], fwd_evs[1])
             fn()
-            if fwd_evs is not None and i == i_fwd:
-                hev.record(fwd_evs[1])
         if evs is not None:
             hev.record(evs[len(ops)])
 
@@ -282,8 +280,10 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` steps, synchronised on both sides.  The
-    # only events inside it bracket the forward GEMM (the roofline kernel),
-    # on the stream every kernel is launched on.
+    # only events inside it are the forward GEMM's (the roofline kernel),
+    # recorded by that kernel's own dispatch on the stream every kernel is
+    # launched on (fp4q_set_gemm_events), so no marker packets sit between
+    # the step's kernels and the events span the kernel alone.
     fwd_events = [[hev.create() for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -499,6 +499,24 @@ fp4q_status_t fp4q_hot_channels(const void* x, int64_t rows, int64_t cols, int64
                                 int32_t n_hot, int32_t* hot_idx, float* err, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * fp4q_set_gemm_events -- timing of one GEMM kernel without marker packets
+ * between kernels.  The next GEMM kernel that this thread launches (from
+ * fp4q_gemm or any entry point that runs one of the FP4 GEMM kernels) is
+ * dispatched with hipExtLaunchKernel, which records start_event at the
+ * dispatch's start and stop_event at its end; hipEventElapsedTime of the
+ * two is then that kernel's own duration, as a kernel trace reports it.  A
+ * separate hipEventRecord before and after the call would add the marker
+ * packets' queue time to it.
+ *   start_event, stop_event  hipEvent_t (as void*), created by the caller
+ *            and owned by it; either may be NULL.  Both NULL clears a
+ *            pending pair.  The pair is used once (the launch clears it);
+ *            a call that fails before launching leaves it pending.
+ * Always returns FP4Q_OK.  Thread-local: other threads' launches are not
+ * affected.
+ */
+fp4q_status_t fp4q_set_gemm_events(void* start_event, void* stop_event);
+
 const char* fp4q_status_string(fp4q_status_t s);
 const char* fp4q_last_error(void);
 int32_t fp4q_abi_version(void);

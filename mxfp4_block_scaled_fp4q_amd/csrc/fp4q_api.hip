@@ -47,6 +47,11 @@ int32_t fp4q_abi_version(void) { return FP4Q_ABI_VERSION; }
 
 const char* fp4q_last_error(void) { return g_err; }
 
+fp4q_status_t fp4q_set_gemm_events(void* start_event, void* stop_event) {
+    fp4q::set_gemm_launch_events((hipEvent_t)start_event, (hipEvent_t)stop_event);
+    return FP4Q_OK;
+}
+
 const char* fp4q_status_string(fp4q_status_t s) {
     switch (s) {
         case FP4Q_OK: return "ok";

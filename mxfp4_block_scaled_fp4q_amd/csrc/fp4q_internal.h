@@ -51,6 +51,10 @@ hipError_t launch_dge(const void* x, int xdtype, const void* g, int gdtype, int6
 hipError_t launch_gemm_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
                            const uint8_t* as, const uint8_t* bc, const uint8_t* bs, void* c,
                            int cdtype, int64_t ldc, bool accumulate, hipStream_t s);
+// The next GEMM kernel this thread launches records start and stop (either
+// may be null) at its dispatch instead of being launched plainly; both null
+// clears a pending pair.
+void set_gemm_launch_events(hipEvent_t start, hipEvent_t stop);
 // C[M,N] (fp32, row stride ldc) += A B^T for bf16 A [M,K], B [N,K] (K % 32 == 0),
 // on the FP4 GEMM's pipeline with bf16 MFMAs.
 hipError_t launch_gemm_bf16_accum(int64_t M, int64_t N, int64_t K, const uint16_t* a,
