@@ -59,6 +59,8 @@ def parse():
     p.add_argument("--hot-channels", type=int, default=None,
                    help="with --profile-op hcp_residual: use only the first N hot channels")
     p.add_argument("--reps", type=int, default=10)
+    p.add_argument("--sequential", action="store_true",
+                   help="launch every step kernel behind a barrier (no any-order launches)")
     return p.parse_args()
 
 
@@ -170,12 +172,12 @@ def main():
         ("quant_x_dual", lambda: dual(X, fq.RNE, 0, fq.RNE, 0, "xr", "xc"), M * K * qb2, 0),
         # W: COL (W^T, K-major) for the forward GEMM, ROW for dX
         ("quant_w_dual", lambda: dual(W, fq.RNE, 0, fq.RNE, 0, "wr", "wc"), K * N * qb2, 0),
-        ("gemm_fwd", lambda: fq.gemm(*bufs["xr"], *bufs["wc"], c=Y),
-         (M + N) * K * (0.5 + 1 / 32) + M * N * 2, 2.0 * M * N * K),
-        ("dequant_x", lambda: fq.dequantize(*bufs["xr"], 32, out=Xdq), M * K * qb, 0),
         # dY: ROW for dX, COL (dY^T) for dW, stochastic, one random stream
         ("quant_dy_dual_sr", lambda: dual(dY, fq.SR, SR_SEED, fq.SR, SR_SEED, "dyr", "dyc"),
          M * N * qb2, 0),
+        ("gemm_fwd", lambda: fq.gemm(*bufs["xr"], *bufs["wc"], c=Y),
+         (M + N) * K * (0.5 + 1 / 32) + M * N * 2, 2.0 * M * N * K),
+        ("dequant_x", lambda: fq.dequantize(*bufs["xr"], 32, out=Xdq), M * K * qb, 0),
         ("gemm_dx", lambda: fq.gemm(*bufs["dyr"], *bufs["wr"], c=dX),
          (M + K) * N * (0.5 + 1 / 32) + M * K * 2, 2.0 * M * K * N),
         # dW = X^T dY with W's DGE derivative applied in the GEMM's epilogue
@@ -262,6 +264,15 @@ def main():
 
     nev = len(ops) + 1
     i_fwd = [o[0] for o in ops].index("gemm_fwd")
+    # Launches that may start before the stream's earlier kernels finish
+    # (fp4q_set_next_launch any-order): each reads only what a kernel behind
+    # a barrier has already finished (the step's first kernel and the forward
+    # GEMM are plain launches, so they wait for everything before them).
+    # The three quantisers overlap each other's ramp-up and tail; dequantize
+    # and the backward GEMMs fill compute units as the forward GEMM's
+    # workgroups finish.
+    any_order = {"quant_w_dual", "quant_dy_dual_sr", "dequant_x", "gemm_dx", "gemm_dw_dge"}
+    ao = [o[0] in any_order and not args.sequential for o in ops]
 
     hev = HipEvents(torch)
 
@@ -270,7 +281,9 @@ def main():
             if evs is not None:
                 hev.record(evs[i])
             if fwd_evs is not None and i == i_fwd:
-                fq.set_gemm_events(fwd_evs[0], fwd_evs[1])
+                fq.set_next_launch(fwd_evs[0], fwd_evs[1])
+            elif ao[i] and evs is None:
+                fq.set_next_launch(any_order=True)
             fn()
         if evs is not None:
             hev.record(evs[len(ops)])
@@ -282,7 +295,7 @@ def main():
     # Timed region: exactly `steps` steps, synchronised on both sides.  The
     # only events inside it are the forward GEMM's (the roofline kernel),
     # recorded by that kernel's own dispatch on the stream every kernel is
-    # launched on (fp4q_set_gemm_events), so no marker packets sit between
+    # launched on (fp4q_set_next_launch), so no marker packets sit between
     # the step's kernels and the events span the kernel alone.
     fwd_events = [[hev.create() for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -385,7 +398,10 @@ def main():
                                "N(0,1), W bf16 2048x5632 N(0,0.02), dY bf16 8192x5632 N(0,1e-3); "
                                "MXFP4 block 32, E2M1 codes, E8M0 scales, fp32 accumulate",
                    "global_batch": M, "parallelism": "none (1 GPU)",
-                   "step_fp4_gflop": round(step_flops / 1e9, 2)},
+                   "step_fp4_gflop": round(step_flops / 1e9, 2),
+                   "launches": "sequential" if args.sequential else
+                               "any-order where independent: " + ", ".join(
+                                   o[0] for o, a in zip(ops, ao) if a)},
         "roofline": roofline,
         "quantize": quant,
         "kernels": per_op,

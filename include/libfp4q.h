@@ -500,22 +500,30 @@ fp4q_status_t fp4q_hot_channels(const void* x, int64_t rows, int64_t cols, int64
                                 size_t workspace_bytes, void* stream);
 
 /*
- * fp4q_set_gemm_events -- timing of one GEMM kernel without marker packets
- * between kernels.  The next GEMM kernel that this thread launches (from
- * fp4q_gemm or any entry point that runs one of the FP4 GEMM kernels) is
- * dispatched with hipExtLaunchKernel, which records start_event at the
- * dispatch's start and stop_event at its end; hipEventElapsedTime of the
- * two is then that kernel's own duration, as a kernel trace reports it.  A
- * separate hipEventRecord before and after the call would add the marker
- * packets' queue time to it.
- *   start_event, stop_event  hipEvent_t (as void*), created by the caller
- *            and owned by it; either may be NULL.  Both NULL clears a
- *            pending pair.  The pair is used once (the launch clears it);
- *            a call that fails before launching leaves it pending.
- * Always returns FP4Q_OK.  Thread-local: other threads' launches are not
- * affected.
+ * fp4q_set_next_launch -- options for the next kernel that this thread
+ * launches through the library (the first kernel of the next entry point
+ * called, for entry points that launch several).  With any option given,
+ * that kernel is dispatched with hipExtLaunchKernel:
+ *   start_event, stop_event  hipEvent_t (as void*), created and owned by
+ *            the caller, either may be NULL: recorded by the dispatch itself
+ *            at the kernel's start and end, so hipEventElapsedTime of the
+ *            pair is that kernel's own duration, as a kernel trace reports
+ *            it (separate hipEventRecord calls around the entry point would
+ *            add the marker packets' queue time).
+ *   flags    0, or FP4Q_LAUNCH_ANY_ORDER: the kernel may start before the
+ *            work queued earlier on its stream has finished (its dispatch
+ *            carries no barrier).  The caller guarantees that the kernel
+ *            reads nothing that earlier, unfinished work writes and writes
+ *            nothing that work reads.  A later launch without the flag (the
+ *            default) waits for everything before it, this kernel included.
+ * The options are used once: the launch that takes them clears them.  An
+ * entry point that fails before launching leaves them pending; calling with
+ * (NULL, NULL, 0) clears them.  Thread-local: other threads' launches are
+ * not affected.
+ * Errors: FP4Q_ERR_INVALID for unknown flag bits (nothing is set).
  */
-fp4q_status_t fp4q_set_gemm_events(void* start_event, void* stop_event);
+#define FP4Q_LAUNCH_ANY_ORDER 1u
+fp4q_status_t fp4q_set_next_launch(void* start_event, void* stop_event, uint32_t flags);
 
 const char* fp4q_status_string(fp4q_status_t s);
 const char* fp4q_last_error(void);

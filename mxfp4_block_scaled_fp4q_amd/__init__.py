@@ -28,7 +28,7 @@ EXPORTS = ["fp4q_channel_mask", "fp4q_quantize_masked", "fp4q_gemm_hcp_split",
            "fp4q_gemm_hcp", "fp4q_hot_channels_workspace_bytes", "fp4q_hot_channels",
            "fp4q_quantize_2d", "fp4q_quantize_2d_tile", "fp4q_quantize_rht", "fp4q_occ_max_nnz",
            "fp4q_occ_workspace_bytes", "fp4q_occ_quantize", "fp4q_occ_spmm",
-           "fp4q_set_gemm_events", "fp4q_status_string",
+           "fp4q_set_next_launch", "fp4q_status_string",
            "fp4q_last_error", "fp4q_abi_version"]
 
 
@@ -82,7 +82,7 @@ def lib():
                                         P, I64, P, P, SZ, P]),
             "fp4q_occ_spmm": (I32, [I64, I64, I64, P, P, P, P, I64, P, I64, P]),
             "fp4q_hot_channels": (I32, [P, I64, I64, I64, I32, P, P, P, SZ, P]),
-            "fp4q_set_gemm_events": (I32, [P, P]),
+            "fp4q_set_next_launch": (I32, [P, P, _ct.c_uint32]),
             "fp4q_status_string": (_ct.c_char_p, [I32]),
             "fp4q_last_error": (_ct.c_char_p, []),
             "fp4q_abi_version": (I32, []),
@@ -261,11 +261,16 @@ def gemm(a_codes, a_scales, b_codes, b_scales, out_dtype=None, c=None, accumulat
     return c
 
 
-def set_gemm_events(start_event, stop_event):
-    """The next GEMM kernel this thread launches records these hipEvent_t
-    handles (ints or ctypes pointers; None for neither) at its own dispatch
-    start and end."""
-    _check(lib().fp4q_set_gemm_events(start_event, stop_event))
+ANY_ORDER = 1
+
+
+def set_next_launch(start_event=None, stop_event=None, any_order=False):
+    """Options for the next kernel this thread launches through the library:
+    hipEvent_t handles (ints or ctypes pointers, or None) that its dispatch
+    records at its start and end, and whether it may start before earlier
+    work on its stream has finished (the caller vouches that it does not
+    depend on that work)."""
+    _check(lib().fp4q_set_next_launch(start_event, stop_event, ANY_ORDER if any_order else 0))
 
 
 def hcp_workspace_bytes(M, N, n_hot):

@@ -72,10 +72,10 @@ template <int OUT_BF16>
 static void dq_dispatch(int block, dim3 grid, hipStream_t s, const uint32_t* c, const uint8_t* sc,
                         uint32_t tc, void* y) {
     switch (block) {
-        case 16: dequantize_kernel<OUT_BF16, 1><<<grid, kThreads, 0, s>>>(c, sc, tc, y); break;
-        case 32: dequantize_kernel<OUT_BF16, 2><<<grid, kThreads, 0, s>>>(c, sc, tc, y); break;
-        case 64: dequantize_kernel<OUT_BF16, 3><<<grid, kThreads, 0, s>>>(c, sc, tc, y); break;
-        default: dequantize_kernel<OUT_BF16, 4><<<grid, kThreads, 0, s>>>(c, sc, tc, y); break;
+        case 16: FP4Q_LAUNCH((dequantize_kernel<OUT_BF16, 1>), grid, kThreads, 0, s, c, sc, tc, y); break;
+        case 32: FP4Q_LAUNCH((dequantize_kernel<OUT_BF16, 2>), grid, kThreads, 0, s, c, sc, tc, y); break;
+        case 64: FP4Q_LAUNCH((dequantize_kernel<OUT_BF16, 3>), grid, kThreads, 0, s, c, sc, tc, y); break;
+        default: FP4Q_LAUNCH((dequantize_kernel<OUT_BF16, 4>), grid, kThreads, 0, s, c, sc, tc, y); break;
     }
 }
 

@@ -9,6 +9,10 @@
 #include "../../include/libfp4q.h"
 #include "fp4q_internal.h"
 
+namespace fp4q {
+thread_local NextLaunch g_next_launch = {nullptr, nullptr, 0u, false};
+}
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -47,8 +51,12 @@ int32_t fp4q_abi_version(void) { return FP4Q_ABI_VERSION; }
 
 const char* fp4q_last_error(void) { return g_err; }
 
-fp4q_status_t fp4q_set_gemm_events(void* start_event, void* stop_event) {
-    fp4q::set_gemm_launch_events((hipEvent_t)start_event, (hipEvent_t)stop_event);
+fp4q_status_t fp4q_set_next_launch(void* start_event, void* stop_event, uint32_t flags) {
+    if (flags & ~(uint32_t)FP4Q_LAUNCH_ANY_ORDER)
+        return fail(FP4Q_ERR_INVALID, "set_next_launch: unknown flags 0x%x", flags);
+    fp4q::g_next_launch = fp4q::NextLaunch{(hipEvent_t)start_event, (hipEvent_t)stop_event, flags,
+                                           start_event != nullptr || stop_event != nullptr ||
+                                               flags != 0};
     return FP4Q_OK;
 }
 

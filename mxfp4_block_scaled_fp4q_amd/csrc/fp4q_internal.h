@@ -1,10 +1,39 @@
 // Internal launcher interface between the C-ABI layer (fp4q_api.hip) and the
 // kernel translation units.  Launchers assume validated arguments.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace fp4q {
+
+// Options for the next kernel this thread launches through the library
+// (fp4q_set_next_launch): events recorded by that kernel's own dispatch, and
+// kAnyOrder, which lets the kernel start before earlier work in its stream
+// has finished.  The launch that takes them clears them.
+constexpr uint32_t kAnyOrder = 1;
+struct NextLaunch {
+    hipEvent_t start, stop;
+    uint32_t flags;
+    bool pending;
+};
+extern thread_local NextLaunch g_next_launch;
+
+// Every kernel launch of the library: plain, or, with options pending, through
+// hipExtLaunchKernel (events at the dispatch; any-order launches carry no
+// barrier behind the stream's earlier packets).
+#define FP4Q_LAUNCH(KERNEL, GRID, BLOCK, LDS, STREAM, ...)                                \
+    do {                                                                                \
+        if (::fp4q::g_next_launch.pending) {                                            \
+            const ::fp4q::NextLaunch nl_ = ::fp4q::g_next_launch;                       \
+            ::fp4q::g_next_launch = ::fp4q::NextLaunch{nullptr, nullptr, 0u, false};    \
+            hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, nl_.start, nl_.stop,  \
+                                  (nl_.flags & ::fp4q::kAnyOrder) ? hipExtAnyOrderLaunch : 0u, \
+                                  __VA_ARGS__);                                         \
+        } else {                                                                        \
+            hipLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, __VA_ARGS__);          \
+        }                                                                               \
+    } while (0)
 
 // n / d for n < 2^31 with a precomputed multiplier (Granlund & Montgomery,
 // "Division by invariant integers using multiplication", PLDI'94, round-up
@@ -51,10 +80,6 @@ hipError_t launch_dge(const void* x, int xdtype, const void* g, int gdtype, int6
 hipError_t launch_gemm_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
                            const uint8_t* as, const uint8_t* bc, const uint8_t* bs, void* c,
                            int cdtype, int64_t ldc, bool accumulate, hipStream_t s);
-// The next GEMM kernel this thread launches records start and stop (either
-// may be null) at its dispatch instead of being launched plainly; both null
-// clears a pending pair.
-void set_gemm_launch_events(hipEvent_t start, hipEvent_t stop);
 // C[M,N] (fp32, row stride ldc) += A B^T for bf16 A [M,K], B [N,K] (K % 32 == 0),
 // on the FP4 GEMM's pipeline with bf16 MFMAs.
 hipError_t launch_gemm_bf16_accum(int64_t M, int64_t N, int64_t K, const uint16_t* a,

@@ -52,8 +52,6 @@
 #include <cstring>
 #include <type_traits>
 
-#include <hip/hip_ext.h>
-
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -1141,32 +1139,6 @@ static int pick_cfg(int64_t M, int64_t N) {
     return e1 < e0 ? 1 : 0;
 }
 
-// Events for the next GEMM kernel this thread launches (set_gemm_launch_events):
-// that launch goes through hipExtLaunchKernel, which records them at the
-// dispatch itself (its start and end), and clears them.
-static thread_local hipEvent_t g_next_start = nullptr, g_next_stop = nullptr;
-
-void set_gemm_launch_events(hipEvent_t start, hipEvent_t stop) {
-    g_next_start = start;
-    g_next_stop = stop;
-}
-
-static bool take_launch_events(hipEvent_t& start, hipEvent_t& stop) {
-    start = g_next_start;
-    stop = g_next_stop;
-    g_next_start = g_next_stop = nullptr;
-    return start != nullptr || stop != nullptr;
-}
-
-#define FP4Q_LAUNCH(KERNEL, GRID, BLOCK, STREAM, ...)                                       \
-    do {                                                                                  \
-        hipEvent_t e0_, e1_;                                                              \
-        if (take_launch_events(e0_, e1_))                                                 \
-            hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, e0_, e1_, 0, __VA_ARGS__); \
-        else                                                                              \
-            hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);              \
-    } while (0)
-
 template <int CFG, int OUT_BF16, int ACCUM, int OPS, int EPI = 0>
 static void launch_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                        const uint8_t* b, const uint8_t* bs, void* c, int64_t ldc, hipStream_t s,
@@ -1181,12 +1153,12 @@ static void launch_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
     if constexpr (OPS != 1) {
         if (K % 128) {
             FP4Q_LAUNCH((gemm_fp4_kernel<CFG, OUT_BF16, ACCUM, OPS, EPI, 1>), grid,
-                        dim3(L::THREADS), s, (int)M, (int)N, (int)K, a, as, b, bs, c, ldc,
+                        dim3(L::THREADS), 0, s, (int)M, (int)N, (int)K, a, as, b, bs, c, ldc,
                         tiles_m, tiles_n, ha, hb, (int)kp, ex, dp, qc, qs);
             return;
         }
     }
-    FP4Q_LAUNCH((gemm_fp4_kernel<CFG, OUT_BF16, ACCUM, OPS, EPI, 0>), grid, dim3(L::THREADS), s,
+    FP4Q_LAUNCH((gemm_fp4_kernel<CFG, OUT_BF16, ACCUM, OPS, EPI, 0>), grid, dim3(L::THREADS), 0, s,
                 (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m, tiles_n, ha, hb, (int)kp,
                 ex, dp, qc, qs);
 }
@@ -1220,7 +1192,7 @@ static void launch_tiles(int64_t M, int64_t N, int64_t K, const uint8_t* a, cons
                 if (v > 0) grid = std::min<int64_t>(grid, v);
             }
             FP4Q_LAUNCH((gemm_fp4_persistent_kernel<OUT_BF16, ACCUM>), dim3((unsigned)grid),
-                        dim3(512), s, (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m,
+                        dim3(512), 0, s, (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m,
                         tiles_n);
             return;
         }

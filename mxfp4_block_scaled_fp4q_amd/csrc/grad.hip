@@ -243,10 +243,10 @@ hipError_t launch_ste(const void* g, int gdtype, int64_t n, void* out, int odtyp
     if (wgs > 65536) wgs = 65536;
     if (wgs < 1) wgs = 1;
     dim3 grid((unsigned)wgs);
-    if (gdtype == BF16 && odtype == BF16) ste_kernel<1, 1><<<grid, kThreads, 0, s>>>(g, n, out);
-    else if (gdtype == BF16) ste_kernel<1, 0><<<grid, kThreads, 0, s>>>(g, n, out);
-    else if (odtype == BF16) ste_kernel<0, 1><<<grid, kThreads, 0, s>>>(g, n, out);
-    else ste_kernel<0, 0><<<grid, kThreads, 0, s>>>(g, n, out);
+    if (gdtype == BF16 && odtype == BF16) FP4Q_LAUNCH((ste_kernel<1, 1>), grid, kThreads, 0, s, g, n, out);
+    else if (gdtype == BF16) FP4Q_LAUNCH((ste_kernel<1, 0>), grid, kThreads, 0, s, g, n, out);
+    else if (odtype == BF16) FP4Q_LAUNCH((ste_kernel<0, 1>), grid, kThreads, 0, s, g, n, out);
+    else FP4Q_LAUNCH((ste_kernel<0, 0>), grid, kThreads, 0, s, g, n, out);
     return hipGetLastError();
 }
 
@@ -257,10 +257,10 @@ static void dge_dispatch(const void* x, const void* g, int64_t rows, int64_t col
         const uint32_t tc = (uint32_t)(rows * cols / 8);
         dim3 grid((tc + kThreads - 1) / kThreads);
         switch (block) {
-            case 16: dge_row_kernel<XB, GB, OB, 16><<<grid, kThreads, 0, s>>>(x, g, tc, out, P); break;
-            case 32: dge_row_kernel<XB, GB, OB, 32><<<grid, kThreads, 0, s>>>(x, g, tc, out, P); break;
-            case 64: dge_row_kernel<XB, GB, OB, 64><<<grid, kThreads, 0, s>>>(x, g, tc, out, P); break;
-            default: dge_row_kernel<XB, GB, OB, 128><<<grid, kThreads, 0, s>>>(x, g, tc, out, P); break;
+            case 16: FP4Q_LAUNCH((dge_row_kernel<XB, GB, OB, 16>), grid, kThreads, 0, s, x, g, tc, out, P); break;
+            case 32: FP4Q_LAUNCH((dge_row_kernel<XB, GB, OB, 32>), grid, kThreads, 0, s, x, g, tc, out, P); break;
+            case 64: FP4Q_LAUNCH((dge_row_kernel<XB, GB, OB, 64>), grid, kThreads, 0, s, x, g, tc, out, P); break;
+            default: FP4Q_LAUNCH((dge_row_kernel<XB, GB, OB, 128>), grid, kThreads, 0, s, x, g, tc, out, P); break;
         }
     } else {
         const int64_t ncg = (cols + 7) / 8;
@@ -269,10 +269,10 @@ static void dge_dispatch(const void* x, const void* g, int64_t rows, int64_t col
         const int64_t ncc = (ncg + cgw - 1) / cgw;
         dim3 grid((unsigned)((nrb * ncc + 3) / 4));
         switch (block) {
-            case 16: dge_col_kernel<XB, GB, OB, 16><<<grid, kThreads, 0, s>>>(x, g, rows, cols, out, P, ncg, nrb, ncc); break;
-            case 32: dge_col_kernel<XB, GB, OB, 32><<<grid, kThreads, 0, s>>>(x, g, rows, cols, out, P, ncg, nrb, ncc); break;
-            case 64: dge_col_kernel<XB, GB, OB, 64><<<grid, kThreads, 0, s>>>(x, g, rows, cols, out, P, ncg, nrb, ncc); break;
-            default: dge_col_kernel<XB, GB, OB, 128><<<grid, kThreads, 0, s>>>(x, g, rows, cols, out, P, ncg, nrb, ncc); break;
+            case 16: FP4Q_LAUNCH((dge_col_kernel<XB, GB, OB, 16>), grid, kThreads, 0, s, x, g, rows, cols, out, P, ncg, nrb, ncc); break;
+            case 32: FP4Q_LAUNCH((dge_col_kernel<XB, GB, OB, 32>), grid, kThreads, 0, s, x, g, rows, cols, out, P, ncg, nrb, ncc); break;
+            case 64: FP4Q_LAUNCH((dge_col_kernel<XB, GB, OB, 64>), grid, kThreads, 0, s, x, g, rows, cols, out, P, ncg, nrb, ncc); break;
+            default: FP4Q_LAUNCH((dge_col_kernel<XB, GB, OB, 128>), grid, kThreads, 0, s, x, g, rows, cols, out, P, ncg, nrb, ncc); break;
         }
     }
 }

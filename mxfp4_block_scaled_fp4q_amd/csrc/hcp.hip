@@ -336,13 +336,13 @@ static hipError_t gather_hot(int64_t M, int64_t N, int64_t K, const void* x, con
             const int rpw = (int)std::min<int64_t>(4, (kLdsBudget - hot_bytes) / row_bytes);
             const size_t lds = (size_t)(hot_bytes + rpw * row_bytes);
             dim3 grid((unsigned)((M + rpw - 1) / rpw));
-            hcp_gather_x_rows<<<grid, kThreads, lds, s>>>((const uint16_t*)x, xqc, xqs, hot, n_hot,
+            FP4Q_LAUNCH((hcp_gather_x_rows), grid, kThreads, lds, s, (const uint16_t*)x, xqc, xqs, hot, n_hot,
                                                           M, K, kp, ap, with_q, rpw, (int)hot_bytes,
                                                           (int)row_bytes);
         } else {
             const int64_t total = M * (kp / 8);
             dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
-            hcp_gather_x<<<grid, kThreads, 0, s>>>((const uint16_t*)x, xqc, xqs, hot, n_hot, M, K,
+            FP4Q_LAUNCH((hcp_gather_x), grid, kThreads, 0, s, (const uint16_t*)x, xqc, xqs, hot, n_hot, M, K,
                                                    kp, ap, with_q);
         }
     }
@@ -354,12 +354,12 @@ static hipError_t gather_hot(int64_t M, int64_t N, int64_t K, const void* x, con
         const int64_t q_bytes = 8 * (K / 2 + K / 32);
         if (with_q && hot_bytes + wh_bytes + q_bytes <= 40 * 1024) {
             dim3 grid((unsigned)((N + 7) / 8));
-            hcp_gather_w_rows<<<grid, kThreads, (size_t)(hot_bytes + wh_bytes + q_bytes), s>>>(
+            FP4Q_LAUNCH((hcp_gather_w_rows), grid, kThreads, (size_t)(hot_bytes + wh_bytes + q_bytes), s,
                 (const uint16_t*)w, wqc, wqs, hot, n_hot, N, K, kp, bp, with_q, (int)hot_bytes,
                 (int)wh_bytes);
         } else {
             dim3 grid((unsigned)((N + 63) / 64), (unsigned)((kp / 8 + 3) / 4));
-            hcp_gather_w<<<grid, kThreads, 0, s>>>((const uint16_t*)w, wqc, wqs, hot, n_hot, N, K,
+            FP4Q_LAUNCH((hcp_gather_w), grid, kThreads, 0, s, (const uint16_t*)w, wqc, wqs, hot, n_hot, N, K,
                                                    kp, bp, with_q);
         }
     }

@@ -278,10 +278,10 @@ hipError_t launch_hot_channels(const uint16_t* x, int64_t rows, int64_t cols, in
     float* partial = (float*)ws;
     float* err = err_out ? err_out : partial + tiles * cols;
     dim3 g1((unsigned)tiles, (unsigned)((cols + kErrCols - 1) / kErrCols));
-    hot_err_partial<<<g1, kErrThreads, 0, s>>>(x, rows, cols, ld, (int)slab, partial);
-    hot_err_final<<<dim3((unsigned)((cols + 63) / 64)), kFinThreads, 0, s>>>(partial, tiles, cols,
+    FP4Q_LAUNCH((hot_err_partial), g1, kErrThreads, 0, s, x, rows, cols, ld, (int)slab, partial);
+    FP4Q_LAUNCH((hot_err_final), dim3((unsigned)((cols + 63) / 64)), kFinThreads, 0, s, partial, tiles, cols,
                                                                              err);
-    if (n_hot > 0) hot_select<<<1, kSelThreads, 0, s>>>(err, (int)cols, n_hot, hot);
+    if (n_hot > 0) FP4Q_LAUNCH((hot_select), 1, kSelThreads, 0, s, err, (int)cols, n_hot, hot);
     return hipGetLastError();
 }
 

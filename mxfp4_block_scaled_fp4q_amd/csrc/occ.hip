@@ -322,21 +322,21 @@ hipError_t launch_occ_quantize(const void* x, int64_t rows, int64_t cols, int64_
     const FastDiv cpr = make_fastdiv((uint32_t)(cols / 8));
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
     const int64_t zn = rows > kOccBins ? rows : kOccBins;
-    occ_zero<<<dim3((unsigned)((zn + kOccThreads - 1) / kOccThreads)), kOccThreads, 0, s>>>(
+    FP4Q_LAUNCH((occ_zero), dim3((unsigned)((zn + kOccThreads - 1) / kOccThreads)), kOccThreads, 0, s,
         w.hist, w.row_cnt, rows);
     const uint32_t hb = (total + kOccHistThreads - 1) / kOccHistThreads;
-    occ_hist<<<dim3(hb < (uint32_t)n_cus ? hb : (uint32_t)n_cus), kOccHistThreads, 0, s>>>(
+    FP4Q_LAUNCH((occ_hist), dim3(hb < (uint32_t)n_cus ? hb : (uint32_t)n_cus), kOccHistThreads, 0, s,
         xb, total, cpr, ld, w.hist);
-    occ_select<<<1, 1024, 0, s>>>(w.hist, j, w.params, t_out);
+    FP4Q_LAUNCH((occ_select), 1, 1024, 0, s, w.hist, j, w.params, t_out);
     const dim3 gq((total + kOccThreads * kOccUnroll - 1) / (kOccThreads * kOccUnroll));
     if (sr)
-        occ_clamp_quant<1><<<gq, kOccThreads, 0, s>>>(xb, total, cpr, ld, w.params, k0, k1, off,
+        FP4Q_LAUNCH((occ_clamp_quant<1>), gq, kOccThreads, 0, s, xb, total, cpr, ld, w.params, k0, k1, off,
                                                      codes, scales, w.mask, w.row_cnt);
     else
-        occ_clamp_quant<0><<<gq, kOccThreads, 0, s>>>(xb, total, cpr, ld, w.params, k0, k1, off,
+        FP4Q_LAUNCH((occ_clamp_quant<0>), gq, kOccThreads, 0, s, xb, total, cpr, ld, w.params, k0, k1, off,
                                                      codes, scales, w.mask, w.row_cnt);
-    occ_scan<<<1, 1024, 0, s>>>(w.row_cnt, rows, row_ptr);
-    occ_fill<<<dim3((unsigned)((rows + 3) / 4)), kOccThreads, 0, s>>>(
+    FP4Q_LAUNCH((occ_scan), 1, 1024, 0, s, w.row_cnt, rows, row_ptr);
+    FP4Q_LAUNCH((occ_fill), dim3((unsigned)((rows + 3) / 4)), kOccThreads, 0, s,
         xb, rows, cols, ld, w.mask, w.params, row_ptr, col_idx, vals);
     return hipGetLastError();
 }
@@ -399,7 +399,7 @@ hipError_t launch_occ_spmm(int64_t M, int64_t N, const int64_t* row_ptr, const i
                            const float* vals, const void* w, int64_t ldw, float* y, int64_t ldy,
                            hipStream_t s) {
     const dim3 grid((unsigned)M, (unsigned)((N / 8 + kOccThreads - 1) / kOccThreads));
-    occ_spmm_kernel<<<grid, kOccThreads, 0, s>>>(N, row_ptr, col_idx, vals, (const uint16_t*)w,
+    FP4Q_LAUNCH((occ_spmm_kernel), grid, kOccThreads, 0, s, N, row_ptr, col_idx, vals, (const uint16_t*)w,
                                                  ldw, y, ldy);
     return hipGetLastError();
 }

@@ -164,7 +164,7 @@ hipError_t launch_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_t
                     (unsigned)((rows + kQ2Rows - 1) / kQ2Rows));
     const uint16_t* xb = (const uint16_t*)x;
 #define FP4Q_Q2D(SR_, T_)                                                                   \
-    quantize_2d_kernel<SR_, T_><<<grid, kQ2Threads, 0, s>>>(xb, rows, cols, ld, k0, k1, off,  \
+    FP4Q_LAUNCH((quantize_2d_kernel<SR_, T_>), grid, kQ2Threads, 0, s, xb, rows, cols, ld, k0, k1, off,  \
                                                           codes_r, scales_r, codes_c, scales_c)
     if (tile == 16) {
         if (sr) FP4Q_Q2D(1, 16); else FP4Q_Q2D(0, 16);

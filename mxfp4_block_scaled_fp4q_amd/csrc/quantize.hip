@@ -240,19 +240,19 @@ static hipError_t row_dispatch(int block, dim3 grid, hipStream_t s, const void* 
     constexpr int U = SR ? 2 : 4;
     switch (block) {
         case 16:
-            quantize_row_kernel<IN_BF16, 16, SR, U, MASK><<<grid, kThreads, 0, s>>>(
+            FP4Q_LAUNCH((quantize_row_kernel<IN_BF16, 16, SR, U, MASK>), grid, kThreads, 0, s,
                 x, tc, cpr, ld, cols, codes, scales, k0, k1, off, zmask);
             break;
         case 32:
-            quantize_row_kernel<IN_BF16, 32, SR, U, MASK><<<grid, kThreads, 0, s>>>(
+            FP4Q_LAUNCH((quantize_row_kernel<IN_BF16, 32, SR, U, MASK>), grid, kThreads, 0, s,
                 x, tc, cpr, ld, cols, codes, scales, k0, k1, off, zmask);
             break;
         case 64:
-            quantize_row_kernel<IN_BF16, 64, SR, U, MASK><<<grid, kThreads, 0, s>>>(
+            FP4Q_LAUNCH((quantize_row_kernel<IN_BF16, 64, SR, U, MASK>), grid, kThreads, 0, s,
                 x, tc, cpr, ld, cols, codes, scales, k0, k1, off, zmask);
             break;
         default:
-            quantize_row_kernel<IN_BF16, 128, SR, U, MASK><<<grid, kThreads, 0, s>>>(
+            FP4Q_LAUNCH((quantize_row_kernel<IN_BF16, 128, SR, U, MASK>), grid, kThreads, 0, s,
                 x, tc, cpr, ld, cols, codes, scales, k0, k1, off, zmask);
             break;
     }
@@ -828,7 +828,7 @@ static hipError_t col_dispatch(int block, int64_t nct, hipStream_t s, const void
     const dim3 grid((unsigned)n_tiles);
     const FastDiv ctd = make_fastdiv((uint32_t)nct);
 #define FP4Q_COL_LAUNCH(B)                                                                    \
-    quantize_col_kernel<IN_BF16, B, SR, AL, ROW, RPT><<<grid, kThreads, 0, s>>>(              \
+    FP4Q_LAUNCH((quantize_col_kernel<IN_BF16, B, SR, AL, ROW, RPT>), grid, kThreads, 0, s,               \
         x, rows, cols, ld, codes, scales, k0, k1, off, nrb, ctd,                              \
         codes_r, scales_r, kr0, kr1, zmask)
     switch (block) {
@@ -931,10 +931,10 @@ __global__ __launch_bounds__(kThreads) void mask_set_kernel(const int32_t* __res
 hipError_t launch_channel_mask(const int32_t* idx, int32_t n, int64_t length, uint32_t* mask,
                                hipStream_t s) {
     const int64_t words = (length + 31) / 32;
-    mask_fill_kernel<<<dim3((unsigned)((words + kThreads - 1) / kThreads)), kThreads, 0, s>>>(
+    FP4Q_LAUNCH((mask_fill_kernel), dim3((unsigned)((words + kThreads - 1) / kThreads)), kThreads, 0, s,
         mask, words);
     if (n > 0)
-        mask_set_kernel<<<dim3((unsigned)((n + kThreads - 1) / kThreads)), kThreads, 0, s>>>(
+        FP4Q_LAUNCH((mask_set_kernel), dim3((unsigned)((n + kThreads - 1) / kThreads)), kThreads, 0, s,
             idx, n, length, mask);
     return hipGetLastError();
 }

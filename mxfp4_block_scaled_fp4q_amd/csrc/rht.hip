@@ -239,10 +239,10 @@ hipError_t launch_quantize_rht(const void* x, int64_t rows, int64_t cols, int64_
         const int64_t chunks = rows * (cols / 8);
         const dim3 grid((unsigned)((chunks + kRhtThreads - 1) / kRhtThreads));
         if (sr)
-            rht_row_kernel<1><<<grid, kRhtThreads, 0, s>>>(xb, rows, cols, ld, signs, k0, k1, off,
+            FP4Q_LAUNCH((rht_row_kernel<1>), grid, kRhtThreads, 0, s, xb, rows, cols, ld, signs, k0, k1, off,
                                                           codes, scales);
         else
-            rht_row_kernel<0><<<grid, kRhtThreads, 0, s>>>(xb, rows, cols, ld, signs, k0, k1, off,
+            FP4Q_LAUNCH((rht_row_kernel<0>), grid, kRhtThreads, 0, s, xb, rows, cols, ld, signs, k0, k1, off,
                                                           codes, scales);
     } else {
         // groups per thread down the rows: 4 (64 contiguous code bytes per
@@ -252,10 +252,10 @@ hipError_t launch_quantize_rht(const void* x, int64_t rows, int64_t cols, int64_
         while (rb > 1 && gx * ((nb + rb - 1) / rb) < 1024) rb >>= 1;
         const dim3 grid((unsigned)gx, (unsigned)((nb + rb - 1) / rb));
         if (sr)
-            rht_col_kernel<1><<<grid, kRhtThreads, 0, s>>>(xb, rows, cols, ld, signs, k0, k1, off,
+            FP4Q_LAUNCH((rht_col_kernel<1>), grid, kRhtThreads, 0, s, xb, rows, cols, ld, signs, k0, k1, off,
                                                           rb, codes, scales);
         else
-            rht_col_kernel<0><<<grid, kRhtThreads, 0, s>>>(xb, rows, cols, ld, signs, k0, k1, off,
+            FP4Q_LAUNCH((rht_col_kernel<0>), grid, kRhtThreads, 0, s, xb, rows, cols, ld, signs, k0, k1, off,
                                                           rb, codes, scales);
     }
     return hipGetLastError();

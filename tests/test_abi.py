@@ -413,3 +413,13 @@ def test_hcp_noalloc_validation(L):
     assert h(1 << 20, 1 << 16, 1024, *args, 64, FAKE, NUL) == 4           # > 64 MiB of scratch
     assert b"static maximum" in L.fp4q_last_error()
     assert fq.hcp_workspace_bytes(1 << 20, 1 << 16, 64) > fq.HCP_NOALLOC_MAX_BYTES
+
+
+def test_set_next_launch_flags(L):
+    """Unknown flag bits are rejected and set nothing; the known ones and the
+    clearing call succeed (host-side state only, no device work)."""
+    assert L.fp4q_set_next_launch(None, None, 2) == 1
+    assert "flags" in L.fp4q_last_error().decode()
+    assert L.fp4q_set_next_launch(None, None, 0xFFFFFFFE) == 1
+    assert L.fp4q_set_next_launch(None, None, fq.ANY_ORDER) == 0
+    assert L.fp4q_set_next_launch(None, None, 0) == 0

@@ -427,40 +427,3 @@ def test_persistent_gemm_chains_tiles(orc, M, N, K, grid, monkeypatch):
         torch.cuda.synchronize()
         assert np.array_equal(host_bits(p).view(np.uint8), host_bits(q).view(np.uint8)), dt
 
-
-@pytest.mark.parametrize("M,N,K", [(1024, 768, 2048), (4096, 5632, 2048)])
-def test_gemm_dispatch_events(M, N, K):
-    """fp4q_set_gemm_events: the next GEMM launch (one tile per workgroup at
-    1024 x 768, the persistent form at 4096 x 5632) records the pair at its
-    own dispatch; its output is the plain launch's bit for bit, and the pair
-    is used once (the launch after it is plain and leaves the events alone)."""
-    import ctypes
-    import os
-    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
-    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
-    for e in ev:
-        assert hip.hipEventCreateWithFlags(ctypes.byref(e), 0) == 0
-    try:
-        rng = np.random.default_rng(M + N)
-        ac = torch.from_numpy(rng.integers(0, 256, (M, K // 2), dtype=np.uint8)).cuda()
-        bc = torch.from_numpy(rng.integers(0, 256, (N, K // 2), dtype=np.uint8)).cuda()
-        as_ = torch.from_numpy(rng.integers(118, 136, (M, K // 32), dtype=np.uint8)).cuda()
-        bs = torch.from_numpy(rng.integers(118, 136, (N, K // 32), dtype=np.uint8)).cuda()
-        plain = fq.gemm(ac, as_, bc, bs)
-        fq.set_gemm_events(ev[0], ev[1])
-        timed = fq.gemm(ac, as_, bc, bs)
-        torch.cuda.synchronize()
-        ms = ctypes.c_float()
-        assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
-        first = ms.value
-        assert 0.0 < first < 1000.0, first
-        after = fq.gemm(ac, as_, bc, bs)
-        torch.cuda.synchronize()
-        assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
-        assert ms.value == first, "a plain launch re-recorded the events"
-        for o in (timed, after):
-            assert np.array_equal(host_bits(o).view(np.uint8), host_bits(plain).view(np.uint8))
-        fq.set_gemm_events(None, None)
-    finally:
-        for e in ev:
-            hip.hipEventDestroy(e)
