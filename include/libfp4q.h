@@ -193,7 +193,7 @@ fp4q_status_t fp4q_grad_estimate(fp4q_grad_t mode, const void* x, fp4q_dtype_t x
  *   atomics, no split-K.  The tile shape (256 x 256 or 128 x 384) is chosen
  *   per M, N from the device's compute-unit count; the environment variable
  *   FP4Q_GEMM_TILE=256x256 or 128x384 forces one.  With 256 x 256 tiles, more
- *   tiles than compute units and K % 2048 == 0, one persistent workgroup per
+ *   tiles than compute units and K % 1024 == 0, one persistent workgroup per
  *   compute unit walks several tiles (FP4Q_GEMM_PERSIST=0 turns this off).
  *   Every form accumulates each output over K in the same order, so all give
  *   bit-identical results.

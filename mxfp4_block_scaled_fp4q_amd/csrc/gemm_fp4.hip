@@ -43,7 +43,7 @@
 // writes 16 contiguous bytes.  Workgroups are remapped so that consecutive
 // tiles of a grouped (4 tile-rows) order run on the same XCD and share its
 // L2.  Where there are more 256 x 256 tiles than compute units and K is a
-// multiple of 2048, a persistent form runs instead (one workgroup per compute
+// multiple of 1024, a persistent form runs instead (one workgroup per compute
 // unit walking its tiles with the operand ring running on across tiles, the
 // workgroups with a tile fewer starting a little late; see
 // gemm_fp4_persistent_kernel).
@@ -766,13 +766,15 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
 // boundaries: the last three K steps of a tile issue the next tile's first
 // three steps (and its first scale group), so those loads are in flight
 // while the tile's epilogue stores C, and the next tile starts without a
-// relaunch or a cold first load.  For K % 2048 == 0 (the K steps of a tile a
-// multiple of 16, so each tile starts at step 0 of the unrolled turn and on
-// scale buffer 0) and plain C; the epilogue stages each wave's rows in the
-// stage and the scale buffer the tile's last step and last group used
-// (st3 and sc1), which the next tile does not touch before the barrier that
-// ends the epilogue.  Every output is summed over K in the same order as the
-// one-tile-per-workgroup kernel, so the two agree bit for bit.
+// relaunch or a cold first load.  For K % 1024 == 0 (the K steps of a tile a
+// multiple of 8, so each tile starts at step 0 of the unrolled turn and of a
+// scale group; HALF: K % 2048 == 1024, a tile ends on a half turn and its
+// first scale buffer alternates from tile to tile) and plain C; the epilogue
+// stages each wave's rows in the stage and the scale buffer the tile's last
+// step and last group used (st3 and that buffer), which the next tile does
+// not touch before the barrier that ends the epilogue.  Every output is
+// summed over K in the same order as the one-tile-per-workgroup kernel, so
+// the two agree bit for bit.
 struct TileRsrc {
     __amdgpu_buffer_rsrc_t ra, rb, rsc;
 };
@@ -902,7 +904,7 @@ __device__ __forceinline__ void persist_epilogue(v16f (&acc)[4][2], uint8_t* reg
     }
 }
 
-template <int OUT_BF16, int ACCUM>
+template <int OUT_BF16, int ACCUM, int HALF>
 __global__ __launch_bounds__(Layout<0>::THREADS, 1) void gemm_fp4_persistent_kernel(
     int M, int N, int K, const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ bc, const uint8_t* __restrict__ bs, void* __restrict__ cptr,
@@ -926,7 +928,7 @@ __global__ __launch_bounds__(Layout<0>::THREADS, 1) void gemm_fp4_persistent_ker
     const int sxor = (l32 >> 3) & 3;
     const int kbytes = K / 2;
     const int kscale = K / 32;
-    const int ksteps = kbytes / BKB;  // a multiple of 16
+    const int ksteps = kbytes / BKB;  // a multiple of 16, or of 8 with HALF
 
     // Workgroups that own one tile fewer than the others (those past
     // ntiles % G in the deal) have a whole tile of slack.  They start about a
@@ -995,8 +997,14 @@ __global__ __launch_bounds__(Layout<0>::THREADS, 1) void gemm_fp4_persistent_ker
 
 #define FP4Q_PIECES(p) ((((p) & 7) >= 4) ? 0 : L::SPIECES / 4)
 #define FP4Q_BEHIND(p) (FP4Q_PIECES((p) + 6) + LC + FP4Q_PIECES((p) + 7) + LC + FP4Q_PIECES(p))
-#define FP4Q_SCUR(P) ((((P) / SG) & 1) ? sc1 : sc0)
-#define FP4Q_SNXT(P) ((((P) / SG) & 1) ? sc0 : sc1)
+    // Scale group j of a tile uses buffer (j + ph_) % 2, ph_ being the buffer
+    // of the tile's first group: 0 for every tile when a tile has an even
+    // number of 8-step groups; with HALF (K % 2048 == 1024: 16-step turns and
+    // a last half turn, an odd number of groups) it alternates from tile to
+    // tile, and each parity has its own copy of the tile's code, so that
+    // every LDS buffer is still named at compile time.
+#define FP4Q_SCUR(P) (((((P) / SG) + ph_) & 1) ? sc1 : sc0)
+#define FP4Q_SNXT(P) (((((P) / SG) + ph_) & 1) ? sc0 : sc1)
     // one K step; the loads it issues (step t_ + 3 and, early in a scale
     // group, the next group's pieces) come from this tile or, past its end,
     // from the next one (or repeat this tile's last step when there is none)
@@ -1035,61 +1043,76 @@ __global__ __launch_bounds__(Layout<0>::THREADS, 1) void gemm_fp4_persistent_ker
         mfma_half<CFG, 0, 1>(FB, sa, sb, acc);                                       \
     } while (0)
 
-    for (;;) {
-        v16f acc[TM][TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-        for (int kt = 0; kt < ksteps; kt += 16) {
-            FP4Q_PSTEP(0, st0, st1, st3);
-            FP4Q_PSTEP(1, st1, st2, st0);
-            FP4Q_PSTEP(2, st2, st3, st1);
-            FP4Q_PSTEP(3, st3, st0, st2);
-            FP4Q_PSTEP(4, st0, st1, st3);
-            FP4Q_PSTEP(5, st1, st2, st0);
-            FP4Q_PSTEP(6, st2, st3, st1);
-            FP4Q_PSTEP(7, st3, st0, st2);
-            FP4Q_PSTEP(8, st0, st1, st3);
-            FP4Q_PSTEP(9, st1, st2, st0);
-            FP4Q_PSTEP(10, st2, st3, st1);
-            FP4Q_PSTEP(11, st3, st0, st2);
-            FP4Q_PSTEP(12, st0, st1, st3);
-            FP4Q_PSTEP(13, st1, st2, st0);
-            FP4Q_PSTEP(14, st2, st3, st1);
-            FP4Q_PSTEP(15, st3, st0, st2);
-        }
-
-        // epilogue through the stage and scale buffer the tile's last step and
-        // last group used (six waves' regions in st3, two in sc1)
-        {
-            constexpr int ESZ = OUT_BF16 ? 2 : 4;
-            constexpr int CW = OUT_BF16 ? 64 : 32;
-            constexpr int EREG = 32 * (CW * ESZ + 16);
-            static_assert(6 * EREG <= STAGE && 2 * EREG <= SCALE_BUF, "staging fits");
-            uint8_t* reg = wave < 6 ? st3 + wave * EREG : sc1 + (wave - 6) * EREG;
-            persist_epilogue<OUT_BF16, ACCUM>(acc, reg, cptr, ldc, M, N, m0 + wm * L::WROWS,
-                                              n0 + wn * L::WCOLS, lane);
-        }
-        __syncthreads();  // st3 and sc1 are free again before the next tile refills them
-        if (!has_next) break;
-        tseq += G;
-        m0 = m1;
-        n0 = n1;
-        cur = nxt;
-        has_next = tseq + G < ntiles;
-        if (has_next) {
-            tile_origin(tseq + G, ntiles, tiles_m, tiles_n, m1, n1);
-            nxt = tile_rsrc(ac, as, bc, bs, M, N, m1, n1, kbytes, kscale, wave);
-        }
-        // the next tile's step 0 and scale group 0 landed before the last
-        // step's barrier; read them again (nothing was kept across the epilogue)
-        read_scales<CFG, 0>(sc0, sxor << 2, wm, wn, lane, ra, rb);
-        read_frags<CFG>(st0, off0, wm, wn, FA);
+    // One tile: its K steps (turns of 16; with HALF the last turn stops after
+    // its first 8 steps),
+    // its epilogue through the stage and the scale buffer that its last step
+    // and last group used (six waves' regions in st3, two in SC_LAST), then
+    // on to the next tile, whose first scale group sits in SC_FIRST.  The
+    // scale group j of a tile uses buffer (j + PH) % 2; with HALF (an odd
+    // number of groups per tile) PH alternates, so the loop body holds two
+    // tiles, one of each parity, and every LDS buffer is still named at
+    // compile time.
+#define FP4Q_TILE(PH, SC_LAST, SC_FIRST)                                                \
+    {                                                                                   \
+        constexpr int ph_ = (PH);                                                       \
+        v16f acc[TM][TN];                                                               \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                  \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                  \
+        _Pragma("unroll") for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;             \
+        for (int kt = 0; kt < ksteps; kt += 16) {                                       \
+            FP4Q_PSTEP(0, st0, st1, st3);                                           \
+            FP4Q_PSTEP(1, st1, st2, st0);                                           \
+            FP4Q_PSTEP(2, st2, st3, st1);                                           \
+            FP4Q_PSTEP(3, st3, st0, st2);                                           \
+            FP4Q_PSTEP(4, st0, st1, st3);                                           \
+            FP4Q_PSTEP(5, st1, st2, st0);                                           \
+            FP4Q_PSTEP(6, st2, st3, st1);                                           \
+            FP4Q_PSTEP(7, st3, st0, st2);                                           \
+            if (!HALF || kt + 16 <= ksteps) {                                           \
+                FP4Q_PSTEP(8, st0, st1, st3);                                       \
+                FP4Q_PSTEP(9, st1, st2, st0);                                       \
+                FP4Q_PSTEP(10, st2, st3, st1);                                      \
+                FP4Q_PSTEP(11, st3, st0, st2);                                      \
+                FP4Q_PSTEP(12, st0, st1, st3);                                      \
+                FP4Q_PSTEP(13, st1, st2, st0);                                      \
+                FP4Q_PSTEP(14, st2, st3, st1);                                      \
+                FP4Q_PSTEP(15, st3, st0, st2);                                      \
+            }                                                                           \
+        }                                                                               \
+        {                                                                               \
+            constexpr int ESZ = OUT_BF16 ? 2 : 4;                                       \
+            constexpr int CW = OUT_BF16 ? 64 : 32;                                      \
+            constexpr int EREG = 32 * (CW * ESZ + 16);                                  \
+            static_assert(6 * EREG <= STAGE && 2 * EREG <= SCALE_BUF, "staging fits");  \
+            uint8_t* reg = wave < 6 ? st3 + wave * EREG : (SC_LAST) + (wave - 6) * EREG; \
+            persist_epilogue<OUT_BF16, ACCUM>(acc, reg, cptr, ldc, M, N,                \
+                                              m0 + wm * L::WROWS, n0 + wn * L::WCOLS, lane); \
+        }                                                                               \
+        __syncthreads(); /* the staging buffers are free before the next tile refills them */ \
+        if (!has_next) break;                                                           \
+        tseq += G;                                                                      \
+        m0 = m1;                                                                        \
+        n0 = n1;                                                                        \
+        cur = nxt;                                                                      \
+        has_next = tseq + G < ntiles;                                                   \
+        if (has_next) {                                                                 \
+            tile_origin(tseq + G, ntiles, tiles_m, tiles_n, m1, n1);                    \
+            nxt = tile_rsrc(ac, as, bc, bs, M, N, m1, n1, kbytes, kscale, wave);        \
+        }                                                                               \
+        /* the next tile's step 0 and scale group 0 landed before the last step's */    \
+        /* barrier; read them again (nothing was kept across the epilogue) */           \
+        read_scales<CFG, 0>(SC_FIRST, sxor << 2, wm, wn, lane, ra, rb);                 \
+        read_frags<CFG>(st0, off0, wm, wn, FA);                                          \
     }
+    for (;;) {
+        if (HALF) {
+            FP4Q_TILE(0, sc0, sc1)
+            FP4Q_TILE(1, sc1, sc0)
+        } else {
+            FP4Q_TILE(0, sc1, sc0)
+        }
+    }
+#undef FP4Q_TILE
 #undef FP4Q_PSTEP
 #undef FP4Q_PIECES
 #undef FP4Q_BEHIND
@@ -1164,10 +1187,10 @@ static void launch_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
 }
 
 // Whether the persistent form runs: plain FP4 GEMMs on 256 x 256 tiles with
-// K % 2048 == 0 and more tiles than compute units (FP4Q_GEMM_PERSIST=0
+// K % 1024 == 0 and more tiles than compute units (FP4Q_GEMM_PERSIST=0
 // disables it, =1 forces it wherever it applies).
 static bool use_persistent(int64_t M, int64_t N, int64_t K) {
-    if (K % 2048) return false;
+    if (K % 1024) return false;
     const char* e = getenv("FP4Q_GEMM_PERSIST");
     if (e && !strcmp(e, "0")) return false;
     const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
@@ -1191,9 +1214,14 @@ static void launch_tiles(int64_t M, int64_t N, int64_t K, const uint8_t* a, cons
                 const long v = strtol(g, nullptr, 10);
                 if (v > 0) grid = std::min<int64_t>(grid, v);
             }
-            FP4Q_LAUNCH((gemm_fp4_persistent_kernel<OUT_BF16, ACCUM>), dim3((unsigned)grid),
-                        dim3(512), 0, s, (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m,
-                        tiles_n);
+            if (K % 2048)
+                FP4Q_LAUNCH((gemm_fp4_persistent_kernel<OUT_BF16, ACCUM, 1>),
+                            dim3((unsigned)grid), dim3(512), 0, s, (int)M, (int)N, (int)K, a, as,
+                            b, bs, c, ldc, tiles_m, tiles_n);
+            else
+                FP4Q_LAUNCH((gemm_fp4_persistent_kernel<OUT_BF16, ACCUM, 0>),
+                            dim3((unsigned)grid), dim3(512), 0, s, (int)M, (int)N, (int)K, a, as,
+                            b, bs, c, ldc, tiles_m, tiles_n);
             return;
         }
     }

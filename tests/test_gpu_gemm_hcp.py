@@ -402,13 +402,16 @@ def test_outlier_layer_single_kernel_hcp(orc):
 
 
 @pytest.mark.parametrize("M,N,K,grid", [(700, 1000, 2048, 5), (257, 513, 4096, 2),
-                                        (1024, 1024, 2048, 7), (300, 260, 2048, 1)])
+                                        (1024, 1024, 2048, 7), (300, 260, 2048, 1),
+                                        (300, 520, 3072, 3), (260, 300, 5120, 1)])
 def test_persistent_gemm_chains_tiles(orc, M, N, K, grid, monkeypatch):
     """The persistent form (one workgroup walking several tiles, the operand
     ring running on across tile boundaries) against the oracle over every
     output, bf16, fp32 and accumulated fp32, with fewer workgroups than tiles
     so that each chains several; and bit for bit equal to the
-    one-tile-per-workgroup kernel."""
+    one-tile-per-workgroup kernel.  K = 3072 and 5120 end each tile on a half
+    turn of the K loop, so the tiles' first scale buffers alternate (four
+    tiles on one workgroup at 260 x 300 x 5120)."""
     a = inputs.with_outliers(inputs.normal((M, K), M + 31), M + 32, M * K // 100, 50.0)
     b = inputs.with_outliers(inputs.normal((N, K), N + 33), N + 34, N * K // 100, 50.0)
     A, B = qpair(orc, a, b)
