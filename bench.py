@@ -356,7 +356,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4_TFLOPS, 4),
                 "traffic": measured_traffic(),
-                "kernel": "gemm_fp4_persistent_kernel<1, 0> 8192x5632x2048 bf16 out",
+                "kernel": "gemm_fp4_persistent_kernel<1, 0, 0> 8192x5632x2048 bf16 out",
                 "per_launch_flops": fwd_flops, "launch_us_mean": round(fwd_mean_us, 2),
                 "launch_us_min": round(float(np.min(fwd_us)), 2),
                 "launch_us_median": round(float(np.median(fwd_us)), 2),
