@@ -466,7 +466,8 @@ __device__ __forceinline__ void gemm_kloop(v16f (&acc)[Layout<CFG>::TM][Layout<C
 }
 
 // OPS: 0 = FP4 operands; 1 = bf16 operands (ac, bc hold bf16 rows, no
-// scales); 2 = FP4 over K, then bf16 over the kp-deep operands ha, hb into
+// scales; with ACCUM, kp is the size of the first round of workgroups, see
+// below); 2 = FP4 over K, then bf16 over the kp-deep operands ha, hb into
 // the same accumulators (the single-kernel hot-channel compensation).
 // EPI = 1 (fp32 C, 256 x 256 tiles, M % 32 == 0): C is multiplied in the
 // epilogue by the DGE derivative of ex [M, N] (bf16, dense) with ex's column
@@ -507,6 +508,18 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
     const int tn = in_grp / gsize;
     const int m0 = tm * L::BM, n0 = tn * L::BN;
 
+    // The accumulating bf16 form (the D-mode residual: C += ..., a read-
+    // modify-write of C after each tile's K loop) with several rounds of
+    // tiles: kp is the first round's size, and its odd workgroups start about
+    // half a tile late (0.5 us per K step + 10 us, a bounded wait on the
+    // real-time counter), so that the compute units' read-modify-write phases
+    // alternate instead of all hitting memory at once.  13B-shaped residual
+    // (461 hot channels): 832 -> 805 us with the gathers, the same bits.
+    if (OPS == 1 && ACCUM && (int)blockIdx.x < kp && (blockIdx.x & 1)) {
+        const uint64_t until =
+            __builtin_amdgcn_s_memrealtime() + (uint64_t)(K / 32) * 50 + 1000;
+        while (__builtin_amdgcn_s_memrealtime() < until) __builtin_amdgcn_s_sleep(16);
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1180,6 +1193,11 @@ static void launch_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const 
                         tiles_m, tiles_n, ha, hb, (int)kp, ex, dp, qc, qs);
             return;
         }
+    }
+    // the accumulating bf16 form takes the first round's size in kp (see the kernel)
+    if constexpr (OPS == 1 && ACCUM) {
+        const int64_t cus = device_cus();
+        kp = (int64_t)tiles_m * tiles_n > 2 * cus ? cus : 0;
     }
     FP4Q_LAUNCH((gemm_fp4_kernel<CFG, OUT_BF16, ACCUM, OPS, EPI, 0>), grid, dim3(L::THREADS), 0, s,
                 (int)M, (int)N, (int)K, a, as, b, bs, c, ldc, tiles_m, tiles_n, ha, hb, (int)kp,
