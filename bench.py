@@ -375,6 +375,7 @@ def main():
         # 13B-shaped outlier layer
         extra["tiny_ref"] = bench_tiny_ref(torch, fq, inputs, dev)
         extra["activation_sweep"] = bench_activation_sweep(torch, fq, inputs, dev)
+        extra["occ_fidelity"] = bench_occ_fidelity(torch, fq, inputs, dev)
         extra["outlier_layer"] = bench_outlier_layer(torch, fq, inputs, dev)
 
     cpu = None
@@ -538,6 +539,40 @@ def _rate(nbytes, us, us_graph=None):
         d["us_graph"] = round(us_graph, 2)
     d.update({"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)})
     return d
+
+
+def bench_occ_fidelity(torch, fq, inputs, dev):
+    """Context for the outlier pages' fidelity figures (cosine, MSE, SNR of
+    the quantised activation against the original): the activation workload
+    (Student-t(3) x 0.5, bf16 4096 x 2048) quantised directly (ROW blocks of
+    32, nearest-even) and with outlier clamping and compensation (values
+    beyond the 99th percentile of |x| clamped before quantisation, their
+    excess kept in the sparse residual).  Every step runs in the library's
+    kernels: the reconstruction of the compensated path is the dequantised
+    clamped codes plus R I, R's product with a bf16 identity through
+    fp4q_occ_spmm; only the three metrics are torch reductions."""
+    d = inputs.activation_sweep()
+    x = torch.from_numpy(d["X"].view(np.int16)).view(torch.bfloat16).to(dev)
+    R, K = x.shape
+    ref = x.float().double()
+
+    def metrics(xh):
+        e = xh.double() - ref
+        cos = float((xh.double() * ref).sum() / (xh.double().norm() * ref.norm()))
+        mse = float((e * e).mean())
+        snr = float(10.0 * torch.log10((ref * ref).sum() / (e * e).sum()))
+        return {"cosine": round(cos, 6), "mse": mse, "snr_db": round(snr, 3)}
+
+    direct = fq.dequantize(*fq.quantize(x, 32), 32, torch.float32)
+    codes, scales, rp, ci, v, _ = fq.occ_quantize(x, 0.99)
+    comp = fq.dequantize(codes, scales, 32, torch.float32)
+    eye = torch.eye(K, dtype=torch.bfloat16, device=dev)
+    fq.occ_spmm(rp, ci, v, eye, comp)
+    torch.cuda.synchronize()
+    nnz = int(rp[-1].item())
+    return {"input": f"bf16 {R}x{K} Student-t(3) x 0.5 (the activation workload)",
+            "quantile": 0.99, "outliers": nnz,
+            "direct": metrics(direct), "clamp_and_compensate": metrics(comp)}
 
 
 def bench_activation_sweep(torch, fq, inputs, dev, ncopies=32):
