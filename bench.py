@@ -13,17 +13,24 @@ through every kernel of the path:
             dW' = GEMM 2048x5632x8192 -> fp32 with DGE(W, col blocks, k=5,
                   clamp 3) applied in its epilogue (one kernel; the unfused
                   GEMM + DGE pair is timed aside)
-  The 13B-shaped outlier layer's hot-channel residual has its own shape and
-  is timed aside with --hcp.
+  The quantisers of W and dY, dequantize and the backward GEMMs are launched
+  any-order (each depends only on kernels that a plain launch before it has
+  waited for); --sequential launches everything plainly.
+
+The other workloads (the tiny case, the activation sweep, the 13B-shaped
+outlier layer with its hot-channel residual, the outlier-compensation
+fidelity) are measured in the same default run; --skip-configs leaves them
+out.
 
 `value` = FP4 GEMM flops of the step / step time (TFLOPS), i.e. whole-step
 throughput over the timed steps.  The roofline object reports the forward
 GEMM (the dominant kernel) against the dense FP4 MFMA peak, its launch time
-taken from HIP events around it inside the timed region (on the stream the
-kernels run on, created without a system-scope fence so that recording them
-does not flush L2), and its HBM traffic from committed counter runs.  A second
-pass with an event between every two kernels gives the per-kernel table.
-The CPU baseline times the single-threaded oracle on a bounded sample.
+taken from HIP events that its own dispatch records inside the timed region
+(fp4q_set_next_launch; on the stream the kernels run on, created without a
+system-scope fence), and its HBM traffic from committed counter runs.  A
+second pass, every launch plain, times each kernel by its own dispatch
+events for the per-kernel table.  The CPU baseline times the
+single-threaded oracle on a bounded sample.
 """
 import argparse
 import json
@@ -82,6 +89,11 @@ def measured_traffic():
     if rec.get("kernel_source_sha256") != src:
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+# asides timed by event records around the call rather than by the
+# dispatch's own events: not a single library kernel
+MARKER_TIMED = {"copy_dy", "occ_quantize_x"}
 
 
 class HipEvents:
@@ -161,6 +173,7 @@ def main():
     dW = torch.empty((K, N), dtype=torch.float32, device=dev)
     dWo = torch.empty((K, N), dtype=torch.float32, device=dev)
     dYg = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dXg = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
 
     # (name, callable, algorithmic bytes, algorithmic flops)
     qb = 2 + 0.5 + 1 / 32  # bf16 in, codes + E8M0 bytes out, per element
@@ -243,6 +256,11 @@ def main():
         # tensor as the attainable rate for that traffic
         ("ste_dy", lambda: fq.grad_estimate(fq.STE, None, dY, 32, fq.ROW, out=dYg), M * N * 4, 0),
         ("copy_dy", lambda: dYg.copy_(dY), M * N * 4, 0),
+        # the activation quantiser's DGE backward at the layer's size: X's ROW
+        # blocks (scales recomputed from X), applied to the data gradient dX
+        # (bf16 x, g and out, 6 B per element)
+        ("dge_x", lambda: fq.grad_estimate(fq.DGE, X, dX, 32, fq.ROW, 5.0, 3.0, out=dXg),
+         M * K * 6, 0),
     ]
     step_flops = sum(o[3] for o in ops)
 
@@ -262,7 +280,6 @@ def main():
         torch.cuda.synchronize()
         return
 
-    nev = len(ops) + 1
     i_fwd = [o[0] for o in ops].index("gemm_fwd")
     # Launches that may start before the stream's earlier kernels finish
     # (fp4q_set_next_launch any-order): each reads only what a kernel behind
@@ -277,16 +294,16 @@ def main():
     hev = HipEvents(torch)
 
     def run_step(evs=None, fwd_evs=None):
+        # evs: a start/stop pair per kernel, recorded by each kernel's own
+        # dispatch (the per-kernel pass, every launch plain)
         for i, (_, fn, _, _) in enumerate(ops):
             if evs is not None:
-                hev.record(evs[i])
-            if fwd_evs is not None and i == i_fwd:
+                fq.set_next_launch(evs[2 * i], evs[2 * i + 1])
+            elif fwd_evs is not None and i == i_fwd:
                 fq.set_next_launch(fwd_evs[0], fwd_evs[1])
-            elif ao[i] and evs is None:
+            elif ao[i]:
                 fq.set_next_launch(any_order=True)
             fn()
-        if evs is not None:
-            hev.record(evs[len(ops)])
 
     for _ in range(args.warmup):
         run_step()
@@ -307,10 +324,9 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     fwd_us = [hev.elapsed_us(e[0], e[1]) for e in fwd_events]
 
-    # Per-kernel breakdown: the same steps again with an event between every
-    # two kernels (each event adds a little queue turnaround to the kernel
-    # after it, so these times are slight upper bounds).
-    events = [[hev.create() for _ in range(nev)] for _ in range(args.steps)]
+    # Per-kernel breakdown: the same steps again, every launch plain, each
+    # kernel's duration from the events its own dispatch records.
+    events = [[hev.create() for _ in range(2 * len(ops))] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for s in range(args.steps):
         run_step(events[s])
@@ -330,19 +346,25 @@ def main():
 
     per_op = {}
     for i, (name, _, nbytes, nflops) in enumerate(ops):
-        ts = [hev.elapsed_us(events[s][i], events[s][i + 1]) for s in range(args.steps)]
+        ts = [hev.elapsed_us(events[s][2 * i], events[s][2 * i + 1]) for s in range(args.steps)]
         per_op[name] = op_stats(ts, nbytes, nflops)
 
-    # aside: the unfused dW GEMM and DGE kernel, each timed alone
+    # asides, each timed alone: one library kernel by its own dispatch's
+    # events; torch's copy and the six-kernel outlier quantisation by event
+    # records around the call (which add the queue's turnaround to them)
     aside = {}
     for name, fn, nbytes, nflops in aside_ops:
         fn()
         torch.cuda.synchronize()
         evs = [hev.create() for _ in range(2 * args.steps)]
         for s_ in range(args.steps):
-            hev.record(evs[2 * s_])
-            fn()
-            hev.record(evs[2 * s_ + 1])
+            if name in MARKER_TIMED:
+                hev.record(evs[2 * s_])
+                fn()
+                hev.record(evs[2 * s_ + 1])
+            else:
+                fq.set_next_launch(evs[2 * s_], evs[2 * s_ + 1])
+                fn()
         torch.cuda.synchronize()
         ts = [hev.elapsed_us(evs[2 * s_], evs[2 * s_ + 1]) for s_ in range(args.steps)]
         aside[name] = op_stats(ts, nbytes, nflops)
@@ -418,7 +440,7 @@ def quantize_headline(torch, fq, hev, dY, M, N, bufs, qb, reps):
     """The quantiser on dY (8192x5632 bf16, ROW blocks of 32, RNE and SR) one
     launch at a time, cold: before each launch a 1 GiB buffer is read (a sum),
     which evicts dY from the L2s and the 256 MB Infinity Cache without leaving
-    dirty lines behind; HIP events around the launch alone."""
+    dirty lines behind; the launch's own dispatch records its events."""
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dY.device)
     out = {}
     for name, rnd in (("rne", fq.RNE), ("sr", fq.SR)):
@@ -429,9 +451,8 @@ def quantize_headline(torch, fq, hev, dY, M, N, bufs, qb, reps):
         evs = [hev.create() for _ in range(2 * reps)]
         for r in range(reps):
             flush.sum()
-            hev.record(evs[2 * r])
+            fq.set_next_launch(evs[2 * r], evs[2 * r + 1])
             fn()
-            hev.record(evs[2 * r + 1])
         torch.cuda.synchronize()
         us = float(np.mean([hev.elapsed_us(evs[2 * r], evs[2 * r + 1]) for r in range(reps)]))
         gbps = M * N * qb / (us * 1e-6) / 1e9
