@@ -232,6 +232,10 @@ def main():
          (M + N) * K * (0.5 + 1 / 32) + M * N * (2 + 0.5 + 1 / 32), 2.0 * M * N * K),
         ("quant_y_row", lambda: fq.quantize(Y, 32, fq.ROW, codes=yq[0], scales=yq[1]),
          M * N * qb, 0),
+        # the quantiser headline's stochastic case on its own: dY, ROW blocks
+        # of 32, Philox seed 1234
+        ("quant_dy_row_sr", lambda: fq.quantize(dY, 32, fq.ROW, fq.SR, SR_SEED, codes=yq[0],
+                                                scales=yq[1]), M * N * qb, 0),
         ("gemm_dw", lambda: fq.gemm(*bufs["xc"], *bufs["dyc"], c=dW),
          (K + N) * M * (0.5 + 1 / 32) + K * N * 4, 2.0 * K * N * M),
         ("dge_dw", lambda: fq.grad_estimate(fq.DGE, W, dW, 32, fq.COL, 5.0, 3.0, out=dWo),

@@ -11,13 +11,15 @@
 // layouts with scales per 16 elements: a quantise/dequantise form (the
 // hardware GEMM takes one scale per 32 elements).
 //
-// One workgroup of 4 waves owns a 128 x 128 region.  Thread t takes row t/2
-// and the 64 columns of half t%2 (two 32-wide or four 16-wide squares' row
-// segments, eight 16-byte loads); the rows of a square are lanes of one
-// parity within one wave, so a square's maximum is a 5-step (TILE 32) or
-// 4-step (TILE 16) lane exchange.  Codes go out in the ROW layout straight
-// from registers (32 contiguous bytes per row) and through LDS for the COL
-// layout (each column's 16 bytes per 32 rows from one nibble transpose).  SR
+// One workgroup of 4 waves owns a 128 x 128 region, wave w its 32-row
+// block w.  Lane l takes the 16-byte chunk l % 16 of rows 32w + 4q + l / 16
+// (q = 0..7): each load instruction reads four whole 256-byte row segments
+// of the region.  A square's maximum is the lanes' own maxima combined over
+// the chunks of its columns and the four row phases (four lane exchanges,
+// three for TILE 16, whose thread rows hold two squares).  Codes go out in
+// the ROW layout straight from registers (4 bytes per lane, 64 contiguous
+// bytes per row) and through LDS for the COL layout (each column's 16 bytes
+// per 32 rows from one nibble transpose).  SR
 // draws element (r, c) from counter r*cols + c + offset, the ROW
 // quantiser's stream, so the codes are those of one quantisation.
 #include "fp4q_device.h"
@@ -36,57 +38,62 @@ __global__ __launch_bounds__(kQ2Threads) void quantize_2d_kernel(
     uint32_t k1, uint64_t off, uint8_t* __restrict__ codes_r, uint8_t* __restrict__ scales_r,
     uint8_t* __restrict__ codes_c, uint8_t* __restrict__ scales_c) {
     static_assert(TILE == 16 || TILE == 32, "16 x 16 or 32 x 32 squares");
-    constexpr int SQ = 64 / TILE;   // squares in a thread's 64 columns
-    constexpr int QPS = TILE / 8;   // 16-byte loads per square row segment
     constexpr int NT = 128 / TILE;  // squares per region side
     __shared__ __align__(16) uint8_t stage[kQ2Rows * kQ2Stride];
     __shared__ uint8_t tsc[NT][NT];
     const int tid = threadIdx.x;
     const int64_t r0 = (int64_t)blockIdx.y * kQ2Rows, c0 = (int64_t)blockIdx.x * kQ2Cols;
-    const int r = tid >> 1, h = tid & 1;
-    const int64_t gr = r0 + r;
-    const bool rok = gr < rows;
+    // Wave w takes the region's rows 32w .. 32w+31 (one 32-row block); lane
+    // l takes the 16-byte chunk l % 16 (columns 8 (l % 16) .. +7) of rows
+    // 32w + 4q + l / 16, q = 0..7, so that each load instruction reads four
+    // whole 256-byte row segments.  A square's maximum is the lanes' own
+    // maxima combined over the chunks of its columns (lane bits 0..1 for
+    // TILE 32, bit 0 for TILE 16) and the four row phases (bits 4, 5); with
+    // TILE 16 the rows of q < 4 and q >= 4 are two squares.
+    const int lane = tid & 63, w = tid >> 6;
+    const int ch = lane & 15, ph = lane >> 4;
+    const int64_t gc = c0 + 8 * ch;
+    const bool blk = r0 + 32 * w < rows && gc < cols;  // rows, cols % 32 == 0
+    constexpr int HALVES = TILE == 16 ? 2 : 1;  // squares down a thread's rows
 
     uint4 v[8];
-    uint32_t amax[SQ];
 #pragma unroll
-    for (int sq = 0; sq < SQ; ++sq) {
-        const int64_t gc = c0 + 64 * h + TILE * sq;
-        const bool ok = rok && gc < cols;  // cols % 32 == 0: squares wholly in or out
-#pragma unroll
-        for (int q = 0; q < QPS; ++q)
-            v[sq * QPS + q] =
-                ok ? *(const uint4*)(x + gr * ld + gc + 8 * q) : make_uint4(0u, 0u, 0u, 0u);
-        u16x2_t m = __builtin_bit_cast(u16x2_t, v[sq * QPS].x & 0x7FFF7FFFu);
-#pragma unroll
-        for (int q = 0; q < QPS; ++q) {
-            const uint4 w = v[sq * QPS + q];
-            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w.x & 0x7FFF7FFFu));
-            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w.y & 0x7FFF7FFFu));
-            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w.z & 0x7FFF7FFFu));
-            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w.w & 0x7FFF7FFFu));
-        }
-        amax[sq] = ((uint32_t)max(m.x, m.y)) << 16;
+    for (int q = 0; q < 8; ++q) {
+        const int64_t gr = r0 + 32 * w + 4 * q + ph;
+        v[q] = blk ? *(const uint4*)(x + gr * ld + gc) : make_uint4(0u, 0u, 0u, 0u);
     }
-    // the square's maximum: the TILE lanes of this wave with this parity whose
-    // rows lie in the square (lane = 2 (row % 32) + parity)
+    uint32_t amax[HALVES];
 #pragma unroll
-    for (int sq = 0; sq < SQ; ++sq)
+    for (int hv = 0; hv < HALVES; ++hv) {
+        u16x2_t m = __builtin_bit_cast(u16x2_t, 0u);
 #pragma unroll
-        for (int msk = 2; msk < 2 * TILE; msk <<= 1)
-            amax[sq] = max(amax[sq], (uint32_t)__shfl_xor((int)amax[sq], msk, 64));
+        for (int q = hv * (8 / HALVES); q < (hv + 1) * (8 / HALVES); ++q) {
+            const uint4 t = v[q];
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, t.x & 0x7FFF7FFFu));
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, t.y & 0x7FFF7FFFu));
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, t.z & 0x7FFF7FFFu));
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, t.w & 0x7FFF7FFFu));
+        }
+        uint32_t a = ((uint32_t)max(m.x, m.y)) << 16;
+        a = max(a, (uint32_t)__shfl_xor((int)a, 1, 64));
+        if (TILE == 32) a = max(a, (uint32_t)__shfl_xor((int)a, 2, 64));
+        a = max(a, (uint32_t)__shfl_xor((int)a, 16, 64));
+        a = max(a, (uint32_t)__shfl_xor((int)a, 32, 64));
+        amax[hv] = a;
+    }
 
     uint32_t cw[8];
+    uint32_t bytes[HALVES];
 #pragma unroll
-    for (int sq = 0; sq < SQ; ++sq) {
-        const bool nf = amax[sq] >= 0x7F800000u;
-        const uint32_t byte = nf ? 0xFFu : e8m0_from_amax(amax[sq]);
+    for (int hv = 0; hv < HALVES; ++hv) {
+        const bool nf = amax[hv] >= 0x7F800000u;
+        const uint32_t byte = nf ? 0xFFu : e8m0_from_amax(amax[hv]);
         const float sc = e8m0_scale_f32(nf ? 0u : byte);
-        const int64_t gc = c0 + 64 * h + TILE * sq;
+        bytes[hv] = byte;
 #pragma unroll
-        for (int q = 0; q < QPS; ++q) {
-            const uint4 w = v[sq * QPS + q];
-            const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+        for (int q = hv * (8 / HALVES); q < (hv + 1) * (8 / HALVES); ++q) {
+            const uint4 t = v[q];
+            const uint32_t w0 = t.x, w1 = t.y, w2 = t.z, w3 = t.w;
             uint32_t packed = 0;
             if (!SR) {
                 packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
@@ -98,25 +105,35 @@ __global__ __launch_bounds__(kQ2Threads) void quantize_2d_kernel(
                 packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
                     packed, __builtin_bit_cast(bf16x2_t, w3), sc, 3);
             } else {
-                const uint64_t p0 = (uint64_t)gr * (uint64_t)cols + (uint64_t)(gc + 8 * q) + off;
+                const int64_t gr = r0 + 32 * w + 4 * q + ph;
+                const uint64_t p0 = (uint64_t)gr * (uint64_t)cols + (uint64_t)gc + off;
                 uint32_t wr[4];
                 sr_words8(p0, k0, k1, wr);
                 const float xf[8] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1),
                                      bf16_lo(w2), bf16_hi(w2), bf16_lo(w3), bf16_hi(w3)};
                 packed = sr_pack8(xf, sc, wr);
             }
-            cw[sq * QPS + q] = nf ? 0u : packed;
+            cw[q] = nf ? 0u : packed;
         }
-        if (rok && gc < cols) scales_r[gr * (cols / TILE) + gc / TILE] = (uint8_t)byte;
-        // one lane per square row-block writes the region's scale table
-        if ((r % TILE) == 0) tsc[r / TILE][(64 * h) / TILE + sq] = (uint8_t)byte;
     }
+    // ROW codes: 4 bytes per row from each lane (a 64-byte row segment per 16
+    // lanes); ROW scales: one byte per row and square, from the square's
+    // first chunk; the staged codes feed the COL layout below
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int64_t gc = c0 + 64 * h + 32 * t;
-        const uint4 o = make_uint4(cw[4 * t], cw[4 * t + 1], cw[4 * t + 2], cw[4 * t + 3]);
-        if (rok && gc < cols) *(uint4*)(codes_r + gr * (cols / 2) + gc / 2) = o;
-        *(uint4*)(stage + r * kQ2Stride + 32 * h + 16 * t) = o;
+    for (int q = 0; q < 8; ++q) {
+        const int rl = 32 * w + 4 * q + ph;
+        const int64_t gr = r0 + rl;
+        if (blk) {
+            *(uint32_t*)(codes_r + gr * (cols / 2) + gc / 2) = cw[q];
+            if ((ch % (TILE / 8)) == 0)
+                scales_r[gr * (cols / TILE) + gc / TILE] = (uint8_t)bytes[q / (8 / HALVES)];
+        }
+        *(uint32_t*)(stage + rl * kQ2Stride + 4 * ch) = cw[q];
+    }
+    if (ph == 0 && (ch % (TILE / 8)) == 0) {
+#pragma unroll
+        for (int hv = 0; hv < HALVES; ++hv)
+            tsc[(32 * w) / TILE + hv][(8 * ch) / TILE] = (uint8_t)bytes[hv];
     }
     __syncthreads();
 
