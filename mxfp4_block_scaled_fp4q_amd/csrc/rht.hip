@@ -20,9 +20,9 @@
 //    lanes one group: strides 1..4 in registers, 8 and 16 across the quad by
 //    DPP; codes as the ROW quantiser lays them out.
 //  * rht_col_kernel: a thread holds two adjacent columns x 32 rows (one group
-//    per column) in registers, all five strides in registers, for up to four
-//    consecutive groups down the rows (up to 64 contiguous code bytes per
-//    column); stochastic bits come from a shared LDS fill.
+//    per column) in registers, all five strides in registers, one group down
+//    the rows per workgroup unless the grid's y extent needs more;
+//    stochastic bits come from a shared LDS fill.
 #include "fp4q_device.h"
 #include "fp4q_internal.h"
 
@@ -245,11 +245,14 @@ hipError_t launch_quantize_rht(const void* x, int64_t rows, int64_t cols, int64_
             FP4Q_LAUNCH((rht_row_kernel<0>), grid, kRhtThreads, 0, s, xb, rows, cols, ld, signs, k0, k1, off,
                                                           codes, scales);
     } else {
-        // groups per thread down the rows: 4 (64 contiguous code bytes per
-        // column) unless that leaves the grid under 1024 workgroups
+        // one group per thread down the rows (the grid's y extent allowing):
+        // measured on MI355X, dY 8192 x 5632 SR 50.1 / 51.0 / 56.4 us with
+        // 1 / 2 / 4 groups per thread, X 8192 x 2048 14.8 / 17.4 / 17.0 us
+        // (the longer code runs per column of more groups do not pay for the
+        // lost parallelism)
         const int64_t gx = (cols / 2 + kRhtThreads - 1) / kRhtThreads, nb = rows / 32;
-        int rb = 4;
-        while (rb > 1 && gx * ((nb + rb - 1) / rb) < 1024) rb >>= 1;
+        int rb = 1;
+        while ((nb + rb - 1) / rb > 65535) rb <<= 1;
         const dim3 grid((unsigned)gx, (unsigned)((nb + rb - 1) / rb));
         if (sr)
             FP4Q_LAUNCH((rht_col_kernel<1>), grid, kRhtThreads, 0, s, xb, rows, cols, ld, signs, k0, k1, off,
