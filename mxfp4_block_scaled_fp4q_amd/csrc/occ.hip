@@ -159,7 +159,8 @@ __global__ __launch_bounds__(1024) void occ_select(const uint32_t* __restrict__ 
 static constexpr int kOccUnroll = 4;  // chunks per clamp-quantise thread
 
 template <int SR>
-__device__ __forceinline__ void occ_chunk(uint4 v, uint32_t g, FastDiv cpr, uint32_t tb, bool tfin,
+__device__ __forceinline__ void occ_chunk(uint4 v, uint32_t g, bool valid, FastDiv cpr, uint32_t tb,
+                                          bool tfin,
                                           uint32_t k0, uint32_t k1, uint64_t off,
                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                           uint8_t* __restrict__ mask,
@@ -178,8 +179,23 @@ __device__ __forceinline__ void occ_chunk(uint4 v, uint32_t g, FastDiv cpr, uint
         mb |= (olo ? 1u : 0u) << (2 * k);
         mb |= (ohi ? 1u : 0u) << (2 * k + 1);
     }
-    mask[g] = (uint8_t)mb;
-    if (mb) atomicAdd(&row_cnt[r], (uint32_t)__builtin_popcount(mb));
+    if (!valid) mb = 0;
+    if (valid) mask[g] = (uint8_t)mb;
+    // the row's outlier count: one atomic per wave when the wave's valid
+    // chunks lie in one row (the common case; lane 0 holds the wave's first
+    // chunk, and if it is past the end so are all), else one per chunk
+    // holding outliers.  Every lane of the wave runs this.
+    const uint32_t n = (uint32_t)__builtin_popcount(mb);
+    const uint32_t r_first = __builtin_amdgcn_readfirstlane(r);
+    if (__builtin_amdgcn_ballot_w64(valid && r != r_first) == 0) {
+        uint32_t sum = n;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) sum += (uint32_t)__shfl_xor((int)sum, m, 64);
+        if (sum && __lane_id() == 0) atomicAdd(&row_cnt[r_first], sum);
+    } else if (n) {
+        atomicAdd(&row_cnt[r], n);
+    }
+    if (!valid) return;
     const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
     const u16x2_t m0 = __builtin_bit_cast(u16x2_t, w0 & 0x7FFF7FFFu);
     const u16x2_t m1 = __builtin_bit_cast(u16x2_t, w1 & 0x7FFF7FFFu);
@@ -231,9 +247,9 @@ __global__ __launch_bounds__(kOccThreads) void occ_clamp_quant(
         }
     }
 #pragma unroll
-    for (int u = 0; u < kOccUnroll; ++u)
-        if (g[u] < total)
-            occ_chunk<SR>(v[u], g[u], cpr, tb, tfin, k0, k1, off, codes, scales, mask, row_cnt);
+    for (int u = 0; u < kOccUnroll; ++u)  // every lane: the row counts are summed across the wave
+        occ_chunk<SR>(v[u], g[u], g[u] < total, cpr, tb, tfin, k0, k1, off, codes, scales, mask,
+                      row_cnt);
 }
 
 // Thread t owns rows [t per, (t + 1) per); up to 16 rows per thread (16384
