@@ -52,7 +52,11 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--settle-s", type=float, default=0.3,
+                   help="run whole steps for at least this many seconds before the warm-up "
+                        "steps: an idle MI355X takes tens of milliseconds of load to reach its "
+                        "steady clocks, and steps timed before that run up to 15%% slower")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--hcp", action="store_true",
@@ -309,6 +313,19 @@ def main():
                 fq.set_next_launch(any_order=True)
             fn()
 
+    # Clock settling, then the warm-up steps: the device runs whole steps
+    # until it has been busy for settle_s seconds (an idle GPU's clocks ramp
+    # up over the first tens of milliseconds of load; measured on MI355X, 5
+    # warm-up steps left the timed steps 16% slower than 200 did), so the
+    # timed steps see the steady state a continuous training job runs in.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(10):
+            run_step()
+        torch.cuda.synchronize()
+        settle_steps += 10
+    settle_s = time.perf_counter() - t_settle
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
@@ -415,6 +432,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"seconds": round(settle_s, 3), "steps": settle_steps},
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
