@@ -576,7 +576,11 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
     // the group before it is added and stored), instead of one
     // read-then-write round trip per chunk.  (256 x 256 tiles: 8 chunks per
     // lane per group.  Reading the first group before the K loop would keep
-    // 32 more registers live through it, which spills.)
+    // 32 more registers live through it, which spills.)  C is read with
+    // non-temporal loads, as it is written with non-temporal stores: a
+    // stream of C through the L2 evicts the operand rows that the other
+    // tiles' K loops read (13B-shaped residual, 461 hot channels: 805 ->
+    // 650 us per call with its gathers, the same bits).
     constexpr bool YPF = ACCUM && !OUT_BF16 && EPI == 0 && PASSES <= 8 && L::TM == 4;
     auto c_chunk = [&](int i, int p, int64_t& off) __attribute__((always_inline)) -> bool {
         const int rl = p * ROWS_PER_PASS + lane / LANES_PER_ROW;
@@ -591,7 +595,9 @@ __global__ __launch_bounds__(Layout<CFG>::THREADS, 1) void gemm_fp4_kernel(
 #pragma unroll
             for (int p = 0; p < PASSES; ++p) {
                 int64_t off;
-                if (c_chunk(i, p, off)) y[p] = *(const float4*)((const float*)cptr + off);
+                if (c_chunk(i, p, off))
+                    y[p] = __builtin_bit_cast(
+                        float4, __builtin_nontemporal_load((const u32x4*)((const float*)cptr + off)));
             }
         }
     };
@@ -884,7 +890,9 @@ __device__ __forceinline__ void persist_epilogue(v16f (&acc)[4][2], uint8_t* reg
                 const int64_t off = (int64_t)row * ldc + col;
                 if (vec_ok && col + CHUNK_ELEMS <= N) {
                     if (ACCUM) {
-                        float4 o = *(const float4*)((const float*)cptr + off);
+                        float4 o = __builtin_bit_cast(
+                            float4,
+                            __builtin_nontemporal_load((const u32x4*)((const float*)cptr + off)));
                         o.x += as_f32(v.x);
                         o.y += as_f32(v.y);
                         o.z += as_f32(v.z);
