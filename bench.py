@@ -27,7 +27,9 @@ throughput over the timed steps.  The roofline object reports the forward
 GEMM (the dominant kernel) against the dense FP4 MFMA peak, its launch time
 taken from HIP events that its own dispatch records inside the timed region
 (fp4q_set_next_launch; on the stream the kernels run on, created without a
-system-scope fence), and its HBM traffic from committed counter runs.  A
+system-scope fence), and its HBM traffic from rocprofv3 counter passes this
+run starts as child processes after its timed region (or, failing those,
+from the committed counter record while the GEMM source matches it).  A
 second pass, every launch plain, times each kernel by its own dispatch
 events for the per-kernel table.  The CPU baseline times the
 single-threaded oracle on a bounded sample.
@@ -70,6 +72,10 @@ def parse():
     p.add_argument("--hot-channels", type=int, default=None,
                    help="with --profile-op hcp_residual: use only the first N hot channels")
     p.add_argument("--reps", type=int, default=10)
+    p.add_argument("--traffic", choices=("live", "record", "off"), default="live",
+                   help="the roofline's HBM traffic: 'live' runs four short rocprofv3 counter "
+                        "passes as child processes (falling back to the committed record), "
+                        "'record' reads the committed record only")
     p.add_argument("--sequential", action="store_true",
                    help="launch every step kernel behind a barrier (no any-order launches)")
     return p.parse_args()
@@ -77,6 +83,70 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemm_fwd_traffic.json")
 KERNEL_SRC = os.path.join(HERE, "mxfp4_block_scaled_fp4q_amd", "csrc", "gemm_fp4.hip")
+
+
+def live_traffic(timeout_s=150.0):
+    """HBM bytes per forward-GEMM launch measured by this run: four rocprofv3
+    counter passes, each a child process (this script with --profile-op, five
+    launches): FETCH_SIZE and WRITE_SIZE of the GEMM, each scaled by what the
+    same counter reads for a plain 256 MiB device copy (FETCH_SIZE counts a
+    128-byte read as 64 bytes).  Returns (bytes, details) or (None, reason)."""
+    import csv
+    import glob
+    import shutil
+    import signal
+    import subprocess
+    import tempfile
+    prof = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
+    if not os.path.exists(prof):
+        return None, "rocprofv3 not found"
+    tmp = tempfile.mkdtemp(prefix="fp4q_traffic_")
+    env = dict(os.environ, TMPDIR=tempfile.gettempdir())
+
+    def one_pass(counter, op, kname, min_kib):
+        d = os.path.join(tmp, op + "_" + counter)
+        cmd = [prof, "--pmc", counter, "-d", d, "-o", "p", "--output-format", "csv", "--",
+               sys.executable, os.path.abspath(__file__), "--profile-op", op, "--reps", "5"]
+        child = subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL,
+                                 env=env, cwd=HERE, start_new_session=True)
+        try:
+            child.wait(timeout=timeout_s)
+        except subprocess.TimeoutExpired:
+            os.killpg(child.pid, signal.SIGKILL)
+            child.wait()
+            return None
+        # the profiler may exit non-zero after the program ended with its
+        # results whole: the counter file decides
+        per = {}
+        for f in glob.glob(os.path.join(d, "**", "p_counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    if kname in row["Kernel_Name"] and row["Counter_Name"] == counter:
+                        k = row["Dispatch_Id"]
+                        per[k] = per.get(k, 0.0) + float(row["Counter_Value"])
+        vals = [v for v in per.values() if v >= min_kib]
+        return float(np.median(vals)) if len(vals) >= 3 else None
+
+    try:
+        gk = "gemm_fp4_persistent_kernel<1, 0, 0>"
+        got = {"gemm_fetch_kib": one_pass("FETCH_SIZE", "gemm_fwd", gk, 1.0),
+               "gemm_write_kib": one_pass("WRITE_SIZE", "gemm_fwd", gk, 1.0),
+               "copy_fetch_kib": one_pass("FETCH_SIZE", "copy", "copyBuffer", 1024.0),
+               "copy_write_kib": one_pass("WRITE_SIZE", "copy", "copyBuffer", 1024.0)}
+    except OSError as e:
+        return None, "could not run rocprofv3: " + str(e)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    if any(v is None for v in got.values()):
+        return None, "a counter pass gave no result: " + ", ".join(
+            k for k, v in got.items() if v is None)
+    copy_kib = 256.0 * 1024  # 64 Mi floats read and written
+    fs, ws = copy_kib / got["copy_fetch_kib"], copy_kib / got["copy_write_kib"]
+    if not (0.5 < fs < 4.0 and 0.5 < ws < 4.0):
+        return None, "implausible copy calibration %.3f / %.3f" % (fs, ws)
+    traffic = int(round(got["gemm_fetch_kib"] * 1024 * fs + got["gemm_write_kib"] * 1024 * ws))
+    got.update(fetch_scale=round(fs, 4), write_scale=round(ws, 4))
+    return traffic, got
 
 
 def measured_traffic():
@@ -398,12 +468,25 @@ def main():
     achieved = fwd_flops / (fwd_mean_us * 1e-6) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4_TFLOPS, 4),
-                "traffic": measured_traffic(),
+                "traffic": None,
                 "kernel": "gemm_fp4_persistent_kernel<1, 0, 0> 8192x5632x2048 bf16 out",
                 "per_launch_flops": fwd_flops, "launch_us_mean": round(fwd_mean_us, 2),
                 "launch_us_min": round(float(np.min(fwd_us)), 2),
                 "launch_us_median": round(float(np.median(fwd_us)), 2),
                 "launch_us_p10": round(float(np.percentile(fwd_us, 10)), 2)}
+    if args.traffic == "live":
+        traffic, info = live_traffic()
+        if traffic is not None:
+            roofline["traffic"] = traffic
+            roofline["traffic_source"] = ("this run: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
+                                          "passes of the kernel, scaled by a 256 MiB copy")
+            roofline["traffic_counters"] = info
+        else:
+            roofline["traffic_live_error"] = info
+    if roofline["traffic"] is None and args.traffic != "off":
+        roofline["traffic"] = measured_traffic()
+        if roofline["traffic"] is not None:
+            roofline["traffic_source"] = "committed record " + os.path.relpath(TRAFFIC_FILE, HERE)
     q = per_op["quant_dy_dual_sr"]
     qr = per_op["quant_x_dual"]
     quant = {"quant_bf16_dual_rne_GBps": qr["GBps"], "quant_bf16_dual_rne_frac": qr["frac_hbm_peak"],
