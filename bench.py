@@ -97,6 +97,9 @@ def live_traffic(timeout_s=150.0):
     import signal
     import subprocess
     import tempfile
+    if any(k.startswith("ROCP") for k in os.environ) or "rocprof" in os.environ.get(
+            "LD_PRELOAD", ""):
+        return None, "running under a profiler: no nested counter passes"
     prof = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
     if not os.path.exists(prof):
         return None, "rocprofv3 not found"
