@@ -328,12 +328,17 @@ static hipError_t gather_hot(int64_t M, int64_t N, int64_t K, const void* x, con
     uint16_t* ap = (uint16_t*)ws;
     uint16_t* bp = (uint16_t*)((uint8_t*)ws + round_up((size_t)(M * kp * 2), 256));
     {
-        // rows staged whole in LDS when a row and the hot list fit in 40 KB
+        // rows staged whole in LDS when a row and the hot list fit in 40 KB;
+        // about 8 KB of rows per workgroup (1 to 4): the workgroups resident
+        // on a compute unit, not the rows each stages, keep its loads in
+        // flight (13B-shaped X, 13 KB rows: 83 -> 70 us with one row per
+        // workgroup instead of two; 140 us with four)
         const int64_t hot_bytes = kp * 4;  // the slot -> column table
         const int64_t row_bytes = (int64_t)round_up((size_t)(K * 2 + (with_q ? K / 2 + K / 32 : 0)), 16);
         constexpr int64_t kLdsBudget = 40 * 1024;
         if (hot_bytes + row_bytes <= kLdsBudget) {
-            const int rpw = (int)std::min<int64_t>(4, (kLdsBudget - hot_bytes) / row_bytes);
+            const int rpw = (int)std::max<int64_t>(
+                1, std::min<int64_t>({4, 8192 / row_bytes, (kLdsBudget - hot_bytes) / row_bytes}));
             const size_t lds = (size_t)(hot_bytes + rpw * row_bytes);
             dim3 grid((unsigned)((M + rpw - 1) / rpw));
             FP4Q_LAUNCH((hcp_gather_x_rows), grid, kThreads, lds, s, (const uint16_t*)x, xqc, xqs, hot, n_hot,
