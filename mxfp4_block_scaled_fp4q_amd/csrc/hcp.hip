@@ -39,8 +39,8 @@
 //    read whole costs a few full-line loads.
 //  * hcp_gather_x: one lane = 8 consecutive K' slots of one row of A', read
 //    straight from global memory (rows too long to stage in LDS).
-//  * hcp_gather_w_rows: a workgroup forms 8 rows of B' from LDS-staged
-//    pieces (the hot rows' values at those 8 columns, and Wq's 8 K-major code
+//  * hcp_gather_w_rows: a workgroup forms 4 rows of B' from LDS-staged
+//    pieces (the hot rows' values at those 4 columns, and Wq's 4 K-major code
 //    and scale rows read whole).
 //  * hcp_gather_w: one lane = one column j and 8 consecutive K' slots; lanes
 //    of a wave take consecutive j, so the reads of W's hot rows coalesce
@@ -59,6 +59,10 @@
 namespace fp4q {
 
 static constexpr int kThreads = 256;
+// rows of B' per workgroup of the row-staged W gather: 4 (about 18 KB of LDS
+// at the 13B shape, 8 workgroups per compute unit) rather than 8 (33 KB, 4
+// per unit): 51 -> 44 us in a same-box A/B
+static constexpr int kGatherWRows = 4;
 
 __device__ __forceinline__ float deq_nibble(const uint8_t* codes_row, const uint8_t* scales_row,
                                             int c) {
@@ -228,17 +232,18 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_w(const uint16_t* __restr
 }
 
 // Row-staged gather of B' = [W_H ; -Wq_H]^T (with_q): a workgroup forms
-// JB = 8 consecutive rows j of B'.  Dynamic LDS holds the slot -> column
-// table (kp int32), the hot rows' values W[hot[h], j0 .. j0+7] transposed to
-// [8][n_hot rounded up to 8] (read 16 bytes per hot row when the rows allow)
-// and the 8 K-major code rows (K/2 bytes each) and scale rows (K/32 bytes
+// JB = 4 consecutive rows j of B'.  Dynamic LDS holds the slot -> column
+// table (kp int32), the hot rows' values W[hot[h], j0 .. j0+3] transposed to
+// [4][n_hot rounded up to 8] (read 8 bytes per hot row when the rows allow)
+// and the 4 K-major code rows (K/2 bytes each) and scale rows (K/32 bytes
 // each) of Wq; the output rows then leave as consecutive 16-byte chunks.
 // K % 32 == 0.  A hot index outside [0, K) reads as zero.
 __global__ __launch_bounds__(kThreads) void hcp_gather_w_rows(
     const uint16_t* __restrict__ w, const uint8_t* __restrict__ wqc,
     const uint8_t* __restrict__ wqs, const int32_t* __restrict__ hot, int n_hot, int64_t N,
     int64_t K, int64_t kp, uint16_t* __restrict__ b, int with_q, int hot_bytes, int wh_bytes) {
-    constexpr int JB = 8;
+    constexpr int JB = kGatherWRows;
+    static_assert(JB == 4, "8-byte loads of the hot rows' values");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     int32_t* hs = (int32_t*)smem;                  // slot -> column (kp entries)
     uint16_t* wh = (uint16_t*)(smem + hot_bytes);  // [JB][hp]: W[hot[h], j0 + jj]
@@ -250,23 +255,24 @@ __global__ __launch_bounds__(kThreads) void hcp_gather_w_rows(
     const int nj = (int)std::min<int64_t>(JB, N - j0);
     fill_slot_columns(hs, hot, n_hot, kp, 1, K);
     __syncthreads();
-    const bool vec = (N % 8) == 0 && nj == JB;  // 16-byte aligned, whole
+    const bool vec = (N % JB) == 0 && nj == JB;  // 8-byte aligned, whole
     for (int h = tid; h < hp; h += kThreads) {
         const int c = h < n_hot ? hs[h] : -1;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        uint32_t e[JB / 2];
+#pragma unroll
+        for (int q = 0; q < JB / 2; ++q) e[q] = 0u;
         if (c >= 0) {
             const uint16_t* src = w + (int64_t)c * N + j0;
             if (vec) {
-                v = *(const uint4*)src;
+                const uint2 v = *(const uint2*)src;
+                e[0] = v.x;
+                e[1] = v.y;
             } else {
-                uint32_t e[JB];
 #pragma unroll
-                for (int q = 0; q < JB; ++q) e[q] = q < nj ? (uint32_t)src[q] : 0u;
-                v = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                               e[6] | (e[7] << 16));
+                for (int q = 0; q < JB; ++q)
+                    e[q >> 1] |= (q < nj ? (uint32_t)src[q] : 0u) << (16 * (q & 1));
             }
         }
-        const uint32_t e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int q = 0; q < JB; ++q) wh[q * hp + h] = (uint16_t)(e[q >> 1] >> (16 * (q & 1)));
     }
@@ -352,13 +358,14 @@ static hipError_t gather_hot(int64_t M, int64_t N, int64_t K, const void* x, con
         }
     }
     {
-        // eight rows of B' per workgroup, staged in LDS, when they fit in 40 KB
+        // four rows of B' per workgroup, staged in LDS, when they fit in 40 KB
         // (with_q only: W's hot rows alone are read coalesced by the kernel below)
+        constexpr int JB = kGatherWRows;
         const int64_t hot_bytes = kp * 4;
-        const int64_t wh_bytes = (int64_t)round_up((size_t)n_hot, 8) * 16;
-        const int64_t q_bytes = 8 * (K / 2 + K / 32);
+        const int64_t wh_bytes = (int64_t)round_up((size_t)n_hot, 8) * 2 * JB;
+        const int64_t q_bytes = JB * (K / 2 + K / 32);
         if (with_q && hot_bytes + wh_bytes + q_bytes <= 40 * 1024) {
-            dim3 grid((unsigned)((N + 7) / 8));
+            dim3 grid((unsigned)((N + JB - 1) / JB));
             FP4Q_LAUNCH((hcp_gather_w_rows), grid, kThreads, (size_t)(hot_bytes + wh_bytes + q_bytes), s,
                 (const uint16_t*)w, wqc, wqs, hot, n_hot, N, K, kp, bp, with_q, (int)hot_bytes,
                 (int)wh_bytes);

@@ -301,11 +301,13 @@ def test_outlier_layer_gemm_and_hcp(orc):
 
 @pytest.mark.parametrize("M,N,K,n_hot", [(64, 96, 256, 23), (300, 257, 512, 46),
                                          (1, 33, 128, 1), (128, 128, 256, 256),
-                                         # rows too long to stage in LDS: both gathers
-                                         # read global memory directly
+                                         # X's rows too long to stage in LDS (its gather
+                                         # reads global memory directly), W's staged
                                          (64, 40, 16384, 37),
-                                         # X's rows staged, W's pieces too large
-                                         (48, 40, 8192, 500)])
+                                         # both staged, several hundred hot channels
+                                         (48, 40, 8192, 500),
+                                         # rows too long to stage for either gather
+                                         (16, 24, 20480, 61)])
 def test_hcp_small(orc, M, N, K, n_hot):
     x = inputs.to_bf16_bits(inputs.normal((M, K), M + K))
     w = inputs.to_bf16_bits(inputs.normal((K, N), N + K, 0.02))
