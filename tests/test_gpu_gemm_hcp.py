@@ -306,6 +306,8 @@ def test_outlier_layer_gemm_and_hcp(orc):
                                          (64, 40, 16384, 37),
                                          # both staged, several hundred hot channels
                                          (48, 40, 8192, 500),
+                                         # three X rows per workgroup, the last one ragged
+                                         (50, 40, 1024, 70),
                                          # rows too long to stage for either gather
                                          (16, 24, 20480, 61)])
 def test_hcp_small(orc, M, N, K, n_hot):
