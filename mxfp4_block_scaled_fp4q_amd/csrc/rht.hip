@@ -165,13 +165,26 @@ __global__ __launch_bounds__(kRhtThreads) void rht_col_kernel(
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
     __shared__ __align__(16) uint32_t rnd[SR ? 32 * kRhtThreads : 1];
     const int tid = threadIdx.x;
-    const int64_t cbase = (int64_t)blockIdx.x * kRhtThreads * 2;
+    const int64_t nb = rows / 32;
+    const uint32_t ny = (uint32_t)((nb + rb_per - 1) / rb_per);
+    // Workgroups are dealt to the eight XCDs in turn; remap so that each XCD
+    // takes a contiguous run of tiles ordered by column block, row groups
+    // fastest: the 16-byte code pieces and scale bytes that consecutive row
+    // groups write into one line of a column's output then meet in that
+    // XCD's L2 and leave it as whole lines (dY's codes: 3.2x the algorithmic
+    // bytes written before).
+    uint32_t tile = blockIdx.x;
+    {
+        const uint32_t full = (gridDim.x / 8) * 8;
+        if (tile < full) tile = (tile % 8) * (full / 8) + tile / 8;
+    }
+    const uint32_t xblk = tile / ny, yblk = tile - xblk * ny;
+    const int64_t cbase = (int64_t)xblk * kRhtThreads * 2;
     const int64_t c = cbase + 2 * tid;
     const bool cok = c < cols;  // no early exit: the workgroup meets at barriers
     const float cc = as_f32(kRhtC);
-    const int64_t nb = rows / 32;
     for (int t = 0; t < rb_per; ++t) {
-        const int64_t b = (int64_t)blockIdx.y * rb_per + t;
+        const int64_t b = (int64_t)yblk * rb_per + t;
         if (b >= nb) break;  // uniform over the workgroup
         const int64_t r0 = b * 32;
         // this group's 32 rows are loaded first, so their latency passes
@@ -245,15 +258,15 @@ hipError_t launch_quantize_rht(const void* x, int64_t rows, int64_t cols, int64_
             FP4Q_LAUNCH((rht_row_kernel<0>), grid, kRhtThreads, 0, s, xb, rows, cols, ld, signs, k0, k1, off,
                                                           codes, scales);
     } else {
-        // one group per thread down the rows (the grid's y extent allowing):
+        // one group per thread down the rows (the grid's size allowing):
         // measured on MI355X, dY 8192 x 5632 SR 50.1 / 51.0 / 56.4 us with
         // 1 / 2 / 4 groups per thread, X 8192 x 2048 14.8 / 17.4 / 17.0 us
         // (the longer code runs per column of more groups do not pay for the
         // lost parallelism)
         const int64_t gx = (cols / 2 + kRhtThreads - 1) / kRhtThreads, nb = rows / 32;
         int rb = 1;
-        while ((nb + rb - 1) / rb > 65535) rb <<= 1;
-        const dim3 grid((unsigned)gx, (unsigned)((nb + rb - 1) / rb));
+        while (gx * ((nb + rb - 1) / rb) > 0x7FFFFFFF) rb <<= 1;
+        const dim3 grid((unsigned)(gx * ((nb + rb - 1) / rb)));
         if (sr)
             FP4Q_LAUNCH((rht_col_kernel<1>), grid, kRhtThreads, 0, s, xb, rows, cols, ld, signs, k0, k1, off,
                                                           rb, codes, scales);
