@@ -513,7 +513,6 @@ fp4q_status_t fp4q_quantize_2d_tile(const void* x, int64_t rows, int64_t cols, i
     if (round != FP4Q_RNE && round != FP4Q_SR)
         return fail(FP4Q_ERR_INVALID, "quantize_2d: bad round");
     if (rows > kMaxElems / ld_x) return fail(FP4Q_ERR_INVALID, "quantize_2d: tensor too large");
-    if (rows / 128 >= 65535) return fail(FP4Q_ERR_UNSUPPORTED, "quantize_2d: too many rows");
     if (!aligned16(x) || !aligned16(row_codes) || !aligned16(row_scales) ||
         !aligned16(col_codes) || !aligned16(col_scales) || ld_x % 8)
         return fail(FP4Q_ERR_ALIGNMENT,

@@ -42,7 +42,20 @@ __global__ __launch_bounds__(kQ2Threads) void quantize_2d_kernel(
     __shared__ __align__(16) uint8_t stage[kQ2Rows * kQ2Stride];
     __shared__ uint8_t tsc[NT][NT];
     const int tid = threadIdx.x;
-    const int64_t r0 = (int64_t)blockIdx.y * kQ2Rows, c0 = (int64_t)blockIdx.x * kQ2Cols;
+    // Workgroups are dealt to the eight XCDs in turn; remap so that each XCD
+    // takes a contiguous run of regions in row-major order: the two 64-byte
+    // halves of a row's code line (adjacent regions), most rows' scale lines
+    // and, where a run holds whole pairs of region rows, the halves of a
+    // column's code line then meet in one L2 and leave it whole (W 2048 x
+    // 5632: 15.5 MB written for 11.6 MB of output with a 2D grid before).
+    uint32_t reg = blockIdx.x;
+    {
+        const uint32_t full = (gridDim.x / 8) * 8;
+        if (reg < full) reg = (reg % 8) * (full / 8) + reg / 8;
+    }
+    const uint32_t gx = (uint32_t)((cols + kQ2Cols - 1) / kQ2Cols);
+    const uint32_t ry = reg / gx, rx = reg - ry * gx;
+    const int64_t r0 = (int64_t)ry * kQ2Rows, c0 = (int64_t)rx * kQ2Cols;
     // Wave w takes the region's rows 32w .. 32w+31 (one 32-row block); lane
     // l takes the 16-byte chunk l % 16 (columns 8 (l % 16) .. +7) of rows
     // 32w + 4q + l / 16, q = 0..7, so that each load instruction reads four
@@ -177,8 +190,9 @@ hipError_t launch_quantize_2d(const void* x, int64_t rows, int64_t cols, int64_t
                               uint8_t* scales_r, uint8_t* codes_c, uint8_t* scales_c,
                               hipStream_t s) {
     const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-    const dim3 grid((unsigned)((cols + kQ2Cols - 1) / kQ2Cols),
-                    (unsigned)((rows + kQ2Rows - 1) / kQ2Rows));
+    const int64_t regions = ((cols + kQ2Cols - 1) / kQ2Cols) * ((rows + kQ2Rows - 1) / kQ2Rows);
+    if (regions >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)regions);
     const uint16_t* xb = (const uint16_t*)x;
 #define FP4Q_Q2D(SR_, T_)                                                                   \
     FP4Q_LAUNCH((quantize_2d_kernel<SR_, T_>), grid, kQ2Threads, 0, s, xb, rows, cols, ld, k0, k1, off,  \
