@@ -85,12 +85,14 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemm_fwd_traffic.json")
 KERNEL_SRC = os.path.join(HERE, "mxfp4_block_scaled_fp4q_amd", "csrc", "gemm_fp4.hip")
 
 
-def live_traffic(timeout_s=150.0):
+def live_traffic(budget_s=120.0, pass_s=60.0):
     """HBM bytes per forward-GEMM launch measured by this run: four rocprofv3
     counter passes, each a child process (this script with --profile-op, five
     launches): FETCH_SIZE and WRITE_SIZE of the GEMM, each scaled by what the
     same counter reads for a plain 256 MiB device copy (FETCH_SIZE counts a
-    128-byte read as 64 bytes).  Returns (bytes, details) or (None, reason)."""
+    128-byte read as 64 bytes).  A pass takes a few seconds; each is cut at
+    pass_s and all four at budget_s, and the first pass without a result
+    ends the measurement.  Returns (bytes, details) or (None, reason)."""
     import csv
     import glob
     import shutil
@@ -105,15 +107,19 @@ def live_traffic(timeout_s=150.0):
         return None, "rocprofv3 not found"
     tmp = tempfile.mkdtemp(prefix="fp4q_traffic_")
     env = dict(os.environ, TMPDIR=tempfile.gettempdir())
+    deadline = time.perf_counter() + budget_s
 
     def one_pass(counter, op, kname, min_kib):
+        left = min(pass_s, deadline - time.perf_counter())
+        if left <= 1.0:
+            return None
         d = os.path.join(tmp, op + "_" + counter)
         cmd = [prof, "--pmc", counter, "-d", d, "-o", "p", "--output-format", "csv", "--",
                sys.executable, os.path.abspath(__file__), "--profile-op", op, "--reps", "5"]
         child = subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL,
                                  env=env, cwd=HERE, start_new_session=True)
         try:
-            child.wait(timeout=timeout_s)
+            child.wait(timeout=left)
         except subprocess.TimeoutExpired:
             os.killpg(child.pid, signal.SIGKILL)
             child.wait()
@@ -130,19 +136,24 @@ def live_traffic(timeout_s=150.0):
         vals = [v for v in per.values() if v >= min_kib]
         return float(np.median(vals)) if len(vals) >= 3 else None
 
+    gk = "gemm_fp4_persistent_kernel<1, 0, 0>"
+    passes = (("gemm_fetch_kib", "FETCH_SIZE", "gemm_fwd", gk, 1.0),
+              ("gemm_write_kib", "WRITE_SIZE", "gemm_fwd", gk, 1.0),
+              ("copy_fetch_kib", "FETCH_SIZE", "copy", "copyBuffer", 1024.0),
+              ("copy_write_kib", "WRITE_SIZE", "copy", "copyBuffer", 1024.0))
+    got = dict((p[0], None) for p in passes)
     try:
-        gk = "gemm_fp4_persistent_kernel<1, 0, 0>"
-        got = {"gemm_fetch_kib": one_pass("FETCH_SIZE", "gemm_fwd", gk, 1.0),
-               "gemm_write_kib": one_pass("WRITE_SIZE", "gemm_fwd", gk, 1.0),
-               "copy_fetch_kib": one_pass("FETCH_SIZE", "copy", "copyBuffer", 1024.0),
-               "copy_write_kib": one_pass("WRITE_SIZE", "copy", "copyBuffer", 1024.0)}
+        for key, counter, op, kname, min_kib in passes:
+            got[key] = one_pass(counter, op, kname, min_kib)
+            if got[key] is None:
+                break
     except OSError as e:
         return None, "could not run rocprofv3: " + str(e)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    if any(v is None for v in got.values()):
-        return None, "a counter pass gave no result: " + ", ".join(
-            k for k, v in got.items() if v is None)
+    for key, counter, op, _, _ in passes:
+        if got[key] is None:
+            return None, "the %s pass of --profile-op %s gave no result" % (counter, op)
     copy_kib = 256.0 * 1024  # 64 Mi floats read and written
     fs, ws = copy_kib / got["copy_fetch_kib"], copy_kib / got["copy_write_kib"]
     if not (0.5 < fs < 4.0 and 0.5 < ws < 4.0):
