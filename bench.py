@@ -28,8 +28,9 @@ GEMM (the dominant kernel) against the dense FP4 MFMA peak, its launch time
 taken from HIP events that its own dispatch records inside the timed region
 (fp4q_set_next_launch; on the stream the kernels run on, created without a
 system-scope fence), and its HBM traffic from rocprofv3 counter passes this
-run starts as child processes after its timed region (or, failing those,
-from the committed counter record while the GEMM source matches it).  A
+run starts as child processes after everything else is measured (or,
+failing those, from the committed counter record while the GEMM source
+matches it).  A
 second pass, every launch plain, times each kernel by its own dispatch
 events for the per-kernel table.  The CPU baseline times the
 single-threaded oracle on a bounded sample.
@@ -488,19 +489,6 @@ def main():
                 "launch_us_min": round(float(np.min(fwd_us)), 2),
                 "launch_us_median": round(float(np.median(fwd_us)), 2),
                 "launch_us_p10": round(float(np.percentile(fwd_us, 10)), 2)}
-    if args.traffic == "live":
-        traffic, info = live_traffic()
-        if traffic is not None:
-            roofline["traffic"] = traffic
-            roofline["traffic_source"] = ("this run: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
-                                          "passes of the kernel, scaled by a 256 MiB copy")
-            roofline["traffic_counters"] = info
-        else:
-            roofline["traffic_live_error"] = info
-    if roofline["traffic"] is None and args.traffic != "off":
-        roofline["traffic"] = measured_traffic()
-        if roofline["traffic"] is not None:
-            roofline["traffic_source"] = "committed record " + os.path.relpath(TRAFFIC_FILE, HERE)
     q = per_op["quant_dy_dual_sr"]
     qr = per_op["quant_x_dual"]
     quant = {"quant_bf16_dual_rne_GBps": qr["GBps"], "quant_bf16_dual_rne_frac": qr["frac_hbm_peak"],
@@ -521,6 +509,21 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(f, b, step_flops, args.cpu_budget_s)
+
+    # the counter passes last: they leave the GPU idle for several seconds
+    if args.traffic == "live":
+        traffic, info = live_traffic()
+        if traffic is not None:
+            roofline["traffic"] = traffic
+            roofline["traffic_source"] = ("this run: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
+                                          "passes of the kernel, scaled by a 256 MiB copy")
+            roofline["traffic_counters"] = info
+        else:
+            roofline["traffic_live_error"] = info
+    if roofline["traffic"] is None and args.traffic != "off":
+        roofline["traffic"] = measured_traffic()
+        if roofline["traffic"] is not None:
+            roofline["traffic_source"] = "committed record " + os.path.relpath(TRAFFIC_FILE, HERE)
 
     out = {
         "metric": "MXFP4 quantize GB/s + FP4 GEMM TFLOPS (8192x5632x2048), % of roofline",
