@@ -37,6 +37,7 @@ namespace fp4q {
 
 static constexpr int kOccBins = 32768;
 static constexpr int kOccHistThreads = 1024;
+static constexpr int kOccScanLds = 8192;  // rows whose scan is staged in LDS (8 per thread)
 static constexpr int kOccThreads = 256;
 
 struct OccWs {
@@ -260,6 +261,34 @@ __global__ __launch_bounds__(1024) void occ_scan(const uint32_t* __restrict__ ro
     const int64_t per = (rows + 1023) / 1024;
     const int64_t r0 = (int64_t)threadIdx.x * per;
     uint64_t s = 0;
+    if (rows <= kOccScanLds) {
+        // up to 8192 rows: counts and pointers staged in LDS, so that the
+        // global loads and stores are coalesced (a thread's own run of
+        // consecutive rows, read and written directly, puts one address per
+        // lane 8 to 16 words apart into every instruction)
+        __shared__ uint32_t cnt[kOccScanLds];
+        __shared__ int64_t ptr[kOccScanLds];
+        for (int64_t i = threadIdx.x; i < rows; i += 1024) cnt[i] = row_cnt[i];
+        __syncthreads();
+        uint32_t c[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            c[i] = (i < per && r0 + i < rows) ? cnt[r0 + i] : 0u;
+            s += c[i];
+        }
+        uint64_t base = block_excl_scan64(s, wtot);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i < per && r0 + i < rows) {
+                ptr[r0 + i] = (int64_t)base;
+                base += c[i];
+            }
+        }
+        if (r0 < rows && r0 + per >= rows) row_ptr[rows] = (int64_t)base;  // the last owner
+        __syncthreads();
+        for (int64_t i = threadIdx.x; i < rows; i += 1024) row_ptr[i] = ptr[i];
+        return;
+    }
     if (per <= 16) {
         uint32_t c[16];
 #pragma unroll

@@ -43,7 +43,9 @@ def run_and_check(orc, xb, xd, q, rnd, seed=0, off=0):
 
 @pytest.mark.parametrize("rnd", ["rne", "sr"])
 @pytest.mark.parametrize("shape,q", [((1, 32), 0.99), ((37, 96), 0.99), ((130, 416), 0.9),
-                                     ((64, 2048), 0.99), ((300, 160), 0.5), ((50, 64), 1.0)])
+                                     ((64, 2048), 0.99), ((300, 160), 0.5), ((50, 64), 1.0),
+                                     # more rows than the row-count scan stages in LDS
+                                     ((8200, 32), 0.99)])
 def test_occ_quantize_parity(orc, shape, q, rnd):
     xb = inputs.to_bf16_bits(inputs.with_outliers(inputs.student_t(shape, shape[0] + 7), 11,
                                                   max(1, shape[0] * shape[1] // 150), 30.0))
