@@ -86,6 +86,24 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemm_fwd_traffic.json")
 KERNEL_SRC = os.path.join(HERE, "mxfp4_block_scaled_fp4q_amd", "csrc", "gemm_fp4.hip")
 
 
+def counter_median(files, kname, counter, min_value, min_dispatches=3):
+    """Median over dispatches of one counter in rocprofv3 CSV counter files
+    (`--output-format csv`): rows of kernels whose name contains kname are
+    summed per Dispatch_Id (a counter may come in several rows per
+    dispatch); dispatches below min_value (a kernel of the same name on a
+    tiny buffer) are left out; None with fewer than min_dispatches."""
+    import csv
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if kname in row["Kernel_Name"] and row["Counter_Name"] == counter:
+                    k = row["Dispatch_Id"]
+                    per[k] = per.get(k, 0.0) + float(row["Counter_Value"])
+    vals = [v for v in per.values() if v >= min_value]
+    return float(np.median(vals)) if len(vals) >= min_dispatches else None
+
+
 def live_traffic(budget_s=120.0, pass_s=60.0):
     """HBM bytes per forward-GEMM launch measured by this run: four rocprofv3
     counter passes, each a child process (this script with --profile-op, five
@@ -94,7 +112,6 @@ def live_traffic(budget_s=120.0, pass_s=60.0):
     128-byte read as 64 bytes).  A pass takes a few seconds; each is cut at
     pass_s and all four at budget_s, and the first pass without a result
     ends the measurement.  Returns (bytes, details) or (None, reason)."""
-    import csv
     import glob
     import shutil
     import signal
@@ -127,15 +144,8 @@ def live_traffic(budget_s=120.0, pass_s=60.0):
             return None
         # the profiler may exit non-zero after the program ended with its
         # results whole: the counter file decides
-        per = {}
-        for f in glob.glob(os.path.join(d, "**", "p_counter_collection.csv"), recursive=True):
-            with open(f) as fh:
-                for row in csv.DictReader(fh):
-                    if kname in row["Kernel_Name"] and row["Counter_Name"] == counter:
-                        k = row["Dispatch_Id"]
-                        per[k] = per.get(k, 0.0) + float(row["Counter_Value"])
-        vals = [v for v in per.values() if v >= min_kib]
-        return float(np.median(vals)) if len(vals) >= 3 else None
+        files = glob.glob(os.path.join(d, "**", "p_counter_collection.csv"), recursive=True)
+        return counter_median(files, kname, counter, min_kib)
 
     gk = "gemm_fp4_persistent_kernel<1, 0, 0>"
     passes = (("gemm_fetch_kib", "FETCH_SIZE", "gemm_fwd", gk, 1.0),
